@@ -1,0 +1,333 @@
+"""Plain fp64 CPU oracle of the compressed-attention hot path (one sequence at a time).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code
+with the GPU library and never imports it.
+
+Sources (cited by page and section):
+
+* [digest] V4 report digest, https://gitcode.csdn.net/69eb1ea054b52172bc6fc291.html
+  - section 三: CSA folds every m KV rows into one entry, a Lightning Indexer
+    scores the compressed entries and only the top-k of them take part in the
+    core attention (Flash m=4, k=512; Pro m=4, k=1024); HCA folds every m'=128
+    rows and attends densely, without top-k; both branches also see the newest
+    n_win=128 tokens uncompressed.
+  - section 七: the KV cache splits into a compressed ("classical") cache and a
+    state cache holding the sliding window and the tokens whose block has not
+    been folded yet.
+* [book] "Evolution map" chapter, https://igloomatics.github.io/DeepSeek-V4-book/chapters/ch01.html
+  - section 4: CSA turns each m=4 tokens into one super-KV and attends over the
+    top-k=1024 of them (4096 fine tokens); HCA folds m'=128 tokens, giving
+    n/m' = 8K dense entries at 1M context.
+* [summary] structured summary, https://www.10100.com/article/149217299
+  - section 2.1 / 2.2: the same constants (4:1, k=1024/512, window 128, 128:1).
+
+Readings where the pages are silent (each is fixed here and used by the GPU
+library in the same way):
+
+* Compressor: each compressor owns one logit per slot, z in R^m, shared by the
+  tensors it folds; weights alpha = softmax(z); entry j is
+  sum_s alpha_s * x[j*m + s].  Blocks do not overlap; a trailing partial block
+  is not emitted (its tokens are reached through the window).
+* Visibility: entry j (covering positions j*m .. j*m+m-1) is visible to the
+  query at position t iff its block ends at or before t, i.e. j < (t+1) // m.
+* Indexer score: I(t, j) = sum_h w[t,h] * ReLU(qI[t,h] . kI[j]) with one key
+  row per entry shared by all indexer heads; top-k is per query token and
+  shared by all attention heads; ties go to the lower entry index.
+* Attention: one KV head shared by all query heads; one softmax over the
+  multiset (selected entries) + (raw window rows max(0, t-W+1) .. t), with the
+  same scale for both kinds; a token may count once raw and once inside its
+  block's entry.  An empty set gives o = 0 and lse = -inf.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats
+
+
+# ----------------------------------------------------------------------------- compressor
+
+
+def compressor_weights(z) -> np.ndarray:
+    """Slot weights of one block compressor: softmax of its m logits, in fp64.
+
+    [digest] section 三 and [book] section 4 give the folding of m rows into one
+    entry; the weights are a softmax of learned per-slot logits (reading above).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - np.max(z))
+    return e / np.sum(e)
+
+
+def compress_exact(x, z, m: int, entry_begin: int = 0, entry_end: int | None = None,
+                   raw_base: int = 0) -> np.ndarray:
+    """Exact (fp64) block sums for entries [entry_begin, entry_end).
+
+    ``x`` holds raw rows for positions raw_base .. raw_base + len(x) - 1.
+    Entry j is sum_s alpha_s * x[position j*m + s]; every needed position must
+    be present.  [digest] section 三; [book] section 4.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    alpha = compressor_weights(z)
+    assert alpha.shape == (m,)
+    if entry_end is None:
+        entry_end = (raw_base + x.shape[0]) // m
+    n_ent = entry_end - entry_begin
+    if n_ent <= 0:
+        return np.zeros((0, x.shape[1]), dtype=np.float64)
+    lo = entry_begin * m - raw_base
+    hi = entry_end * m - raw_base
+    assert lo >= 0 and hi <= x.shape[0], "compressed blocks must lie inside the raw rows"
+    blocks = x[lo:hi].reshape(n_ent, m, x.shape[1])
+    return np.einsum("s,jsd->jd", alpha, blocks)
+
+
+def store(sums: np.ndarray, dtype: str):
+    """Round exact entries once to the storage type.
+
+    Returns a dict with ``values`` (float64 image of what is stored) and, for
+    e4m3, ``codes`` (uint8) and ``scale`` (float32 per entry).  e4m3 follows
+    ``formats.e4m3_quantize_rows``: the binary32 image of the exact sum is
+    quantised with a per-entry absmax/448 scale.
+    """
+    if dtype == "f32":
+        return {"values": formats.round_to_f32(sums)}
+    if dtype == "bf16":
+        return {"values": formats.round_to_bf16(sums)}
+    if dtype == "e4m3":
+        codes, scale, stored = formats.e4m3_quantize_rows(sums.astype(np.float32))
+        return {"values": stored, "codes": codes, "scale": scale}
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------- visibility
+
+
+def visible_entries(t: int, m: int, n_alloc: int | None = None) -> int:
+    """Number of compressed entries visible at position t: blocks ending at or before t."""
+    c = (t + 1) // m
+    return c if n_alloc is None else min(c, n_alloc)
+
+
+def window_positions(t: int, W: int) -> np.ndarray:
+    """Raw positions of the sliding window at t: the newest W tokens up to t ([digest] section 三)."""
+    return np.arange(max(0, t - W + 1), t + 1, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------- indexer
+
+
+def index_scores(q_idx, w, k_idx, t0: int, m: int) -> np.ndarray:
+    """Lightning-Indexer scores I[t, j] in fp64; invisible entries are -inf.
+
+    q_idx [T, H_I, d_I], w [T, H_I] (None means all ones), k_idx [N, d_I]
+    (decoded stored values).  Query i sits at position t0 + i.
+    I(t, j) = sum_h w[t,h] * max(0, q_idx[t,h] . k_idx[j]).
+    [digest] sections 三 and 七; [summary] section 2.1.
+    """
+    q_idx = np.asarray(q_idx, dtype=np.float64)
+    k_idx = np.asarray(k_idx, dtype=np.float64)
+    T, H_I, _ = q_idx.shape
+    N = k_idx.shape[0]
+    w = np.ones((T, H_I)) if w is None else np.asarray(w, dtype=np.float64)
+    out = np.full((T, N), -np.inf)
+    for i in range(T):
+        c = visible_entries(t0 + i, m, N)
+        if c == 0:
+            continue
+        dots = q_idx[i] @ k_idx[:c].T  # [H_I, c]
+        out[i, :c] = w[i] @ np.maximum(dots, 0.0)
+    return out
+
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Per query, the min(k, #visible) best visible entries; -1 pads the rest.
+
+    The decision is taken on the binary32 images of the scores (the precision
+    the GPU selects in), ordered by (score descending, index ascending).  The
+    output lists entries in that order.  [digest] section 三; [book] section 4.
+    """
+    T, N = scores.shape
+    out = np.full((T, k), -1, dtype=np.int64)
+    if k == 0:
+        return out
+    s32 = scores.astype(np.float32).astype(np.float64)
+    for i in range(T):
+        vis = np.nonzero(np.isfinite(scores[i]))[0]
+        if vis.size == 0:
+            continue
+        order = np.lexsort((vis, -s32[i, vis]))  # primary key: -score, then index
+        kk = min(k, vis.size)
+        out[i, :kk] = vis[order[:kk]]
+    return out
+
+
+def topk_is_valid(G, scores_row: np.ndarray, k: int, rel_band: float = 1e-5):
+    """Check one query's selected set against exact fp64 scores.
+
+    Valid iff |G| = kk = min(k, #visible), the members are distinct and
+    visible, every member scores >= s_k - beta and every visible non-member
+    scores <= s_k + beta, where s_k is the kk-th best exact score and
+    beta = rel_band * |s_k|.  Returns (ok, reason, n_in_band_swaps).
+    """
+    G = np.asarray(G, dtype=np.int64)
+    G = G[G >= 0]
+    vis = np.nonzero(np.isfinite(scores_row))[0]
+    kk = min(k, vis.size)
+    if G.size != kk:
+        return False, f"|G|={G.size} expected {kk}", 0
+    if np.unique(G).size != G.size:
+        return False, "duplicate members", 0
+    if kk == 0:
+        return True, "", 0
+    if not np.all(np.isfinite(scores_row[G])):
+        return False, "invisible member", 0
+    s_sorted = np.sort(scores_row[vis])[::-1]
+    s_k = s_sorted[kk - 1]
+    beta = rel_band * abs(s_k)
+    inG = np.zeros(scores_row.shape[0], dtype=bool)
+    inG[G] = True
+    if np.any(scores_row[G] < s_k - beta):
+        return False, "member below the k-th score band", 0
+    out_vis = vis[~inG[vis]]
+    if out_vis.size and np.any(scores_row[out_vis] > s_k + beta):
+        return False, "non-member above the k-th score band", 0
+    exact = set(vis[np.argsort(-scores_row[vis], kind="stable")[:kk]].tolist())
+    swaps = len(exact.symmetric_difference(set(G.tolist()))) // 2
+    return True, "", swaps
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def attend_entries(q_t, K_e, V_e, scale: float):
+    """Softmax attention of H query heads over an explicit entry list (one shared KV head).
+
+    q_t [H, d]; K_e, V_e [E, d] (E may be 0).  Returns (o [H, d], lse [H]).
+    """
+    q_t = np.asarray(q_t, dtype=np.float64)
+    H, d = q_t.shape
+    if K_e.shape[0] == 0:
+        return np.zeros((H, d)), np.full(H, -np.inf)
+    logits = scale * (q_t @ np.asarray(K_e, np.float64).T)  # [H, E]
+    mx = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - mx)
+    den = p.sum(axis=1, keepdims=True)
+    o = (p @ np.asarray(V_e, np.float64)) / den
+    lse = mx[:, 0] + np.log(den[:, 0])
+    return o, lse
+
+
+def _window_rows(t, W, k_raw, v_raw, raw_base):
+    pos = window_positions(t, W)
+    rows = pos - raw_base
+    assert rows.size == 0 or (rows[0] >= 0 and rows[-1] < k_raw.shape[0]), "window not covered by raw rows"
+    return k_raw[rows], v_raw[rows]
+
+
+def csa_attend(q, k_cmp, v_cmp, idx, k_raw, v_raw, raw_base: int, t0: int, W: int,
+               m: int, scale: float):
+    """CSA core attention: selected compressed entries plus the raw window, one softmax.
+
+    q [T, H, d]; k_cmp, v_cmp [N, d]; idx [T, k] (entries outside
+    0 <= j < visible_entries(t) are skipped, so -1 pads); k_raw, v_raw hold raw
+    rows for positions raw_base.. .  Returns (o [T, H, d], lse [T, H]).
+    [digest] section 三 (selected entries + uncompressed window); [book] section 4.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cmp = np.asarray(k_cmp, np.float64)
+    v_cmp = np.asarray(v_cmp, np.float64)
+    k_raw = np.asarray(k_raw, np.float64)
+    v_raw = np.asarray(v_raw, np.float64)
+    T, H, d = q.shape
+    o = np.zeros((T, H, d))
+    lse = np.full((T, H), -np.inf)
+    for i in range(T):
+        t = t0 + i
+        c = visible_entries(t, m, k_cmp.shape[0])
+        sel = np.asarray(idx[i], dtype=np.int64)
+        sel = sel[(sel >= 0) & (sel < c)]
+        kw, vw = _window_rows(t, W, k_raw, v_raw, raw_base)
+        K_e = np.concatenate([k_cmp[sel], kw], axis=0)
+        V_e = np.concatenate([v_cmp[sel], vw], axis=0)
+        o[i], lse[i] = attend_entries(q[i], K_e, V_e, scale)
+    return o, lse
+
+
+def hca_attend(q, k_cmp, v_cmp, m_heavy: int, k_raw, v_raw, raw_base: int, t0: int,
+               W: int, scale: float):
+    """HCA attention: every visible heavy entry plus the raw window, one softmax.
+
+    Entries j < min(N, (t+1) // m_heavy) are all attended (no top-k).
+    [digest] section 三; [book] section 4; [summary] section 2.2.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cmp = np.asarray(k_cmp, np.float64)
+    v_cmp = np.asarray(v_cmp, np.float64)
+    k_raw = np.asarray(k_raw, np.float64)
+    v_raw = np.asarray(v_raw, np.float64)
+    T, H, d = q.shape
+    o = np.zeros((T, H, d))
+    lse = np.full((T, H), -np.inf)
+    for i in range(T):
+        t = t0 + i
+        c = visible_entries(t, m_heavy, k_cmp.shape[0])
+        kw, vw = _window_rows(t, W, k_raw, v_raw, raw_base)
+        K_e = np.concatenate([k_cmp[:c], kw], axis=0)
+        V_e = np.concatenate([v_cmp[:c], vw], axis=0)
+        o[i], lse[i] = attend_entries(q[i], K_e, V_e, scale)
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine attention results over disjoint parts of one entry multiset.
+
+    Part s has normalised output o_s and log-normaliser lse_s (-inf when
+    empty).  With L = logsumexp_s(lse_s): o = sum_s exp(lse_s - L) * o_s and
+    lse = L.  All parts empty gives o = 0, lse = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)  # [S, ..., d]
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)  # [S, ...]
+    mx = np.max(lse_parts, axis=0)
+    safe = np.where(np.isfinite(mx), mx, 0.0)
+    wts = np.exp(lse_parts - safe)  # exp(-inf) = 0 for empty parts
+    den = np.sum(wts, axis=0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o = np.sum(wts[..., None] * o_parts, axis=0) / den[..., None]
+        lse = safe + np.log(den)
+    empty = ~np.isfinite(mx)
+    o = np.where(empty[..., None], 0.0, o)
+    lse = np.where(empty, -np.inf, lse)
+    return o, lse
+
+
+# ----------------------------------------------------------------------------- whole layers
+
+
+def csa_layer(q, k_raw, v_raw, q_idx, k_idx_raw, w, z, m: int, top_k: int, W: int,
+              scale: float, t0: int, cmp_dtype: str = "f32", idx_key_dtype: str = "f32"):
+    """One CSA layer for one sequence whose raw rows start at position 0.
+
+    Compress K, V and the indexer keys with the same compressor, score, select
+    top-k and attend.  Returns a dict with every intermediate.
+    """
+    n = k_raw.shape[0]
+    k_c = store(compress_exact(k_raw, z, m), cmp_dtype)
+    v_c = store(compress_exact(v_raw, z, m), cmp_dtype)
+    ki_c = store(compress_exact(k_idx_raw, z, m), idx_key_dtype)
+    scores = index_scores(q_idx, w, ki_c["values"], t0, m)
+    idx = select_topk(scores, top_k)
+    o, lse = csa_attend(q, k_c["values"], v_c["values"], idx, k_raw, v_raw, 0, t0, W, m, scale)
+    assert n >= t0 + q.shape[0]
+    return {"k_cmp": k_c, "v_cmp": v_c, "k_idx": ki_c, "scores": scores, "idx": idx,
+            "o": o, "lse": lse}
+
+
+def hca_layer(q, k_raw, v_raw, z, m_heavy: int, W: int, scale: float, t0: int,
+              cmp_dtype: str = "f32"):
+    """One HCA layer for one sequence whose raw rows start at position 0."""
+    k_c = store(compress_exact(k_raw, z, m_heavy), cmp_dtype)
+    v_c = store(compress_exact(v_raw, z, m_heavy), cmp_dtype)
+    o, lse = hca_attend(q, k_c["values"], v_c["values"], m_heavy, k_raw, v_raw, 0, t0, W, scale)
+    return {"k_cmp": k_c, "v_cmp": v_c, "o": o, "lse": lse}

@@ -1,0 +1,329 @@
+"""Pins of the oracle's method steps against closed forms, library routines and brute force.
+
+Each test is chosen so that a plausible mistake in ``oracle.method`` (a dropped
+term, a wrong sign or index, a transposed operand, an off-by-one block or
+visibility bound) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute, formats, method
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------- compressor
+
+
+def test_weights_are_softmax_and_shift_invariant():
+    z = rnd(0, 4)
+    a = method.compressor_weights(z)
+    assert abs(a.sum() - 1) < 1e-15 and np.all(a > 0)
+    np.testing.assert_allclose(method.compressor_weights(z + 3.7), a, rtol=1e-14)
+    # larger logit -> larger weight, slot order preserved
+    assert np.argmax(a) == np.argmax(z)
+
+
+def test_compress_m1_is_a_copy():
+    x = rnd(1, 37, 8)
+    np.testing.assert_array_equal(method.compress_exact(x, [0.3], 1), x)
+
+
+@pytest.mark.parametrize("m", [4, 128])
+def test_uniform_logits_give_mean_pooling(m):
+    x = np.random.default_rng(2).integers(-1000, 1000, (m * 5 + 3, 16)).astype(np.float64)
+    got = method.compress_exact(x, np.full(m, 0.25), m)
+    exp = x[: m * 5].reshape(5, m, 16).mean(axis=1)
+    np.testing.assert_array_equal(got, exp)  # 1/m is exact; integer sums are exact
+
+
+def test_dominant_logit_picks_its_slot():
+    x = rnd(3, 40, 4)
+    for s in range(4):
+        z = np.zeros(4)
+        z[s] = 800.0  # exp(-800) underflows: alpha is one-hot
+        np.testing.assert_array_equal(method.compress_exact(x, z, 4), x[s::4][:10])
+
+
+def test_compress_is_linear_and_drops_partial_block():
+    x, y = rnd(4, 23, 6), rnd(5, 23, 6)
+    z = rnd(6, 4)
+    cx, cy = method.compress_exact(x, z, 4), method.compress_exact(y, z, 4)
+    assert cx.shape == (5, 6)
+    np.testing.assert_allclose(method.compress_exact(2 * x - 3 * y, z, 4), 2 * cx - 3 * cy,
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_compress_subrange_with_raw_base_matches_full():
+    x = rnd(7, 64, 5)
+    z = rnd(8, 4)
+    full = method.compress_exact(x, z, 4)
+    part = method.compress_exact(x[20:], z, 4, entry_begin=5, entry_end=16, raw_base=20)
+    np.testing.assert_array_equal(part, full[5:16])
+
+
+def test_compress_matches_brute_force():
+    x = rnd(9, 61, 7)
+    z = rnd(10, 4) * 0.5
+    got = method.compress_exact(x, z, 4)
+    exp = np.array(brute.compress(x.tolist(), z.tolist(), 4))
+    np.testing.assert_allclose(got, exp, rtol=1e-14, atol=1e-15)
+
+
+def test_store_rounds_once():
+    s = rnd(11, 10, 64)
+    np.testing.assert_array_equal(method.store(s, "bf16")["values"], formats.round_to_bf16(s))
+    np.testing.assert_array_equal(method.store(s, "f32")["values"], s.astype(np.float32))
+    e = method.store(s, "e4m3")
+    np.testing.assert_array_equal(
+        e["values"], formats.e4m3_decode(e["codes"]) * e["scale"][:, None].astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- visibility
+
+
+def test_visibility_closed_form():
+    m = 4
+    assert method.visible_entries(m - 2, m) == 0
+    assert method.visible_entries(m - 1, m) == 1  # block 0 ends at position m-1
+    assert method.visible_entries(2 * m - 2, m) == 1
+    n = 1 << 20
+    assert method.visible_entries(n - 1, 4) == n // 4
+    assert method.visible_entries(n - 1, 128) == 8192  # n/m' = 8K at 1M context
+    assert method.visible_entries(n - 1, 4, n_alloc=1000) == 1000
+    np.testing.assert_array_equal(method.window_positions(5, 128), np.arange(6))
+    np.testing.assert_array_equal(method.window_positions(500, 128), np.arange(373, 501))
+    assert method.window_positions(10, 0).size == 0
+
+
+# ----------------------------------------------------------------------------- indexer
+
+
+def test_single_head_unit_weight_positive_dots_is_a_matrix_product():
+    rng = np.random.default_rng(12)
+    q = np.abs(rng.standard_normal((9, 1, 16)))
+    k = np.abs(rng.standard_normal((30, 16)))
+    s = method.index_scores(q, None, k, t0=119, m=4)  # position >= 119: all 30 visible
+    np.testing.assert_allclose(s, q[:, 0, :] @ k.T, rtol=1e-14)
+
+
+def test_scores_sign_scaling_and_zero_head():
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((5, 3, 8))
+    k = rng.standard_normal((20, 8))
+    w = rng.standard_normal((5, 3))
+    s = method.index_scores(q, w, k, 100, 4)
+    np.testing.assert_allclose(method.index_scores(q, 2.5 * w, k, 100, 4), 2.5 * s, rtol=1e-14)
+    np.testing.assert_allclose(method.index_scores(0.5 * q, w, k, 100, 4), 0.5 * s, rtol=1e-14)
+    # one head with w = -1: score = -ReLU(q.k)
+    s1 = method.index_scores(q[:, :1], -np.ones((5, 1)), k, 100, 4)
+    np.testing.assert_allclose(s1, -np.maximum(q[:, 0] @ k.T, 0), rtol=1e-14)
+    # a head with zero weight contributes nothing
+    w0 = w.copy()
+    w0[:, 2] = 0
+    np.testing.assert_allclose(method.index_scores(q, w0, k, 100, 4),
+                               method.index_scores(q[:, :2], w[:, :2], k, 100, 4), rtol=1e-14)
+
+
+def test_scores_visibility_mask():
+    q = rnd(14, 6, 2, 4)
+    k = rnd(15, 10, 4)
+    s = method.index_scores(q, None, k, t0=2, m=4)  # positions 2..7
+    for i in range(6):
+        c = (2 + i + 1) // 4
+        assert np.all(np.isfinite(s[i, :c])) and np.all(np.isneginf(s[i, c:]))
+
+
+def test_scores_match_brute_force():
+    q = rnd(16, 4, 3, 5)
+    k = rnd(17, 12, 5)
+    w = rnd(18, 4, 3)
+    s = method.index_scores(q, w, k, t0=47, m=4)  # (47+1)//4 = 12: all entries visible
+    for i in range(4):
+        for j in range(12):
+            assert math.isclose(s[i, j], brute.score(q[i].tolist(), w[i].tolist(), k[j].tolist()),
+                                rel_tol=1e-13, abs_tol=1e-14)
+
+
+# ----------------------------------------------------------------------------- top-k
+
+
+def test_topk_matches_torch_topk_on_distinct_scores():
+    s = rnd(19, 7, 300)
+    got = method.select_topk(s, 25)
+    exp = torch.topk(torch.from_numpy(s), 25, dim=1).indices.numpy()
+    for i in range(7):
+        assert set(got[i]) == set(exp[i])
+
+
+def test_topk_short_list_pads_and_ties_go_low():
+    s = np.full((2, 10), -np.inf)
+    s[0, :6] = [1.0, 3.0, 3.0, 2.0, 3.0, 0.5]
+    s[1, :3] = [0.0, 0.0, 0.0]
+    got = method.select_topk(s, 4)
+    assert list(got[0]) == [1, 2, 4, 3]  # three-way tie at 3.0 ordered by index
+    assert list(got[1]) == [0, 1, 2, -1]
+
+
+def test_topk_permutation_equivariance():
+    s = rnd(20, 3, 50)
+    perm = np.random.default_rng(21).permutation(50)
+    a = method.select_topk(s, 10)
+    b = method.select_topk(s[:, perm], 10)
+    for i in range(3):
+        assert set(perm[b[i]]) == set(a[i])
+
+
+def test_topk_validity_checker_accepts_oracle_and_rejects_planted_swap():
+    s = rnd(22, 1, 200)[0]
+    sel = method.select_topk(s[None], 20)[0]
+    ok, _, swaps = method.topk_is_valid(sel, s, 20)
+    assert ok and swaps == 0
+    order = np.argsort(-s)
+    bad = sel.copy()
+    bad[np.where(bad == order[19])[0][0]] = order[40]  # swap the 20th for the 41st
+    assert not method.topk_is_valid(bad, s, 20)[0]
+    assert not method.topk_is_valid(sel[:19], s, 20)[0]
+    dup = sel.copy()
+    dup[0] = dup[1]
+    assert not method.topk_is_valid(dup, s, 20)[0]
+    # members inside the tie band are accepted
+    s2 = s.copy()
+    s2[order[20]] = s2[order[19]] * (1 - 1e-7)
+    swapped = sel.copy()
+    swapped[np.where(swapped == order[19])[0][0]] = order[20]
+    ok, _, swaps = method.topk_is_valid(swapped, s2, 20)
+    assert ok and swaps == 1
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def _sdpa(q, K, V, scale, mask):
+    """torch CPU scaled_dot_product_attention in float64 with one shared KV head."""
+    T, H, d = q.shape
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]  # [1, H, T, d]
+    Kt = torch.from_numpy(K)[None, None].expand(1, H, *K.shape)
+    Vt = torch.from_numpy(V)[None, None].expand(1, H, *V.shape)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mask, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _layer(seed, n, T, t0, H, d, m, k, W, hi=2, di=8):
+    """Random layer inputs, binary32-representable (entries are stored as binary32)."""
+    rng = np.random.default_rng(seed)
+
+    def r(*shape):
+        return rng.standard_normal(shape).astype(np.float32).astype(np.float64)
+
+    return r(T, H, d), r(n, d), r(n, d), r(T, hi, di), r(n, di), r(T, hi), r(m) * 0.5
+
+
+def test_m1_all_selected_no_window_is_full_causal_attention():
+    n, H, d = 48, 3, 16
+    q, K, V, qi, ki, w, _ = _layer(30, n, n, 0, H, d, 1, n, 0)
+    res = method.csa_layer(q, K, V, qi, ki, w, [0.0], m=1, top_k=n, W=0, scale=0.25, t0=0)
+    mask = torch.ones(n, n, dtype=torch.bool).tril()
+    np.testing.assert_allclose(res["o"], _sdpa(q, K, V, 0.25, mask), rtol=1e-12, atol=1e-13)
+    logits = torch.from_numpy(0.25 * np.einsum("thd,sd->ths", q, K)).masked_fill(~mask[:, None, :], -np.inf)
+    np.testing.assert_allclose(res["lse"], torch.logsumexp(logits, dim=-1).numpy(), rtol=1e-13)
+
+
+def test_m1_all_selected_with_window_is_causal_attention_with_ln2_bias():
+    n, H, d, W = 40, 2, 8, 6
+    q, K, V, qi, ki, w, _ = _layer(31, n, n, 0, H, d, 1, n, W)
+    res = method.csa_layer(q, K, V, qi, ki, w, [0.0], m=1, top_k=n, W=W, scale=0.3, t0=0)
+    t = torch.arange(n)[:, None]
+    s = torch.arange(n)[None, :]
+    bias = torch.zeros(n, n, dtype=torch.float64)
+    bias[(s <= t) & (s > t - W)] = math.log(2.0)  # a window token counts twice
+    bias[s > t] = -math.inf
+    np.testing.assert_allclose(res["o"], _sdpa(q, K, V, 0.3, bias), rtol=1e-12, atol=1e-13)
+
+
+def test_csa_with_k_covering_all_entries_equals_hca_with_same_block():
+    n, T, t0, H, d, m, W = 64, 20, 44, 4, 8, 4, 5
+    q, K, V, qi, ki, w, z = _layer(32, n, T, t0, H, d, m, 1000, W)
+    c = method.csa_layer(q, K, V, qi, ki, w, z, m=m, top_k=1000, W=W, scale=0.35, t0=t0)
+    h = method.hca_layer(q, K, V, z, m_heavy=m, W=W, scale=0.35, t0=t0)
+    np.testing.assert_allclose(c["o"], h["o"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(c["lse"], h["lse"], rtol=1e-13)
+
+
+def test_no_visible_entry_is_sliding_window_attention():
+    n, T, H, d, W = 30, 30, 2, 8, 7
+    q, K, V, qi, ki, w, z = _layer(33, n, T, 0, H, d, 4, 5, W)
+    res = method.csa_layer(q, K, V, qi, ki, w, z, m=4, top_k=0, W=W, scale=0.4, t0=0)
+    t = torch.arange(n)[:, None]
+    s = torch.arange(n)[None, :]
+    band = (s <= t) & (s > t - W)
+    np.testing.assert_allclose(res["o"], _sdpa(q, K, V, 0.4, band), rtol=1e-12, atol=1e-13)
+    # HCA with blocks longer than the sequence sees only the window too
+    h = method.hca_layer(q, K, V, rnd(34, 64), m_heavy=64, W=W, scale=0.4, t0=0)
+    np.testing.assert_allclose(h["o"], res["o"], rtol=1e-12, atol=1e-13)
+
+
+def test_constant_values_give_constant_output_and_empty_set_gives_zero():
+    n, T, H, d = 24, 24, 2, 4
+    q, K, _, qi, ki, w, z = _layer(35, n, T, 0, H, d, 4, 3, 0)
+    V = np.full((n, d), 1.75)
+    res = method.csa_layer(q, K, V, qi, ki, w, z, m=4, top_k=3, W=0, scale=0.5, t0=0)
+    # positions 0..2 see nothing (no window, no complete block)
+    np.testing.assert_array_equal(res["o"][:3], 0.0)
+    assert np.all(np.isneginf(res["lse"][:3]))
+    np.testing.assert_allclose(res["o"][3:], 1.75, rtol=1e-14)
+
+
+def test_attention_skips_invalid_and_invisible_indices():
+    n, H, d, W, m = 40, 2, 8, 3, 4
+    q, K, V, *_ = _layer(36, n, 1, 0, H, d, m, 0, W)
+    kc, vc = K[:10], V[:10]
+    t0 = 19  # 5 visible entries
+    a = method.csa_attend(q, kc, vc, np.array([[2, -1, 7, 4, 9]]), K, V, 0, t0, W, m, 0.3)
+    b = method.csa_attend(q, kc, vc, np.array([[2, 4]]), K, V, 0, t0, W, m, 0.3)
+    np.testing.assert_array_equal(a[0], b[0])
+
+
+def test_attention_matches_brute_force():
+    n, T, t0, H, d, m, W, k = 44, 6, 38, 3, 5, 4, 4, 3
+    q, K, V, qi, ki, w, z = _layer(37, n, T, t0, H, d, m, k, W)
+    res = method.csa_layer(q, K, V, qi, ki, w, z, m=m, top_k=k, W=W, scale=0.45, t0=t0)
+    kc = res["k_cmp"]["values"].tolist()
+    vc = res["v_cmp"]["values"].tolist()
+    for i in range(T):
+        bo, bl = brute.csa_query(t0 + i, q[i].tolist(), kc, vc, res["idx"][i].tolist(),
+                                 K.tolist(), V.tolist(), W, m, 0.45)
+        np.testing.assert_allclose(res["o"][i], bo, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(res["lse"][i], bl, rtol=1e-13)
+        # the selected set is the brute-force top-k over visible entries
+        c = (t0 + i + 1) // m
+        sc = [(j, brute.score(qi[i].tolist(), w[i].tolist(), res["k_idx"]["values"][j].tolist()))
+              for j in range(c)]
+        assert set(brute.topk(sc, k)) == set(j for j in res["idx"][i] if j >= 0)
+    z8 = rnd(39, 8) * 0.5
+    h = method.hca_layer(q, K, V, z8, m_heavy=8, W=W, scale=0.45, t0=t0)
+    hk = method.store(method.compress_exact(K, z8, 8), "f32")["values"].tolist()
+    hv = method.store(method.compress_exact(V, z8, 8), "f32")["values"].tolist()
+    for i in range(T):
+        bo, bl = brute.hca_query(t0 + i, q[i].tolist(), hk, hv, 8, K.tolist(), V.tolist(), W, 0.45)
+        np.testing.assert_allclose(h["o"][i], bo, rtol=1e-12, atol=1e-13)
+
+
+def test_merge_of_parts_equals_whole():
+    rng = np.random.default_rng(38)
+    q = rng.standard_normal((4, 8))
+    K = rng.standard_normal((50, 8))
+    V = rng.standard_normal((50, 8))
+    o, lse = method.attend_entries(q, K, V, 0.3)
+    cuts = [0, 7, 7, 30, 50]  # includes an empty part
+    parts = [method.attend_entries(q, K[a:b], V[a:b], 0.3) for a, b in zip(cuts[:-1], cuts[1:])]
+    mo, ml = method.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    np.testing.assert_allclose(mo, o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(ml, lse, rtol=1e-14)
+    eo, el = method.merge_partials(np.zeros((2, 4, 8)), np.full((2, 4), -np.inf))
+    assert np.all(eo == 0) and np.all(np.isneginf(el))
