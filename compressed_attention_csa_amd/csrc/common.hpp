@@ -1,0 +1,137 @@
+// Device-side helpers shared by the gfx950 kernels of libcsa.
+//
+// Number formats: bf16 is kept as raw uint16 bits (upper half of a binary32);
+// fp8 is the OCP e4m3fn byte format.  Every conversion here is exact or
+// round-to-nearest-even, so that stored values are reproducible bit for bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef uint16_t bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float u32_as_f32(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f32_as_u32(float f) { return __float_as_uint(f); }
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return u32_as_f32(uint32_t(h) << 16); }
+
+// Round a binary32 to bf16, nearest-even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = f32_as_u32(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+// Round a binary64 to bf16 with a single nearest-even rounding.  The value is
+// first narrowed to binary32 with round-to-odd (truncate, then set the last bit
+// if anything was dropped): binary32 keeps 16 more bits than bf16 in every
+// range, so the second, nearest-even, rounding then equals one direct rounding.
+__device__ __forceinline__ bf16_t f64_to_bf16(double x) {
+  float f = float(x);  // nearest-even
+  double back = double(f);
+  if (back != x && x == x) {
+    uint32_t u = f32_as_u32(f);
+    if (fabs(back) > fabs(x)) u -= 1u;  // rounded away from zero: step back (truncation)
+    u |= 1u;                            // sticky bit
+    f = u32_as_f32(u);
+  }
+  return f32_to_bf16(f);
+}
+
+// ---------------------------------------------------------------- fp8 e4m3fn
+
+// Encode a binary32 as e4m3fn, nearest-even.  Magnitudes up to 464 round to at
+// most 448 (464 ties to the even code 448); larger magnitudes and NaN give NaN.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+  uint32_t u = f32_as_u32(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(v);
+  if (!(a == a)) return uint8_t(sign | 0x7fu);
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9 (m = 8 is the first normal)
+    code = uint32_t(rintf(a * 512.0f));
+  } else {
+    uint32_t ua = f32_as_u32(a);
+    uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) & 0xfff00000u;  // keep 3 mantissa bits
+    int e = int(r >> 23) - 127;
+    uint32_t mant = (r >> 20) & 7u;
+    if (e > 8 || (e == 8 && mant == 7u)) return uint8_t(sign | 0x7fu);
+    code = (uint32_t(e + 7) << 3) | mant;
+  }
+  return uint8_t(sign | code);
+}
+
+// Decode four e4m3fn bytes (packed little-endian in a uint32) into bf16 bit
+// patterns (exact: every e4m3 value is a bf16 value).  Uses the gfx950 packed
+// fp8 -> fp32 converter, whose OCP e4m3fn decoding is exact.
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t packed, uint32_t& lo, uint32_t& hi) {
+  f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(int(packed), false);
+  f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(int(packed), true);
+  lo = (f32_as_u32(a[0]) >> 16) | (f32_as_u32(a[1]) & 0xffff0000u);
+  hi = (f32_as_u32(b[0]) >> 16) | (f32_as_u32(b[1]) & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------- ordering keys
+
+// Order-preserving image of a binary32 score: a > b  <=>  key(a) > key(b).
+// -0 is folded onto +0 first so that equal scores get equal keys.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = f32_as_u32(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return u32_as_f32(u);
+}
+// Total order used by the selection: higher score first, then lower index.
+__device__ __forceinline__ uint64_t rank_key(uint32_t key, uint32_t idx) {
+  return (uint64_t(key) << 32) | uint64_t(0xffffffffu - idx);
+}
+__device__ __forceinline__ uint32_t rank_key_idx(uint64_t rk) {
+  return 0xffffffffu - uint32_t(rk & 0xffffffffu);
+}
+
+// ---------------------------------------------------------------- MFMA
+
+// D = A(16x32) * B(32x16) + C.  Lane l holds A row l%16 / B column l%16, k-slots
+// 8*(l/16) .. 8*(l/16)+7; C/D lane l holds column l%16, rows 4*(l/16) .. +3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T as(const void* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+
+__device__ __forceinline__ bf16x8_t u32x4_as_bf16x8(uint4 v) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace csa

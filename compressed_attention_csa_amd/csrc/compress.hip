@@ -1,0 +1,160 @@
+// Block KV compressor (CSA m = 4, HCA m' = 128) for gfx950.
+//
+// Entry j of a sequence is sum_s alpha_s * x[j*m + s] with alpha = softmax of the
+// compressor's per-slot logits (V4 report digest, section 三; "Evolution map",
+// section 4).  The m rows of one block are contiguous in memory, so each
+// thread streams the same 8-column slice of the m rows of one entry with
+// 16-byte (bf16) or 32-byte (fp32) loads: consecutive threads read consecutive
+// 16 B of a row, a wave covers whole rows, and every byte is read once.
+// Sums are accumulated in fp64 and rounded once to the output type.
+#include "common.hpp"
+#include "kernels.h"
+
+namespace csa {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename TIn>
+struct Row8;  // 8 consecutive elements converted to double
+
+template <>
+struct Row8<float> {
+  static __device__ __forceinline__ void load(const float* p, double (&v)[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+template <>
+struct Row8<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, double (&v)[8]) {
+    uint4 a = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = u32_as_f32(w[i] << 16);
+      v[2 * i + 1] = u32_as_f32(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+// OUT: 0 = fp32, 1 = bf16, 2 = e4m3 + per-entry fp32 scale.
+template <typename TIn, int OUT>
+__global__ __launch_bounds__(kThreads) void compress_kernel(
+    const TIn* __restrict__ x, int64_t n_raw, int d, int64_t raw_base,
+    const float* __restrict__ logits, int m, int64_t entry_begin, int64_t n_ent, int64_t N_alloc,
+    void* __restrict__ out, float* __restrict__ out_scale) {
+  __shared__ double alpha[128];
+  __shared__ float zmax_s;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+
+  // Slot weights: softmax of the logits, in fp64.
+  if (tid < kWave) {
+    float v = -INFINITY;
+    for (int s = tid; s < m; s += kWave) v = fmaxf(v, logits[s]);
+    v = wave_max(v);
+    if (tid == 0) zmax_s = v;
+  }
+  __syncthreads();
+  for (int s = tid; s < m; s += kThreads) alpha[s] = exp(double(logits[s]) - double(zmax_s));
+  __syncthreads();
+  double total = 0.0;
+  for (int s = 0; s < m; ++s) total += alpha[s];
+  __syncthreads();
+  for (int s = tid; s < m; s += kThreads) alpha[s] = alpha[s] / total;
+  __syncthreads();
+
+  const int tpe = d >> 3;  // threads per entry, 8 columns each
+  const int epb = kThreads / tpe;
+  const int64_t e_local = int64_t(blockIdx.x) * epb + tid / tpe;
+  const int seg = tid % tpe;
+  const bool valid = tid < epb * tpe && e_local < n_ent;
+  const int64_t j = entry_begin + e_local;
+
+  double acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  if (valid) {
+    const TIn* src = x + (int64_t(b) * n_raw + (j * m - raw_base)) * d + seg * 8;
+#pragma unroll 8
+    for (int s = 0; s < m; ++s) {
+      double v[8];
+      Row8<TIn>::load(src + int64_t(s) * d, v);
+      const double a = alpha[s];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fma(a, v[i], acc[i]);
+    }
+  }
+
+  const int64_t orow = int64_t(b) * N_alloc + j;
+  if (OUT == 0) {
+    if (valid) {
+      float* o = reinterpret_cast<float*>(out) + orow * d + seg * 8;
+      *reinterpret_cast<float4*>(o) = make_float4(float(acc[0]), float(acc[1]), float(acc[2]), float(acc[3]));
+      *reinterpret_cast<float4*>(o + 4) = make_float4(float(acc[4]), float(acc[5]), float(acc[6]), float(acc[7]));
+    }
+  } else if (OUT == 1) {
+    if (valid) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = uint32_t(f64_to_bf16(acc[2 * i])) | (uint32_t(f64_to_bf16(acc[2 * i + 1])) << 16);
+      bf16_t* o = reinterpret_cast<bf16_t*>(out) + orow * d + seg * 8;
+      *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    // e4m3: binary32 image of the sum, per-entry absmax / 448 scale.
+    float r[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      r[i] = float(acc[i]);
+      amax = fmaxf(amax, fabsf(r[i]));
+    }
+    for (int o = tpe >> 1; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    float scale = amax / 448.0f;
+    if (amax == 0.0f) scale = 1.0f;
+    if (valid) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= uint32_t(f32_to_e4m3(r[i] / scale)) << (8 * i);
+        hi |= uint32_t(f32_to_e4m3(r[i + 4] / scale)) << (8 * i);
+      }
+      uint8_t* o = reinterpret_cast<uint8_t*>(out) + orow * d + seg * 8;
+      *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+      if (seg == 0) out_scale[orow] = scale;
+    }
+  }
+}
+
+template <typename TIn, int OUT>
+hipError_t launch(const CompressArgs& a) {
+  const int tpe = a.d / 8;
+  const int epb = kThreads / tpe;
+  const int64_t n_ent = a.entry_end - a.entry_begin;
+  dim3 grid(unsigned((n_ent + epb - 1) / epb), unsigned(a.B));
+  hipLaunchKernelGGL((compress_kernel<TIn, OUT>), grid, dim3(kThreads), 0, a.stream,
+                     reinterpret_cast<const TIn*>(a.x), a.n_raw, a.d, a.raw_base, a.logits, a.m,
+                     a.entry_begin, n_ent, a.N_alloc, a.out, a.out_scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs& a) {
+  if (a.entry_end <= a.entry_begin) return hipSuccess;
+  if (a.x_bf16) {
+    if (a.out_kind == 0) return launch<bf16_t, 0>(a);
+    if (a.out_kind == 1) return launch<bf16_t, 1>(a);
+    return launch<bf16_t, 2>(a);
+  }
+  if (a.out_kind == 0) return launch<float, 0>(a);
+  if (a.out_kind == 1) return launch<float, 1>(a);
+  return launch<float, 2>(a);
+}
+
+}  // namespace csa

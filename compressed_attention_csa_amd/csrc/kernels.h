@@ -1,0 +1,119 @@
+// Internal interface between the validated C ABI (api.cpp) and the gfx950 kernels.
+// Argument structs carry already-validated values; launchers only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct CompressArgs {
+  const void* x;
+  bool x_bf16;
+  int B;
+  int64_t n_raw;
+  int d;
+  int64_t raw_base;
+  const float* logits;
+  int m;
+  int64_t entry_begin, entry_end, N_alloc;
+  void* out;
+  int out_kind;  // 0 fp32, 1 bf16, 2 e4m3 + scale
+  float* out_scale;
+  hipStream_t stream;
+};
+hipError_t launch_compress(const CompressArgs& a);
+
+// ------------------------------------------------------------------ indexer + top-k
+
+enum KeyKind { kKeyF32 = 0, kKeyBF16 = 1, kKeyE4M3 = 2 };
+
+struct IndexArgs {
+  const void* q_idx;  // [B, T, H_I, d_I]
+  const float* w;     // [B, T, H_I] or null
+  const void* k_idx;  // [B, N_alloc, d_I]
+  const float* k_scale;
+  int key_kind;
+  int B;
+  int64_t T;
+  int H_I, d_I;
+  int64_t N_alloc, t0;
+  int m, top_k;
+  int32_t* out_idx;
+  float* out_score;
+  void* ws;
+  hipStream_t stream;
+};
+
+// Workspace layout shared by every call.  The first kHeaderBytes hold control
+// words only (arrival counters, row histograms) at fixed offsets that do not
+// depend on the call's shape; every call returns them to zero.  Data regions
+// (keys, staging, partial results) start after the header and are always
+// written before they are read, so any sequence of calls of any shapes may
+// share one workspace that was zero-filled once.
+constexpr size_t kHeaderBytes = size_t(2) << 20;
+constexpr size_t kAttendCtrlOff = 0;          // 256 rows x 16 B
+constexpr int64_t kAttendCtrlRows = 256;
+constexpr size_t kIndexCtrlOff = 8192;        // 64 rows x 16 B
+constexpr size_t kIndexHistOff = 16384;       // 64 rows x 16 KB
+constexpr int64_t kIndexChunkRows = 64;       // rows per multi-slice launch
+
+// Slicing plan of the general (rows x slices) indexer path; shared by the
+// workspace-size query and the launcher so both agree.
+struct IndexPlan {
+  int64_t rows;        // B * T
+  int64_t c_max;       // largest visible-entry count over the rows
+  int64_t slice;       // entries per slice (multiple of 256, <= kMaxSlice)
+  int64_t slices;      // slices of the longest row
+  int64_t chunk_rows;  // rows per launch pair when rows have several slices
+  size_t ws_bytes;     // workspace bytes
+  // data offsets (after the header); indexed by the row's position in its chunk
+  size_t off_keys, off_stage_a, off_stage_b, off_counts;
+};
+constexpr int64_t kMaxSlice = 4096;
+constexpr int kHistBins = 4096;  // top 12 bits of the score key
+IndexPlan plan_index(int B, int64_t T, int64_t N_alloc, int top_k);
+hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p);
+
+// ------------------------------------------------------------------ attention
+
+struct AttendArgs {
+  bool hca;        // dense over heavy entries (no idx)
+  bool bf16;       // q / K / V dtype (else fp32)
+  const void* q;   // [B, T, H, d]
+  const void* k_cmp;
+  const void* v_cmp;  // [B, N_alloc, d]
+  int64_t N_alloc;
+  int m;  // block size for visibility (CSA m or HCA m_heavy)
+  const int32_t* idx;
+  int top_k;
+  const void* k_raw;
+  const void* v_raw;  // [B, n_raw, d]
+  int64_t raw_base, n_raw;
+  int B;
+  int64_t T;
+  int H, d;
+  int64_t t0;
+  int window;
+  float scale;
+  void* out;
+  bool out_bf16;
+  float* lse;
+  void* ws;
+  hipStream_t stream;
+};
+
+struct AttendPlan {
+  int64_t rows;      // B * T
+  int64_t slots;     // longest slot list (entries + window)
+  int64_t per_split; // slots per split (multiple of the tile)
+  int64_t splits;    // splits of the longest row
+  size_t ws_bytes;
+  size_t off_part, off_ml;  // data offsets (after the header)
+};
+// max_entries: top_k for CSA, N_alloc for HCA.
+AttendPlan plan_attend(bool hca, int B, int64_t T, int H, int d, int64_t max_entries, int window);
+hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p);
+
+}  // namespace csa

@@ -1,0 +1,199 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) compressed-attention library (libcsa.so).
+ *
+ * The library computes the attention hot path of a CSA/HCA hybrid-attention
+ * transformer layer:
+ *
+ *   csa_compress    block KV compressor (CSA block m = 4, HCA block m' = 128)
+ *   csa_index_topk  Lightning-Indexer scores of compressed entries + per-query top-k
+ *   csa_attend      attention over the selected compressed entries and the raw
+ *                   sliding window, under one softmax
+ *   hca_attend      dense attention over every visible heavy entry and the window
+ *
+ * Method sources (pages on the web, cited by section):
+ *   [digest]  V4 report digest, https://gitcode.csdn.net/69eb1ea054b52172bc6fc291.html
+ *             section 三 (CSA / HCA / window), section 七 (low-precision indexer QK
+ *             path, compressed cache vs. state cache)
+ *   [book]    "Evolution map", https://igloomatics.github.io/DeepSeek-V4-book/chapters/ch01.html
+ *             section 4 (m = 4 super-KV, top-k = 1024, m' = 128, n/m' dense entries)
+ *   [summary] https://www.10100.com/article/149217299 sections 2.1, 2.2, 五
+ *
+ * Conventions for every call
+ *   - Tensor arguments are DEVICE pointers to row-major arrays whose innermost
+ *     dimension is contiguous, with the shapes given below; base addresses must
+ *     be 16-byte aligned.  Sizes are element counts.
+ *   - B sequences in a call share the context length and query positions.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL means the null
+ *     stream) and is asynchronous: a call never synchronises and never allocates
+ *     device memory.  The caller owns every buffer.
+ *   - Every argument is validated before any HIP call; a non-OK status means
+ *     nothing was enqueued.  csa_last_error() then returns a thread-local
+ *     description.  CSA_E_HIP reports a failed launch (with the HIP error text).
+ *   - Workspaces: the *_workspace() functions return the bytes a call needs for
+ *     the given shape (0: none needed, NULL allowed).  A workspace must be
+ *     zero-filled before its first use with this library.  Its first 2 MiB hold
+ *     control words (arrival counters, histograms) at offsets that do not depend
+ *     on the shape, and every call returns them to zero when its last kernel
+ *     finishes; the rest is scratch that a call writes before it reads.  One
+ *     zero fill at allocation therefore serves any sequence of calls, of any
+ *     function and shape, that share the workspace, provided the calls are
+ *     ordered (same stream, or synchronised); concurrent calls on one
+ *     workspace race.
+ *   - Numerics: compressor sums are accumulated in fp64 and rounded once to the
+ *     output type; dot products accumulate in fp32 (bf16 x bf16 products are
+ *     exact in fp32); softmax statistics are fp32; the softmax weights enter the
+ *     value product as a bf16 hi + lo pair (about 16 significant bits).
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+  CSA_F32 = 0,      /* IEEE binary32 */
+  CSA_BF16 = 1,     /* bfloat16 (upper half of a binary32) */
+  CSA_FP8_E4M3 = 2  /* OCP fp8 e4m3fn, one byte per value, with a per-row fp32 scale */
+} csa_dtype_t;
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_E_NULL = 1,        /* a required pointer is NULL */
+  CSA_E_SHAPE = 2,       /* a size is out of range or inconsistent */
+  CSA_E_DTYPE = 3,       /* unsupported dtype or dtype combination */
+  CSA_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  CSA_E_WORKSPACE = 5,   /* workspace NULL or smaller than *_workspace() */
+  CSA_E_UNSUPPORTED = 6, /* valid request this build does not implement */
+  CSA_E_HIP = 7          /* a HIP runtime call failed */
+} csa_status_t;
+
+typedef void* csa_stream_t; /* hipStream_t */
+
+/* Version of this header's ABI (CSA_ABI_VERSION of the built library). */
+int csa_abi_version(void);
+/* Static name of a status code. */
+const char* csa_status_string(int status);
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* csa_last_error(void);
+
+/*
+ * csa_compress -- fold every m consecutive raw rows into one compressed entry.
+ *
+ * [digest] 三 and [book] 4: CSA folds each block of m = 4 tokens into one
+ * entry, HCA each block of m' = 128.  Here entry j of a sequence is
+ *     out[b, j, :] = sum_{s<m} alpha_s * x[position j*m + s, :],
+ *     alpha = softmax(logits)      (one learned logit per slot)
+ * over non-overlapping blocks; a trailing partial block is never emitted.
+ *
+ *   x          [B, n_raw, d] of x_dt (CSA_F32 | CSA_BF16): raw rows for the
+ *              positions raw_base .. raw_base + n_raw - 1.
+ *   logits     [m] fp32, device.  1 <= m <= 128.
+ *   entries    [entry_begin, entry_end) of each sequence are written; every
+ *              covered position must lie inside x:
+ *              raw_base <= entry_begin*m and entry_end*m <= raw_base + n_raw,
+ *              0 <= entry_begin <= entry_end <= N_alloc.
+ *   out        [B, N_alloc, d] of out_dt: CSA_F32 | CSA_BF16 (sum rounded once,
+ *              nearest-even), or CSA_FP8_E4M3 (bytes) with out_scale.
+ *   out_scale  [B, N_alloc] fp32, required iff out_dt == CSA_FP8_E4M3, else
+ *              must be NULL.  The fp32 image r of the sum is stored as
+ *              scale = f32(max_i |r_i| / 448) (1 for an all-zero row) and
+ *              code_i = e4m3(f32(r_i / scale)), nearest-even.
+ *   d          8 <= d <= 512, d % 8 == 0 (a power of two >= 16 for CSA_FP8_E4M3).
+ * An empty entry range is a no-op.  No workspace.
+ */
+csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw, int d,
+                          int64_t raw_base, const float* logits, int m, int64_t entry_begin,
+                          int64_t entry_end, int64_t N_alloc, void* out, csa_dtype_t out_dt,
+                          float* out_scale, csa_stream_t stream);
+
+/*
+ * csa_index_topk -- Lightning-Indexer scores and per-query top-k selection.
+ *
+ * [digest] 三: an indexer scores the compressed entries and only the top-k take
+ * part in the core attention; [digest] 七: its cached keys are kept in low
+ * precision.  Query i of every sequence sits at position t = t0 + i and sees
+ * the entries whose block ends at or before t:  j < c(t) = min(N_alloc, (t+1)/m).
+ * Its score of entry j is
+ *     I(t, j) = sum_{h<H_I} w[b,i,h] * max(0, q_idx[b,i,h,:] . k_idx[b,j,:])
+ * computed in fp32, and the selected set is the min(top_k, c(t)) entries with
+ * the highest I (ties to the lower j), shared by all attention heads.
+ *
+ *   q_idx     [B, T, H_I, d_I] of q_dt
+ *   w         [B, T, H_I] fp32, or NULL for all ones
+ *   k_idx     [B, N_alloc, d_I] of k_dt; CSA_FP8_E4M3 keys need k_scale
+ *             [B, N_alloc] fp32 (the key row is code * scale), else k_scale NULL.
+ *   dtypes    (q_dt, k_dt) = (CSA_F32, CSA_F32), (CSA_BF16, CSA_BF16) or
+ *             (CSA_BF16, CSA_FP8_E4M3).
+ *   out_idx   [B, T, top_k] int32: the selected entries in no particular order,
+ *             then -1 in unused slots.
+ *   out_score [B, T, top_k] fp32 or NULL: the fp32 score of each listed entry
+ *             (-inf in unused slots).
+ *   limits    1 <= H_I <= 16, d_I in {32, 64}, 1 <= top_k <= 2048, m >= 1,
+ *             T >= 0, t0 >= 0, N_alloc >= 0, B >= 1.
+ */
+size_t csa_index_topk_workspace(int B, int64_t T, int H_I, int d_I, int64_t N_alloc, int top_k,
+                                csa_dtype_t k_dt);
+csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w, const void* k_idx,
+                            csa_dtype_t k_dt, const float* k_scale, int B, int64_t T, int H_I,
+                            int d_I, int64_t N_alloc, int64_t t0, int m, int top_k,
+                            int32_t* out_idx, float* out_score, void* workspace,
+                            size_t workspace_bytes, csa_stream_t stream);
+
+/*
+ * csa_attend -- CSA core attention: selected compressed entries + raw window.
+ *
+ * [digest] 三: attention runs over the top-k compressed entries, and the newest
+ * window tokens are added uncompressed.  For query i at t = t0 + i and head h,
+ * over the multiset E(t) = {k_cmp/v_cmp rows idx[b,i,:] with 0 <= j < c(t)}
+ * plus {k_raw/v_raw rows of positions max(0, t-window+1) .. t}:
+ *     o[b,i,h,:] = sum_e softmax_e(scale * q[b,i,h,:] . K_e) * V_e
+ *     lse[b,i,h] = ln sum_e exp(scale * q . K_e)
+ * one softmax over both kinds of entry; an empty E gives o = 0, lse = -inf.
+ * Listed indices that are negative, >= N_alloc or not yet visible
+ * (j >= (t+1)/m) are skipped; a repeated index counts once per listing.
+ *
+ *   q        [B, T, H, d] of dt;  k_cmp, v_cmp [B, N_alloc, d] of dt
+ *   idx      [B, T, top_k] int32 (top_k may be 0: window only)
+ *   k_raw, v_raw [B, n_raw, d] of dt for positions raw_base ..; every window
+ *            position of every query must be inside (else CSA_E_SHAPE).
+ *   v may alias k (models with K = V).
+ *   out      [B, T, H, d] of out_dt (CSA_F32 | CSA_BF16);  lse [B, T, H] fp32 or NULL
+ *   dtypes   dt = CSA_BF16: d in {64, 128}, H % 16 == 0, H <= 128;
+ *            dt = CSA_F32:  d in {32, 64, 128}, 1 <= H <= 32.
+ *   limits   0 <= window <= 1024, 0 <= top_k <= 2048, m >= 1.
+ */
+size_t csa_attend_workspace(int B, int64_t T, int H, int d, int top_k, int window);
+csa_status_t csa_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
+                        int64_t N_alloc, int m, const int32_t* idx, int top_k, const void* k_raw,
+                        const void* v_raw, int64_t raw_base, int64_t n_raw, int B, int64_t T,
+                        int H, int d, int64_t t0, int window, float scale, void* out,
+                        csa_dtype_t out_dt, float* lse, void* workspace, size_t workspace_bytes,
+                        csa_stream_t stream);
+
+/*
+ * hca_attend -- HCA attention: every visible heavy entry + raw window, one softmax.
+ *
+ * [digest] 三 and [book] 4: HCA folds every m' tokens and attends densely to all
+ * n/m' heavy entries (no top-k), plus the window.  E(t) = {heavy entries
+ * j < min(N_alloc, (t+1)/m_heavy)} plus the raw window; the formulas, layouts,
+ * dtypes and limits are those of csa_attend.
+ */
+size_t hca_attend_workspace(int B, int64_t T, int H, int d, int64_t N_alloc, int m_heavy,
+                            int window);
+csa_status_t hca_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
+                        int64_t N_alloc, int m_heavy, const void* k_raw, const void* v_raw,
+                        int64_t raw_base, int64_t n_raw, int B, int64_t T, int H, int d,
+                        int64_t t0, int window, float scale, void* out, csa_dtype_t out_dt,
+                        float* lse, void* workspace, size_t workspace_bytes, csa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

@@ -1,0 +1,314 @@
+"""GPU parity of every kernel stage against the fp64 CPU oracle (through the C ABI).
+
+Each stage receives the same inputs on both sides; inputs of a later stage are
+the oracle's stored outputs of the earlier one (never a GPU result), so every
+comparison is stage-local.  Shapes span several tiles and slices with ragged
+tails, and the edge cases of the method: rows that see nothing, k above the
+visible count, invalid / invisible / repeated indices, window off, HCA blocks
+longer than the context seen so far.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_attention_csa_amd as csa
+import inputgen
+from oracle import formats, method
+from parity_util import (check_attention, check_e4m3, check_topk_rows, f64, bf16_bits,
+                         to_dev_bf16, to_dev_f32, ulp_diff_bf16)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def gen(name, shape, dtype, seed=0, std=1.0):
+    return inputgen.normal(name, shape, seed, dtype, std=std)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ----------------------------------------------------------------------------- compressor
+
+COMPRESS_CASES = [
+    # x_dt, out_dt, m, d, n_raw, raw_base, entry_begin, entry_end, N_alloc
+    ("bf16", "bf16", 4, 128, 1003, 0, 0, 250, 250),
+    ("bf16", "f32", 4, 64, 517, 0, 0, 129, 129),
+    ("bf16", "e4m3", 4, 64, 1000, 0, 0, 250, 250),
+    ("bf16", "e4m3", 4, 32, 999, 0, 0, 249, 260),
+    ("f32", "f32", 4, 32, 4096, 0, 0, 1024, 1024),
+    ("f32", "bf16", 128, 64, 1000, 0, 0, 7, 7),
+    ("bf16", "bf16", 128, 128, 4096, 0, 0, 32, 32),
+    ("bf16", "bf16", 4, 128, 300, 100, 25, 100, 120),  # sub-range after raw_base
+    ("bf16", "bf16", 1, 64, 77, 0, 0, 77, 77),         # m = 1 copies
+    ("bf16", "bf16", 5, 16, 103, 0, 3, 20, 20),        # odd block, narrow rows
+]
+
+
+@pytest.mark.parametrize("case", COMPRESS_CASES, ids=[f"{c[0]}-{c[1]}-m{c[2]}-d{c[3]}-n{c[4]}" for c in COMPRESS_CASES])
+def test_compress(case):
+    x_dt, out_dt, m, d, n_raw, raw_base, eb, ee, N = case
+    say("compress", case)
+    B = 2
+    x = gen("cmp_x", (B, n_raw, d), x_dt, seed=n_raw + d)
+    z = gen("cmp_z", (m,), "f32", seed=m, std=0.5)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.uint8}[out_dt]
+    sentinel = 0x55 if out_dt == "e4m3" else 7.0
+    out = torch.full((B, N, d), sentinel, dtype=tdt, device=DEV)
+    scale = torch.full((B, N), 7.0, device=DEV) if out_dt == "e4m3" else None
+    csa.csa_compress(x.to(DEV), z.to(DEV), m, out, scale, raw_base=raw_base, entry_begin=eb,
+                     entry_end=ee)
+    torch.cuda.synchronize()
+    z64 = f64(z)
+    for b in range(B):
+        sums = method.compress_exact(f64(x[b]), z64, m, eb, ee, raw_base)
+        if out_dt == "bf16":
+            got = bf16_bits(out[b, eb:ee])
+            exp = formats.f64_to_bf16_bits(sums)
+            diff = ulp_diff_bf16(got, exp)
+            assert diff.max() <= 1
+            assert (diff == 0).mean() >= 0.9999, f"exact-match rate {(diff == 0).mean()}"
+        elif out_dt == "f32":
+            got = f64(out[b, eb:ee])
+            exp = formats.round_to_f32(sums)
+            np.testing.assert_allclose(got, exp, rtol=1e-6, atol=0)
+        else:
+            n_bad = check_e4m3(out[b, eb:ee].cpu().numpy(), scale[b, eb:ee].cpu().numpy(),
+                               sums.astype(np.float32))
+            assert n_bad <= max(2, sums.size // 10000)
+        # entries outside the range are untouched
+        if out_dt == "e4m3":
+            assert (out[b, :eb] == 0x55).all() and (out[b, ee:] == 0x55).all()
+            assert (scale[b, :eb] == 7.0).all() and (scale[b, ee:] == 7.0).all()
+        else:
+            assert (out[b, :eb] == 7.0).all() and (out[b, ee:] == 7.0).all()
+
+
+# ----------------------------------------------------------------------------- indexer + top-k
+
+
+def make_keys(kind, B, N, d_I, seed):
+    """Stored indexer keys: (device tensor, device scale or None, float64 values)."""
+    if kind == "e4m3":
+        r = gen("idx_k", (B, N, d_I), "f32", seed=seed).numpy()
+        codes, scale, stored = formats.e4m3_quantize_rows(r)
+        return (torch.from_numpy(codes).to(DEV), torch.from_numpy(scale).to(DEV), stored)
+    k = gen("idx_k", (B, N, d_I), kind, seed=seed)
+    return k.to(DEV), None, f64(k)
+
+
+INDEX_CASES = [
+    # kind, B, T, H_I, d_I, N, t0, m, k, with_w
+    ("bf16", 3, 1, 8, 64, 20000, 4 * 20000 - 1, 4, 512, True),     # decode, many slices
+    ("e4m3", 2, 1, 8, 64, 33000, 4 * 33000 - 1, 4, 1024, True),    # decode, fp8 keys
+    ("bf16", 2, 1, 8, 64, 20000, 4 * 15000 + 1, 4, 300, True),     # only 15000 visible
+    ("e4m3", 2, 3, 8, 32, 9000, 4 * 9000 - 3, 4, 100, False),      # T=3 rows, w = 1
+    ("bf16", 2, 37, 8, 64, 300, 1100, 4, 64, True),                # prefill-like, one slice
+    ("bf16", 1, 9, 4, 32, 100, 0, 4, 16, True),                    # rows with 0..2 visible
+    ("bf16", 1, 2, 8, 64, 1500, 4 * 1500 - 1, 4, 2048, True),      # k above visible count
+    ("bf16", 2, 1, 16, 64, 12000, 4 * 12000 - 1, 4, 1, True),      # k = 1, 16 heads
+    ("f32", 1, 40, 4, 32, 1024, 4000, 4, 64, True),                # fp32 path
+    ("f32", 2, 1, 4, 64, 6000, 4 * 6000 - 1, 4, 200, True),        # fp32, many slices
+]
+
+
+@pytest.mark.parametrize("case", INDEX_CASES, ids=[f"{c[0]}-B{c[1]}T{c[2]}-N{c[5]}-k{c[8]}" for c in INDEX_CASES])
+def test_index_topk(case):
+    kind, B, T, H_I, d_I, N, t0, m, k, with_w = case
+    say("index_topk", case)
+    qdt = "f32" if kind == "f32" else "bf16"
+    q = gen("idx_q", (B, T, H_I, d_I), qdt, seed=N + T)
+    w = gen("idx_w", (B, T, H_I), "f32", seed=N + 1) if with_w else None
+    kd, ks, k64 = make_keys(kind, B, N, d_I, seed=N)
+    out_idx = torch.full((B, T, k), 12345, dtype=torch.int32, device=DEV)
+    out_score = torch.full((B, T, k), 5.0, dtype=torch.float32, device=DEV)
+    qd, wd = q.to(DEV), (None if w is None else w.to(DEV))
+    csa.csa_index_topk(qd, wd, kd, ks, t0, m, k, out_idx, out_score)
+    again = torch.full_like(out_idx, 777)
+    csa.csa_index_topk(qd, wd, kd, ks, t0, m, k, again)
+    torch.cuda.synchronize()
+    assert torch.equal(out_idx, again), "selection order is not deterministic"
+    idx = out_idx.cpu().numpy()
+    sc = out_score.cpu().numpy()
+    swaps = 0
+    for b in range(B):
+        scores = method.index_scores(f64(q[b]), None if w is None else f64(w[b]), k64[b], t0, m)
+        swaps += check_topk_rows(idx[b], sc[b], scores, k)
+    say("  in-band swaps:", swaps)
+
+
+def test_index_topk_exact_ties_go_to_lower_index():
+    B, N, d_I, k = 1, 2000, 64, 100
+    base = gen("tie_k", (1, 50, d_I), "bf16", seed=3)
+    keys = base.repeat(1, 40, 1)  # row j equals row j % 50
+    q = gen("tie_q", (B, 1, 8, d_I), "bf16", seed=4)
+    out = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    csa.csa_index_topk(q.to(DEV), None, keys.to(DEV).contiguous(), None, 4 * N - 1, 4, k, out)
+    torch.cuda.synchronize()
+    scores = method.index_scores(f64(q[0]), None, f64(keys[0]), 4 * N - 1, 4)
+    exp = np.sort(method.select_topk(scores, k)[0])
+    np.testing.assert_array_equal(np.sort(out[0, 0].cpu().numpy()), exp)
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def make_idx(B, T, k, t0, m, N, seed, bad_frac=0.1):
+    """Random selections of distinct visible entries, with some slots set to -1, to
+    entries not yet visible, to entries past the cache, and one repeated entry."""
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, T, k), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(T):
+            c = min(N, (t0 + i + 1) // m)
+            n = min(k, c)
+            if n:
+                idx[b, i, :n] = rng.choice(c, n, replace=False)
+            nbad = int(bad_frac * k)
+            pos = rng.choice(k, nbad, replace=False)
+            p1, p2, p3 = pos[: nbad // 3], pos[nbad // 3: 2 * nbad // 3], pos[2 * nbad // 3:]
+            idx[b, i, p1] = -1
+            idx[b, i, p2] = c + rng.integers(0, 5, len(p2))  # not yet visible
+            idx[b, i, p3] = N + 7                             # past the cache
+            if n >= 2 and nbad and 0 not in pos and 1 not in pos:
+                idx[b, i, 1] = idx[b, i, 0]                   # counted twice
+    return idx
+
+
+ATTEND_CASES = [
+    # name, dt, B, T, H, d, N, m, k, W, t0, out_dt
+    ("csa-decode", "bf16", 2, 1, 128, 128, 3000, 4, 1024, 128, 4 * 3000 - 1, "f32"),
+    ("csa-decode-h64", "bf16", 3, 1, 64, 128, 3000, 4, 512, 128, 4 * 3000 - 1, "bf16"),
+    ("csa-prefill", "bf16", 1, 37, 64, 128, 300, 4, 64, 128, 1100, "f32"),
+    ("csa-nowin-d64", "bf16", 2, 20, 16, 64, 100, 4, 40, 0, 60, "f32"),
+    ("csa-empty-rows", "bf16", 1, 12, 32, 128, 50, 4, 8, 0, 0, "f32"),
+    ("csa-f32", "f32", 1, 50, 8, 64, 1024, 4, 64, 128, 3000, "f32"),
+    ("csa-f32-d32", "f32", 2, 9, 3, 32, 200, 4, 100, 7, 700, "f32"),
+    ("csa-f32-decode", "f32", 2, 1, 8, 128, 3000, 4, 1024, 128, 4 * 3000 - 1, "f32"),
+    ("hca-decode", "bf16", 2, 1, 128, 128, 2000, 128, 0, 128, 128 * 2000 - 1, "f32"),
+    ("hca-short", "bf16", 3, 1, 64, 128, 200, 128, 0, 128, 128 * 200 - 1, "bf16"),
+    ("hca-prefill", "bf16", 1, 40, 64, 128, 10, 128, 0, 128, 300, "f32"),
+    ("hca-f32", "f32", 1, 33, 8, 64, 32, 128, 0, 128, 4000, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", ATTEND_CASES, ids=[c[0] for c in ATTEND_CASES])
+def test_attend(case):
+    name, dt, B, T, H, d, N, m, k, W, t0, out_dt = case
+    say("attend", case)
+    hca = name.startswith("hca")
+    n_raw = t0 + T + 3
+    q = gen("att_q", (B, T, H, d), dt, seed=H + T)
+    kc = gen("att_kc", (B, N, d), dt, seed=N, std=0.6)
+    vc = gen("att_vc", (B, N, d), dt, seed=N + 1, std=0.6)
+    kr = gen("att_kr", (B, n_raw, d), dt, seed=7)
+    vr = gen("att_vr", (B, n_raw, d), dt, seed=8)
+    scale = 1.0 / math.sqrt(d)
+    odt = torch.bfloat16 if out_dt == "bf16" else torch.float32
+    out = torch.full((B, T, H, d), 9.0, dtype=odt, device=DEV)
+    lse = torch.full((B, T, H), 9.0, device=DEV)
+    if hca:
+        csa.hca_attend(q.to(DEV), kc.to(DEV), vc.to(DEV), m, kr.to(DEV), vr.to(DEV), t0, W, scale,
+                       out, lse)
+    else:
+        idx = make_idx(B, T, k, t0, m, N, seed=N + k)
+        csa.csa_attend(q.to(DEV), kc.to(DEV), vc.to(DEV), m, torch.from_numpy(idx).to(DEV),
+                       kr.to(DEV), vr.to(DEV), t0, W, scale, out, lse)
+    torch.cuda.synchronize()
+    for b in range(B):
+        if hca:
+            o_ref, l_ref = method.hca_attend(f64(q[b]), f64(kc[b]), f64(vc[b]), m, f64(kr[b]),
+                                             f64(vr[b]), 0, t0, W, scale)
+        else:
+            o_ref, l_ref = method.csa_attend(f64(q[b]), f64(kc[b]), f64(vc[b]), idx[b], f64(kr[b]),
+                                             f64(vr[b]), 0, t0, W, m, scale)
+        check_attention(f64(out[b]), f64(lse[b]), o_ref, l_ref, dt, what=f"{name} b={b}",
+                        out_bf16=(out_dt == "bf16"))
+
+
+def test_attend_is_deterministic_and_consistent_across_splits():
+    """Same call twice: identical bits.  Decode rows (split) equal the same rows
+    computed inside a prefill call (unsplit), within tolerance."""
+    B, H, d, N, m, k, W = 2, 64, 128, 2000, 4, 1024, 128
+    t_last = 4 * N - 1
+    T = 6
+    t0 = t_last - T + 1
+    q = gen("det_q", (B, T, H, d), "bf16", seed=1).to(DEV)
+    kc = gen("det_kc", (B, N, d), "bf16", seed=2, std=0.6).to(DEV)
+    vc = gen("det_vc", (B, N, d), "bf16", seed=3, std=0.6).to(DEV)
+    kr = gen("det_kr", (B, t_last + 1, d), "bf16", seed=4).to(DEV)
+    vr = gen("det_vr", (B, t_last + 1, d), "bf16", seed=5).to(DEV)
+    idx = torch.from_numpy(make_idx(B, T, k, t0, m, N, seed=9, bad_frac=0.0)).to(DEV)
+    outs = []
+    for _ in range(2):
+        o = torch.empty((B, T, H, d), device=DEV)
+        csa.csa_attend(q, kc, vc, m, idx, kr, vr, t0, W, 0.088, o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    last = torch.empty((B, 1, H, d), device=DEV)
+    csa.csa_attend(q[:, -1:].contiguous(), kc, vc, m, idx[:, -1:].contiguous(), kr, vr, t_last, W,
+                   0.088, last)
+    torch.cuda.synchronize()
+    ref = f64(outs[0][:, -1])
+    diff = np.abs(f64(last[:, 0]) - ref).max(axis=-1)
+    assert np.all(diff <= 1e-5 * np.abs(ref).max(axis=-1))
+
+
+# ----------------------------------------------------------------------------- end to end, fp32
+
+
+def test_tiny_prefill_f32_end_to_end():
+    """Tiny CSA + HCA prefill in fp32, fully independent: the GPU runs compress ->
+    index/top-k -> attend on its own outputs; the oracle runs its own pipeline.
+    Rows whose selected set differs (only possible inside the tie band) are
+    validated as sets and excluded from the output comparison."""
+    wl = inputgen.WORKLOADS["tiny_prefill_f32"]
+    say("end-to-end", wl)
+    x = inputgen.make_inputs(wl, seed=0)
+    dev = {k: v.to(DEV) for k, v in x.items()}
+    n, N, Nh = wl.n, wl.N_c, wl.N_h
+    kc = torch.empty((1, N, wl.d), device=DEV)
+    vc = torch.empty((1, N, wl.d), device=DEV)
+    kic = torch.empty((1, N, wl.d_I), device=DEV)
+    csa.csa_compress(dev["k_raw"], dev["z_csa"], wl.m, kc)
+    csa.csa_compress(dev["v_raw"], dev["z_csa"], wl.m, vc)
+    csa.csa_compress(dev["k_idx_raw"], dev["z_csa"], wl.m, kic)
+    idx = torch.empty((1, wl.T, wl.k), dtype=torch.int32, device=DEV)
+    csa.csa_index_topk(dev["q_idx"], dev["w"], kic, None, wl.t0, wl.m, wl.k, idx)
+    o = torch.empty((1, wl.T, wl.H, wl.d), device=DEV)
+    lse = torch.empty((1, wl.T, wl.H), device=DEV)
+    csa.csa_attend(dev["q"], kc, vc, wl.m, idx, dev["k_raw"], dev["v_raw"], wl.t0, wl.W, wl.scale,
+                   o, lse)
+    hk = torch.empty((1, Nh, wl.d), device=DEV)
+    hv = torch.empty((1, Nh, wl.d), device=DEV)
+    csa.csa_compress(dev["k_raw"], dev["z_hca"], wl.m_heavy, hk)
+    csa.csa_compress(dev["v_raw"], dev["z_hca"], wl.m_heavy, hv)
+    ho = torch.empty_like(o)
+    hl = torch.empty_like(lse)
+    csa.hca_attend(dev["q"], hk, hv, wl.m_heavy, dev["k_raw"], dev["v_raw"], wl.t0, wl.W, wl.scale,
+                   ho, hl)
+    torch.cuda.synchronize()
+
+    ref = method.csa_layer(f64(x["q"][0]), f64(x["k_raw"][0]), f64(x["v_raw"][0]),
+                           f64(x["q_idx"][0]), f64(x["k_idx_raw"][0]), f64(x["w"][0]),
+                           f64(x["z_csa"]), wl.m, wl.k, wl.W, wl.scale, wl.t0)
+    np.testing.assert_array_equal(f64(kc[0]), ref["k_cmp"]["values"])
+    np.testing.assert_array_equal(f64(kic[0]), ref["k_idx"]["values"])
+    g = idx[0].cpu().numpy()
+    same = np.array([set(g[i][g[i] >= 0]) == set(ref["idx"][i][ref["idx"][i] >= 0])
+                     for i in range(wl.T)])
+    mism = np.nonzero(~same)[0]
+    for i in mism:
+        ok, why, _ = method.topk_is_valid(g[i], ref["scores"][i], wl.k)
+        assert ok, f"row {i}: {why}"
+    say("  rows with an in-band set difference:", len(mism))
+    assert len(mism) <= wl.T // 100
+    check_attention(f64(o[0])[same], f64(lse[0])[same], ref["o"][same], ref["lse"][same], "f32", "csa e2e")
+    href = method.hca_layer(f64(x["q"][0]), f64(x["k_raw"][0]), f64(x["v_raw"][0]),
+                            f64(x["z_hca"]), wl.m_heavy, wl.W, wl.scale, wl.t0)
+    np.testing.assert_array_equal(f64(hk[0]), href["k_cmp"]["values"])
+    check_attention(f64(ho[0]), f64(hl[0]), href["o"], href["lse"], "f32", "hca e2e")
