@@ -47,6 +47,8 @@ SIGNATURES = {
     "hca_attend_workspace": (_sz, [_i32, _i64, _i32, _i32, _i64, _i32, _i32]),
     "hca_attend": (_i32, [_vp, _i32, _vp, _vp, _i64, _i32, _vp, _vp, _i64, _i64, _i32, _i64,
                           _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "csa_profile_enable": (_i32, [_i32]),
+    "csa_profile_report": (_i32, [ctypes.c_char_p, _sz]),
 }
 
 _lib = None
@@ -180,3 +182,18 @@ def hca_attend(q, k_cmp, v_cmp, m_heavy, k_raw, v_raw, t0, window, scale, out, l
                           0 if ws is None else ws.numel(), _stream(q))
     _check("hca_attend", st)
     return out
+
+
+def profile_enable(on: bool = True) -> bool:
+    """Turn per-kernel event timing on or off for this thread; returns the old setting."""
+    return bool(lib().csa_profile_enable(1 if on else 0))
+
+
+def profile_report() -> dict:
+    """Per-kernel {"launches", "total_ms"} since the last report (waits for the events)."""
+    import json
+    buf = ctypes.create_string_buffer(1 << 16)
+    n = lib().csa_profile_report(buf, len(buf))
+    if n < 0:
+        raise CsaError("csa_profile_report", 7, "event query failed")
+    return json.loads(buf.value.decode())

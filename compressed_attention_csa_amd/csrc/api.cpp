@@ -6,7 +6,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/csa.h"
+#include "csa.h"
 #include "kernels.h"
 
 namespace {
@@ -223,7 +223,7 @@ static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const v
   }
   const csa::AttendPlan p =
       csa::plan_attend(hca, B, T, H, d, hca ? N_alloc : int64_t(top_k), window);
-  REQUIRE(p.rows * p.splits <= kMaxGrid, CSA_E_SHAPE, "too many query rows");
+  REQUIRE(p.groups * p.group_stride <= kMaxGrid, CSA_E_SHAPE, "too many query rows");
   REQUIRE(p.ws_bytes == 0 || workspace != nullptr, CSA_E_WORKSPACE, "workspace is NULL");
   REQUIRE(workspace_bytes >= p.ws_bytes, CSA_E_WORKSPACE, "workspace has %zu bytes, needs %zu",
           workspace_bytes, p.ws_bytes);

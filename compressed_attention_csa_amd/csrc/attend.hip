@@ -8,15 +8,20 @@
 //     then raw positions max(0, t-W+1) .. t
 // and every head h computes o = softmax(scale * q_h . K) V over all slots.
 //
-// One workgroup handles a contiguous range of slots ("split") of one row for
-// all heads: all query heads share the one KV head, so a K/V row fetched once
-// feeds every head.  bf16 path: 32-slot tiles are gathered into LDS (K
-// row-major, V transposed); S^T = K Q^T on 16x16x32 MFMA puts one head per
-// lane column and 8 slots per lane, which is exactly the B-operand layout of
-// O^T = V^T P^T, so the softmax weights never move between lanes.  P enters
-// the MFMA as a bf16 hi + lo pair (16 significant bits).  fp32 path: fp32 FMA,
-// one slot per lane.  With several splits, each writes (O, max, sum) partials
-// and the last split of the row to finish merges them (log-sum-exp).
+// Work split.  A workgroup handles one row, one group of up to 64 heads and one
+// contiguous range of slots ("split").  All query heads share the one KV head,
+// so a K/V row fetched once feeds every head of the group; the head groups of
+// one (row, split) get block ids that are equal modulo 8, which places them on
+// the same XCD so that the second group finds the rows in that XCD's L2.
+//
+// bf16 path: 32-slot tiles are gathered into LDS (K row-major, V transposed)
+// while the next tile's rows are already being loaded into registers.
+// S^T = K Q^T on 16x16x32 MFMA puts one head per lane column and 8 slots per
+// lane, which is exactly the B-operand layout of O^T = V^T P^T, so the softmax
+// weights never move between lanes.  P enters the MFMA as a bf16 hi + lo pair
+// (16 significant bits).  fp32 path: fp32 FMA with one slot per lane.
+// With several splits, each writes (O, max, sum) partials and the last split of
+// the (row, head group) to finish merges them (log-sum-exp).
 #include "common.hpp"
 #include "kernels.h"
 
@@ -24,8 +29,9 @@ namespace csa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 32;           // bf16 slots per tile
-constexpr int kTileF32 = 64;        // fp32 slots per tile
+constexpr int kTile = 32;      // bf16 slots per tile
+constexpr int kTileF32 = 64;   // fp32 slots per tile
+constexpr int kMaxSplits = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -55,23 +61,23 @@ __device__ __forceinline__ RowSlots row_slots(const AttendArgs& a, const AttendP
   return x;
 }
 
-// Source row of slot `slot`, or null when the slot is skipped.
-template <typename T>
-__device__ __forceinline__ const T* slot_row(const AttendArgs& a, const RowSlots& x, int64_t slot,
-                                             bool value) {
-  const T* cmp = reinterpret_cast<const T*>(value ? a.v_cmp : a.k_cmp);
-  const T* raw = reinterpret_cast<const T*>(value ? a.v_raw : a.k_raw);
+// Element offset of the source row of `slot` in the compressed (cmp=true) or raw
+// tensors, or -1 when the slot is skipped.
+__device__ __forceinline__ int64_t slot_offset(const AttendArgs& a, const RowSlots& x, int64_t slot,
+                                               bool& cmp) {
   const int64_t nsel = a.hca ? x.c : int64_t(a.top_k);
   if (slot < nsel) {
+    cmp = true;
     int64_t j = slot;
     if (!a.hca) {
       j = a.idx[x.r * a.top_k + slot];
-      if (j < 0 || j >= x.c) return nullptr;
+      if (j < 0 || j >= x.c) return -1;
     }
-    return cmp + (x.b * a.N_alloc + j) * a.d;
+    return (x.b * a.N_alloc + j) * a.d;
   }
+  cmp = false;
   const int64_t pos = x.wstart + (slot - nsel);
-  return raw + (x.b * a.n_raw + (pos - a.raw_base)) * a.d;
+  return (x.b * a.n_raw + (pos - a.raw_base)) * a.d;
 }
 
 struct SplitCtrl {
@@ -79,48 +85,92 @@ struct SplitCtrl {
   uint32_t pad[3];
 };
 
-// Merge the S partials of row r (all heads) and write out / lse.
-// part: [S][H][d] un-normalised O; ml: [S][H][2] (max in log2 units, sum).
-__device__ void merge_row(const AttendArgs& a, const float* part, const float* ml, int64_t S,
-                          int64_t r) {
-  const int H = a.H, d = a.d;
-  for (int x = threadIdx.x; x < H * d; x += kThreads) {
-    const int h = x / d;
-    float M = -INFINITY;
-    for (int64_t s = 0; s < S; ++s) M = fmaxf(M, ml[(s * H + h) * 2]);
-    float Lsum = 0.0f, O = 0.0f;
-    if (M != -INFINITY) {
-      for (int64_t s = 0; s < S; ++s) {
-        const float ms = ml[(s * H + h) * 2];
-        const float f = exp2f(ms - M);  // 0 for empty splits (ms = -inf)
-        Lsum = fmaf(f, ml[(s * H + h) * 2 + 1], Lsum);
-        O = fmaf(f, part[(s * H + h) * int64_t(d) + (x - h * d)], O);
-      }
-    }
-    const float o = (Lsum > 0.0f) ? O / Lsum : 0.0f;
-    const int64_t oi = (r * H + h) * int64_t(d) + (x - h * d);
-    if (a.out_bf16) reinterpret_cast<bf16_t*>(a.out)[oi] = f32_to_bf16(o);
-    else reinterpret_cast<float*>(a.out)[oi] = o;
-    if (a.lse && x - h * d == 0) a.lse[r * H + h] = (Lsum > 0.0f) ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
-  }
+__device__ __forceinline__ float4 load_dev4(const float* p) {
+  return make_float4(load_dev(p), load_dev(p + 1), load_dev(p + 2), load_dev(p + 3));
 }
 
-// Publish this split's partials; the last split of the row merges.  Returns
-// after the merge (or immediately for non-last splits).
-__device__ void finish_split(const AttendArgs& a, const AttendPlan& p, const RowSlots& x, int64_t s,
-                             uint32_t* s_flag) {
+struct MergeLds {
+  float f[kMaxSplits][kAttendGroupHeads];  // per-split weight exp2(m_s - M) / L
+  float lse[kAttendGroupHeads];
+};
+
+// Merge the S partials of one (row, head group) and write out / lse.
+// part: [S][nhs][d] un-normalised O; ml: [S][nhs][2] (max in log2 units, sum);
+// nhs is the per-group stride, nh <= nhs the group's heads.
+__device__ void merge_group(const AttendArgs& a, const float* part, const float* ml, int64_t S,
+                            int64_t r, int h_begin, int nh, int nhs, MergeLds& M) {
+  const int d = a.d, tid = threadIdx.x;
+  for (int h = tid; h < nh; h += kThreads) {
+    float mx = -INFINITY;
+    for (int64_t s = 0; s < S; ++s) mx = fmaxf(mx, load_dev(&ml[(s * nhs + h) * 2]));
+    float Lsum = 0.0f;
+    if (mx != -INFINITY)
+      for (int64_t s = 0; s < S; ++s)
+        Lsum = fmaf(exp2f(load_dev(&ml[(s * nhs + h) * 2]) - mx), load_dev(&ml[(s * nhs + h) * 2 + 1]), Lsum);
+    const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+    for (int64_t s = 0; s < S; ++s)
+      M.f[s][h] = (mx == -INFINITY) ? 0.0f : exp2f(load_dev(&ml[(s * nhs + h) * 2]) - mx) * inv;
+    M.lse[h] = Lsum > 0.0f ? (mx + log2f(Lsum)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  const int cpr = d / 4;  // float4 chunks per head
+  for (int c = tid; c < nh * cpr; c += kThreads) {
+    const int h = c / cpr, col = (c % cpr) * 4;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    int64_t s = 0;
+    for (; s + 4 <= S; s += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = load_dev4(part + ((s + u) * nhs + h) * int64_t(d) + col);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float f = M.f[s + u][h];
+        acc.x = fmaf(f, v[u].x, acc.x); acc.y = fmaf(f, v[u].y, acc.y);
+        acc.z = fmaf(f, v[u].z, acc.z); acc.w = fmaf(f, v[u].w, acc.w);
+      }
+    }
+    for (; s < S; ++s) {
+      const float4 v = load_dev4(part + (s * nhs + h) * int64_t(d) + col);
+      const float f = M.f[s][h];
+      acc.x = fmaf(f, v.x, acc.x); acc.y = fmaf(f, v.y, acc.y);
+      acc.z = fmaf(f, v.z, acc.z); acc.w = fmaf(f, v.w, acc.w);
+    }
+    const int64_t oi = (r * a.H + h_begin + h) * int64_t(d) + col;
+    if (a.out_bf16) {
+      const uint32_t w0 = uint32_t(f32_to_bf16(acc.x)) | (uint32_t(f32_to_bf16(acc.y)) << 16);
+      const uint32_t w1 = uint32_t(f32_to_bf16(acc.z)) | (uint32_t(f32_to_bf16(acc.w)) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + oi) = make_uint2(w0, w1);
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) = acc;
+    }
+  }
+  if (a.lse)
+    for (int h = tid; h < nh; h += kThreads) a.lse[r * a.H + h_begin + h] = M.lse[h];
+}
+
+// Publish this split's partials; the last split of the (row, group) merges.
+__device__ void finish_split(const AttendArgs& a, const AttendPlan& p, const RowSlots& x,
+                             int64_t unit, int h_begin, int nh, int nhs, uint32_t* s_flag,
+                             MergeLds& M) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
-  SplitCtrl* ctrl = reinterpret_cast<SplitCtrl*>(ws + kAttendCtrlOff) + x.r;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_flag[0] = (atomicAdd(&ctrl->arrive, 1u) == uint32_t(x.S - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!s_flag[0]) return;
-  __threadfence();
-  const float* part = reinterpret_cast<const float*>(ws + p.off_part) + x.r * p.splits * a.H * a.d;
-  const float* ml = reinterpret_cast<const float*>(ws + p.off_ml) + x.r * p.splits * a.H * 2;
-  merge_row(a, part, ml, x.S, x.r);
+  SplitCtrl* ctrl = reinterpret_cast<SplitCtrl*>(ws + kAttendCtrlOff) + unit;
+  if (!arrive_last(&ctrl->arrive, uint32_t(x.S), s_flag)) return;
+  const float* part = reinterpret_cast<const float*>(ws + p.off_part) + unit * p.splits * nhs * a.d;
+  const float* ml = reinterpret_cast<const float*>(ws + p.off_ml) + unit * p.splits * nhs * 2;
+  merge_group(a, part, ml, x.S, x.r, h_begin, nh, nhs, M);
   if (threadIdx.x == 0) ctrl->arrive = 0;
+}
+
+// Block id -> (head group, row, split).  Each group spans group_stride ids (a
+// multiple of 8), so the groups of one (row, split) share id mod 8 and hence
+// an XCD.  Returns false for the padding ids.
+__device__ __forceinline__ bool decode_block(const AttendPlan& p, int64_t& hg, int64_t& r, int64_t& s) {
+  hg = blockIdx.x / p.group_stride;
+  const int64_t rem = blockIdx.x % p.group_stride;
+  if (rem >= p.rows * p.splits) return false;
+  r = rem / p.splits;
+  s = rem % p.splits;
+  return true;
 }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel
@@ -129,83 +179,89 @@ template <int D>
 struct LdsBF16 {
   bf16_t k[kTile][D + 8];   // row-major K tile (padded rows)
   bf16_t vt[D][kTile + 8];  // transposed V tile
+  uint32_t live[kTile];
   uint32_t flag[4];
+  MergeLds merge;
 };
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
   __shared__ LdsBF16<D> L;
-  const int64_t r = blockIdx.x / p.splits;
-  const int64_t s = blockIdx.x % p.splits;
+  int64_t hg, r, s;
+  if (!decode_block(p, hg, r, s)) return;
   const RowSlots x = row_slots(a, p, r, s);
   if (s >= x.S) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
   const int H = a.H;
-  const int NG = H / 16;  // head groups of 16
+  const int h_begin = int(hg) * kAttendGroupHeads;
+  const int nh = (H - h_begin) < kAttendGroupHeads ? (H - h_begin) : kAttendGroupHeads;
+  const int h0 = h_begin + wid * 16;  // this wave's 16 heads
+  const bool has = wid * 16 < nh;
   constexpr int KS = D / 32;   // k-steps of the QK product
   constexpr int DVT = D / 16;  // 16-column tiles of the output
-  // This wave's head groups: wid and wid + 4.
-  const int hg0 = wid, hg1 = wid + 4;
-  const bool has0 = hg0 < NG, has1 = hg1 < NG;
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  constexpr int NCH = kTile * CPR / kThreads;  // chunks per thread per tensor
 
-  bf16x8_t qb[2][KS];
+  bf16x8_t qb[KS];
   const bf16_t* qrow = reinterpret_cast<const bf16_t*>(a.q) + r * int64_t(H) * D;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int hg = u == 0 ? hg0 : hg1;
-    const bool has = u == 0 ? has0 : has1;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (has) v = *reinterpret_cast<const uint4*>(qrow + (hg * 16 + col) * D + 32 * kk + 8 * g);
-      qb[u][kk] = u32x4_as_bf16x8(v);
-    }
+  for (int kk = 0; kk < KS; ++kk) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (has) v = *reinterpret_cast<const uint4*>(qrow + (h0 + col) * D + 32 * kk + 8 * g);
+    qb[kk] = u32x4_as_bf16x8(v);
   }
   const float sl2 = a.scale * kLog2e;
-  f32x4_t o[2][DVT];
+  f32x4_t o[DVT];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int v = 0; v < DVT; ++v) o[u][v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float mrun[2] = {-INFINITY, -INFINITY};
-  float lpart[2] = {0.0f, 0.0f};
+  for (int v = 0; v < DVT; ++v) o[v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float mrun = -INFINITY, lpart = 0.0f;
 
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  for (int64_t t0 = x.lo; t0 < x.hi; t0 += kTile) {
-    // Gather the K / V rows of 32 slots into LDS.
-    for (int c = tid; c < kTile * CPR; c += kThreads) {
-      const int sl = c / CPR, ch = c % CPR;
+  const bf16_t* kc = reinterpret_cast<const bf16_t*>(a.k_cmp);
+  const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.v_cmp);
+  const bf16_t* kr = reinterpret_cast<const bf16_t*>(a.k_raw);
+  const bf16_t* vr = reinterpret_cast<const bf16_t*>(a.v_raw);
+  uint4 pk[NCH], pv[NCH];
+  bool plive[NCH];
+  auto fetch = [&](int64_t t0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int id = tid + c * kThreads, sl = id / CPR, ch = id % CPR;
       const int64_t slot = t0 + sl;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      pk[c] = make_uint4(0, 0, 0, 0);
+      pv[c] = make_uint4(0, 0, 0, 0);
+      plive[c] = false;
       if (slot < x.hi) {
-        const bf16_t* kr = slot_row<bf16_t>(a, x, slot, false);
-        if (kr) {
-          const bf16_t* vr = slot_row<bf16_t>(a, x, slot, true);
-          kv = *reinterpret_cast<const uint4*>(kr + ch * 8);
-          vv = *reinterpret_cast<const uint4*>(vr + ch * 8);
+        bool cmp;
+        const int64_t off = slot_offset(a, x, slot, cmp);
+        if (off >= 0) {
+          plive[c] = true;
+          pk[c] = *reinterpret_cast<const uint4*>((cmp ? kc : kr) + off + ch * 8);
+          pv[c] = *reinterpret_cast<const uint4*>((cmp ? vc : vr) + off + ch * 8);
         }
       }
-      *reinterpret_cast<uint4*>(&L.k[sl][ch * 8]) = kv;
-      const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int id = tid + c * kThreads, sl = id / CPR, ch = id % CPR;
+      *reinterpret_cast<uint4*>(&L.k[sl][ch * 8]) = pk[c];
+      const uint32_t w4[4] = {pv[c].x, pv[c].y, pv[c].z, pv[c].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         L.vt[ch * 8 + 2 * i][sl] = bf16_t(w4[i] & 0xffffu);
         L.vt[ch * 8 + 2 * i + 1][sl] = bf16_t(w4[i] >> 16);
       }
+      if (ch == 0) L.live[sl] = plive[c] ? 1u : 0u;
     }
+  };
+
+  if (x.lo < x.hi) fetch(x.lo);
+  for (int64_t t0 = x.lo; t0 < x.hi; t0 += kTile) {
+    stash();
     __syncthreads();
-    // Which of this tile's slots are live (lane-independent per slot index).
-    bool live[2][4];
-#pragma unroll
-    for (int cg = 0; cg < 2; ++cg)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t slot = t0 + cg * 16 + 4 * g + j;
-        live[cg][j] = slot < x.hi && slot_row<bf16_t>(a, x, slot, false) != nullptr;
-      }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (!(u == 0 ? has0 : has1)) continue;
+    if (t0 + kTile < x.hi) fetch(t0 + kTile);  // next tile in flight during the math
+    if (has) {
       f32x4_t sc[2];
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) {
@@ -213,46 +269,46 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, Att
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
           const uint4 kv = *reinterpret_cast<const uint4*>(&L.k[cg * 16 + col][32 * kk + 8 * g]);
-          acc = mfma16x16x32(u32x4_as_bf16x8(kv), qb[u][kk], acc);
+          acc = mfma16x16x32(u32x4_as_bf16x8(kv), qb[kk], acc);
         }
         sc[cg] = acc;
       }
-      // Online softmax in log2 units; lane holds head (16*hg + col), 8 slots.
+      // Online softmax in log2 units; lane holds head h0 + col and 8 slots.
       float tmax = -INFINITY;
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = live[cg][j] ? sc[cg][j] * sl2 : -INFINITY;
+          const float v = L.live[cg * 16 + 4 * g + j] ? sc[cg][j] * sl2 : -INFINITY;
           sc[cg][j] = v;
           tmax = fmaxf(tmax, v);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(mrun[u], tmax);
-      const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun[u] - mnew);
-      mrun[u] = mnew;
+      const float mnew = fmaxf(mrun, tmax);
+      const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun - mnew);
+      mrun = mnew;
       float psum = 0.0f;
       uint32_t phi[4], plo[4];
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {
-          float p0 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j] - mnew);
-          float p1 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j + 1] - mnew);
+          const float p0 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j] - mnew);
+          const float p1 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j + 1] - mnew);
           psum += p0 + p1;
-          const bf16_t h0 = f32_to_bf16(p0), h1 = f32_to_bf16(p1);
-          const bf16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0));
-          const bf16_t l1 = f32_to_bf16(p1 - bf16_to_f32(h1));
-          phi[cg * 2 + j / 2] = uint32_t(h0) | (uint32_t(h1) << 16);
+          const bf16_t h0b = f32_to_bf16(p0), h1b = f32_to_bf16(p1);
+          const bf16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0b));
+          const bf16_t l1 = f32_to_bf16(p1 - bf16_to_f32(h1b));
+          phi[cg * 2 + j / 2] = uint32_t(h0b) | (uint32_t(h1b) << 16);
           plo[cg * 2 + j / 2] = uint32_t(l0) | (uint32_t(l1) << 16);
         }
-      lpart[u] = lpart[u] * corr + psum;
+      lpart = lpart * corr + psum;
       const bf16x8_t pb_hi = u32x4_as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
       const bf16x8_t pb_lo = u32x4_as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
 #pragma unroll
       for (int v = 0; v < DVT; ++v) {
-        f32x4_t acc = o[u][v];
+        f32x4_t acc = o[v];
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] *= corr;
         const uint2 a0 = *reinterpret_cast<const uint2*>(&L.vt[v * 16 + col][4 * g]);
@@ -260,61 +316,53 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, Att
         const bf16x8_t va = u32x4_as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
         acc = mfma16x16x32(va, pb_hi, acc);
         acc = mfma16x16x32(va, pb_lo, acc);
-        o[u][v] = acc;
+        o[v] = acc;
       }
     }
     __syncthreads();
   }
 
-  // Per-head totals; lane (g, col) holds head 16*hg+col, dv = 16v + 4g + j.
-  float lt[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    float v = lpart[u];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    lt[u] = v;
-  }
+  // Per-head totals; lane (g, col) holds head h0 + col, columns 16v + 4g + j.
+  float lt = lpart;
+  lt += __shfl_xor(lt, 16);
+  lt += __shfl_xor(lt, 32);
+  const int h = h0 + col;
   if (x.S == 1) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (!(u == 0 ? has0 : has1)) continue;
-      const int h = (u == 0 ? hg0 : hg1) * 16 + col;
-      const float inv = lt[u] > 0.0f ? 1.0f / lt[u] : 0.0f;
+    if (has) {
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
       for (int v = 0; v < DVT; ++v) {
         const int64_t oi = (r * H + h) * int64_t(D) + v * 16 + 4 * g;
         if (a.out_bf16) {
-          uint32_t w0 = uint32_t(f32_to_bf16(o[u][v][0] * inv)) | (uint32_t(f32_to_bf16(o[u][v][1] * inv)) << 16);
-          uint32_t w1 = uint32_t(f32_to_bf16(o[u][v][2] * inv)) | (uint32_t(f32_to_bf16(o[u][v][3] * inv)) << 16);
+          uint32_t w0 = uint32_t(f32_to_bf16(o[v][0] * inv)) | (uint32_t(f32_to_bf16(o[v][1] * inv)) << 16);
+          uint32_t w1 = uint32_t(f32_to_bf16(o[v][2] * inv)) | (uint32_t(f32_to_bf16(o[v][3] * inv)) << 16);
           *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + oi) = make_uint2(w0, w1);
         } else {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) =
-              make_float4(o[u][v][0] * inv, o[u][v][1] * inv, o[u][v][2] * inv, o[u][v][3] * inv);
+              make_float4(o[v][0] * inv, o[v][1] * inv, o[v][2] * inv, o[v][3] * inv);
         }
       }
-      if (a.lse && g == 0)
-        a.lse[r * H + h] = lt[u] > 0.0f ? (mrun[u] + log2f(lt[u])) * kLn2 : -INFINITY;
+      if (a.lse && g == 0) a.lse[r * H + h] = lt > 0.0f ? (mrun + log2f(lt)) * kLn2 : -INFINITY;
     }
     return;
   }
+  const int64_t unit = hg * p.rows + r;
+  const int nhs = H < kAttendGroupHeads ? H : kAttendGroupHeads;  // partial stride per group
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
-  float* part = reinterpret_cast<float*>(ws + p.off_part) + (r * p.splits + s) * int64_t(H) * D;
-  float* ml = reinterpret_cast<float*>(ws + p.off_ml) + (r * p.splits + s) * int64_t(H) * 2;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    if (!(u == 0 ? has0 : has1)) continue;
-    const int h = (u == 0 ? hg0 : hg1) * 16 + col;
+  float* part = reinterpret_cast<float*>(ws + p.off_part) + (unit * p.splits + s) * int64_t(nhs) * D;
+  float* ml = reinterpret_cast<float*>(ws + p.off_ml) + (unit * p.splits + s) * int64_t(nhs) * 2;
+  if (has) {
+    const int hl = wid * 16 + col;
 #pragma unroll
     for (int v = 0; v < DVT; ++v)
-      *reinterpret_cast<float4*>(part + int64_t(h) * D + v * 16 + 4 * g) =
-          make_float4(o[u][v][0], o[u][v][1], o[u][v][2], o[u][v][3]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store_dev(part + int64_t(hl) * D + v * 16 + 4 * g + j, o[v][j]);
     if (g == 0) {
-      ml[h * 2] = mrun[u];
-      ml[h * 2 + 1] = lt[u];
+      store_dev(&ml[hl * 2], mrun);
+      store_dev(&ml[hl * 2 + 1], lt);
     }
   }
-  finish_split(a, p, x, s, L.flag);
+  finish_split(a, p, x, unit, h_begin, nh, nhs, L.flag, L.merge);
 }
 
 // ---------------------------------------------------------------- fp32 kernel
@@ -326,21 +374,26 @@ struct LdsF32 {
   float q[32][D];
   float pr[32][kTileF32];
   uint32_t flag[4];
+  MergeLds merge;
 };
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, AttendPlan p) {
   __shared__ LdsF32<D> L;
-  const int64_t r = blockIdx.x / p.splits;
-  const int64_t s = blockIdx.x % p.splits;
+  int64_t hg, r, s;
+  if (!decode_block(p, hg, r, s)) return;
   const RowSlots x = row_slots(a, p, r, s);
   if (s >= x.S) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int H = a.H;
+  const int H = a.H;  // <= 32: one head group
   constexpr int DPL = (D + 63) / 64;  // output columns per lane
   const float* qrow = reinterpret_cast<const float*>(a.q) + r * int64_t(H) * D;
   for (int i = tid; i < H * D; i += kThreads) L.q[i / D][i % D] = qrow[i];
   const float sl2 = a.scale * kLog2e;
+  const float* kc = reinterpret_cast<const float*>(a.k_cmp);
+  const float* vc = reinterpret_cast<const float*>(a.v_cmp);
+  const float* kr = reinterpret_cast<const float*>(a.k_raw);
+  const float* vr = reinterpret_cast<const float*>(a.v_raw);
   float o[8][DPL];
   float mrun[8], lpart[8];
 #pragma unroll
@@ -357,10 +410,11 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
       const int64_t slot = t0 + sl;
       float4 kv = make_float4(0, 0, 0, 0), vv = make_float4(0, 0, 0, 0);
       if (slot < x.hi) {
-        const float* kr = slot_row<float>(a, x, slot, false);
-        if (kr) {
-          kv = *reinterpret_cast<const float4*>(kr + ch * 4);
-          vv = *reinterpret_cast<const float4*>(slot_row<float>(a, x, slot, true) + ch * 4);
+        bool cmp;
+        const int64_t off = slot_offset(a, x, slot, cmp);
+        if (off >= 0) {
+          kv = *reinterpret_cast<const float4*>((cmp ? kc : kr) + off + ch * 4);
+          vv = *reinterpret_cast<const float4*>((cmp ? vc : vr) + off + ch * 4);
         }
       }
       L.k[sl][ch * 4] = kv.x; L.k[sl][ch * 4 + 1] = kv.y; L.k[sl][ch * 4 + 2] = kv.z; L.k[sl][ch * 4 + 3] = kv.w;
@@ -368,35 +422,39 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
     }
     __syncthreads();
     const int64_t slot = t0 + lane;
-    const bool live = slot < x.hi && slot_row<float>(a, x, slot, false) != nullptr;
+    bool cmp;
+    const bool live = slot < x.hi && slot_offset(a, x, slot, cmp) >= 0;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int h = wid + 4 * u;
-      if (h >= H) break;
-      float dot = 0.0f;
-      for (int dd = 0; dd < D; ++dd) dot = fmaf(L.q[h][dd], L.k[lane][dd], dot);
-      const float sv = live ? dot * sl2 : -INFINITY;
-      const float mnew = fmaxf(mrun[u], wave_max(sv));
-      const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun[u] - mnew);
-      const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sv - mnew);
-      mrun[u] = mnew;
-      lpart[u] = lpart[u] * corr + pv;
-      L.pr[h][lane] = pv;
+      if (h < H) {
+        float dot = 0.0f;
+        for (int dd = 0; dd < D; ++dd) dot = fmaf(L.q[h][dd], L.k[lane][dd], dot);
+        const float sv = live ? dot * sl2 : -INFINITY;
+        const float mnew = fmaxf(mrun[u], wave_max(sv));
+        const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun[u] - mnew);
+        const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sv - mnew);
+        mrun[u] = mnew;
+        lpart[u] = lpart[u] * corr + pv;
+        L.pr[h][lane] = pv;
 #pragma unroll
-      for (int c = 0; c < DPL; ++c) o[u][c] *= corr;
+        for (int c = 0; c < DPL; ++c) o[u][c] *= corr;
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int h = wid + 4 * u;
-      if (h >= H) break;
+      if (h < H) {
 #pragma unroll
-      for (int c = 0; c < DPL; ++c) {
-        const int dv = lane + 64 * c;
-        if (dv >= D) continue;
-        float acc = o[u][c];
-        for (int e = 0; e < kTileF32; ++e) acc = fmaf(L.pr[h][e], L.v[e][dv], acc);
-        o[u][c] = acc;
+        for (int c = 0; c < DPL; ++c) {
+          const int dv = lane + 64 * c;
+          if (dv < D) {
+            float acc = o[u][c];
+            for (int e = 0; e < kTileF32; ++e) acc = fmaf(L.pr[h][e], L.v[e][dv], acc);
+            o[u][c] = acc;
+          }
+        }
       }
     }
   }
@@ -407,39 +465,43 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int h = wid + 4 * u;
-      if (h >= H) break;
-      const float inv = lt[u] > 0.0f ? 1.0f / lt[u] : 0.0f;
+      if (h < H) {
+        const float inv = lt[u] > 0.0f ? 1.0f / lt[u] : 0.0f;
 #pragma unroll
-      for (int c = 0; c < DPL; ++c) {
-        const int dv = lane + 64 * c;
-        if (dv >= D) continue;
-        const int64_t oi = (r * H + h) * int64_t(D) + dv;
-        if (a.out_bf16) reinterpret_cast<bf16_t*>(a.out)[oi] = f32_to_bf16(o[u][c] * inv);
-        else reinterpret_cast<float*>(a.out)[oi] = o[u][c] * inv;
+        for (int c = 0; c < DPL; ++c) {
+          const int dv = lane + 64 * c;
+          if (dv < D) {
+            const int64_t oi = (r * H + h) * int64_t(D) + dv;
+            if (a.out_bf16) reinterpret_cast<bf16_t*>(a.out)[oi] = f32_to_bf16(o[u][c] * inv);
+            else reinterpret_cast<float*>(a.out)[oi] = o[u][c] * inv;
+          }
+        }
+        if (a.lse && lane == 0)
+          a.lse[r * H + h] = lt[u] > 0.0f ? (mrun[u] + log2f(lt[u])) * kLn2 : -INFINITY;
       }
-      if (a.lse && lane == 0)
-        a.lse[r * H + h] = lt[u] > 0.0f ? (mrun[u] + log2f(lt[u])) * kLn2 : -INFINITY;
     }
     return;
   }
+  const int64_t unit = r;  // one head group
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
-  float* part = reinterpret_cast<float*>(ws + p.off_part) + (r * p.splits + s) * int64_t(H) * D;
-  float* ml = reinterpret_cast<float*>(ws + p.off_ml) + (r * p.splits + s) * int64_t(H) * 2;
+  float* part = reinterpret_cast<float*>(ws + p.off_part) + (unit * p.splits + s) * int64_t(H) * D;
+  float* ml = reinterpret_cast<float*>(ws + p.off_ml) + (unit * p.splits + s) * int64_t(H) * 2;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int h = wid + 4 * u;
-    if (h >= H) break;
+    if (h < H) {
 #pragma unroll
-    for (int c = 0; c < DPL; ++c) {
-      const int dv = lane + 64 * c;
-      if (dv < D) part[int64_t(h) * D + dv] = o[u][c];
-    }
-    if (lane == 0) {
-      ml[h * 2] = mrun[u];
-      ml[h * 2 + 1] = lt[u];
+      for (int c = 0; c < DPL; ++c) {
+        const int dv = lane + 64 * c;
+        if (dv < D) store_dev(&part[int64_t(h) * D + dv], o[u][c]);
+      }
+      if (lane == 0) {
+        store_dev(&ml[h * 2], mrun[u]);
+        store_dev(&ml[h * 2 + 1], lt[u]);
+      }
     }
   }
-  finish_split(a, p, x, s, L.flag);
+  finish_split(a, p, x, unit, 0, H, H, L.flag, L.merge);
 }
 
 }  // namespace
@@ -448,14 +510,17 @@ AttendPlan plan_attend(bool hca, int B, int64_t T, int H, int d, int64_t max_ent
   (void)hca;
   AttendPlan p{};
   p.rows = int64_t(B) * T;
+  p.groups = (H + kAttendGroupHeads - 1) / kAttendGroupHeads;
   p.slots = max_entries + window;
   const int64_t tile = 64;  // multiple of both tile sizes
-  // Split rows until there are about 256 workgroups, keeping >= 4 tiles per split.
+  // Split rows until there are about 256 workgroups, keeping >= 2 tiles of 64 per split.
+  const int64_t units = p.rows * p.groups;
   int64_t splits = 1;
-  if (p.rows > 0 && p.rows < kAttendCtrlRows) {
-    splits = (256 + p.rows - 1) / p.rows;
-    const int64_t max_splits = (p.slots + 4 * tile - 1) / (4 * tile);
+  if (units > 0 && units <= kAttendCtrlUnits) {
+    splits = (256 + units - 1) / units;
+    const int64_t max_splits = (p.slots + 2 * tile - 1) / (2 * tile);
     if (splits > max_splits) splits = max_splits;
+    if (splits > kMaxSplits) splits = kMaxSplits;
     if (splits < 1) splits = 1;
   }
   int64_t per = (p.slots + splits - 1) / splits;
@@ -464,6 +529,7 @@ AttendPlan plan_attend(bool hca, int B, int64_t T, int H, int d, int64_t max_ent
   p.per_split = per;
   p.splits = (p.slots + per - 1) / per;
   if (p.splits < 1) p.splits = 1;
+  p.group_stride = ((p.rows * p.splits + 7) / 8) * 8;
   size_t off = kHeaderBytes;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -471,16 +537,18 @@ AttendPlan plan_attend(bool hca, int B, int64_t T, int H, int d, int64_t max_ent
     return o;
   };
   const bool multi = p.splits > 1;
-  const size_t R = size_t(p.rows);
-  p.off_part = take(R * size_t(p.splits) * H * d * 4);
-  p.off_ml = take(R * size_t(p.splits) * H * 2 * 4);
+  const size_t U = size_t(units);
+  const size_t nh = size_t(H < kAttendGroupHeads ? H : kAttendGroupHeads);
+  p.off_part = take(U * size_t(p.splits) * nh * d * 4);
+  p.off_ml = take(U * size_t(p.splits) * nh * 2 * 4);
   p.ws_bytes = multi ? off : 0;
   return p;
 }
 
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p) {
   if (p.rows == 0) return hipSuccess;
-  dim3 grid(unsigned(p.rows * p.splits)), block(kThreads);
+  dim3 grid(unsigned(p.groups * p.group_stride)), block(kThreads);
+  ProfScope prof(a.hca ? "hca_attend" : "csa_attend", a.stream);
   if (a.bf16) {
     if (a.d == 128) hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, block, 0, a.stream, a, p);
     else hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, block, 0, a.stream, a, p);

@@ -121,6 +121,40 @@ __device__ __forceinline__ bf16x8_t u32x4_as_bf16x8(uint4 v) {
   return r;
 }
 
+// ---------------------------------------------------------------- cross-workgroup handoff
+//
+// Data that one workgroup hands to another inside the same kernel is written
+// with device-scope stores (they complete at the device coherence point, past
+// the per-XCD L2) and read with device-scope loads.  The writer then waits for
+// its stores to complete before it increments the arrival counter, so no
+// L2 write-back / invalidate fence is needed.
+
+template <typename T>
+__device__ __forceinline__ void store_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this thread issued has completed.
+__device__ __forceinline__ void wait_mem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// All threads: after each thread's device-scope stores, count this workgroup in
+// *counter; returns true in every thread of the workgroup that arrives last.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, uint32_t* s_flag) {
+  wait_mem();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_flag[0] = (__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 expected - 1u) ? 1u : 0u;
+  __syncthreads();
+  return s_flag[0] != 0;
+}
+
 // ---------------------------------------------------------------- reductions
 
 __device__ __forceinline__ float wave_max(float v) {

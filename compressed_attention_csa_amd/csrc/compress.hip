@@ -137,6 +137,7 @@ hipError_t launch(const CompressArgs& a) {
   const int epb = kThreads / tpe;
   const int64_t n_ent = a.entry_end - a.entry_begin;
   dim3 grid(unsigned((n_ent + epb - 1) / epb), unsigned(a.B));
+  ProfScope prof("compress", a.stream);
   hipLaunchKernelGGL((compress_kernel<TIn, OUT>), grid, dim3(kThreads), 0, a.stream,
                      reinterpret_cast<const TIn*>(a.x), a.n_raw, a.d, a.raw_base, a.logits, a.m,
                      a.entry_begin, n_ent, a.N_alloc, a.out, a.out_scale);

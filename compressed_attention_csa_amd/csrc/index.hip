@@ -6,22 +6,25 @@
 //     I(r, j) = sum_h w[r,h] * max(0, q[r,h] . k[j]),  j < c(t) = min(N, (t+1)/m)
 // The selection is the min(k, c(t)) best entries by (score desc, index asc).
 //
-// Design.  A row's visible entries are cut into slices; one workgroup scores one
-// slice of one row.  Every WG keeps its fp32 scores as order-preserving uint32
-// keys in LDS.
-//   * A row with one slice is finished by that WG: an LDS radix select finds
-//     the kk-th best (score, index) and the winners are written in index order.
-//   * A longer row uses two kernels.  Kernel 1: each WG adds its 4096-bin
-//     histogram of the top 12 key bits to the row histogram and stores its
-//     keys; the last WG of the row to arrive locates the bin holding the kk-th
-//     best score.  Kernel 2: each WG compacts its entries above that bin and
-//     its entries inside it (in index order) into per-slice staging; the last
-//     WG concatenates the slices in order and radix-selects the boundary bin.
-// The output order is deterministic: the winners above the boundary bin in
-// increasing entry index, then the boundary winners in increasing entry index.
+// Design (one kernel).  A row's visible entries are cut into slices; one
+// workgroup scores one slice, keeping the fp32 scores as order-preserving
+// uint32 keys in LDS, and ranks entries by the 64-bit key (score, ~index) so
+// that all ranks are distinct.
+//   * A row with a single slice is finished by its WG: an LDS radix select
+//     finds the threshold of the kk best and the winners are written.
+//   * A longer row: every WG writes its exact local top-K_loc (K_loc about 4x
+//     the slice's expected share of the row's winners) plus a certificate,
+//     the threshold below which it dropped entries.  The last WG of the row
+//     to arrive radix-selects the row's kk best among all candidates.  A slice
+//     whose certificate lies above that threshold may have dropped a winner;
+//     the last WG then rescores exactly those slices and adds the dropped
+//     entries above the threshold before selecting again, so the result is
+//     exact for any input; on typical inputs no slice needs it.
+// Output order is deterministic (slice order, then entry index).
 // bf16 / e4m3 keys are scored with 16x16x32 bf16 MFMA (query heads as rows,
-// entries as columns; e4m3 codes are widened exactly to bf16 in registers);
-// fp32 keys use fp32 FMA with one entry per lane.
+// entries as columns; e4m3 codes are widened exactly to bf16 in registers),
+// with 8 groups of 16 keys in flight per wave; fp32 keys use fp32 FMA with one
+// entry per lane.
 #include "common.hpp"
 #include "kernels.h"
 
@@ -30,13 +33,14 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kUnroll = 8;  // 16-key groups in flight per wave
 
 struct RowCtrl {
-  uint32_t arrive1, arrive2, bin, above;
+  uint32_t arrive, pad0, pad1, pad2;
 };
 
 struct RowInfo {
-  int64_t r, b, i, t, c, kk, S, lo, hi;
+  int64_t r, b, i, t, c, kk, S, lo, hi, kloc;
 };
 
 __device__ __forceinline__ RowInfo row_info(const IndexArgs& a, const IndexPlan& p, int64_t r,
@@ -55,6 +59,12 @@ __device__ __forceinline__ RowInfo row_info(const IndexArgs& a, const IndexPlan&
   int64_t hi = ri.lo + p.slice;
   ri.hi = hi < ri.c ? hi : ri.c;
   if (ri.hi < ri.lo) ri.hi = ri.lo;
+  // Local candidates per slice: about 4x the slice's expected share of winners.
+  int64_t share = (ri.kk + ri.S - 1) / ri.S;
+  int64_t kl = ((4 * share + 31) / 32) * 32;
+  if (kl < 32) kl = 32;
+  if (kl > p.slice) kl = p.slice;
+  ri.kloc = kl;
   return ri;
 }
 
@@ -78,6 +88,23 @@ __device__ __forceinline__ int block_rank(bool flag, int* s_wave, int& total) {
   return off + in_wave;
 }
 
+// Inclusive block-wide prefix sum of one uint32 per thread (thread order).
+__device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* s_scan) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t n = __shfl_up(v, o);
+    if (lane >= o) v += n;
+  }
+  if (lane == kWave - 1) s_scan[wid] = v;
+  __syncthreads();
+  uint32_t pre = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) pre += (w < wid) ? s_scan[w] : 0u;
+  __syncthreads();
+  return v + pre;
+}
+
 // ---------------------------------------------------------------- scoring
 
 // Scores of entries [lo, hi) of row ri into keys[0 .. hi-lo).
@@ -94,17 +121,18 @@ __device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* key
     __syncthreads();
     const float* kbase = reinterpret_cast<const float*>(a.k_idx) + (ri.b * a.N_alloc + ri.lo) * d_I;
     for (int64_t e = tid; e < n; e += kThreads) {
-      float kv[64];
       const float4* kp = reinterpret_cast<const float4*>(kbase + e * d_I);
-      for (int v = 0; v < d_I / 4; ++v) {
-        float4 x = kp[v];
-        kv[4 * v] = x.x; kv[4 * v + 1] = x.y; kv[4 * v + 2] = x.z; kv[4 * v + 3] = x.w;
-      }
       float score = 0.0f;
       for (int h = 0; h < H_I; ++h) {
         const float* qh = s_q + h * d_I;
         float dot = 0.0f;
-        for (int dd = 0; dd < d_I; ++dd) dot = fmaf(qh[dd], kv[dd], dot);
+        for (int v = 0; v < d_I / 4; ++v) {
+          const float4 x = kp[v];
+          dot = fmaf(qh[4 * v], x.x, dot);
+          dot = fmaf(qh[4 * v + 1], x.y, dot);
+          dot = fmaf(qh[4 * v + 2], x.z, dot);
+          dot = fmaf(qh[4 * v + 3], x.w, dot);
+        }
         score = fmaf(s_q[16 * 64 + h], fmaxf(dot, 0.0f), score);
       }
       keys[e] = score_key(score);
@@ -114,7 +142,9 @@ __device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* key
   } else {
     const int lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
     const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q_idx) + qrow * d_I;
-    // A operands: row = head col (zero past H_I), k-slots 8g..8g+7.
+    // A operands: row = head col (zero past H_I), k-slots 8g..8g+7.  For d_I = 64
+    // the k-slots of the two products map to dims 16g..16g+7 and 16g+8..16g+15,
+    // so a lane reads 16 contiguous dims of its key.
     bf16x8_t qa0, qa1;
     {
       uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
@@ -137,90 +167,173 @@ __device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* key
     }
     const int64_t kb = ri.b * a.N_alloc + ri.lo;
     const int64_t ngroups = (n + 15) / 16;
-    for (int64_t gi = wid; gi < ngroups; gi += kWaves) {
-      const int64_t e = gi * 16 + col;
-      const bool valid = e < n;
-      uint4 k0 = make_uint4(0, 0, 0, 0), k1 = make_uint4(0, 0, 0, 0);
-      float ksc = 1.0f;
-      if (valid) {
-        if (KK == kKeyBF16) {
-          const bf16_t* kp = reinterpret_cast<const bf16_t*>(a.k_idx) + (kb + e) * d_I;
-          if (d_I == 64) {
-            k0 = *reinterpret_cast<const uint4*>(kp + 16 * g);
-            k1 = *reinterpret_cast<const uint4*>(kp + 16 * g + 8);
+    for (int64_t g0 = wid; g0 < ngroups; g0 += kWaves * kUnroll) {
+      uint4 k0[kUnroll], k1[kUnroll];
+      float ksc[kUnroll];
+      // Issue every load of this round first.
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t e = (g0 + int64_t(u) * kWaves) * 16 + col;
+        k0[u] = make_uint4(0, 0, 0, 0);
+        k1[u] = make_uint4(0, 0, 0, 0);
+        ksc[u] = 1.0f;
+        if (e < n) {
+          if (KK == kKeyBF16) {
+            const bf16_t* kp = reinterpret_cast<const bf16_t*>(a.k_idx) + (kb + e) * d_I;
+            if (d_I == 64) {
+              k0[u] = *reinterpret_cast<const uint4*>(kp + 16 * g);
+              k1[u] = *reinterpret_cast<const uint4*>(kp + 16 * g + 8);
+            } else {
+              k0[u] = *reinterpret_cast<const uint4*>(kp + 8 * g);
+            }
           } else {
-            k0 = *reinterpret_cast<const uint4*>(kp + 8 * g);
-          }
-        } else {
-          const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k_idx) + (kb + e) * d_I;
-          ksc = a.k_scale[kb + e];
-          if (d_I == 64) {
-            uint4 raw = *reinterpret_cast<const uint4*>(kp + 16 * g);
-            e4m3x4_to_bf16x4(raw.x, k0.x, k0.y);
-            e4m3x4_to_bf16x4(raw.y, k0.z, k0.w);
-            e4m3x4_to_bf16x4(raw.z, k1.x, k1.y);
-            e4m3x4_to_bf16x4(raw.w, k1.z, k1.w);
-          } else {
-            uint2 raw = *reinterpret_cast<const uint2*>(kp + 8 * g);
-            e4m3x4_to_bf16x4(raw.x, k0.x, k0.y);
-            e4m3x4_to_bf16x4(raw.y, k0.z, k0.w);
+            const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k_idx) + (kb + e) * d_I;
+            if (d_I == 64) {
+              k0[u] = *reinterpret_cast<const uint4*>(kp + 16 * g);
+            } else {
+              const uint2 r2 = *reinterpret_cast<const uint2*>(kp + 8 * g);
+              k0[u] = make_uint4(r2.x, r2.y, 0, 0);
+            }
+            ksc[u] = a.k_scale[kb + e];
           }
         }
       }
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = mfma16x16x32(qa0, u32x4_as_bf16x8(k0), acc);
-      if (d_I == 64) acc = mfma16x16x32(qa1, u32x4_as_bf16x8(k1), acc);
-      float part = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part = fmaf(wr[j], fmaxf(acc[j], 0.0f), part);
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if (KK == kKeyE4M3) part *= ksc;
-      if (valid && g == 0) keys[e] = score_key(part);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t e = (g0 + int64_t(u) * kWaves) * 16 + col;
+        uint4 b0 = k0[u], b1 = k1[u];
+        if (KK == kKeyE4M3) {
+          const uint4 raw = k0[u];
+          e4m3x4_to_bf16x4(raw.x, b0.x, b0.y);
+          e4m3x4_to_bf16x4(raw.y, b0.z, b0.w);
+          if (d_I == 64) {
+            e4m3x4_to_bf16x4(raw.z, b1.x, b1.y);
+            e4m3x4_to_bf16x4(raw.w, b1.z, b1.w);
+          }
+        }
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = mfma16x16x32(qa0, u32x4_as_bf16x8(b0), acc);
+        if (d_I == 64) acc = mfma16x16x32(qa1, u32x4_as_bf16x8(b1), acc);
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part = fmaf(wr[j], fmaxf(acc[j], 0.0f), part);
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (KK == kKeyE4M3) part *= ksc[u];
+        if (e < n && g == 0) keys[e] = score_key(part);
+      }
     }
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- radix selection
+//
+// Thresholds are found by MSB-first radix selection on 12-bit digits of the
+// 64-bit rank keys (counting in a 4096-bin LDS histogram).  Rank keys of real
+// entries are never 0, so 0 marks an empty register slot.
 
-// The need-th largest 64-bit rank key among n candidates whose top `fixed_bits`
-// bits equal `prefix` (callers guarantee that).  get(i) returns candidate i.
-// All threads call it; the result is uniform.
-template <typename Get>
-__device__ uint64_t kth_largest(int64_t n, int64_t need, uint64_t prefix, int fixed_bits, Get get,
-                                uint32_t* hist, uint32_t* s_misc) {
+constexpr int kDigitBits = 12;
+constexpr int kBins = 1 << kDigitBits;
+
+struct SelLds {
+  uint32_t scan[kWaves];
+  uint32_t misc[4];
+};
+
+// After the histogram of the current digit is complete: pick the digit that
+// holds the need-th largest key.  Returns (digit, keys above it, keys in it).
+__device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t nb, int64_t need, SelLds& S,
+                                           uint32_t& dstar, uint32_t& above, uint32_t& in_digit) {
   const int tid = threadIdx.x;
-  int hi_bit = 64 - fixed_bits;  // bits [0, hi_bit) still open
+  const uint32_t bpt = nb >= kThreads ? nb / kThreads : 1u;  // bins per thread
+  const uint32_t nthr = nb / bpt;
+  uint32_t local = 0;
+  if (uint32_t(tid) < nthr)
+    for (uint32_t j = 0; j < bpt; ++j) local += hist[nb - 1 - (tid * bpt + j)];
+  const uint32_t inc = block_inclusive_sum(local, S.scan);
+  const uint32_t ex = inc - local;
+  if (uint32_t(tid) < nthr && int64_t(ex) < need && int64_t(inc) >= need) {
+    uint32_t cum = ex;
+    for (uint32_t j = 0; j < bpt; ++j) {
+      const uint32_t dd = nb - 1 - (tid * bpt + j);
+      const uint32_t h = hist[dd];
+      if (int64_t(cum + h) >= need) {
+        S.misc[0] = dd;
+        S.misc[1] = cum;
+        S.misc[2] = h;
+        break;
+      }
+      cum += h;
+    }
+  }
+  __syncthreads();
+  dstar = S.misc[0];
+  above = S.misc[1];
+  in_digit = S.misc[2];
+  __syncthreads();
+}
+
+// Threshold T with exactly `need` keys >= T among the non-zero keys (1 <= need <=
+// their count; keys distinct).  Keys live in registers: KPT per thread.
+template <int KPT>
+__device__ uint64_t select_regs(const uint64_t (&v)[KPT], int64_t need, uint32_t* hist, SelLds& S) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0;
+  int hi_bit = 64;
   while (hi_bit > 0) {
-    const int width = hi_bit >= 8 ? 8 : hi_bit;
+    const int width = hi_bit >= kDigitBits ? kDigitBits : hi_bit;
     const int shift = hi_bit - width;
-    for (int x = tid; x < 256; x += kThreads) hist[x] = 0;
+    const uint32_t nb = 1u << width;
+    for (int x = tid; x < kBins; x += kThreads) hist[x] = 0;
+    __syncthreads();
+    const uint64_t hi_mask = (hi_bit >= 64) ? 0ull : (~0ull << hi_bit);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (v[u] != 0 && (v[u] & hi_mask) == prefix)
+        atomicAdd(&hist[uint32_t(v[u] >> shift) & (nb - 1u)], 1u);
+    __syncthreads();
+    uint32_t dstar, above, in_digit;
+    pick_digit(hist, nb, need, S, dstar, above, in_digit);
+    prefix |= uint64_t(dstar) << shift;
+    need -= int64_t(above);
+    hi_bit = shift;
+    if (int64_t(in_digit) == need) break;  // every key in this digit is selected
+  }
+  return prefix;  // remaining low bits zero
+}
+
+// The same selection over n keys produced by get(i) (used for long candidate lists).
+template <typename Get>
+__device__ uint64_t select_get(int64_t n, int64_t need, Get get, uint32_t* hist, SelLds& S) {
+  const int tid = threadIdx.x;
+  uint64_t prefix = 0;
+  int hi_bit = 64;
+  while (hi_bit > 0) {
+    const int width = hi_bit >= kDigitBits ? kDigitBits : hi_bit;
+    const int shift = hi_bit - width;
+    const uint32_t nb = 1u << width;
+    for (int x = tid; x < kBins; x += kThreads) hist[x] = 0;
     __syncthreads();
     const uint64_t hi_mask = (hi_bit >= 64) ? 0ull : (~0ull << hi_bit);
     for (int64_t i = tid; i < n; i += kThreads) {
-      uint64_t v = get(i);
-      if ((v & hi_mask) == (prefix & hi_mask))
-        atomicAdd(&hist[uint32_t(v >> shift) & ((1u << width) - 1u)], 1u);
+      const uint64_t v = get(i);
+      if ((v & hi_mask) == prefix) atomicAdd(&hist[uint32_t(v >> shift) & (nb - 1u)], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      int64_t cum = 0;
-      int dstar = 0;
-      for (int dd = (1 << width) - 1; dd >= 0; --dd) {
-        if (cum + hist[dd] >= need) { dstar = dd; break; }
-        cum += hist[dd];
-      }
-      s_misc[0] = uint32_t(dstar);
-      s_misc[1] = uint32_t(cum);
-    }
-    __syncthreads();
-    prefix |= uint64_t(s_misc[0]) << shift;
-    need -= int64_t(s_misc[1]);
+    uint32_t dstar, above, in_digit;
+    pick_digit(hist, nb, need, S, dstar, above, in_digit);
+    prefix |= uint64_t(dstar) << shift;
+    need -= int64_t(above);
     hi_bit = shift;
-    __syncthreads();
+    if (int64_t(in_digit) == need) break;
   }
   return prefix;
+}
+
+__device__ __forceinline__ void write_out(const IndexArgs& a, int64_t r, int64_t slot, uint64_t v) {
+  a.out_idx[r * a.top_k + slot] = int32_t(rank_key_idx(v));
+  if (a.out_score) a.out_score[r * a.top_k + slot] = key_score(uint32_t(v >> 32));
 }
 
 __device__ __forceinline__ void write_pads(const IndexArgs& a, int64_t r, int64_t from) {
@@ -230,19 +343,52 @@ __device__ __forceinline__ void write_pads(const IndexArgs& a, int64_t r, int64_
   }
 }
 
-struct LdsSel {
-  uint32_t keys[kMaxSlice];
-  uint32_t hist[kHistBins];
-  float q[16 * 64 + 16];
-  int wave[kWaves];
-  uint32_t misc[4];
-};
+// Emit the register keys >= T in element order (element x = tid + 256*u); dst(pos, v)
+// stores one.  Returns the count.
+template <int KPT, typename Dst>
+__device__ int64_t emit_regs(const uint64_t (&v)[KPT], uint64_t T, int64_t from, Dst dst, int* s_wave) {
+  int64_t done = from;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const bool win = v[u] != 0 && v[u] >= T;
+    int total;
+    const int pos = block_rank(win, s_wave, total);
+    if (win) dst(done + pos, v[u]);
+    done += total;
+  }
+  return done - from;
+}
 
-// ---------------------------------------------------------------- kernel 1
+template <typename Get, typename Dst>
+__device__ int64_t emit_get(int64_t n, uint64_t T, Get get, int64_t from, Dst dst, int* s_wave) {
+  int64_t done = from;
+  for (int64_t x0 = 0; x0 < n; x0 += kThreads) {
+    const int64_t x = x0 + threadIdx.x;
+    const uint64_t v = x < n ? get(x) : 0ull;
+    const bool win = x < n && v >= T;
+    int total;
+    const int pos = block_rank(win, s_wave, total);
+    if (win) dst(done + pos, v);
+    done += total;
+  }
+  return done - from;
+}
+
+constexpr int kKeysPerThread = kMaxSlice / kThreads;  // 16
+constexpr int kCandPerThread = 16;                    // last-WG register capacity
+
+struct LdsIdx {
+  uint32_t keys[kMaxSlice];  // slice keys, then the radix histogram (kBins == kMaxSlice)
+  float q[16 * 64 + 16];
+  SelLds sel;
+  int wave[kWaves];
+  uint32_t flag[4];
+};
+static_assert(kBins == kMaxSlice, "the key buffer doubles as the histogram");
 
 template <int KK>
-__global__ __launch_bounds__(kThreads) void idx_score_kernel(IndexArgs a, IndexPlan p, int64_t row0) {
-  __shared__ LdsSel L;
+__global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPlan p, int64_t row0) {
+  __shared__ LdsIdx L;
   const int64_t lr = blockIdx.x / p.slices;  // row within this launch
   const int64_t r = row0 + lr;
   const int64_t s = blockIdx.x % p.slices;
@@ -252,182 +398,93 @@ __global__ __launch_bounds__(kThreads) void idx_score_kernel(IndexArgs a, IndexP
   const int64_t n = ri.hi - ri.lo;
 
   score_slice<KK>(a, ri, L.keys, L.q);
+  const uint32_t base = uint32_t(ri.lo);
+  uint64_t v[kKeysPerThread];
+#pragma unroll
+  for (int u = 0; u < kKeysPerThread; ++u) {
+    const int64_t x = tid + int64_t(u) * kThreads;
+    v[u] = x < n ? rank_key(L.keys[x], base + uint32_t(x)) : 0ull;
+  }
+  __syncthreads();  // L.keys is the histogram from here on
+  auto out_dst = [&](int64_t pos, uint64_t val) { write_out(a, r, pos, val); };
 
-  if (ri.S == 1) {
-    // Whole row in this WG.
-    const int64_t kk = ri.kk;
-    if (kk < n) {
-      const uint32_t base = uint32_t(ri.lo);
-      auto get = [&](int64_t x) { return rank_key(L.keys[x], base + uint32_t(x)); };
-      const uint64_t kstar = kth_largest(n, kk, 0ull, 0, get, L.hist, L.misc);
-      int64_t done = 0;
-      for (int64_t x0 = 0; x0 < n; x0 += kThreads) {
-        const int64_t x = x0 + tid;
-        const bool win = x < n && get(x) >= kstar;
-        int total;
-        const int pos = block_rank(win, L.wave, total);
-        if (win) {
-          a.out_idx[r * a.top_k + done + pos] = int32_t(ri.lo + x);
-          if (a.out_score) a.out_score[r * a.top_k + done + pos] = key_score(L.keys[x]);
-        }
-        done += total;
-      }
-    } else {
-      for (int64_t x = tid; x < n; x += kThreads) {
-        a.out_idx[r * a.top_k + x] = int32_t(ri.lo + x);
-        if (a.out_score) a.out_score[r * a.top_k + x] = key_score(L.keys[x]);
-      }
+  if (ri.S == 1) {  // the whole row is in this WG
+    if (ri.kk > 0) {
+      const uint64_t T = (ri.kk < n) ? select_regs(v, ri.kk, L.keys, L.sel) : 1ull;
+      emit_regs(v, T, 0, out_dst, L.wave);
     }
-    write_pads(a, r, kk);
+    write_pads(a, r, ri.kk);
     return;
   }
 
-  // Multi-slice row: publish keys and histogram.
+  // ---- several slices: exact local top-kloc + certificate, handed over with
+  // device-scope stores.
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
   RowCtrl* ctrl = reinterpret_cast<RowCtrl*>(ws + kIndexCtrlOff) + lr;
-  uint32_t* ghist = reinterpret_cast<uint32_t*>(ws + kIndexHistOff) + lr * kHistBins;
-  uint32_t* gkeys = reinterpret_cast<uint32_t*>(ws + p.off_keys) + lr * a.N_alloc;
-  for (int x = tid; x < kHistBins; x += kThreads) L.hist[x] = 0;
-  __syncthreads();
-  for (int64_t x = tid; x < n; x += kThreads) {
-    const uint32_t k = L.keys[x];
-    gkeys[ri.lo + x] = k;
-    atomicAdd(&L.hist[k >> 20], 1u);
-  }
-  __syncthreads();
-  for (int x = tid; x < kHistBins; x += kThreads)
-    if (L.hist[x]) atomicAdd(&ghist[x], L.hist[x]);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) L.misc[0] = (atomicAdd(&ctrl->arrive1, 1u) == uint32_t(ri.S - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!L.misc[0]) return;
-  __threadfence();
-  // Last WG of the row: find the bin that holds the kk-th best key.
-  for (int x = tid; x < kHistBins; x += kThreads) {
-    L.hist[x] = __hip_atomic_load(&ghist[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ghist[x] = 0;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t cum = 0, bin = kHistBins;
-    const uint32_t kk = uint32_t(ri.kk);
-    if (kk > 0) {
-      for (int x = kHistBins - 1; x >= 0; --x) {
-        if (cum + L.hist[x] >= kk) { bin = uint32_t(x); break; }
-        cum += L.hist[x];
-      }
-    }
-    ctrl->bin = bin;
-    ctrl->above = cum;
-    ctrl->arrive1 = 0;
-  }
-}
+  uint64_t* cand = reinterpret_cast<uint64_t*>(ws + p.off_cand) + lr * a.N_alloc;
+  uint64_t* tau = reinterpret_cast<uint64_t*>(ws + p.off_tau) + lr * p.slices;
+  uint64_t* over = reinterpret_cast<uint64_t*>(ws + p.off_over) + lr * a.N_alloc;
+  const int64_t kl = n < ri.kloc ? n : ri.kloc;
+  const uint64_t Ts = (n > kl) ? select_regs(v, kl, L.keys, L.sel) : 1ull;
+  uint64_t* my_cand = cand + s * ri.kloc;
+  emit_regs(v, Ts, 0, [&](int64_t pos, uint64_t val) { store_dev(&my_cand[pos], val); }, L.wave);
+  if (tid == 0) store_dev(&tau[s], uint64_t(n > kl ? Ts : 0ull));  // dropped entries are all below it
+  if (!arrive_last(&ctrl->arrive, uint32_t(ri.S), L.flag)) return;
 
-// ---------------------------------------------------------------- kernel 2
-
-__global__ __launch_bounds__(kThreads) void idx_select_kernel(IndexArgs a, IndexPlan p, int64_t row0) {
-  __shared__ uint32_t hist[256];
-  __shared__ int s_wave[kWaves];
-  __shared__ uint32_t misc[4];
-  __shared__ int64_t s_pref_a[1025], s_pref_b[1025];
-  const int64_t lr = blockIdx.x / p.slices;
-  const int64_t r = row0 + lr;
-  const int64_t s = blockIdx.x % p.slices;
-  const RowInfo ri = row_info(a, p, r, s);
-  if (ri.S == 1 || s >= ri.S) return;
-  const int tid = threadIdx.x;
-  uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
-  RowCtrl* ctrl = reinterpret_cast<RowCtrl*>(ws + kIndexCtrlOff) + lr;
-  const uint32_t* gkeys = reinterpret_cast<const uint32_t*>(ws + p.off_keys) + lr * a.N_alloc;
-  uint32_t* stage_a = reinterpret_cast<uint32_t*>(ws + p.off_stage_a) + lr * a.N_alloc;
-  uint64_t* stage_b = reinterpret_cast<uint64_t*>(ws + p.off_stage_b) + lr * a.N_alloc;
-  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + p.off_counts) + lr * p.slices * 2;
-  const uint32_t bin = ctrl->bin;
-
-  int64_t na = 0, nb = 0;
-  for (int64_t x0 = ri.lo; x0 < ri.hi; x0 += kThreads) {
-    const int64_t j = x0 + tid;
-    const bool in = j < ri.hi;
-    const uint32_t k = in ? gkeys[j] : 0u;
-    const bool isa = in && (k >> 20) > bin;
-    const bool isb = in && (k >> 20) == bin;
-    int ta, tb;
-    const int pa = block_rank(isa, s_wave, ta);
-    const int pb = block_rank(isb, s_wave, tb);
-    if (isa) stage_a[ri.lo + na + pa] = uint32_t(j);
-    if (isb) stage_b[ri.lo + nb + pb] = rank_key(k, uint32_t(j));
-    na += ta;
-    nb += tb;
-  }
-  if (tid == 0) {
-    counts[2 * s] = uint32_t(na);
-    counts[2 * s + 1] = uint32_t(nb);
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) misc[0] = (atomicAdd(&ctrl->arrive2, 1u) == uint32_t(ri.S - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!misc[0]) return;
-  __threadfence();
-
-  // Last WG: concatenate the slices in order.
-  const int64_t S = ri.S;
-  if (tid == 0) {
-    int64_t ca = 0, cb = 0;
-    for (int64_t x = 0; x < S; ++x) {
-      s_pref_a[x] = ca;
-      s_pref_b[x] = cb;
-      ca += __hip_atomic_load(&counts[2 * x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      cb += __hip_atomic_load(&counts[2 * x + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ---- last WG of the row.  Slice x's candidates sit at cand[x*kloc ...]; every
+  // slice but the last holds exactly kloc of them.
+  const int64_t last_n = ri.c - (ri.S - 1) * p.slice;
+  const int64_t total = (ri.S - 1) * ri.kloc + (last_n < ri.kloc ? last_n : ri.kloc);
+  auto get_c = [&](int64_t g) { return load_dev(&cand[g]); };
+  const bool in_regs = total <= int64_t(kCandPerThread) * kThreads;
+  uint64_t c[kCandPerThread];
+  uint64_t T;
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < kCandPerThread; ++u) {
+      const int64_t g = tid + int64_t(u) * kThreads;
+      c[u] = g < total ? get_c(g) : 0ull;
     }
-    s_pref_a[S] = ca;
-    s_pref_b[S] = cb;
+    T = select_regs(c, ri.kk, L.keys, L.sel);
+  } else {
+    T = select_get(total, ri.kk, get_c, L.keys, L.sel);
   }
-  __syncthreads();
-  const int64_t tot_a = s_pref_a[S], tot_b = s_pref_b[S];
-  auto slice_of = [&](const int64_t* pref, int64_t g) {
-    int64_t lo = 0, hi = S - 1;  // last x with pref[x] <= g
-    while (lo < hi) {
-      int64_t mid = (lo + hi + 1) >> 1;
-      if (pref[mid] <= g) lo = mid; else hi = mid - 1;
+  // Certificate check: slice x may hold more winners iff its threshold is above T.
+  bool viol = false;
+  for (int64_t x = tid; x < ri.S; x += kThreads) viol |= load_dev(&tau[x]) > T;
+  if (!__syncthreads_or(viol)) {
+    if (in_regs) emit_regs(c, T, 0, out_dst, L.wave);
+    else emit_get(total, T, get_c, 0, out_dst, L.wave);
+    write_pads(a, r, ri.kk);
+    if (tid == 0) ctrl->arrive = 0;
+    return;
+  }
+  // Rare path: rescore every slice whose certificate is above T and add the
+  // entries it dropped that reach T, then select again over everything.
+  int64_t n_over = 0;
+  for (int64_t x = 0; x < ri.S; ++x) {
+    const uint64_t tx = load_dev(&tau[x]);
+    if (tx <= T) continue;
+    RowInfo rx = row_info(a, p, r, x);
+    score_slice<KK>(a, rx, L.keys, L.q);
+    const uint32_t bx = uint32_t(rx.lo);
+    const int64_t nx = rx.hi - rx.lo;
+    for (int64_t y0 = 0; y0 < nx; y0 += kThreads) {
+      const int64_t y = y0 + tid;
+      const uint64_t val = y < nx ? rank_key(L.keys[y], bx + uint32_t(y)) : 0ull;
+      const bool add = y < nx && val >= T && val < tx;
+      int cnt;
+      const int pos = block_rank(add, L.wave, cnt);
+      if (add) over[n_over + pos] = val;
+      n_over += cnt;
     }
-    return lo;
-  };
-  for (int64_t gidx = tid; gidx < tot_a; gidx += kThreads) {
-    const int64_t x = slice_of(s_pref_a, gidx);
-    const uint32_t j = stage_a[x * p.slice + (gidx - s_pref_a[x])];
-    a.out_idx[r * a.top_k + gidx] = int32_t(j);
-    if (a.out_score) a.out_score[r * a.top_k + gidx] = key_score(gkeys[j]);
+    __syncthreads();
   }
-  const int64_t need = ri.kk - tot_a;
-  if (need > 0) {
-    auto get = [&](int64_t gidx) {
-      const int64_t x = slice_of(s_pref_b, gidx);
-      return stage_b[x * p.slice + (gidx - s_pref_b[x])];
-    };
-    uint64_t kstar = 0;
-    if (need < tot_b) kstar = kth_largest(tot_b, need, uint64_t(bin) << 52, 12, get, hist, misc);
-    int64_t done = 0;
-    for (int64_t g0 = 0; g0 < tot_b; g0 += kThreads) {
-      const int64_t gidx = g0 + tid;
-      const uint64_t v = gidx < tot_b ? get(gidx) : 0ull;
-      const bool win = gidx < tot_b && v >= kstar;
-      int total;
-      const int pos = block_rank(win, s_wave, total);
-      if (win) {
-        a.out_idx[r * a.top_k + tot_a + done + pos] = int32_t(rank_key_idx(v));
-        if (a.out_score) a.out_score[r * a.top_k + tot_a + done + pos] = key_score(uint32_t(v >> 32));
-      }
-      done += total;
-    }
-  }
+  auto get_all = [&](int64_t g) { return g < total ? get_c(g) : over[g - total]; };
+  T = select_get(total + n_over, ri.kk, get_all, L.keys, L.sel);
+  emit_get(total + n_over, T, get_all, 0, out_dst, L.wave);
   write_pads(a, r, ri.kk);
-  if (tid == 0) {
-    ctrl->arrive2 = 0;
-    ctrl->bin = 0;
-    ctrl->above = 0;
-  }
+  if (tid == 0) ctrl->arrive = 0;
 }
 
 }  // namespace
@@ -454,10 +511,9 @@ IndexPlan plan_index(int B, int64_t T, int64_t N_alloc, int top_k) {
     return o;
   };
   const size_t R = size_t(p.chunk_rows);
-  p.off_keys = take(R * size_t(N_alloc) * 4);
-  p.off_stage_a = take(R * size_t(N_alloc) * 4);
-  p.off_stage_b = take(R * size_t(N_alloc) * 8);
-  p.off_counts = take(R * size_t(p.slices) * 8);
+  p.off_cand = take(R * size_t(N_alloc) * 8);
+  p.off_tau = take(R * size_t(p.slices) * 8);
+  p.off_over = take(R * size_t(N_alloc) * 8);
   p.ws_bytes = multi ? off : 0;
   return p;
 }
@@ -468,19 +524,15 @@ hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p) {
   for (int64_t row0 = 0; row0 < p.rows; row0 += p.chunk_rows) {
     const int64_t nr = (p.rows - row0) < p.chunk_rows ? (p.rows - row0) : p.chunk_rows;
     const dim3 grid(unsigned(nr * p.slices));
+    ProfScope prof("index_topk", a.stream);
     if (a.key_kind == kKeyF32)
-      hipLaunchKernelGGL(idx_score_kernel<kKeyF32>, grid, block, 0, a.stream, a, p, row0);
+      hipLaunchKernelGGL(idx_topk_kernel<kKeyF32>, grid, block, 0, a.stream, a, p, row0);
     else if (a.key_kind == kKeyBF16)
-      hipLaunchKernelGGL(idx_score_kernel<kKeyBF16>, grid, block, 0, a.stream, a, p, row0);
+      hipLaunchKernelGGL(idx_topk_kernel<kKeyBF16>, grid, block, 0, a.stream, a, p, row0);
     else
-      hipLaunchKernelGGL(idx_score_kernel<kKeyE4M3>, grid, block, 0, a.stream, a, p, row0);
+      hipLaunchKernelGGL(idx_topk_kernel<kKeyE4M3>, grid, block, 0, a.stream, a, p, row0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p.slices > 1) {
-      hipLaunchKernelGGL(idx_select_kernel, grid, block, 0, a.stream, a, p, row0);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
   }
   return hipSuccess;
 }

@@ -8,6 +8,19 @@
 
 namespace csa {
 
+// Brackets one kernel launch with HIP events when per-kernel timing is enabled
+// (csa_profile_enable); otherwise does nothing.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  void* start_;
+};
+
 struct CompressArgs {
   const void* x;
   bool x_bf16;
@@ -53,10 +66,9 @@ struct IndexArgs {
 // written before they are read, so any sequence of calls of any shapes may
 // share one workspace that was zero-filled once.
 constexpr size_t kHeaderBytes = size_t(2) << 20;
-constexpr size_t kAttendCtrlOff = 0;          // 256 rows x 16 B
-constexpr int64_t kAttendCtrlRows = 256;
-constexpr size_t kIndexCtrlOff = 8192;        // 64 rows x 16 B
-constexpr size_t kIndexHistOff = 16384;       // 64 rows x 16 KB
+constexpr size_t kAttendCtrlOff = 0;          // 1024 (row, head group) units x 16 B
+constexpr int64_t kAttendCtrlUnits = 1024;
+constexpr size_t kIndexCtrlOff = 16384;       // 64 rows x 16 B
 constexpr int64_t kIndexChunkRows = 64;       // rows per multi-slice launch
 
 // Slicing plan of the general (rows x slices) indexer path; shared by the
@@ -69,10 +81,9 @@ struct IndexPlan {
   int64_t chunk_rows;  // rows per launch pair when rows have several slices
   size_t ws_bytes;     // workspace bytes
   // data offsets (after the header); indexed by the row's position in its chunk
-  size_t off_keys, off_stage_a, off_stage_b, off_counts;
+  size_t off_cand, off_tau, off_over;
 };
 constexpr int64_t kMaxSlice = 4096;
-constexpr int kHistBins = 4096;  // top 12 bits of the score key
 IndexPlan plan_index(int B, int64_t T, int64_t N_alloc, int top_k);
 hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p);
 
@@ -106,12 +117,15 @@ struct AttendArgs {
 
 struct AttendPlan {
   int64_t rows;      // B * T
+  int64_t groups;    // head groups of 64 heads (one workgroup covers one group)
   int64_t slots;     // longest slot list (entries + window)
   int64_t per_split; // slots per split (multiple of the tile)
   int64_t splits;    // splits of the longest row
+  int64_t group_stride;  // block ids per head group (rows * splits rounded up to 8)
   size_t ws_bytes;
   size_t off_part, off_ml;  // data offsets (after the header)
 };
+constexpr int kAttendGroupHeads = 64;
 // max_entries: top_k for CSA, N_alloc for HCA.
 AttendPlan plan_attend(bool hca, int B, int64_t T, int H, int d, int64_t max_entries, int window);
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p);

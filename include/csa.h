@@ -192,6 +192,19 @@ csa_status_t hca_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const 
                         int64_t t0, int window, float scale, void* out, csa_dtype_t out_dt,
                         float* lse, void* workspace, size_t workspace_bytes, csa_stream_t stream);
 
+/*
+ * Per-kernel timing (diagnostics, not part of the method).  While enabled on the
+ * calling thread, every kernel the library enqueues from that thread is
+ * bracketed by two HIP events on its stream; the work itself is unchanged.
+ * csa_profile_report waits for the recorded events, writes a JSON object
+ * {"<kernel>": {"launches": n, "total_ms": t}, ...} into buf (truncated to n
+ * bytes, NUL-terminated), forgets the records, and returns the JSON length
+ * (-1 if an event query failed).  Do not enable it while capturing a graph.
+ * csa_profile_enable returns the previous setting.
+ */
+int csa_profile_enable(int on);
+int csa_profile_report(char* buf, size_t n);
+
 #ifdef __cplusplus
 }
 #endif

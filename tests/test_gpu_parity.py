@@ -153,6 +153,44 @@ def test_index_topk_exact_ties_go_to_lower_index():
     np.testing.assert_array_equal(np.sort(out[0, 0].cpu().numpy()), exp)
 
 
+@pytest.mark.parametrize("kind", ["bf16", "e4m3"])
+def test_index_topk_winners_concentrated_in_few_slices(kind):
+    """Entries 5000..5599 score far above the rest, so a few slices hold every
+    winner: their local candidate lists cannot cover them and the exact
+    fallback (rescoring those slices) must produce the true top-k."""
+    B, N, d_I, k = 2, 24000, 64, 512
+    r = gen("conc_k", (B, N, d_I), "f32", seed=11).numpy()
+    r[:, 5000:5600] *= 4.0
+    q = gen("conc_q", (B, 1, 8, d_I), "bf16", seed=12)
+    w = gen("conc_w", (B, 1, 8), "f32", seed=13).abs()
+    if kind == "e4m3":
+        codes, scale, k64 = formats.e4m3_quantize_rows(r)
+        kd, ks = torch.from_numpy(codes).to(DEV), torch.from_numpy(scale).to(DEV)
+    else:
+        k64 = formats.round_to_bf16(r.astype(np.float64))
+        kd, ks = to_dev_bf16(k64), None
+    out = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    sc = torch.empty((B, 1, k), device=DEV)
+    csa.csa_index_topk(q.to(DEV), w.to(DEV), kd, ks, 4 * N - 1, 4, k, out, sc)
+    torch.cuda.synchronize()
+    for b in range(B):
+        scores = method.index_scores(f64(q[b]), f64(w[b]), k64[b], 4 * N - 1, 4)
+        check_topk_rows(out[b].cpu().numpy(), sc[b].cpu().numpy(), scores, k)
+        assert (out[b, 0].cpu().numpy() >= 5000).mean() > 0.9
+
+
+def test_index_topk_all_scores_equal():
+    """Identical keys: every score ties, the winners are the lowest indices, all
+    inside the first slice."""
+    B, N, d_I, k = 1, 20000, 64, 700
+    keys = gen("eq_k", (1, 1, d_I), "bf16", seed=5).expand(B, N, d_I).contiguous()
+    q = gen("eq_q", (B, 1, 8, d_I), "bf16", seed=6)
+    out = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    csa.csa_index_topk(q.to(DEV), None, keys.to(DEV), None, 4 * N - 1, 4, k, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np.sort(out[0, 0].cpu().numpy()), np.arange(k))
+
+
 # ----------------------------------------------------------------------------- attention
 
 
@@ -188,7 +226,9 @@ ATTEND_CASES = [
     ("csa-f32", "f32", 1, 50, 8, 64, 1024, 4, 64, 128, 3000, "f32"),
     ("csa-f32-d32", "f32", 2, 9, 3, 32, 200, 4, 100, 7, 700, "f32"),
     ("csa-f32-decode", "f32", 2, 1, 8, 128, 3000, 4, 1024, 128, 4 * 3000 - 1, "f32"),
+    ("csa-decode-h80", "bf16", 3, 1, 80, 128, 3000, 4, 1024, 128, 4 * 3000 - 1, "f32"),
     ("hca-decode", "bf16", 2, 1, 128, 128, 2000, 128, 0, 128, 128 * 2000 - 1, "f32"),
+    ("hca-decode-b16", "bf16", 16, 1, 128, 128, 700, 128, 0, 128, 128 * 700 - 1, "f32"),
     ("hca-short", "bf16", 3, 1, 64, 128, 200, 128, 0, 128, 128 * 200 - 1, "bf16"),
     ("hca-prefill", "bf16", 1, 40, 64, 128, 10, 128, 0, 128, 300, "f32"),
     ("hca-f32", "f32", 1, 33, 8, 64, 32, 128, 0, 128, 4000, "f32"),
