@@ -273,11 +273,12 @@ def time_workload(name, seed, steps, warmup, graph=True):
 
 def summarize(res):
     alg, ms = res["alg"], res["ms_per_step"]
-    out = {"ms_per_step": round(ms, 6), "steps": res["steps"], "cache_cold_replicas": res["replicas"]}
+    out = {"ms_per_step": round(ms, 6), "steps": res["steps"], "cache_cold_replicas": res["replicas"],
+           "query_tokens_per_s": alg["queries"] / (ms * 1e-3)}
     if alg.get("bytes"):
         gbps = alg["bytes"] / (ms * 1e-3) / 1e9
-        out.update({"query_tokens_per_s": alg["queries"] / (ms * 1e-3), "hbm_gbps": round(gbps, 1),
-                    "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg["bytes"]})
+        out.update({"hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                    "alg_bytes": alg["bytes"]})
     tf = alg["flops"] / (ms * 1e-3) / 1e12
     out.update({"tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
                 "alg_flops": alg["flops"]})
@@ -455,8 +456,8 @@ def main():
         "config": {"workload": args.workload, "B": wl.B, "context": wl.n, "H": wl.H, "d": wl.d,
                    "H_I": wl.H_I, "d_I": wl.d_I, "m": wl.m, "top_k": wl.k, "window": wl.W,
                    "indexer_keys": wl.idx_key_dtype, "cache_cold_replicas": head["replicas"]},
-        "hbm_gbps": hs["hbm_gbps"],
-        "hbm_frac": hs["hbm_frac"],
+        "hbm_gbps": hs.get("hbm_gbps"),
+        "hbm_frac": hs.get("hbm_frac"),
         "roofline": roofline(head),
         "kernel_ms": hs["kernel_ms"],
         "legs": legs,

@@ -148,11 +148,10 @@ csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw,
 
 size_t csa_index_topk_workspace(int B, int64_t T, int H_I, int d_I, int64_t N_alloc, int top_k,
                                 csa_dtype_t k_dt) {
-  (void)H_I;
   (void)d_I;
-  (void)k_dt;
   if (B < 1 || T < 0 || N_alloc < 0) return 0;
-  return csa::plan_index(B, T, N_alloc, top_k).ws_bytes;
+  const int kind = k_dt == CSA_F32 ? csa::kKeyF32 : (k_dt == CSA_BF16 ? csa::kKeyBF16 : csa::kKeyE4M3);
+  return csa::plan_index(B, T, H_I, N_alloc, top_k, kind).ws_bytes;
 }
 
 csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w, const void* k_idx,
@@ -177,8 +176,10 @@ csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w,
   REQUIRE(t0 >= 0, CSA_E_SHAPE, "t0 < 0");
   REQUIRE(m >= 1, CSA_E_SHAPE, "m < 1");
   REQUIRE(top_k >= 1 && top_k <= 2048, CSA_E_SHAPE, "top_k=%d out of range [1, 2048]", top_k);
-  const csa::IndexPlan p = csa::plan_index(B, T, N_alloc, top_k);
-  REQUIRE(p.rows * p.slices <= kMaxGrid, CSA_E_SHAPE, "too many query rows");
+  const int kind = k_dt == CSA_F32 ? csa::kKeyF32 : (k_dt == CSA_BF16 ? csa::kKeyBF16 : csa::kKeyE4M3);
+  const csa::IndexPlan p = csa::plan_index(B, T, H_I, N_alloc, top_k, kind);
+  REQUIRE(p.prefill ? (T + csa::kPrefillQPB - 1) / csa::kPrefillQPB <= kMaxGrid
+                    : p.rows * p.slices <= kMaxGrid, CSA_E_SHAPE, "too many query rows");
   REQUIRE(p.ws_bytes == 0 || workspace != nullptr, CSA_E_WORKSPACE, "workspace is NULL");
   REQUIRE(workspace_bytes >= p.ws_bytes, CSA_E_WORKSPACE, "workspace has %zu bytes, needs %zu",
           workspace_bytes, p.ws_bytes);

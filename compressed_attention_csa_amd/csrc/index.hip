@@ -489,10 +489,17 @@ __global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPl
 
 }  // namespace
 
-IndexPlan plan_index(int B, int64_t T, int64_t N_alloc, int top_k) {
-  (void)top_k;
+IndexPlan plan_index(int B, int64_t T, int H_I, int64_t N_alloc, int top_k, int key_kind) {
   IndexPlan p{};
   p.rows = int64_t(B) * T;
+  if (prefill_path(T, H_I, key_kind) && N_alloc > 0) {
+    p.prefill = true;
+    p.cap = 4096;
+    if (p.cap < 2 * int64_t(top_k) + 256) p.cap = 2 * int64_t(top_k) + 256;
+    p.off_cand = kHeaderBytes;
+    p.ws_bytes = kHeaderBytes + size_t(p.rows) * size_t(p.cap) * 8;
+    return p;
+  }
   p.c_max = N_alloc;
   // Aim for about 512 workgroups over the chip (256 CUs), slices of 256..4096 entries.
   int64_t want = (p.rows > 0) ? (p.c_max * p.rows + 511) / 512 : 1;
@@ -520,6 +527,7 @@ IndexPlan plan_index(int B, int64_t T, int64_t N_alloc, int top_k) {
 
 hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p) {
   if (p.rows == 0) return hipSuccess;
+  if (p.prefill) return launch_index_prefill(a, p);
   const dim3 block(kThreads);
   for (int64_t row0 = 0; row0 < p.rows; row0 += p.chunk_rows) {
     const int64_t nr = (p.rows - row0) < p.chunk_rows ? (p.rows - row0) : p.chunk_rows;

@@ -73,7 +73,14 @@ constexpr int64_t kIndexChunkRows = 64;       // rows per multi-slice launch
 
 // Slicing plan of the general (rows x slices) indexer path; shared by the
 // workspace-size query and the launcher so both agree.
+// Prefill path (many query rows per sequence): one workgroup per 32 queries.
+constexpr int kPrefillQPW = 8;                        // queries per wave
+constexpr int kPrefillQPB = 4 * kPrefillQPW;          // queries per workgroup
+constexpr int64_t kPrefillMinT = 64;                  // rows per sequence to use it
+
 struct IndexPlan {
+  bool prefill;        // streaming top-k path (query-tiled)
+  int64_t cap;         // prefill: candidate buffer entries per query
   int64_t rows;        // B * T
   int64_t c_max;       // largest visible-entry count over the rows
   int64_t slice;       // entries per slice (multiple of 256, <= kMaxSlice)
@@ -84,8 +91,10 @@ struct IndexPlan {
   size_t off_cand, off_tau, off_over;
 };
 constexpr int64_t kMaxSlice = 4096;
-IndexPlan plan_index(int B, int64_t T, int64_t N_alloc, int top_k);
+IndexPlan plan_index(int B, int64_t T, int H_I, int64_t N_alloc, int top_k, int key_kind);
 hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p);
+bool prefill_path(int64_t T, int H_I, int key_kind);
+hipError_t launch_index_prefill(const IndexArgs& a, const IndexPlan& p);
 
 // ------------------------------------------------------------------ attention
 

@@ -110,6 +110,11 @@ INDEX_CASES = [
     ("bf16", 1, 9, 4, 32, 100, 0, 4, 16, True),                    # rows with 0..2 visible
     ("bf16", 1, 2, 8, 64, 1500, 4 * 1500 - 1, 4, 2048, True),      # k above visible count
     ("bf16", 2, 1, 16, 64, 12000, 4 * 12000 - 1, 4, 1, True),      # k = 1, 16 heads
+    ("bf16", 2, 100, 8, 64, 3000, 11900, 4, 256, True),            # prefill path (T >= 64)
+    ("e4m3", 1, 70, 8, 64, 40000, 4 * 40000 - 70, 4, 64, True),    # prefill, many compactions
+    ("bf16", 1, 130, 4, 32, 9000, 30000, 4, 512, False),           # prefill, d_I 32, ragged T
+    ("e4m3", 2, 64, 8, 32, 500, 0, 4, 100, True),                  # prefill, rows see 0..16
+    ("bf16", 1, 96, 8, 64, 20000, 4 * 20000 - 96, 4, 2048, True),  # prefill, k = 2048
     ("f32", 1, 40, 4, 32, 1024, 4000, 4, 64, True),                # fp32 path
     ("f32", 2, 1, 4, 64, 6000, 4 * 6000 - 1, 4, 200, True),        # fp32, many slices
 ]
