@@ -5,130 +5,206 @@
 // full score matrix (queries x entries) is far too large to materialise, so the
 // selection is fused into the scoring sweep.
 //
-// Work split.  A workgroup owns 32 query tokens of one sequence (8 per wave) and
-// sweeps every entry visible to any of them.  Entry keys are staged in LDS in
-// tiles of 128 (16-byte chunks XOR-swizzled by entry so the MFMA operand reads
-// are conflict-free) and shared by the four waves; the next tile is already in
-// registers while the current one is scored.
+// Work split.  A workgroup owns 32 query tokens of one sequence, 4 per wave over
+// 8 waves (two waves per SIMD, so one wave's matrix products overlap the other
+// wave's vector epilogue), and sweeps every entry visible to any of them.  Entry
+// keys are staged in LDS in tiles of 128 entries (16-byte chunks XOR-swizzled by
+// entry so the operand reads are conflict-free), double-buffered: while a tile
+// is scored, the next one is already in LDS and the one after is in flight in
+// registers.  All workgroups sweep the entries in the same order, so the
+// workgroups of one XCD mostly hit its L2 for the shared keys.
 //
-// MFMA layout.  16x16x32 bf16 products with entries as columns.  A wave's query
-// rows are arranged as tile pairs: tile A holds heads 0-3 and tile B heads 4-7
-// of the same 4 queries (row 4*q + h), so lane (g, col) receives all 8 head dots
-// of query g for entry col and forms sum_h w_h * ReLU(dot_h) without any
-// cross-lane exchange.
+// MFMA layout.  16x16x32 bf16 products with entries as columns.  A wave's 4
+// queries fill a tile pair: tile A holds heads 0-3 and tile B heads 4-7 of the
+// same 4 queries (row 4*q + h), so lane (g, col) receives all 8 head dots of
+// query g for entry col and forms sum_h w_h * ReLU(dot_h) without any
+// cross-lane exchange.  The products of the next 16 entries are issued before
+// the current ones are reduced.
 //
 // Exact top-k.  Each query keeps a candidate buffer in the workspace and a
-// threshold (a 64-bit rank key: score, then lower index first).  Entries whose
-// rank exceeds the threshold are appended with wave ballots, so the order is
-// deterministic.  When a buffer is nearly full, one wave-local histogram pass
-// raises the threshold to the lower edge of the bin holding the k-th best
-// candidate and compacts the buffer; everything dropped ranks below k
-// candidates already kept, so the final exact selection over the buffer gives
-// the exact top-k.
+// threshold tau (a 64-bit rank key: score, then lower index first).  A binary32
+// compare against tau's score screens every pair; only pairs that pass it build
+// their rank key and are appended with wave ballots, in entry order, to a small
+// LDS staging area (so the scoring loop issues no global stores, whose pending
+// completion would otherwise make every wait also drain the key prefetch).  A
+// staging area that cannot take another tile is drained to the buffer between
+// tiles.  When the buffer cannot take it, a histogram pass over the keys
+// relative to tau (bins spanning tau .. the largest key appended) and, if
+// needed, finer radix passes raise tau to a bin edge that keeps between k and
+// 5k/4 candidates, and the buffer is compacted in order.  Everything dropped ranks below at least k
+// candidates already kept, so the final exact selection over the buffer is the
+// exact top-k; the output lists the winners by increasing entry index.
 #include "common.hpp"
 #include "kernels.h"
 
 namespace csa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kWaves = kPrefillWaves;
+constexpr int kThreads = kWaves * kWave;
 constexpr int kTileE = 128;  // entries per LDS tile
-constexpr int kHBits = 11;   // histogram digit
+constexpr int kHBits = 10;   // histogram digit
 constexpr int kHBins = 1 << kHBits;
+constexpr int kBatch = 8;    // buffer keys per lane per batch of loads
+constexpr int kStage = 256;  // LDS staging slots per query
 
 struct LdsPrefill {
-  uint4 tile[kTileE * 8];        // up to 128 B per entry
-  float scale[kTileE];
+  uint4 tile[2][kTileE * 8];  // up to 128 B per entry, two buffers
+  float scale[2][kTileE];
   uint32_t hist[kWaves][kHBins];
-  uint32_t cnt[kWaves][kPrefillQPW];
+  uint64_t stg[kWaves][kPrefillQPW][kStage];  // appended keys not yet in the workspace
 };
 
-// Chunk position of chunk c of entry e (cpe chunks per entry, power of two).
-__device__ __forceinline__ int chunk_pos(int e, int c, int cpe) { return e * cpe + (c ^ (e & (cpe - 1))); }
+// LDS position (in 16-byte chunks) of chunk c of entry e, for cpe = 4 or 8
+// chunks per entry.  The chunk index is XORed with a function of the entry so
+// that 8 lanes reading one chunk of 8 consecutive entries, 16 lanes reading
+// one chunk of 16 consecutive entries, and 8 or 16 lanes writing consecutive
+// chunks all hit distinct 16-byte bank groups.
+__device__ __forceinline__ int chunk_pos(int e, int c, int cpe) {
+  const int h = cpe == 8 ? ((e & 7) ^ ((e >> 3) & 1)) : (((e >> 1) & 3) ^ ((e >> 3) & 1));
+  return e * cpe + (c ^ h);
+}
+
+// max(x, 0) as one integer max on the bit pattern: every negative binary32
+// (-0 included) has its sign bit set and maps to +0.  (fmaxf would add a NaN
+// quieting step per call.)
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+  const uint32_t lo = __shfl(uint32_t(v), src), hi = __shfl(uint32_t(v >> 32), src);
+  return (uint64_t(hi) << 32) | lo;
+}
 
 // ---------------------------------------------------------------- wave-local selection
+//
+// buf holds n rank keys of one query, written by this wave; the caller has
+// waited for its own stores to complete.
 
-// Radix threshold over the n keys of buf (one wave).  exact: the threshold T with
-// exactly `need` keys >= T.  Otherwise T may keep more: the search stops at the
-// first digit whose keys above-and-in fit in `keep_max`.  Returns T and sets kept.
-__device__ uint64_t wave_threshold(const uint64_t* buf, int n, int need, bool exact, int keep_max,
-                                   uint32_t* hist, int& kept) {
+// Histogram (in hist[0 .. kHBins)) of digit(v) over the keys of buf[0..n) with
+// v & mask == prefix; digit() must return a value below kHBins for those keys.
+template <typename Digit>
+__device__ void wave_hist(const uint64_t* buf, int n, uint64_t mask, uint64_t prefix, uint32_t* hist,
+                          Digit digit) {
   const int lane = threadIdx.x & 63;
-  uint64_t prefix = 0;
-  int hi_bit = 64, above_total = 0;
-  kept = n;
+  for (int x = lane; x < kHBins; x += kWave) hist[x] = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int x0 = 0; x0 < n; x0 += kWave * kBatch) {
+    uint64_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int x = x0 + u * kWave + lane;
+      v[u] = x < n ? buf[x] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int x = x0 + u * kWave + lane;
+      if (x < n && (v[u] & mask) == prefix) atomicAdd(&hist[digit(v[u]) & (kHBins - 1)], 1u);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Over bins [0, nb) taken from the top: the bin d where the count from the top
+// first reaches need; above = keys in bins above d, indig = keys in bin d.
+__device__ void wave_find(const uint32_t* hist, uint32_t nb, int need, uint32_t& dstar, uint32_t& above,
+                          uint32_t& indig) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t bpl = nb >= kWave ? nb / kWave : 1u;  // bins per lane, descending
+  uint32_t local = 0;
+  if (uint32_t(lane) * bpl < nb)
+    for (uint32_t j = 0; j < bpl; ++j) local += hist[nb - 1 - (lane * bpl + j)];
+  uint32_t inc = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  const uint32_t ex = inc - local;
+  uint32_t d = 0, ab = 0, in = 0;
+  bool mine = false;
+  if (uint32_t(lane) * bpl < nb && int(ex) < need && int(inc) >= need) {
+    uint32_t cum = ex;
+    for (uint32_t j = 0; j < bpl; ++j) {
+      const uint32_t dd = nb - 1 - (lane * bpl + j);
+      const uint32_t h = hist[dd];
+      if (int(cum + h) >= need) {
+        d = dd;
+        ab = cum;
+        in = h;
+        break;
+      }
+      cum += h;
+    }
+    mine = true;
+  }
+  const uint64_t who = __ballot(mine);
+  const int src = __ffsll((long long)who) - 1;
+  dstar = __shfl(d, src);
+  above = __shfl(ab, src);
+  indig = __shfl(in, src);
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Threshold T over the n keys of buf (1 <= need <= n) with kept = #(keys >= T)
+// >= need: exactly need if `exact`, else at most max(need, keep_max).  Every
+// key is > floor_key and has its upper half <= top_hi.  The first pass bins the
+// upper halves between floor_key's and top_hi; later passes refine 11 bits at
+// a time inside the bin that holds the need-th key.
+__device__ uint64_t wave_threshold(const uint64_t* buf, int n, int need, bool exact, int keep_max,
+                                   uint64_t floor_key, uint32_t top_hi, uint32_t* hist, int& kept) {
+  const uint32_t lo_hi = uint32_t(floor_key >> 32);
+  int sh = 0;
+  while ((top_hi >> sh) - (lo_hi >> sh) >= uint32_t(kHBins)) ++sh;
+  const uint32_t base = lo_hi >> sh;
+  wave_hist(buf, n, 0ull, 0ull, hist, [&](uint64_t v) { return int((uint32_t(v >> 32) >> sh) - base); });
+  uint32_t d, above, indig;
+  wave_find(hist, uint32_t(kHBins), need, d, above, indig);
+  int hi_bit = 32 + sh;
+  uint64_t prefix = uint64_t(base + d) << hi_bit;
+  need -= int(above);
+  int above_total = int(above);
+  kept = above_total + int(indig);
+  if (int(indig) == need || (!exact && kept <= keep_max)) return prefix;
   while (hi_bit > 0) {
     const int width = hi_bit >= kHBits ? kHBits : hi_bit;
     const int shift = hi_bit - width;
-    const uint32_t nb = 1u << width;
-    for (int x = lane; x < kHBins; x += kWave) hist[x] = 0;
-    __builtin_amdgcn_wave_barrier();
-    const uint64_t hi_mask = (hi_bit >= 64) ? 0ull : (~0ull << hi_bit);
-    for (int x = lane; x < n; x += kWave) {
-      const uint64_t v = buf[x];
-      if ((v & hi_mask) == prefix) atomicAdd(&hist[uint32_t(v >> shift) & (nb - 1u)], 1u);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // Bins in descending order, nb/64 per lane (at least one lane-bin when nb < 64).
-    const uint32_t bpl = nb >= kWave ? nb / kWave : 1u;
-    uint32_t local = 0;
-    if (uint32_t(lane) * bpl < nb)
-      for (uint32_t j = 0; j < bpl; ++j) local += hist[nb - 1 - (lane * bpl + j)];
-    uint32_t inc = local;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t t = __shfl_up(inc, o);
-      if (lane >= o) inc += t;
-    }
-    const uint32_t ex = inc - local;
-    uint32_t dstar = 0, above = 0, indig = 0;
-    bool mine = false;
-    if (uint32_t(lane) * bpl < nb && int(ex) < need && int(inc) >= need) {
-      uint32_t cum = ex;
-      for (uint32_t j = 0; j < bpl; ++j) {
-        const uint32_t dd = nb - 1 - (lane * bpl + j);
-        const uint32_t h = hist[dd];
-        if (int(cum + h) >= need) {
-          dstar = dd;
-          above = cum;
-          indig = h;
-          break;
-        }
-        cum += h;
-      }
-      mine = true;
-    }
-    const uint64_t who = __ballot(mine);
-    const int src = __ffsll((long long)who) - 1;
-    dstar = __shfl(dstar, src);
-    above = __shfl(above, src);
-    indig = __shfl(indig, src);
-    __builtin_amdgcn_wave_barrier();
-    prefix |= uint64_t(dstar) << shift;
+    const uint64_t mask = hi_bit >= 64 ? 0ull : (~0ull << hi_bit);
+    wave_hist(buf, n, mask, prefix, hist, [&](uint64_t v) { return int(uint32_t(v >> shift) & ((1u << width) - 1u)); });
+    wave_find(hist, 1u << width, need, d, above, indig);
+    prefix |= uint64_t(d) << shift;
     need -= int(above);
     above_total += int(above);
     hi_bit = shift;
     kept = above_total + int(indig);
-    if (int(indig) == need) break;
-    if (!exact && kept <= keep_max) break;
+    if (int(indig) == need || (!exact && kept <= keep_max)) break;
   }
   return prefix;
 }
 
 // Keep the keys >= T of buf[0..n) in order (in place); returns the new count.
+// Each batch is loaded whole before any of its keys is written back, and the
+// write position never passes the read position.
 __device__ int wave_compact(uint64_t* buf, int n, uint64_t T) {
   const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int out = 0;
-  for (int x0 = 0; x0 < n; x0 += kWave) {
-    const int x = x0 + lane;
-    const uint64_t v = x < n ? buf[x] : 0ull;
-    const bool keep = x < n && v >= T;
-    const uint64_t m = __ballot(keep);
-    const int pos = __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-    __builtin_amdgcn_wave_barrier();
-    if (keep) buf[out + pos] = v;
-    out += __popcll(m);
+  for (int x0 = 0; x0 < n; x0 += kWave * kBatch) {
+    uint64_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int x = x0 + u * kWave + lane;
+      v[u] = x < n ? buf[x] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int x = x0 + u * kWave + lane;
+      const bool keep = x < n && v[u] >= T;
+      const uint64_t m = __ballot(keep);
+      if (keep) buf[out + __popcll(m & below)] = v[u];
+      out += __popcll(m);
+    }
   }
   return out;
 }
@@ -139,25 +215,25 @@ template <int KK, int DI>
 __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, IndexPlan p) {
   __shared__ LdsPrefill L;
   constexpr int KB = (KK == kKeyE4M3) ? 1 : 2;  // key bytes per element
-  constexpr int CPE = DI * KB / 16;              // 16-byte chunks per entry
+  constexpr int CPG = DI * KB / 16;              // 16-byte chunks per entry in memory
+  constexpr int CPE = DI / 8;                    // 16-byte chunks per entry in LDS (bf16)
   constexpr int KSTEP = DI / 32;                 // 32-wide k-steps of one dot product
-  constexpr int LOADS = kTileE * CPE / kThreads; // chunks per thread per tile
+  constexpr int CHUNKS = kTileE * CPG;
+  constexpr int LOADS = (CHUNKS + kThreads - 1) / kThreads;  // chunks per thread per tile
+  constexpr int GROUPS = kTileE / 16;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
   const int64_t b = blockIdx.y;
   const int64_t i0 = int64_t(blockIdx.x) * kPrefillQPB;
   const int H_I = a.H_I;
   const int64_t rowbase = b * a.T;
+  const int64_t qw0 = i0 + kPrefillQPW * wid;  // this wave's first query
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  // ---- per-lane query state: pair pp covers queries i0 + 8*wid + 4*pp + (0..3)
-  bf16x8_t qa[2][2][KSTEP];  // [pair][head half][k-step]
-  float wv[2][8];
-  int64_t cq[2], iq[2];
-  uint64_t tau[2] = {0ull, 0ull};
-  const bf16_t* qbase = reinterpret_cast<const bf16_t*>(a.q_idx);
-#pragma unroll
-  for (int pp = 0; pp < 2; ++pp) {
-    // A operand row `col`: query col/4 of the pair, head 4*hf + col%4.
-    const int64_t qi = i0 + 8 * wid + 4 * pp + col / 4;
+  // ---- A operands: row `col` = query col/4 of the wave, head 4*hf + col%4.
+  bf16x8_t qa[2][KSTEP];
+  {
+    const int64_t qi = qw0 + col / 4;
+    const bf16_t* qbase = reinterpret_cast<const bf16_t*>(a.q_idx);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int h = 4 * hf + col % 4;
@@ -167,167 +243,241 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
       for (int ks = 0; ks < KSTEP; ++ks) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (ok) v = *reinterpret_cast<const uint4*>(qr + (DI == 64 ? 16 * g + 8 * ks : 8 * g));
-        qa[pp][hf][ks] = u32x4_as_bf16x8(v);
+        qa[hf][ks] = u32x4_as_bf16x8(v);
       }
     }
-    // Output side: lane (g, col) holds query 4*pp + g of this wave.
-    iq[pp] = i0 + 8 * wid + 4 * pp + g;
-    const bool valid = iq[pp] < a.T;
-    int64_t c = valid ? (a.t0 + iq[pp] + 1) / a.m : 0;
-    cq[pp] = c < a.N_alloc ? c : a.N_alloc;
-#pragma unroll
-    for (int h = 0; h < 8; ++h)
-      wv[pp][h] = (valid && h < H_I) ? (a.w ? a.w[(rowbase + iq[pp]) * H_I + h] : 1.0f) : 0.0f;
   }
-  if (lane < kPrefillQPW) L.cnt[wid][lane] = 0;
+  // ---- output side: the lanes of group g score query qw0 + g.
+  const int64_t iq = qw0 + g;
+  const bool qvalid = iq < a.T;
+  int cq = 0;  // entries visible to the query
+  if (qvalid) {
+    const int64_t c = (a.t0 + iq + 1) / a.m;
+    cq = int(c < a.N_alloc ? c : a.N_alloc);
+  }
+  const int need_l = cq < a.top_k ? cq : a.top_k;
+  float wv[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+    wv[h] = (qvalid && h < H_I) ? (a.w ? a.w[(rowbase + iq) * H_I + h] : 1.0f) : 0.0f;
+  uint64_t tau = 0ull;             // every key appended from now on is > tau
+  float tau_s = key_score(0u);     // screening score of tau (NaN: admits everything)
+  uint32_t top_hi = 0u;            // largest upper key half this lane appended
+  int cnt = 0;                     // keys in the query's workspace buffer
+  int scnt = 0;                    // keys staged in LDS for the query
 
   // Entries visible to the last query of this workgroup bound the sweep.
   const int64_t ilast = (i0 + kPrefillQPB < a.T ? i0 + kPrefillQPB : a.T) - 1;
-  int64_t cmax = (a.t0 + ilast + 1) / a.m;
-  if (cmax > a.N_alloc) cmax = a.N_alloc;
-  const int64_t ntiles = (cmax + kTileE - 1) / kTileE;
+  int64_t cmax64 = (a.t0 + ilast + 1) / a.m;
+  if (cmax64 > a.N_alloc) cmax64 = a.N_alloc;
+  const int cmax = int(cmax64);
+  const int ntiles = (cmax + kTileE - 1) / kTileE;
   uint64_t* bufs = reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(a.ws) + p.off_cand);
   const int cap = int(p.cap);
+  uint64_t* mystg = L.stg[wid][g];
 
   const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(a.k_idx) + b * a.N_alloc * int64_t(DI * KB);
-  uint4 pre[LOADS];
+  // Tile prefetch registers (at most two 16-byte chunks per thread).  Every
+  // thread always issues the same loads (entries past the last visible one read
+  // that entry again; their scores are never candidates), so the number of loads
+  // issued after any append store is fixed and the waits for those stores never
+  // have to drain the prefetch too.
+  static_assert(LOADS >= 1 && LOADS <= 2, "tile chunks per thread");
+  uint4 pre0 = make_uint4(0, 0, 0, 0), pre1 = make_uint4(0, 0, 0, 0);
   float psc = 1.0f;
-  auto fetch = [&](int64_t t) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int id = tid + u * kThreads, e = id / CPE, c = id % CPE;
-      const int64_t ge = t * kTileE + e;
-      pre[u] = ge < cmax ? *reinterpret_cast<const uint4*>(kbytes + ge * (DI * KB) + c * 16)
-                         : make_uint4(0, 0, 0, 0);
-    }
-    if (KK == kKeyE4M3 && tid < kTileE) {
-      const int64_t ge = t * kTileE + tid;
-      psc = ge < cmax ? a.k_scale[b * a.N_alloc + ge] : 1.0f;
+  const int id0 = tid % CHUNKS, id1 = (tid + kThreads) % CHUNKS;
+  auto chunk_ptr = [&](int t, int id) {
+    const int ge = min(t * kTileE + id / CPG, cmax - 1);
+    return reinterpret_cast<const uint4*>(kbytes + int64_t(ge) * (DI * KB) + (id % CPG) * 16);
+  };
+  auto fetch = [&](int t) {
+    pre0 = *chunk_ptr(t, id0);
+    if (LOADS > 1) pre1 = *chunk_ptr(t, id1);
+    if (KK == kKeyE4M3) psc = a.k_scale[b * a.N_alloc + min(t * kTileE + (tid & (kTileE - 1)), cmax - 1)];
+  };
+  // Writes the prefetched chunks to LDS buffer `buf`; fp8 keys are widened to
+  // bf16 here, once per workgroup, rather than by every wave that reads them.
+  auto put = [&](int buf, int id, const uint4& v) {
+    const int e = id / CPG, c = id % CPG;
+    if (KK == kKeyBF16) {
+      L.tile[buf][chunk_pos(e, c, CPE)] = v;
+    } else {
+      uint4 lo, hi;
+      e4m3x4_to_bf16x4(v.x, lo.x, lo.y);
+      e4m3x4_to_bf16x4(v.y, lo.z, lo.w);
+      e4m3x4_to_bf16x4(v.z, hi.x, hi.y);
+      e4m3x4_to_bf16x4(v.w, hi.z, hi.w);
+      L.tile[buf][chunk_pos(e, 2 * c, CPE)] = lo;
+      L.tile[buf][chunk_pos(e, 2 * c + 1, CPE)] = hi;
     }
   };
-  if (ntiles > 0) fetch(0);
+  auto stage = [&](int buf) {
+    if (tid < CHUNKS) put(buf, id0, pre0);
+    if (LOADS > 1 && tid + kThreads < CHUNKS) put(buf, id1, pre1);
+    if (KK == kKeyE4M3 && tid < kTileE) L.scale[buf][tid] = psc;
+  };
+  // B operands of entry group gi (16 entries) of LDS buffer `buf`: dims
+  // 16g..16g+15 (DI = 64) or 8g..8g+7 (DI = 32) of entry 16*gi + col.
+  auto operands = [&](int buf, int gi, uint4& b0, uint4& b1) {
+    const int e = gi * 16 + col;
+    if (DI == 64) {
+      b0 = L.tile[buf][chunk_pos(e, 2 * g, CPE)];
+      b1 = L.tile[buf][chunk_pos(e, 2 * g + 1, CPE)];
+    } else {
+      b0 = L.tile[buf][chunk_pos(e, g, CPE)];
+      b1 = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto products = [&](const uint4& b0, const uint4& b1, f32x4_t (&acc)[2]) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+      z = mfma16x16x32(qa[hf][0], u32x4_as_bf16x8(b0), z);
+      if (DI == 64) z = mfma16x16x32(qa[hf][KSTEP - 1], u32x4_as_bf16x8(b1), z);
+      acc[hf] = z;
+    }
+  };
 
-  for (int64_t t = 0; t < ntiles; ++t) {
+  // Moves the keys staged for query q of this wave into its workspace buffer.
+  // When they would not fit, the buffer is first compacted: tau rises to a bin
+  // edge that keeps between k and 5k/4 of its keys, and staged keys that do not
+  // exceed the new tau are dropped as well.
+  auto drain = [&](int q) {
+    const int ns = __builtin_amdgcn_readlane(scnt, 16 * q);
+    int n = __builtin_amdgcn_readlane(cnt, 16 * q);
+    uint64_t tq = shfl64(tau, 16 * q);
+    uint64_t* buf = bufs + (rowbase + qw0 + q) * cap;
+    if (n + ns > cap) {  // then n > cap - kStage >= 5k/4 >= need
+      uint32_t tp = top_hi;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int id = tid + u * kThreads, e = id / CPE, c = id % CPE;
-      L.tile[chunk_pos(e, c, CPE)] = pre[u];
-    }
-    if (KK == kKeyE4M3 && tid < kTileE) L.scale[tid] = psc;
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
-    const int64_t e0 = t * kTileE;
-    for (int gi = 0; gi < kTileE / 16; ++gi) {
-      const int e = gi * 16 + col;
-      const int64_t ge = e0 + e;
-      // B operands: dims 16g..16g+15 (DI = 64) or 8g..8g+7 (DI = 32) of entry e.
-      uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
-      if (KK == kKeyBF16) {
-        if (DI == 64) {
-          b0 = L.tile[chunk_pos(e, 2 * g, CPE)];
-          b1 = L.tile[chunk_pos(e, 2 * g + 1, CPE)];
-        } else {
-          b0 = L.tile[chunk_pos(e, g, CPE)];
-        }
-      } else {
-        if (DI == 64) {
-          const uint4 raw = L.tile[chunk_pos(e, g, CPE)];
-          e4m3x4_to_bf16x4(raw.x, b0.x, b0.y);
-          e4m3x4_to_bf16x4(raw.y, b0.z, b0.w);
-          e4m3x4_to_bf16x4(raw.z, b1.x, b1.y);
-          e4m3x4_to_bf16x4(raw.w, b1.z, b1.w);
-        } else {
-          const uint4 raw = L.tile[chunk_pos(e, g / 2, CPE)];
-          const uint32_t w0 = (g & 1) ? raw.z : raw.x, w1 = (g & 1) ? raw.w : raw.y;
-          e4m3x4_to_bf16x4(w0, b0.x, b0.y);
-          e4m3x4_to_bf16x4(w1, b0.z, b0.w);
-        }
-      }
-      const float sc = (KK == kKeyE4M3) ? L.scale[e] : 1.0f;
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        f32x4_t acc[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-          z = mfma16x16x32(qa[pp][hf][0], u32x4_as_bf16x8(b0), z);
-          if (DI == 64) z = mfma16x16x32(qa[pp][hf][KSTEP - 1], u32x4_as_bf16x8(b1), z);
-          acc[hf] = z;
-        }
-        float s = 0.0f;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) s = fmaf(wv[pp][4 * hf + j], fmaxf(acc[hf][j], 0.0f), s);
-        if (KK == kKeyE4M3) s *= sc;
-        const uint64_t rk = rank_key(score_key(s), uint32_t(ge));
-        const bool cand = ge < cq[pp] && rk > tau[pp];
-        const uint64_t m = __ballot(cand);
-        if (m) {  // rare after the first tiles
-          const uint32_t mg = uint32_t(m >> (16 * g)) & 0xffffu;
-          const int q = 4 * pp + g;
-          const int base = int(L.cnt[wid][q]);
-          __builtin_amdgcn_wave_barrier();
-          if (cand) {
-            const int pos = __popc(mg & ((1u << col) - 1u));
-            bufs[(rowbase + iq[pp]) * cap + base + pos] = rk;
-          }
-          if (col == 0) L.cnt[wid][q] = uint32_t(base + __popc(mg));
-          __builtin_amdgcn_wave_barrier();
-        }
-      }
-    }
-    // Raise thresholds of queries whose buffers are nearly full.
-#pragma unroll 1
-    for (int q = 0; q < kPrefillQPW; ++q) {
-      const int n = int(L.cnt[wid][q]);
-      if (n <= cap - kTileE) continue;
-      const int pp = q / 4, gq = q % 4;
-      const int64_t qi = i0 + 8 * wid + q;
-      int64_t cqq = (a.t0 + qi + 1) / a.m;
-      if (cqq > a.N_alloc) cqq = a.N_alloc;
-      const int need = int(cqq < a.top_k ? cqq : a.top_k);
-      uint64_t* buf = bufs + (rowbase + qi) * cap;
-      wait_mem();
+      for (int o = 8; o > 0; o >>= 1) tp = max(tp, __shfl_xor(tp, o));
+      tp = __shfl(tp, 16 * q);
+      const int need = __shfl(need_l, 16 * q);
       int kept;
-      const uint64_t T = wave_threshold(buf, n, need, false, cap / 2, L.hist[wid], kept);
-      const int m2 = wave_compact(buf, n, T);
-      wait_mem();
-      if (lane == 0) L.cnt[wid][q] = uint32_t(m2);
-      if (g == gq && T > tau[pp]) tau[pp] = T;
-      __builtin_amdgcn_wave_barrier();
+      const uint64_t T = wave_threshold(buf, n, need, false, need + need / 4, tq, tp, L.hist[wid], kept);
+      n = wave_compact(buf, n, T);
+      tq = T > tq ? T : tq;
     }
+    const uint64_t* st = L.stg[wid][q];
+    for (int x0 = 0; x0 < ns; x0 += kWave) {
+      const int x = x0 + lane;
+      const uint64_t v = x < ns ? st[x] : 0ull;
+      const bool keep = x < ns && v > tq;
+      const uint64_t m = __ballot(keep);
+      if (keep) buf[n + __popcll(m & below)] = v;
+      n += __popcll(m);
+    }
+    wait_mem();  // the buffer is complete before it is read again
+    if (g == q) {
+      cnt = n;
+      scnt = 0;
+      if (tq > tau) {
+        tau = tq;
+        tau_s = key_score(uint32_t(tq >> 32));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  if (ntiles > 0) {
+    fetch(0);
+    stage(0);
+    fetch(ntiles > 1 ? 1 : 0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const int e0 = t * kTileE;
+    // Tile t+1 (loaded during the previous tile) goes to the other buffer, which
+    // every wave finished reading before the last barrier; tile t+2 then stays
+    // in flight for the whole of this tile.
+    if (t + 1 < ntiles) stage(cur ^ 1);
+    fetch(t + 2 < ntiles ? t + 2 : ntiles - 1);
+    // All B operands of the tile are read up front, so the LDS latency is paid
+    // once per tile rather than once per group.
+    uint4 bo0[GROUPS], bo1[GROUPS];
+#pragma unroll
+    for (int gi = 0; gi < GROUPS; ++gi) operands(cur, gi, bo0[gi], bo1[gi]);
+    f32x4_t acc[2], nxt[2];
+    products(bo0[0], bo1[0], acc);
+#pragma unroll
+    for (int gi = 0; gi < GROUPS; ++gi) {
+      if (gi + 1 < GROUPS) products(bo0[gi + 1], bo1[gi + 1], nxt);
+      const int e = gi * 16 + col;
+      float s = 0.0f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * hf + j], relu(acc[hf][j]), s);
+      if (KK == kKeyE4M3) s *= L.scale[cur][e];
+      const int ge = e0 + e;
+      const bool screen = ge < cq && !(s < tau_s);
+      if (__ballot(screen)) {
+        const uint64_t rk = rank_key(score_key(s), uint32_t(ge));
+        const bool cand = screen && rk > tau;
+        const uint64_t m = __ballot(cand);
+        const uint32_t mg = uint32_t(m >> (16 * g)) & 0xffffu;
+        if (cand) {
+          mystg[scnt + __popc(mg & uint32_t(below >> (16 * g)))] = rk;
+          const uint32_t hk = uint32_t(rk >> 32);
+          top_hi = hk > top_hi ? hk : top_hi;
+        }
+        scnt += __popc(mg);
+      }
+      if (gi + 1 < GROUPS) {
+        acc[0] = nxt[0];
+        acc[1] = nxt[1];
+      }
+    }
+    // Staging areas that cannot take another tile are drained.
+#pragma unroll 1
+    for (int q = 0; q < kPrefillQPW; ++q)
+      if (__builtin_amdgcn_readlane(scnt, 16 * q) > kStage - kTileE) drain(q);
     __syncthreads();
   }
+#pragma unroll 1
+  for (int q = 0; q < kPrefillQPW; ++q)
+    if (__builtin_amdgcn_readlane(scnt, 16 * q) > 0) drain(q);
 
-  // ---- final exact selection per query of this wave
+  // ---- final exact selection for each query of this wave
+  uint32_t grp_top = top_hi;
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) grp_top = max(grp_top, __shfl_xor(grp_top, o));
 #pragma unroll 1
   for (int q = 0; q < kPrefillQPW; ++q) {
-    const int64_t qi = i0 + 8 * wid + q;
+    const int64_t qi = qw0 + q;
     if (qi >= a.T) break;
-    int64_t cqq = (a.t0 + qi + 1) / a.m;
-    if (cqq > a.N_alloc) cqq = a.N_alloc;
-    const int need = int(cqq < a.top_k ? cqq : a.top_k);
-    const int n = int(L.cnt[wid][q]);
-    uint64_t* buf = bufs + (rowbase + qi) * cap;
+    const int n = __builtin_amdgcn_readlane(cnt, 16 * q);
+    const int need = __shfl(need_l, 16 * q);
+    const uint64_t tq = shfl64(tau, 16 * q);
+    const uint32_t tp = __shfl(grp_top, 16 * q);
+    const uint64_t* buf = bufs + (rowbase + qi) * cap;
     const int64_t orow = (rowbase + qi) * a.top_k;
-    wait_mem();
     int kept = 0;
-    uint64_t T = 1ull;
-    if (need > 0 && need < n) T = wave_threshold(buf, n, need, true, 0, L.hist[wid], kept);
+    uint64_t T = 1ull;  // every rank key is >= 1
+    if (need > 0 && need < n) T = wave_threshold(buf, n, need, true, 0, tq, tp, L.hist[wid], kept);
     int out = 0;
     if (need > 0) {
-      for (int x0 = 0; x0 < n; x0 += kWave) {
-        const int x = x0 + lane;
-        const uint64_t v = x < n ? buf[x] : 0ull;
-        const bool win = x < n && v >= T;
-        const uint64_t mm = __ballot(win);
-        const int pos = __popcll(mm & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-        if (win) {
-          a.out_idx[orow + out + pos] = int32_t(rank_key_idx(v));
-          if (a.out_score) a.out_score[orow + out + pos] = key_score(uint32_t(v >> 32));
+      for (int x0 = 0; x0 < n; x0 += kWave * kBatch) {
+        uint64_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int x = x0 + u * kWave + lane;
+          v[u] = x < n ? buf[x] : 0ull;
         }
-        out += __popcll(mm);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int x = x0 + u * kWave + lane;
+          const bool win = x < n && v[u] >= T;
+          const uint64_t mm = __ballot(win);
+          const int pos = out + __popcll(mm & below);
+          if (win) {
+            a.out_idx[orow + pos] = int32_t(rank_key_idx(v[u]));
+            if (a.out_score) a.out_score[orow + pos] = key_score(uint32_t(v[u] >> 32));
+          }
+          out += __popcll(mm);
+        }
       }
     }
     for (int x = out + lane; x < a.top_k; x += kWave) {

@@ -74,8 +74,9 @@ constexpr int64_t kIndexChunkRows = 64;       // rows per multi-slice launch
 // Slicing plan of the general (rows x slices) indexer path; shared by the
 // workspace-size query and the launcher so both agree.
 // Prefill path (many query rows per sequence): one workgroup per 32 queries.
-constexpr int kPrefillQPW = 8;                        // queries per wave
-constexpr int kPrefillQPB = 4 * kPrefillQPW;          // queries per workgroup
+constexpr int kPrefillQPW = 4;                        // queries per wave
+constexpr int kPrefillWaves = 8;                      // waves per workgroup
+constexpr int kPrefillQPB = kPrefillWaves * kPrefillQPW;  // queries per workgroup
 constexpr int64_t kPrefillMinT = 64;                  // rows per sequence to use it
 
 struct IndexPlan {
