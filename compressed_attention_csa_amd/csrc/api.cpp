@@ -7,6 +7,8 @@
 #include <string>
 
 #include "csa.h"
+
+#include <algorithm>
 #include "kernels.h"
 
 namespace {
@@ -199,13 +201,15 @@ csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w,
 
 size_t csa_attend_workspace(int B, int64_t T, int H, int d, int top_k, int window) {
   if (B < 1 || T < 0 || H < 1 || d < 1 || top_k < 0 || window < 0) return 0;
-  return csa::plan_attend(false, B, T, H, d, top_k, window).ws_bytes;
+  return std::max(csa::plan_attend(true, B, T, H, d, top_k, window).ws_bytes,
+                  csa::plan_attend(false, B, T, H, d, top_k, window).ws_bytes);
 }
 
 size_t hca_attend_workspace(int B, int64_t T, int H, int d, int64_t N_alloc, int m_heavy, int window) {
   (void)m_heavy;
   if (B < 1 || T < 0 || H < 1 || d < 1 || N_alloc < 0 || window < 0) return 0;
-  return csa::plan_attend(true, B, T, H, d, N_alloc, window).ws_bytes;
+  return std::max(csa::plan_attend(true, B, T, H, d, N_alloc, window).ws_bytes,
+                  csa::plan_attend(false, B, T, H, d, N_alloc, window).ws_bytes);
 }
 
 static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const void* k_cmp,
@@ -223,8 +227,8 @@ static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const v
     REQUIRE(idx == nullptr || aligned16(idx), CSA_E_ALIGN, "idx is not 16-byte aligned");
   }
   const csa::AttendPlan p =
-      csa::plan_attend(hca, B, T, H, d, hca ? N_alloc : int64_t(top_k), window);
-  REQUIRE(p.groups * p.group_stride <= kMaxGrid, CSA_E_SHAPE, "too many query rows");
+      csa::plan_attend(dt == CSA_BF16, B, T, H, d, hca ? N_alloc : int64_t(top_k), window);
+  REQUIRE(csa::attend_grid(p, dt == CSA_BF16) <= kMaxGrid, CSA_E_SHAPE, "too many query rows");
   REQUIRE(p.ws_bytes == 0 || workspace != nullptr, CSA_E_WORKSPACE, "workspace is NULL");
   REQUIRE(workspace_bytes >= p.ws_bytes, CSA_E_WORKSPACE, "workspace has %zu bytes, needs %zu",
           workspace_bytes, p.ws_bytes);

@@ -174,195 +174,335 @@ __device__ __forceinline__ bool decode_block(const AttendPlan& p, int64_t& hg, i
 }
 
 // ---------------------------------------------------------------- bf16 MFMA kernel
+//
+// One workgroup = one (row, split) and every head of the row: wave w owns heads
+// 16w .. 16w+15, so each K/V row is read from memory once per split.  Tiles of
+// 32 slots go through two LDS buffers; SETS further tiles are always in flight
+// in registers (about 64 KB per workgroup), enough to cover memory latency in
+// decode, where a split is a few tiles long.  Loads are issued unconditionally
+// (dead slots read the query row instead), so the compiler's wait counts stay
+// exact and no wait drains the prefetch.
+
+constexpr int kTB = 32;           // slots per tile
+constexpr int kMaxTable = 3072;   // selected-entry slots of one CSA split (top_k + window bound)
 
 template <int D>
-struct LdsBF16 {
-  bf16_t k[kTile][D + 8];   // row-major K tile (padded rows)
-  bf16_t vt[D][kTile + 8];  // transposed V tile
-  uint32_t live[kTile];
-  uint32_t flag[4];
-  MergeLds merge;
+struct LdsB {
+  uint4 k[2][kTB * D / 8];  // K rows, 16-byte chunks swizzled for row-wise reads
+  uint4 v[2][kTB * D / 8];  // V rows, swizzled for transposing reads
+  uint32_t live[2][kTB];
+  int32_t src[kMaxTable];   // selected compressed entry of each CSA slot of the split, -1 if skipped
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
-  __shared__ LdsBF16<D> L;
-  int64_t hg, r, s;
-  if (!decode_block(p, hg, r, s)) return;
+// K chunk position: 16 lanes reading one chunk of 16 consecutive rows, and 16
+// lanes writing one row, hit distinct 16-byte bank groups.
+template <int CPR>
+__device__ __forceinline__ int k_pos(int sl, int ch) {
+  if (CPR == 16) return sl * 16 + (ch ^ (sl & 15));
+  return sl * 8 + (ch ^ ((sl & 7) ^ ((sl >> 3) & 1)));
+}
+// V chunk position: the transposing read of 4 consecutive rows x 2 adjacent
+// chunks by 16 lanes hits distinct 8-byte bank pairs.
+template <int CPR>
+__device__ __forceinline__ int v_pos(int sl, int ch) {
+  return sl * CPR + (ch ^ (2 * (sl & 3)));
+}
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
+  constexpr int kT = NW * 64;
+  constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  constexpr int CT = kTB * CPR;                  // chunks per tensor per tile
+  constexpr int CPT = CT >= kT ? CT / kT : 1;    // chunks per thread per tensor per tile
+  constexpr int SETS = CPT >= 4 ? 2 : 4;         // tiles in flight in registers
+  constexpr int KS = D / 32;                     // k-steps of the QK product
+  constexpr int DVT = D / 16;                    // 16-column tiles of the output
+  __shared__ LdsB<D> L;
+  const int64_t r = blockIdx.x / p.splits, s = blockIdx.x % p.splits;
   const RowSlots x = row_slots(a, p, r, s);
   if (s >= x.S) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
   const int H = a.H;
-  const int h_begin = int(hg) * kAttendGroupHeads;
-  const int nh = (H - h_begin) < kAttendGroupHeads ? (H - h_begin) : kAttendGroupHeads;
-  const int h0 = h_begin + wid * 16;  // this wave's 16 heads
-  const bool has = wid * 16 < nh;
-  constexpr int KS = D / 32;   // k-steps of the QK product
-  constexpr int DVT = D / 16;  // 16-column tiles of the output
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
-  constexpr int NCH = kTile * CPR / kThreads;  // chunks per thread per tensor
+  const int h0 = wid * 16;  // this wave's 16 heads
+  const bool has = h0 < H;
+  const int64_t nsel = a.hca ? x.c : int64_t(a.top_k);
 
-  bf16x8_t qb[KS];
+  // Selected entries of this split (CSA), checked against visibility once.
+  if (!a.hca) {
+    const int64_t e_end = x.hi < nsel ? x.hi : nsel;
+    for (int64_t sl = x.lo + tid; sl < e_end; sl += kT) {
+      const int32_t j = a.idx[x.r * a.top_k + sl];
+      L.src[sl - x.lo] = (j >= 0 && j < x.c) ? j : -1;
+    }
+  }
+
   const bf16_t* qrow = reinterpret_cast<const bf16_t*>(a.q) + r * int64_t(H) * D;
+  bf16x8_t qb[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
     uint4 v = make_uint4(0, 0, 0, 0);
     if (has) v = *reinterpret_cast<const uint4*>(qrow + (h0 + col) * D + 32 * kk + 8 * g);
     qb[kk] = u32x4_as_bf16x8(v);
   }
+  __syncthreads();
+
+  const bf16_t* kc = reinterpret_cast<const bf16_t*>(a.k_cmp) + x.b * a.N_alloc * D;
+  const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.v_cmp) + x.b * a.N_alloc * D;
+  const bf16_t* kr = reinterpret_cast<const bf16_t*>(a.k_raw) + (x.b * a.n_raw - a.raw_base) * D;
+  const bf16_t* vr = reinterpret_cast<const bf16_t*>(a.v_raw) + (x.b * a.n_raw - a.raw_base) * D;
+  // Registers of one tile in flight (vectors rather than arrays, so that they
+  // stay in registers).
+  typedef uint32_t chunks_t __attribute__((ext_vector_type(4 * CPT)));
+  struct Pre {
+    chunks_t k, v;
+    uint32_t lv;
+  };
+  // Loads tile t of the split (slots beyond the split or skipped read the query row).
+  auto fetch = [&](Pre& P, int t) __attribute__((always_inline)) {
+    const int64_t t0 = x.lo + int64_t(t) * kTB;
+    uint32_t lv = 0;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int id = (tid + c * kT) % CT, sl = id / CPR, ch = id % CPR;
+      const int64_t slot = t0 + sl;
+      const bf16_t* kp = qrow;
+      const bf16_t* vp = qrow;
+      bool live = false;
+      if (slot < x.hi) {
+        if (slot < nsel) {
+          int64_t j = slot;
+          if (!a.hca) j = L.src[slot - x.lo];
+          if (j >= 0) {
+            kp = kc + j * D;
+            vp = vc + j * D;
+            live = true;
+          }
+        } else {
+          const int64_t pos = x.wstart + (slot - nsel);
+          kp = kr + pos * D;
+          vp = vr + pos * D;
+          live = true;
+        }
+      }
+      const uint4 kw = *reinterpret_cast<const uint4*>(kp + ch * 8);
+      const uint4 vw = *reinterpret_cast<const uint4*>(vp + ch * 8);
+      P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y; P.k[4 * c + 2] = kw.z; P.k[4 * c + 3] = kw.w;
+      P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y; P.v[4 * c + 2] = vw.z; P.v[4 * c + 3] = vw.w;
+      lv |= uint32_t(live) << c;
+    }
+    P.lv = lv;
+  };
+  auto stage = [&](const Pre& P, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int id = tid + c * kT, sl = (id % CT) / CPR, ch = id % CPR;
+      if (id < CT) {
+        L.k[buf][k_pos<CPR>(sl, ch)] = make_uint4(P.k[4 * c], P.k[4 * c + 1], P.k[4 * c + 2], P.k[4 * c + 3]);
+        L.v[buf][v_pos<CPR>(sl, ch)] = make_uint4(P.v[4 * c], P.v[4 * c + 1], P.v[4 * c + 2], P.v[4 * c + 3]);
+        if (ch == 0) L.live[buf][sl] = (P.lv >> c) & 1u;
+      }
+    }
+  };
+
   const float sl2 = a.scale * kLog2e;
   f32x4_t o[DVT];
 #pragma unroll
   for (int v = 0; v < DVT; ++v) o[v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float mrun = -INFINITY, lpart = 0.0f;
 
-  const bf16_t* kc = reinterpret_cast<const bf16_t*>(a.k_cmp);
-  const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.v_cmp);
-  const bf16_t* kr = reinterpret_cast<const bf16_t*>(a.k_raw);
-  const bf16_t* vr = reinterpret_cast<const bf16_t*>(a.v_raw);
-  uint4 pk[NCH], pv[NCH];
-  bool plive[NCH];
-  auto fetch = [&](int64_t t0) {
+  // S^T = K Q^T (lane: head h0 + col, slots 16cg + 4g + j), online softmax in
+  // log2 units, then O^T += V^T P^T with P as a bf16 hi + lo pair.
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    f32x4_t sc[2];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int id = tid + c * kThreads, sl = id / CPR, ch = id % CPR;
-      const int64_t slot = t0 + sl;
-      pk[c] = make_uint4(0, 0, 0, 0);
-      pv[c] = make_uint4(0, 0, 0, 0);
-      plive[c] = false;
-      if (slot < x.hi) {
-        bool cmp;
-        const int64_t off = slot_offset(a, x, slot, cmp);
-        if (off >= 0) {
-          plive[c] = true;
-          pk[c] = *reinterpret_cast<const uint4*>((cmp ? kc : kr) + off + ch * 8);
-          pv[c] = *reinterpret_cast<const uint4*>((cmp ? vc : vr) + off + ch * 8);
-        }
+    for (int cg = 0; cg < 2; ++cg) {
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 kv = L.k[buf][k_pos<CPR>(cg * 16 + col, 4 * kk + g)];
+        acc = mfma16x16x32(u32x4_as_bf16x8(kv), qb[kk], acc);
       }
+      sc[cg] = acc;
     }
-  };
-  auto stash = [&]() {
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int id = tid + c * kThreads, sl = id / CPR, ch = id % CPR;
-      *reinterpret_cast<uint4*>(&L.k[sl][ch * 8]) = pk[c];
-      const uint32_t w4[4] = {pv[c].x, pv[c].y, pv[c].z, pv[c].w};
+    for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        L.vt[ch * 8 + 2 * i][sl] = bf16_t(w4[i] & 0xffffu);
-        L.vt[ch * 8 + 2 * i + 1][sl] = bf16_t(w4[i] >> 16);
+      for (int j = 0; j < 4; ++j) {
+        const float v = L.live[buf][cg * 16 + 4 * g + j] ? sc[cg][j] * sl2 : -INFINITY;
+        sc[cg][j] = v;
+        tmax = fmaxf(tmax, v);
       }
-      if (ch == 0) L.live[sl] = plive[c] ? 1u : 0u;
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(mrun, tmax);
+    const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun - mnew);
+    mrun = mnew;
+    float psum = 0.0f;
+    uint32_t phi[4], plo[4];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const float p0 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j] - mnew);
+        const float p1 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j + 1] - mnew);
+        psum += p0 + p1;
+        const bf16_t h0b = f32_to_bf16(p0), h1b = f32_to_bf16(p1);
+        const bf16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0b));
+        const bf16_t l1 = f32_to_bf16(p1 - bf16_to_f32(h1b));
+        phi[cg * 2 + j / 2] = uint32_t(h0b) | (uint32_t(h1b) << 16);
+        plo[cg * 2 + j / 2] = uint32_t(l0) | (uint32_t(l1) << 16);
+      }
+    lpart = lpart * corr + psum;
+    const bf16x8_t pb_hi = u32x4_as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
+    const bf16x8_t pb_lo = u32x4_as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
+    // A operand of V^T: lane (g, col) needs V[slot][16v + col] for the slots
+    // 4g..4g+3 and 16+4g..16+4g+3; a transposing read of 4 rows returns them.
+    const int vr0 = 4 * g + col / 4, half = col & 1;
+#pragma unroll
+    for (int v = 0; v < DVT; ++v) {
+      const int ch = 2 * v + (col & 3) / 2;
+      const short* b0 = reinterpret_cast<const short*>(&L.v[buf][v_pos<CPR>(vr0, ch)]) + 4 * half;
+      const short* b1 = reinterpret_cast<const short*>(&L.v[buf][v_pos<CPR>(vr0 + 16, ch)]) + 4 * half;
+      const v4s_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b0));
+      const v4s_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b1));
+      uint4 w;
+      __builtin_memcpy(&w.x, &t0, 8);
+      __builtin_memcpy(&w.z, &t1, 8);
+      const bf16x8_t va = u32x4_as_bf16x8(w);
+      f32x4_t acc = o[v];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] *= corr;
+      acc = mfma16x16x32(va, pb_hi, acc);
+      acc = mfma16x16x32(va, pb_lo, acc);
+      o[v] = acc;
     }
   };
 
-  if (x.lo < x.hi) fetch(x.lo);
-  for (int64_t t0 = x.lo; t0 < x.hi; t0 += kTile) {
-    stash();
+  const int nt = int((x.hi - x.lo + kTB - 1) / kTB);
+  // Tile t goes to buffer t&1, last read for tile t-2: every wave passed the
+  // barrier of tile t-1 only after finishing that.  Tiles past the split are
+  // staged and fetched like the others (from the query row) so that every
+  // thread issues the same loads; only their math is skipped.
+  auto step = [&](Pre& P, int t) __attribute__((always_inline)) {
+    stage(P, t & 1);
     __syncthreads();
-    if (t0 + kTile < x.hi) fetch(t0 + kTile);  // next tile in flight during the math
-    if (has) {
-      f32x4_t sc[2];
-#pragma unroll
-      for (int cg = 0; cg < 2; ++cg) {
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(&L.k[cg * 16 + col][32 * kk + 8 * g]);
-          acc = mfma16x16x32(u32x4_as_bf16x8(kv), qb[kk], acc);
-        }
-        sc[cg] = acc;
-      }
-      // Online softmax in log2 units; lane holds head h0 + col and 8 slots.
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int cg = 0; cg < 2; ++cg)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v = L.live[cg * 16 + 4 * g + j] ? sc[cg][j] * sl2 : -INFINITY;
-          sc[cg][j] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(mrun, tmax);
-      const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun - mnew);
-      mrun = mnew;
-      float psum = 0.0f;
-      uint32_t phi[4], plo[4];
-#pragma unroll
-      for (int cg = 0; cg < 2; ++cg)
-#pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          const float p0 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j] - mnew);
-          const float p1 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j + 1] - mnew);
-          psum += p0 + p1;
-          const bf16_t h0b = f32_to_bf16(p0), h1b = f32_to_bf16(p1);
-          const bf16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0b));
-          const bf16_t l1 = f32_to_bf16(p1 - bf16_to_f32(h1b));
-          phi[cg * 2 + j / 2] = uint32_t(h0b) | (uint32_t(h1b) << 16);
-          plo[cg * 2 + j / 2] = uint32_t(l0) | (uint32_t(l1) << 16);
-        }
-      lpart = lpart * corr + psum;
-      const bf16x8_t pb_hi = u32x4_as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
-      const bf16x8_t pb_lo = u32x4_as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
-#pragma unroll
-      for (int v = 0; v < DVT; ++v) {
-        f32x4_t acc = o[v];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] *= corr;
-        const uint2 a0 = *reinterpret_cast<const uint2*>(&L.vt[v * 16 + col][4 * g]);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(&L.vt[v * 16 + col][16 + 4 * g]);
-        const bf16x8_t va = u32x4_as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
-        acc = mfma16x16x32(va, pb_hi, acc);
-        acc = mfma16x16x32(va, pb_lo, acc);
-        o[v] = acc;
-      }
+    fetch(P, t + SETS);
+    if (has && t < nt) compute(t & 1);
+  };
+  Pre P0, P1, P2, P3;
+  fetch(P0, 0);
+  fetch(P1, 1);
+  if (SETS == 4) {
+    fetch(P2, 2);
+    fetch(P3, 3);
+  }
+  for (int t0 = 0; t0 < nt; t0 += SETS) {
+    step(P0, t0);
+    step(P1, t0 + 1);
+    if (SETS == 4) {
+      step(P2, t0 + 2);
+      step(P3, t0 + 3);
     }
-    __syncthreads();
   }
 
   // Per-head totals; lane (g, col) holds head h0 + col, columns 16v + 4g + j.
   float lt = lpart;
   lt += __shfl_xor(lt, 16);
   lt += __shfl_xor(lt, 32);
+  if (!has) return;
   const int h = h0 + col;
   if (x.S == 1) {
-    if (has) {
-      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
-      for (int v = 0; v < DVT; ++v) {
-        const int64_t oi = (r * H + h) * int64_t(D) + v * 16 + 4 * g;
-        if (a.out_bf16) {
-          uint32_t w0 = uint32_t(f32_to_bf16(o[v][0] * inv)) | (uint32_t(f32_to_bf16(o[v][1] * inv)) << 16);
-          uint32_t w1 = uint32_t(f32_to_bf16(o[v][2] * inv)) | (uint32_t(f32_to_bf16(o[v][3] * inv)) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + oi) = make_uint2(w0, w1);
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) =
-              make_float4(o[v][0] * inv, o[v][1] * inv, o[v][2] * inv, o[v][3] * inv);
-        }
+    for (int v = 0; v < DVT; ++v) {
+      const int64_t oi = (r * H + h) * int64_t(D) + v * 16 + 4 * g;
+      if (a.out_bf16) {
+        uint32_t w0 = uint32_t(f32_to_bf16(o[v][0] * inv)) | (uint32_t(f32_to_bf16(o[v][1] * inv)) << 16);
+        uint32_t w1 = uint32_t(f32_to_bf16(o[v][2] * inv)) | (uint32_t(f32_to_bf16(o[v][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + oi) = make_uint2(w0, w1);
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) =
+            make_float4(o[v][0] * inv, o[v][1] * inv, o[v][2] * inv, o[v][3] * inv);
       }
-      if (a.lse && g == 0) a.lse[r * H + h] = lt > 0.0f ? (mrun + log2f(lt)) * kLn2 : -INFINITY;
     }
+    if (a.lse && g == 0) a.lse[r * H + h] = lt > 0.0f ? (mrun + log2f(lt)) * kLn2 : -INFINITY;
     return;
   }
-  const int64_t unit = hg * p.rows + r;
-  const int nhs = H < kAttendGroupHeads ? H : kAttendGroupHeads;  // partial stride per group
+  // Partials for the merge kernel: un-normalised O, running max (log2 units), sum.
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
-  float* part = reinterpret_cast<float*>(ws + p.off_part) + (unit * p.splits + s) * int64_t(nhs) * D;
-  float* ml = reinterpret_cast<float*>(ws + p.off_ml) + (unit * p.splits + s) * int64_t(nhs) * 2;
-  if (has) {
-    const int hl = wid * 16 + col;
+  float* part = reinterpret_cast<float*>(ws + p.off_part) + ((r * p.splits + s) * H + h) * int64_t(D);
+  float* ml = reinterpret_cast<float*>(ws + p.off_ml) + ((r * p.splits + s) * H + h) * 2;
 #pragma unroll
-    for (int v = 0; v < DVT; ++v)
+  for (int v = 0; v < DVT; ++v)
+    *reinterpret_cast<float4*>(part + v * 16 + 4 * g) = make_float4(o[v][0], o[v][1], o[v][2], o[v][3]);
+  if (g == 0) *reinterpret_cast<float2*>(ml) = make_float2(mrun, lt);
+}
+
+// Log-sum-exp merge of the split partials of one row and 16 heads.
+template <int D>
+__global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, AttendPlan p) {
+  __shared__ float f[kMaxSplits][16];
+  __shared__ float lse_s[16];
+  const int hgs = (a.H + 15) / 16;
+  const int64_t r = blockIdx.x / hgs;
+  const int h_begin = int(blockIdx.x % hgs) * 16;
+  const RowSlots x = row_slots(a, p, r, 0);
+  if (x.S <= 1) return;  // written directly by the attention kernel
+  const int64_t S = x.S;
+  const int H = a.H, tid = threadIdx.x;
+  const int nh = (H - h_begin) < 16 ? (H - h_begin) : 16;
+  const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
+  const float* part = reinterpret_cast<const float*>(ws + p.off_part) + r * p.splits * int64_t(H) * D;
+  const float* ml = reinterpret_cast<const float*>(ws + p.off_ml) + r * p.splits * int64_t(H) * 2;
+  if (tid < nh) {
+    const int h = h_begin + tid;
+    float mx = -INFINITY;
+    for (int64_t s = 0; s < S; ++s) mx = fmaxf(mx, ml[(s * H + h) * 2]);
+    float Lsum = 0.0f;
+    if (mx != -INFINITY)
+      for (int64_t s = 0; s < S; ++s) Lsum = fmaf(exp2f(ml[(s * H + h) * 2] - mx), ml[(s * H + h) * 2 + 1], Lsum);
+    const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+    for (int64_t s = 0; s < S; ++s)
+      f[s][tid] = (mx == -INFINITY) ? 0.0f : exp2f(ml[(s * H + h) * 2] - mx) * inv;
+    lse_s[tid] = Lsum > 0.0f ? (mx + log2f(Lsum)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  constexpr int cpr = D / 4;  // float4 chunks per head
+  for (int c = tid; c < nh * cpr; c += 256) {
+    const int hl = c / cpr, cc = (c % cpr) * 4;
+    const float* src = part + int64_t(h_begin + hl) * D + cc;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    int64_t s = 0;
+    for (; s + 4 <= S; s += 4) {
+      float4 v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) store_dev(part + int64_t(hl) * D + v * 16 + 4 * g + j, o[v][j]);
-    if (g == 0) {
-      store_dev(&ml[hl * 2], mrun);
-      store_dev(&ml[hl * 2 + 1], lt);
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(src + (s + u) * H * int64_t(D));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = f[s + u][hl];
+        acc.x = fmaf(w, v[u].x, acc.x); acc.y = fmaf(w, v[u].y, acc.y);
+        acc.z = fmaf(w, v[u].z, acc.z); acc.w = fmaf(w, v[u].w, acc.w);
+      }
+    }
+    for (; s < S; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(src + s * H * int64_t(D));
+      const float w = f[s][hl];
+      acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+    }
+    const int64_t oi = (r * H + h_begin + hl) * int64_t(D) + cc;
+    if (a.out_bf16) {
+      const uint32_t w0 = uint32_t(f32_to_bf16(acc.x)) | (uint32_t(f32_to_bf16(acc.y)) << 16);
+      const uint32_t w1 = uint32_t(f32_to_bf16(acc.z)) | (uint32_t(f32_to_bf16(acc.w)) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + oi) = make_uint2(w0, w1);
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) = acc;
     }
   }
-  finish_split(a, p, x, unit, h_begin, nh, nhs, L.flag, L.merge);
+  if (a.lse && tid < nh) a.lse[r * H + h_begin + tid] = lse_s[tid];
 }
 
 // ---------------------------------------------------------------- fp32 kernel
@@ -506,14 +646,43 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
 
 }  // namespace
 
-AttendPlan plan_attend(bool hca, int B, int64_t T, int H, int d, int64_t max_entries, int window) {
-  (void)hca;
+AttendPlan plan_attend(bool bf16, int B, int64_t T, int H, int d, int64_t max_entries, int window) {
   AttendPlan p{};
   p.rows = int64_t(B) * T;
-  p.groups = (H + kAttendGroupHeads - 1) / kAttendGroupHeads;
   p.slots = max_entries + window;
-  const int64_t tile = 64;  // multiple of both tile sizes
-  // Split rows until there are about 256 workgroups, keeping >= 2 tiles of 64 per split.
+  size_t off = kHeaderBytes;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  if (bf16) {
+    // Every head of a row in one workgroup; split the slots until there are
+    // about 256 workgroups, keeping at least 4 tiles of 32 per split.
+    p.groups = 1;
+    int64_t splits = 1;
+    if (p.rows > 0 && p.rows < 256) {
+      splits = (256 + p.rows - 1) / p.rows;
+      const int64_t max_splits = (p.slots + 4 * kTB - 1) / (4 * kTB);
+      if (splits > max_splits) splits = max_splits;
+      if (splits > kMaxSplits) splits = kMaxSplits;
+      if (splits < 1) splits = 1;
+    }
+    int64_t per = (p.slots + splits - 1) / splits;
+    per = ((per + kTB - 1) / kTB) * kTB;
+    if (per < kTB) per = kTB;
+    p.per_split = per;
+    p.splits = (p.slots + per - 1) / per;
+    if (p.splits < 1) p.splits = 1;
+    p.group_stride = p.rows * p.splits;
+    p.off_part = take(size_t(p.rows * p.splits) * size_t(H) * size_t(d) * 4);
+    p.off_ml = take(size_t(p.rows * p.splits) * size_t(H) * 2 * 4);
+    p.ws_bytes = p.splits > 1 ? off : 0;
+    return p;
+  }
+  p.groups = (H + kAttendGroupHeads - 1) / kAttendGroupHeads;
+  const int64_t tile = 64;  // fp32 tile
+  // Split rows until there are about 256 workgroups, keeping >= 2 tiles per split.
   const int64_t units = p.rows * p.groups;
   int64_t splits = 1;
   if (units > 0 && units <= kAttendCtrlUnits) {
@@ -530,29 +699,38 @@ AttendPlan plan_attend(bool hca, int B, int64_t T, int H, int d, int64_t max_ent
   p.splits = (p.slots + per - 1) / per;
   if (p.splits < 1) p.splits = 1;
   p.group_stride = ((p.rows * p.splits + 7) / 8) * 8;
-  size_t off = kHeaderBytes;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off += (bytes + 255) & ~size_t(255);
-    return o;
-  };
-  const bool multi = p.splits > 1;
   const size_t U = size_t(units);
   const size_t nh = size_t(H < kAttendGroupHeads ? H : kAttendGroupHeads);
   p.off_part = take(U * size_t(p.splits) * nh * d * 4);
   p.off_ml = take(U * size_t(p.splits) * nh * 2 * 4);
-  p.ws_bytes = multi ? off : 0;
+  p.ws_bytes = p.splits > 1 ? off : 0;
   return p;
+}
+
+int64_t attend_grid(const AttendPlan& p, bool bf16) {
+  return bf16 ? p.rows * p.splits : p.groups * p.group_stride;
+}
+
+template <int D>
+static void launch_bf16(const AttendArgs& a, const AttendPlan& p) {
+  const dim3 grid(unsigned(p.rows * p.splits));
+  const int nw = (a.H + 15) / 16;
+  if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2>), grid, dim3(128), 0, a.stream, a, p);
+  else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4>), grid, dim3(256), 0, a.stream, a, p);
+  else hipLaunchKernelGGL((attend_bf16_kernel<D, 8>), grid, dim3(512), 0, a.stream, a, p);
+  if (p.splits > 1)
+    hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(unsigned(p.rows * ((a.H + 15) / 16))), dim3(256), 0,
+                       a.stream, a, p);
 }
 
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p) {
   if (p.rows == 0) return hipSuccess;
-  dim3 grid(unsigned(p.groups * p.group_stride)), block(kThreads);
   ProfScope prof(a.hca ? "hca_attend" : "csa_attend", a.stream);
   if (a.bf16) {
-    if (a.d == 128) hipLaunchKernelGGL(attend_bf16_kernel<128>, grid, block, 0, a.stream, a, p);
-    else hipLaunchKernelGGL(attend_bf16_kernel<64>, grid, block, 0, a.stream, a, p);
+    if (a.d == 128) launch_bf16<128>(a, p);
+    else launch_bf16<64>(a, p);
   } else {
+    dim3 grid(unsigned(p.groups * p.group_stride)), block(kThreads);
     if (a.d == 128) hipLaunchKernelGGL(attend_f32_kernel<128>, grid, block, 0, a.stream, a, p);
     else if (a.d == 64) hipLaunchKernelGGL(attend_f32_kernel<64>, grid, block, 0, a.stream, a, p);
     else hipLaunchKernelGGL(attend_f32_kernel<32>, grid, block, 0, a.stream, a, p);

@@ -127,7 +127,7 @@ struct AttendArgs {
 
 struct AttendPlan {
   int64_t rows;      // B * T
-  int64_t groups;    // head groups of 64 heads (one workgroup covers one group)
+  int64_t groups;    // head groups (bf16: 1, all heads; fp32: groups of 64 heads)
   int64_t slots;     // longest slot list (entries + window)
   int64_t per_split; // slots per split (multiple of the tile)
   int64_t splits;    // splits of the longest row
@@ -136,8 +136,10 @@ struct AttendPlan {
   size_t off_part, off_ml;  // data offsets (after the header)
 };
 constexpr int kAttendGroupHeads = 64;
-// max_entries: top_k for CSA, N_alloc for HCA.
-AttendPlan plan_attend(bool hca, int B, int64_t T, int H, int d, int64_t max_entries, int window);
+// max_entries: top_k for CSA, N_alloc for HCA.  The bf16 and fp32 kernels split
+// the work differently; the workspace query takes the larger of the two.
+AttendPlan plan_attend(bool bf16, int B, int64_t T, int H, int d, int64_t max_entries, int window);
+int64_t attend_grid(const AttendPlan& p, bool bf16);
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p);
 
 }  // namespace csa
