@@ -43,16 +43,16 @@ __device__ __forceinline__ RowSlots row_slots(const AttendArgs& a, const AttendP
                                               int64_t s) {
   RowSlots x;
   x.r = r;
-  x.b = r / a.T;
-  x.t = a.t0 + r % a.T;
-  int64_t c = (x.t + 1) / a.m;
+  x.b = div64(r, a.T);
+  x.t = a.t0 + (r - x.b * a.T);
+  int64_t c = div64(x.t + 1, a.m);
   x.c = c < a.N_alloc ? c : a.N_alloc;
   int64_t ws = x.t - a.window + 1;
   x.wstart = ws > 0 ? ws : 0;
   x.wn = x.t - x.wstart + 1;
   if (a.window == 0) x.wn = 0;
   x.L = (a.hca ? x.c : int64_t(a.top_k)) + x.wn;
-  int64_t S = (x.L + p.per_split - 1) / p.per_split;
+  int64_t S = div64(x.L + p.per_split - 1, p.per_split);
   x.S = S < 1 ? 1 : S;
   x.lo = s * p.per_split;
   int64_t hi = x.lo + p.per_split;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
   constexpr int KS = D / 32;                     // k-steps of the QK product
   constexpr int DVT = D / 16;                    // 16-column tiles of the output
   __shared__ LdsB<D> L;
-  const int64_t r = blockIdx.x / p.splits, s = blockIdx.x % p.splits;
+  const int64_t r = div64(blockIdx.x, p.splits), s = blockIdx.x - r * p.splits;
   const RowSlots x = row_slots(a, p, r, s);
   if (s >= x.S) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
@@ -338,7 +338,9 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float mnew = fmaxf(mrun, tmax);
-    const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun - mnew);
+    // With no live slot yet everything below is zero: subtract 0 instead of -inf.
+    const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
+    const float corr = exp2f(mrun - msafe);
     mrun = mnew;
     float psum = 0.0f;
     uint32_t phi[4], plo[4];
@@ -346,16 +348,17 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
     for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
-        const float p0 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j] - mnew);
-        const float p1 = (mnew == -INFINITY) ? 0.0f : exp2f(sc[cg][j + 1] - mnew);
-        psum += p0 + p1;
-        const bf16_t h0b = f32_to_bf16(p0), h1b = f32_to_bf16(p1);
-        const bf16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0b));
-        const bf16_t l1 = f32_to_bf16(p1 - bf16_to_f32(h1b));
-        phi[cg * 2 + j / 2] = uint32_t(h0b) | (uint32_t(h1b) << 16);
-        plo[cg * 2 + j / 2] = uint32_t(l0) | (uint32_t(l1) << 16);
+        const f32x2_t pp = {exp2f(sc[cg][j] - msafe), exp2f(sc[cg][j + 1] - msafe)};
+        psum += pp[0] + pp[1];
+        // P = hi + lo, both bf16 (hardware round-to-nearest-even conversions).
+        const uint32_t hi = bf16x2_bits(pp);
+        const f32x2_t back = {u32_as_f32(hi << 16), u32_as_f32(hi & 0xffff0000u)};
+        phi[cg * 2 + j / 2] = hi;
+        plo[cg * 2 + j / 2] = bf16x2_bits(pp - back);
       }
     lpart = lpart * corr + psum;
+    // The running max rarely moves after the first tiles: skip the rescale then.
+    const bool rescale = __ballot(corr != 1.0f) != 0;
     const bf16x8_t pb_hi = u32x4_as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
     const bf16x8_t pb_lo = u32x4_as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
     // A operand of V^T: lane (g, col) needs V[slot][16v + col] for the slots
@@ -373,8 +376,9 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
       __builtin_memcpy(&w.z, &t1, 8);
       const bf16x8_t va = u32x4_as_bf16x8(w);
       f32x4_t acc = o[v];
+      if (rescale)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] *= corr;
+        for (int j = 0; j < 4; ++j) acc[j] *= corr;
       acc = mfma16x16x32(va, pb_hi, acc);
       acc = mfma16x16x32(va, pb_lo, acc);
       o[v] = acc;
@@ -441,55 +445,63 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
   if (g == 0) *reinterpret_cast<float2*>(ml) = make_float2(mrun, lt);
 }
 
-// Log-sum-exp merge of the split partials of one row and 16 heads.
+// Log-sum-exp merge of the split partials of one row and HPW heads: every
+// thread owns one 16-byte column chunk of one head and keeps eight splits'
+// loads in flight.
 template <int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, AttendPlan p) {
-  __shared__ float f[kMaxSplits][16];
-  __shared__ float lse_s[16];
-  const int hgs = (a.H + 15) / 16;
+  constexpr int CPH = D / 4;        // float4 chunks per head
+  constexpr int HPW = 256 / CPH;    // heads per workgroup
+  __shared__ float2 mls[kMaxSplits][HPW];
+  __shared__ float f[kMaxSplits][HPW];
+  __shared__ float lse_s[HPW];
+  const int hgs = (a.H + HPW - 1) / HPW;
   const int64_t r = blockIdx.x / hgs;
-  const int h_begin = int(blockIdx.x % hgs) * 16;
+  const int h_begin = int(blockIdx.x % hgs) * HPW;
   const RowSlots x = row_slots(a, p, r, 0);
   if (x.S <= 1) return;  // written directly by the attention kernel
-  const int64_t S = x.S;
+  const int S = int(x.S);
   const int H = a.H, tid = threadIdx.x;
-  const int nh = (H - h_begin) < 16 ? (H - h_begin) : 16;
+  const int nh = (H - h_begin) < HPW ? (H - h_begin) : HPW;
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
   const float* part = reinterpret_cast<const float*>(ws + p.off_part) + r * p.splits * int64_t(H) * D;
   const float* ml = reinterpret_cast<const float*>(ws + p.off_ml) + r * p.splits * int64_t(H) * 2;
+  for (int i = tid; i < S * nh; i += 256) {
+    const int sp = i / nh, hl = i % nh;
+    mls[sp][hl] = *reinterpret_cast<const float2*>(ml + (int64_t(sp) * H + h_begin + hl) * 2);
+  }
+  __syncthreads();
   if (tid < nh) {
-    const int h = h_begin + tid;
     float mx = -INFINITY;
-    for (int64_t s = 0; s < S; ++s) mx = fmaxf(mx, ml[(s * H + h) * 2]);
+    for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, mls[sp][tid].x);
+    const float ms = (mx == -INFINITY) ? 0.0f : mx;
     float Lsum = 0.0f;
-    if (mx != -INFINITY)
-      for (int64_t s = 0; s < S; ++s) Lsum = fmaf(exp2f(ml[(s * H + h) * 2] - mx), ml[(s * H + h) * 2 + 1], Lsum);
+    for (int sp = 0; sp < S; ++sp) Lsum = fmaf(exp2f(mls[sp][tid].x - ms), mls[sp][tid].y, Lsum);
     const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-    for (int64_t s = 0; s < S; ++s)
-      f[s][tid] = (mx == -INFINITY) ? 0.0f : exp2f(ml[(s * H + h) * 2] - mx) * inv;
+    for (int sp = 0; sp < S; ++sp) f[sp][tid] = exp2f(mls[sp][tid].x - ms) * inv;
     lse_s[tid] = Lsum > 0.0f ? (mx + log2f(Lsum)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  constexpr int cpr = D / 4;  // float4 chunks per head
-  for (int c = tid; c < nh * cpr; c += 256) {
-    const int hl = c / cpr, cc = (c % cpr) * 4;
+  const int hl = tid / CPH, cc = (tid % CPH) * 4;
+  if (hl < nh) {
     const float* src = part + int64_t(h_begin + hl) * D + cc;
+    const int64_t stride = int64_t(H) * D;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    int64_t s = 0;
-    for (; s + 4 <= S; s += 4) {
-      float4 v[4];
+    int sp = 0;
+    for (; sp + 8 <= S; sp += 8) {
+      float4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(src + (s + u) * H * int64_t(D));
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(src + (sp + u) * stride);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = f[s + u][hl];
+      for (int u = 0; u < 8; ++u) {
+        const float w = f[sp + u][hl];
         acc.x = fmaf(w, v[u].x, acc.x); acc.y = fmaf(w, v[u].y, acc.y);
         acc.z = fmaf(w, v[u].z, acc.z); acc.w = fmaf(w, v[u].w, acc.w);
       }
     }
-    for (; s < S; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(src + s * H * int64_t(D));
-      const float w = f[s][hl];
+    for (; sp < S; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(src + sp * stride);
+      const float w = f[sp][hl];
       acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
       acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
     }
@@ -718,9 +730,11 @@ static void launch_bf16(const AttendArgs& a, const AttendPlan& p) {
   if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2>), grid, dim3(128), 0, a.stream, a, p);
   else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4>), grid, dim3(256), 0, a.stream, a, p);
   else hipLaunchKernelGGL((attend_bf16_kernel<D, 8>), grid, dim3(512), 0, a.stream, a, p);
-  if (p.splits > 1)
-    hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(unsigned(p.rows * ((a.H + 15) / 16))), dim3(256), 0,
-                       a.stream, a, p);
+  if (p.splits > 1) {
+    constexpr int HPW = 256 / (D / 4);
+    hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(unsigned(p.rows * ((a.H + HPW - 1) / HPW))), dim3(256),
+                       0, a.stream, a, p);
+  }
 }
 
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p) {

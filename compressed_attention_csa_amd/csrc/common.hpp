@@ -49,6 +49,16 @@ __device__ __forceinline__ bf16_t f64_to_bf16(double x) {
   return f32_to_bf16(f);
 }
 
+// Two binary32 values to packed bf16 bits (element 0 in the low half), with the
+// gfx950 conversion instruction (round to nearest even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_bits(f32x2_t v) {
+  const bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
+
 // ---------------------------------------------------------------- fp8 e4m3fn
 
 // Encode a binary32 as e4m3fn, nearest-even.  Magnitudes up to 464 round to at
@@ -154,6 +164,16 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
   __syncthreads();
   return s_flag[0] != 0;
 }
+
+// ---------------------------------------------------------------- integer division
+
+// a / b and a % b for non-negative a and positive b; takes the 32-bit path when
+// both fit (a full 64-bit division is a long instruction sequence on the GPU).
+__device__ __forceinline__ int64_t div64(int64_t a, int64_t b) {
+  if (((uint64_t(a) | uint64_t(b)) >> 32) == 0) return int64_t(uint32_t(a) / uint32_t(b));
+  return a / b;
+}
+__device__ __forceinline__ int64_t mod64(int64_t a, int64_t b) { return a - div64(a, b) * b; }
 
 // ---------------------------------------------------------------- reductions
 

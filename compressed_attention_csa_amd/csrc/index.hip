@@ -20,7 +20,7 @@
 //     the last WG then rescores exactly those slices and adds the dropped
 //     entries above the threshold before selecting again, so the result is
 //     exact for any input; on typical inputs no slice needs it.
-// Output order is deterministic (slice order, then entry index).
+// Output order is deterministic (slice order, then a fixed order within the slice).
 // bf16 / e4m3 keys are scored with 16x16x32 bf16 MFMA (query heads as rows,
 // entries as columns; e4m3 codes are widened exactly to bf16 in registers),
 // with 8 groups of 16 keys in flight per wave; fp32 keys use fp32 FMA with one
@@ -47,20 +47,20 @@ __device__ __forceinline__ RowInfo row_info(const IndexArgs& a, const IndexPlan&
                                             int64_t s) {
   RowInfo ri;
   ri.r = r;
-  ri.b = r / a.T;
-  ri.i = r % a.T;
+  ri.b = div64(r, a.T);
+  ri.i = r - ri.b * a.T;
   ri.t = a.t0 + ri.i;
-  int64_t c = (ri.t + 1) / a.m;
+  int64_t c = div64(ri.t + 1, a.m);
   ri.c = c < a.N_alloc ? c : a.N_alloc;
   ri.kk = ri.c < a.top_k ? ri.c : a.top_k;
-  int64_t S = (ri.c + p.slice - 1) / p.slice;
+  int64_t S = div64(ri.c + p.slice - 1, p.slice);
   ri.S = S < 1 ? 1 : S;
   ri.lo = s * p.slice;
   int64_t hi = ri.lo + p.slice;
   ri.hi = hi < ri.c ? hi : ri.c;
   if (ri.hi < ri.lo) ri.hi = ri.lo;
   // Local candidates per slice: about 4x the slice's expected share of winners.
-  int64_t share = (ri.kk + ri.S - 1) / ri.S;
+  int64_t share = div64(ri.kk + ri.S - 1, ri.S);
   int64_t kl = ((4 * share + 31) / 32) * 32;
   if (kl < 32) kl = 32;
   if (kl > p.slice) kl = p.slice;
@@ -239,6 +239,9 @@ constexpr int kBins = 1 << kDigitBits;
 struct SelLds {
   uint32_t scan[kWaves];
   uint32_t misc[4];
+  uint32_t lo[kWaves], hi[kWaves];
+  uint64_t wb[kWaves];
+  uint64_t res;
 };
 
 // After the histogram of the current digit is complete: pick the digit that
@@ -277,10 +280,9 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t nb, in
 // Threshold T with exactly `need` keys >= T among the non-zero keys (1 <= need <=
 // their count; keys distinct).  Keys live in registers: KPT per thread.
 template <int KPT>
-__device__ uint64_t select_regs(const uint64_t (&v)[KPT], int64_t need, uint32_t* hist, SelLds& S) {
+__device__ uint64_t select_regs(const uint64_t (&v)[KPT], int64_t need, uint32_t* hist, SelLds& S,
+                                uint64_t prefix = 0, int hi_bit = 64) {
   const int tid = threadIdx.x;
-  uint64_t prefix = 0;
-  int hi_bit = 64;
   while (hi_bit > 0) {
     const int width = hi_bit >= kDigitBits ? kDigitBits : hi_bit;
     const int shift = hi_bit - width;
@@ -301,6 +303,52 @@ __device__ uint64_t select_regs(const uint64_t (&v)[KPT], int64_t need, uint32_t
     if (int64_t(in_digit) == need) break;  // every key in this digit is selected
   }
   return prefix;  // remaining low bits zero
+}
+
+// The same threshold with a first pass whose bins span only the occupied range
+// of the keys' upper halves (min .. max), which usually leaves a handful of
+// keys in the bin of the need-th key; finer passes follow only if needed.
+template <int KPT>
+__device__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t need, uint32_t* hist, SelLds& S) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (v[u] != 0) {
+      const uint32_t h = uint32_t(v[u] >> 32);
+      lo = h < lo ? h : lo;
+      hi = h > hi ? h : hi;
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, uint32_t(__shfl_xor(int(lo), o)));
+    hi = max(hi, uint32_t(__shfl_xor(int(hi), o)));
+  }
+  if (lane == 0) {
+    S.lo[wid] = lo;
+    S.hi[wid] = hi;
+  }
+  for (int x = tid; x < kBins; x += kThreads) hist[x] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    lo = min(lo, S.lo[w]);
+    hi = max(hi, S.hi[w]);
+  }
+  int sh = 0;
+  while ((hi >> sh) - (lo >> sh) >= uint32_t(kBins)) ++sh;
+  const uint32_t base = lo >> sh;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (v[u] != 0) atomicAdd(&hist[((uint32_t(v[u] >> 32) >> sh) - base) & (kBins - 1)], 1u);
+  __syncthreads();
+  uint32_t dstar, above, in_digit;
+  pick_digit(hist, kBins, need, S, dstar, above, in_digit);
+  const int hi_bit = 32 + sh;
+  const uint64_t prefix = uint64_t(base + dstar) << hi_bit;
+  need -= int64_t(above);
+  if (int64_t(in_digit) == need) return prefix;
+  return select_regs(v, need, hist, S, prefix, hi_bit);
 }
 
 // The same selection over n keys produced by get(i) (used for long candidate lists).
@@ -331,6 +379,66 @@ __device__ uint64_t select_get(int64_t n, int64_t need, Get get, uint32_t* hist,
   return prefix;
 }
 
+// The same threshold when `need` is small next to the key count.  In every
+// wave, the ceil(need/4)-th largest of the lanes' maxima is found by ranking
+// the 64 maxima against each other; the smallest of those four values is a
+// lower bound of T (need distinct threads hold a key at or above it).  The
+// keys at or above it, usually a few more than need, are then ranked exactly
+// against each other in LDS.  Falls back to select_rel when more than
+// one key per thread passes the bound.
+// scratch: 2 * kThreads uint64 of LDS, free on entry.
+template <int KPT>
+__device__ uint64_t select_small(const uint64_t (&v)[KPT], int64_t need, uint64_t* scratch, uint32_t* hist,
+                                 SelLds& S) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int jw = int((need + kWaves - 1) / kWaves);  // share of each wave
+  if (jw > kWave) return select_rel(v, need, hist, S);
+  uint64_t* tmax = scratch;
+  uint64_t* cand = scratch + kThreads;
+  uint64_t mx = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) mx = v[u] > mx ? v[u] : mx;
+  tmax[tid] = mx;
+  if (lane == 0) S.wb[wid] = 0ull;  // fewer than jw non-empty lanes: no bound
+  __builtin_amdgcn_wave_barrier();
+  if (mx != 0) {
+    const uint64_t* wt = tmax + wid * kWave;
+    int above = 0;
+    for (int t = 0; t < kWave; t += 2) {
+      const uint4 w = *reinterpret_cast<const uint4*>(&wt[t]);
+      above += ((uint64_t(w.y) << 32 | w.x) > mx) + ((uint64_t(w.w) << 32 | w.z) > mx);
+    }
+    if (above == jw - 1) S.wb[wid] = mx;
+  }
+  __syncthreads();
+  uint64_t B = S.wb[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) B = S.wb[w] < B ? S.wb[w] : B;
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) cnt += (v[u] != 0 && v[u] >= B) ? 1 : 0;
+  const uint32_t inc = block_inclusive_sum(uint32_t(cnt), S.scan);
+  if (tid == kThreads - 1) S.misc[3] = inc;
+  __syncthreads();
+  const uint32_t m = S.misc[3];
+  if (m > uint32_t(kThreads)) return select_rel(v, need, hist, S);
+  uint32_t pos = inc - uint32_t(cnt);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (v[u] != 0 && v[u] >= B) cand[pos++] = v[u];
+  __syncthreads();
+  if (uint32_t(tid) < m) {
+    const uint64_t key = cand[tid];
+    int above = 0;
+    for (uint32_t j = 0; j < m; ++j) above += cand[j] > key;
+    if (above == need - 1) S.res = key;
+  }
+  __syncthreads();
+  const uint64_t T = S.res;
+  __syncthreads();
+  return T;
+}
+
 __device__ __forceinline__ void write_out(const IndexArgs& a, int64_t r, int64_t slot, uint64_t v) {
   a.out_idx[r * a.top_k + slot] = int32_t(rank_key_idx(v));
   if (a.out_score) a.out_score[r * a.top_k + slot] = key_score(uint32_t(v >> 32));
@@ -343,20 +451,17 @@ __device__ __forceinline__ void write_pads(const IndexArgs& a, int64_t r, int64_
   }
 }
 
-// Emit the register keys >= T in element order (element x = tid + 256*u); dst(pos, v)
-// stores one.  Returns the count.
+// Emit the register keys >= T in thread order (all of thread 0's, then thread
+// 1's, ...); dst(pos, v) stores one.
 template <int KPT, typename Dst>
-__device__ int64_t emit_regs(const uint64_t (&v)[KPT], uint64_t T, int64_t from, Dst dst, int* s_wave) {
-  int64_t done = from;
+__device__ void emit_regs(const uint64_t (&v)[KPT], uint64_t T, int64_t from, Dst dst, uint32_t* s_scan) {
+  int cnt = 0;
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const bool win = v[u] != 0 && v[u] >= T;
-    int total;
-    const int pos = block_rank(win, s_wave, total);
-    if (win) dst(done + pos, v[u]);
-    done += total;
-  }
-  return done - from;
+  for (int u = 0; u < KPT; ++u) cnt += (v[u] != 0 && v[u] >= T) ? 1 : 0;
+  int64_t pos = from + int64_t(block_inclusive_sum(uint32_t(cnt), s_scan)) - cnt;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (v[u] != 0 && v[u] >= T) dst(pos++, v[u]);
 }
 
 template <typename Get, typename Dst>
@@ -389,9 +494,9 @@ static_assert(kBins == kMaxSlice, "the key buffer doubles as the histogram");
 template <int KK>
 __global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPlan p, int64_t row0) {
   __shared__ LdsIdx L;
-  const int64_t lr = blockIdx.x / p.slices;  // row within this launch
+  const int64_t lr = div64(blockIdx.x, p.slices);  // row within this launch
   const int64_t r = row0 + lr;
-  const int64_t s = blockIdx.x % p.slices;
+  const int64_t s = blockIdx.x - lr * p.slices;
   const RowInfo ri = row_info(a, p, r, s);
   if (s >= ri.S) return;
   const int tid = threadIdx.x;
@@ -399,19 +504,19 @@ __global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPl
 
   score_slice<KK>(a, ri, L.keys, L.q);
   const uint32_t base = uint32_t(ri.lo);
-  uint64_t v[kKeysPerThread];
+  uint64_t v[kKeysPerThread];  // thread tid: slice elements tid + 256 u
 #pragma unroll
   for (int u = 0; u < kKeysPerThread; ++u) {
     const int64_t x = tid + int64_t(u) * kThreads;
     v[u] = x < n ? rank_key(L.keys[x], base + uint32_t(x)) : 0ull;
   }
-  __syncthreads();  // L.keys is the histogram from here on
+  __syncthreads();  // L.keys is the histogram (or selection scratch) from here on
   auto out_dst = [&](int64_t pos, uint64_t val) { write_out(a, r, pos, val); };
 
   if (ri.S == 1) {  // the whole row is in this WG
     if (ri.kk > 0) {
-      const uint64_t T = (ri.kk < n) ? select_regs(v, ri.kk, L.keys, L.sel) : 1ull;
-      emit_regs(v, T, 0, out_dst, L.wave);
+      const uint64_t T = (ri.kk < n) ? select_rel(v, ri.kk, L.keys, L.sel) : 1ull;
+      emit_regs(v, T, 0, out_dst, L.sel.scan);
     }
     write_pads(a, r, ri.kk);
     return;
@@ -425,9 +530,10 @@ __global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPl
   uint64_t* tau = reinterpret_cast<uint64_t*>(ws + p.off_tau) + lr * p.slices;
   uint64_t* over = reinterpret_cast<uint64_t*>(ws + p.off_over) + lr * a.N_alloc;
   const int64_t kl = n < ri.kloc ? n : ri.kloc;
-  const uint64_t Ts = (n > kl) ? select_regs(v, kl, L.keys, L.sel) : 1ull;
+  const uint64_t Ts =
+      (n > kl) ? select_small(v, kl, reinterpret_cast<uint64_t*>(L.keys), L.keys, L.sel) : 1ull;
   uint64_t* my_cand = cand + s * ri.kloc;
-  emit_regs(v, Ts, 0, [&](int64_t pos, uint64_t val) { store_dev(&my_cand[pos], val); }, L.wave);
+  emit_regs(v, Ts, 0, [&](int64_t pos, uint64_t val) { store_dev(&my_cand[pos], val); }, L.sel.scan);
   if (tid == 0) store_dev(&tau[s], uint64_t(n > kl ? Ts : 0ull));  // dropped entries are all below it
   if (!arrive_last(&ctrl->arrive, uint32_t(ri.S), L.flag)) return;
 
@@ -442,10 +548,10 @@ __global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPl
   if (in_regs) {
 #pragma unroll
     for (int u = 0; u < kCandPerThread; ++u) {
-      const int64_t g = tid + int64_t(u) * kThreads;
+      const int64_t g = int64_t(tid) * kCandPerThread + u;  // thread-major: candidate order
       c[u] = g < total ? get_c(g) : 0ull;
     }
-    T = select_regs(c, ri.kk, L.keys, L.sel);
+    T = select_rel(c, ri.kk, L.keys, L.sel);
   } else {
     T = select_get(total, ri.kk, get_c, L.keys, L.sel);
   }
@@ -453,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPl
   bool viol = false;
   for (int64_t x = tid; x < ri.S; x += kThreads) viol |= load_dev(&tau[x]) > T;
   if (!__syncthreads_or(viol)) {
-    if (in_regs) emit_regs(c, T, 0, out_dst, L.wave);
+    if (in_regs) emit_regs(c, T, 0, out_dst, L.sel.scan);
     else emit_get(total, T, get_c, 0, out_dst, L.wave);
     write_pads(a, r, ri.kk);
     if (tid == 0) ctrl->arrive = 0;
