@@ -165,6 +165,36 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected
   return s_flag[0] != 0;
 }
 
+// ---------------------------------------------------------------- DPP wave scans
+//
+// Inclusive scans over the 64 lanes of a wave with DPP row shifts (within rows
+// of 16 lanes) and the two row broadcasts, which need no LDS round trip.  Lanes
+// without a source keep the identity.
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v, uint32_t identity, Op op) {
+  const int e = int(identity);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(e, int(v), 0x111, 0xf, 0xf, false)));  // row_shr:1
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(e, int(v), 0x112, 0xf, 0xf, false)));  // row_shr:2
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(e, int(v), 0x114, 0xf, 0xf, false)));  // row_shr:4
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(e, int(v), 0x118, 0xf, 0xf, false)));  // row_shr:8
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(e, int(v), 0x142, 0xa, 0xf, false)));  // row_bcast:15
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(e, int(v), 0x143, 0xc, 0xf, false)));  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  return wave_scan_dpp(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+// Reductions: the last lane of the inclusive scan, broadcast.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_readlane(
+      int(wave_scan_dpp(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; })), 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_readlane(
+      int(wave_scan_dpp(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; })), 63));
+}
+
 // ---------------------------------------------------------------- integer division
 
 // a / b and a % b for non-negative a and positive b; takes the 32-bit path when

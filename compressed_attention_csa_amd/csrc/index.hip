@@ -91,11 +91,7 @@ __device__ __forceinline__ int block_rank(bool flag, int* s_wave, int& total) {
 // Inclusive block-wide prefix sum of one uint32 per thread (thread order).
 __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* s_scan) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t n = __shfl_up(v, o);
-    if (lane >= o) v += n;
-  }
+  v = wave_incl_sum(v);
   if (lane == kWave - 1) s_scan[wid] = v;
   __syncthreads();
   uint32_t pre = 0;
@@ -242,6 +238,7 @@ struct SelLds {
   uint32_t lo[kWaves], hi[kWaves];
   uint64_t wb[kWaves];
   uint64_t res;
+  uint64_t list[kThreads];  // keys of one histogram bin, ranked exactly
 };
 
 // After the histogram of the current digit is complete: pick the digit that
@@ -280,7 +277,7 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t nb, in
 // Threshold T with exactly `need` keys >= T among the non-zero keys (1 <= need <=
 // their count; keys distinct).  Keys live in registers: KPT per thread.
 template <int KPT>
-__device__ uint64_t select_regs(const uint64_t (&v)[KPT], int64_t need, uint32_t* hist, SelLds& S,
+__device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[KPT], int64_t need, uint32_t* hist, SelLds& S,
                                 uint64_t prefix = 0, int hi_bit = 64) {
   const int tid = threadIdx.x;
   while (hi_bit > 0) {
@@ -307,9 +304,10 @@ __device__ uint64_t select_regs(const uint64_t (&v)[KPT], int64_t need, uint32_t
 
 // The same threshold with a first pass whose bins span only the occupied range
 // of the keys' upper halves (min .. max), which usually leaves a handful of
-// keys in the bin of the need-th key; finer passes follow only if needed.
+// keys in the bin of the need-th key.  Those are then ranked exactly against
+// each other in LDS; finer radix passes follow only if the bin is crowded.
 template <int KPT>
-__device__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t need, uint32_t* hist, SelLds& S) {
+__device__ __forceinline__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t need, uint32_t* hist, SelLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
@@ -319,11 +317,8 @@ __device__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t need, uint32_t*
       lo = h < lo ? h : lo;
       hi = h > hi ? h : hi;
     }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, uint32_t(__shfl_xor(int(lo), o)));
-    hi = max(hi, uint32_t(__shfl_xor(int(hi), o)));
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   if (lane == 0) {
     S.lo[wid] = lo;
     S.hi[wid] = hi;
@@ -345,10 +340,29 @@ __device__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t need, uint32_t*
   uint32_t dstar, above, in_digit;
   pick_digit(hist, kBins, need, S, dstar, above, in_digit);
   const int hi_bit = 32 + sh;
-  const uint64_t prefix = uint64_t(base + dstar) << hi_bit;
+  const uint64_t top = uint64_t(base + dstar);
+  const uint64_t prefix = top << hi_bit;
   need -= int64_t(above);
   if (int64_t(in_digit) == need) return prefix;
-  return select_regs(v, need, hist, S, prefix, hi_bit);
+  if (in_digit > uint32_t(kThreads)) return select_regs(v, need, hist, S, prefix, hi_bit);
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) cnt += (v[u] != 0 && (v[u] >> hi_bit) == top) ? 1 : 0;
+  uint32_t pos = block_inclusive_sum(uint32_t(cnt), S.scan) - uint32_t(cnt);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (v[u] != 0 && (v[u] >> hi_bit) == top) S.list[pos++] = v[u];
+  __syncthreads();
+  if (uint32_t(tid) < in_digit) {
+    const uint64_t key = S.list[tid];
+    int64_t gt = 0;
+    for (uint32_t j = 0; j < in_digit; ++j) gt += S.list[j] > key;
+    if (gt == need - 1) S.res = key;
+  }
+  __syncthreads();
+  const uint64_t T = S.res;
+  __syncthreads();
+  return T;
 }
 
 // The same selection over n keys produced by get(i) (used for long candidate lists).
@@ -388,7 +402,7 @@ __device__ uint64_t select_get(int64_t n, int64_t need, Get get, uint32_t* hist,
 // one key per thread passes the bound.
 // scratch: 2 * kThreads uint64 of LDS, free on entry.
 template <int KPT>
-__device__ uint64_t select_small(const uint64_t (&v)[KPT], int64_t need, uint64_t* scratch, uint32_t* hist,
+__device__ __forceinline__ uint64_t select_small(const uint64_t (&v)[KPT], int64_t need, uint64_t* scratch, uint32_t* hist,
                                  SelLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int jw = int((need + kWaves - 1) / kWaves);  // share of each wave
@@ -454,7 +468,7 @@ __device__ __forceinline__ void write_pads(const IndexArgs& a, int64_t r, int64_
 // Emit the register keys >= T in thread order (all of thread 0's, then thread
 // 1's, ...); dst(pos, v) stores one.
 template <int KPT, typename Dst>
-__device__ void emit_regs(const uint64_t (&v)[KPT], uint64_t T, int64_t from, Dst dst, uint32_t* s_scan) {
+__device__ __forceinline__ void emit_regs(const uint64_t (&v)[KPT], uint64_t T, int64_t from, Dst dst, uint32_t* s_scan) {
   int cnt = 0;
 #pragma unroll
   for (int u = 0; u < KPT; ++u) cnt += (v[u] != 0 && v[u] >= T) ? 1 : 0;
