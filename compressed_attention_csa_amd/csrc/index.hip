@@ -614,7 +614,7 @@ IndexPlan plan_index(int B, int64_t T, int H_I, int64_t N_alloc, int top_k, int 
   p.rows = int64_t(B) * T;
   if (prefill_path(T, H_I, key_kind) && N_alloc > 0) {
     p.prefill = true;
-    // Room for a full LDS staging area (256 keys) above the 5k/4 keys a
+    // Room for a full LDS staging area (384 keys) above the 5k/4 keys a
     // compaction may keep.
     p.cap = 4096;
     if (p.cap < 2 * int64_t(top_k) + 512) p.cap = 2 * int64_t(top_k) + 512;

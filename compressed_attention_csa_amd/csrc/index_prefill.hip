@@ -23,10 +23,12 @@
 //
 // Exact top-k.  Each query keeps a candidate buffer in the workspace and a
 // threshold tau (a 64-bit rank key: score, then lower index first).  A binary32
-// compare against tau's score screens every pair; only pairs that pass it build
-// their rank key and are appended with wave ballots, in entry order, to a small
-// LDS staging area (so the scoring loop issues no global stores, whose pending
-// completion would otherwise make every wait also drain the key prefetch).  A
+// compare against tau's score screens every pair; pairs that pass it are
+// appended as (score, entry) with wave ballots, in entry order, to a small LDS
+// staging area (so the scoring loop issues no global stores, whose pending
+// completion would otherwise make every wait also drain the key prefetch).
+// Rank keys are formed, and tested exactly against tau, when a staging area
+// is drained.  A
 // staging area that cannot take another tile is drained to the buffer between
 // tiles.  When the buffer cannot take it, a histogram pass over the keys
 // relative to tau (bins spanning tau .. the largest key appended) and, if
@@ -43,10 +45,10 @@ namespace {
 constexpr int kWaves = kPrefillWaves;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTileE = 128;  // entries per LDS tile
-constexpr int kHBits = 10;   // histogram digit
+constexpr int kHBits = 9;    // histogram digit
 constexpr int kHBins = 1 << kHBits;
 constexpr int kBatch = 8;    // buffer keys per lane per batch of loads
-constexpr int kStage = 256;  // LDS staging slots per query
+constexpr int kStage = 384;  // LDS staging slots per query
 
 struct LdsPrefill {
   uint4 tile[2][kTileE * 8];  // up to 128 B per entry, two buffers
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     wv[h] = (qvalid && h < H_I) ? (a.w ? a.w[(rowbase + iq) * H_I + h] : 1.0f) : 0.0f;
   uint64_t tau = 0ull;             // every key appended from now on is > tau
   float tau_s = key_score(0u);     // screening score of tau (NaN: admits everything)
-  uint32_t top_hi = 0u;            // largest upper key half this lane appended
+  uint32_t top_hi = 0u;            // largest upper key half in the query's buffer
   int cnt = 0;                     // keys in the query's workspace buffer
   int scnt = 0;                    // keys staged in LDS for the query
 
@@ -275,6 +277,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   uint64_t* bufs = reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(a.ws) + p.off_cand);
   const int cap = int(p.cap);
   uint64_t* mystg = L.stg[wid][g];
+  const uint32_t below_g = uint32_t(below >> (16 * g));  // lanes of this group before this one
 
   const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(a.k_idx) + b * a.N_alloc * int64_t(DI * KB);
   // Tile prefetch registers (at most two 16-byte chunks per thread).  Every
@@ -348,29 +351,35 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     uint64_t tq = shfl64(tau, 16 * q);
     uint64_t* buf = bufs + (rowbase + qw0 + q) * cap;
     if (n + ns > cap) {  // then n > cap - kStage >= 5k/4 >= need
-      uint32_t tp = top_hi;
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) tp = max(tp, __shfl_xor(tp, o));
-      tp = __shfl(tp, 16 * q);
+      wait_mem();  // earlier drains of this wave have reached the buffer
+      const uint32_t tp = __builtin_amdgcn_readlane(top_hi, 16 * q);
       const int need = __shfl(need_l, 16 * q);
       int kept;
       const uint64_t T = wave_threshold(buf, n, need, false, need + need / 4, tq, tp, L.hist[wid], kept);
       n = wave_compact(buf, n, T);
       tq = T > tq ? T : tq;
     }
+    // Staged entries are (score bits, entry) pairs; their rank keys are formed
+    // here, and only keys above the (possibly raised) threshold are kept.
     const uint64_t* st = L.stg[wid][q];
+    uint32_t km = 0u;
     for (int x0 = 0; x0 < ns; x0 += kWave) {
       const int x = x0 + lane;
-      const uint64_t v = x < ns ? st[x] : 0ull;
+      const uint64_t sv = x < ns ? st[x] : 0ull;
+      const uint64_t v = rank_key(score_key(__uint_as_float(uint32_t(sv >> 32))), uint32_t(sv));
       const bool keep = x < ns && v > tq;
       const uint64_t m = __ballot(keep);
-      if (keep) buf[n + __popcll(m & below)] = v;
+      if (keep) {
+        buf[n + __popcll(m & below)] = v;
+        km = max(km, uint32_t(v >> 32));
+      }
       n += __popcll(m);
     }
-    wait_mem();  // the buffer is complete before it is read again
+    km = wave_max_u32(km);
     if (g == q) {
       cnt = n;
       scnt = 0;
+      top_hi = max(top_hi, km);
       if (tq > tau) {
         tau = tq;
         tau_s = key_score(uint32_t(tq >> 32));
@@ -401,6 +410,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     for (int gi = 0; gi < GROUPS; ++gi) operands(cur, gi, bo0[gi], bo1[gi]);
     f32x4_t acc[2], nxt[2];
     products(bo0[0], bo1[0], acc);
+    const int lim = cq - e0 - col;  // entry 16*gi + col of the tile is visible iff 16*gi < lim
 #pragma unroll
     for (int gi = 0; gi < GROUPS; ++gi) {
       if (gi + 1 < GROUPS) products(bo0[gi + 1], bo1[gi + 1], nxt);
@@ -411,18 +421,14 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
 #pragma unroll
         for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * hf + j], relu(acc[hf][j]), s);
       if (KK == kKeyE4M3) s *= L.scale[cur][e];
-      const int ge = e0 + e;
-      const bool screen = ge < cq && !(s < tau_s);
-      if (__ballot(screen)) {
-        const uint64_t rk = rank_key(score_key(s), uint32_t(ge));
-        const bool cand = screen && rk > tau;
-        const uint64_t m = __ballot(cand);
+      // The screen admits every entry whose rank key can exceed tau (and a few
+      // equal-score ones that cannot); the exact test runs when staged entries
+      // are drained, so the per-pair cost here is two compares.
+      const bool screen = 16 * gi < lim && !(s < tau_s);
+      const uint64_t m = __ballot(screen);
+      if (m) {
         const uint32_t mg = uint32_t(m >> (16 * g)) & 0xffffu;
-        if (cand) {
-          mystg[scnt + __popc(mg & uint32_t(below >> (16 * g)))] = rk;
-          const uint32_t hk = uint32_t(rk >> 32);
-          top_hi = hk > top_hi ? hk : top_hi;
-        }
+        if (screen) mystg[scnt + __popc(mg & below_g)] = (uint64_t(__float_as_uint(s)) << 32) | uint32_t(e0 + e);
         scnt += __popc(mg);
       }
       if (gi + 1 < GROUPS) {
@@ -441,6 +447,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     if (__builtin_amdgcn_readlane(scnt, 16 * q) > 0) drain(q);
 
   // ---- final exact selection for each query of this wave
+  wait_mem();  // every drain of this wave has reached the buffers
   uint32_t grp_top = top_hi;
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) grp_top = max(grp_top, __shfl_xor(grp_top, o));
