@@ -190,7 +190,7 @@ template <int D>
 struct LdsB {
   uint4 k[2][kTB * D / 8];  // K rows, 16-byte chunks swizzled for row-wise reads
   uint4 v[2][kTB * D / 8];  // V rows, swizzled for transposing reads
-  uint32_t live[2][kTB];
+  float bias[2][kTB];      // 0 for a live slot, -inf for a skipped one
   int32_t src[kMaxTable];   // selected compressed entry of each CSA slot of the split, -1 if skipped
 };
 
@@ -210,7 +210,7 @@ __device__ __forceinline__ int v_pos(int sl, int ch) {
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 
-template <int D, int NW>
+template <int D, int NW, bool HCA>
 __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
   constexpr int kT = NW * 64;
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
@@ -227,10 +227,10 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
   const int H = a.H;
   const int h0 = wid * 16;  // this wave's 16 heads
   const bool has = h0 < H;
-  const int64_t nsel = a.hca ? x.c : int64_t(a.top_k);
+  const int64_t nsel = HCA ? x.c : int64_t(a.top_k);
 
   // Selected entries of this split (CSA), checked against visibility once.
-  if (!a.hca) {
+  if (!HCA) {
     const int64_t e_end = x.hi < nsel ? x.hi : nsel;
     for (int64_t sl = x.lo + tid; sl < e_end; sl += kT) {
       const int32_t j = a.idx[x.r * a.top_k + sl];
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
       if (slot < x.hi) {
         if (slot < nsel) {
           int64_t j = slot;
-          if (!a.hca) j = L.src[slot - x.lo];
+          if (!HCA) j = L.src[slot - x.lo];
           if (j >= 0) {
             kp = kc + j * D;
             vp = vc + j * D;
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
       if (id < CT) {
         L.k[buf][k_pos<CPR>(sl, ch)] = make_uint4(P.k[4 * c], P.k[4 * c + 1], P.k[4 * c + 2], P.k[4 * c + 3]);
         L.v[buf][v_pos<CPR>(sl, ch)] = make_uint4(P.v[4 * c], P.v[4 * c + 1], P.v[4 * c + 2], P.v[4 * c + 3]);
-        if (ch == 0) L.live[buf][sl] = (P.lv >> c) & 1u;
+        if (ch == 0) L.bias[buf][sl] = ((P.lv >> c) & 1u) ? 0.0f : -INFINITY;
       }
     }
   };
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
     for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float v = L.live[buf][cg * 16 + 4 * g + j] ? sc[cg][j] * sl2 : -INFINITY;
+        const float v = fmaf(sc[cg][j], sl2, L.bias[buf][cg * 16 + 4 * g + j]);
         sc[cg][j] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
     const float mnew = fmaxf(mrun, tmax);
     // With no live slot yet everything below is zero: subtract 0 instead of -inf.
     const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float corr = exp2f(mrun - msafe);
+    const float corr = __builtin_amdgcn_exp2f(mrun - msafe);
     mrun = mnew;
     float psum = 0.0f;
     uint32_t phi[4], plo[4];
@@ -348,7 +348,10 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
     for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
-        const f32x2_t pp = {exp2f(sc[cg][j] - msafe), exp2f(sc[cg][j + 1] - msafe)};
+        // hardware 2^x (results below the normal range flush to 0, far below
+        // what a softmax weight next to the running max can matter)
+        const f32x2_t pp = {__builtin_amdgcn_exp2f(sc[cg][j] - msafe),
+                            __builtin_amdgcn_exp2f(sc[cg][j + 1] - msafe)};
         psum += pp[0] + pp[1];
         // P = hi + lo, both bf16 (hardware round-to-nearest-even conversions).
         const uint32_t hi = bf16x2_bits(pp);
@@ -357,8 +360,14 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
         plo[cg * 2 + j / 2] = bf16x2_bits(pp - back);
       }
     lpart = lpart * corr + psum;
-    // The running max rarely moves after the first tiles: skip the rescale then.
-    const bool rescale = __ballot(corr != 1.0f) != 0;
+    // The running max rarely moves after the first tiles: skip the rescale then
+    // (a wave-uniform branch).
+    if (__builtin_expect(__ballot(corr != 1.0f) != 0, 0)) {
+#pragma unroll
+      for (int v = 0; v < DVT; ++v)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[v][j] *= corr;
+    }
     const bf16x8_t pb_hi = u32x4_as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
     const bf16x8_t pb_lo = u32x4_as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
     // A operand of V^T: lane (g, col) needs V[slot][16v + col] for the slots
@@ -376,9 +385,6 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
       __builtin_memcpy(&w.z, &t1, 8);
       const bf16x8_t va = u32x4_as_bf16x8(w);
       f32x4_t acc = o[v];
-      if (rescale)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] *= corr;
       acc = mfma16x16x32(va, pb_hi, acc);
       acc = mfma16x16x32(va, pb_lo, acc);
       o[v] = acc;
@@ -723,13 +729,13 @@ int64_t attend_grid(const AttendPlan& p, bool bf16) {
   return bf16 ? p.rows * p.splits : p.groups * p.group_stride;
 }
 
-template <int D>
+template <int D, bool HCA>
 static void launch_bf16(const AttendArgs& a, const AttendPlan& p) {
   const dim3 grid(unsigned(p.rows * p.splits));
   const int nw = (a.H + 15) / 16;
-  if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2>), grid, dim3(128), 0, a.stream, a, p);
-  else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4>), grid, dim3(256), 0, a.stream, a, p);
-  else hipLaunchKernelGGL((attend_bf16_kernel<D, 8>), grid, dim3(512), 0, a.stream, a, p);
+  if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2, HCA>), grid, dim3(128), 0, a.stream, a, p);
+  else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4, HCA>), grid, dim3(256), 0, a.stream, a, p);
+  else hipLaunchKernelGGL((attend_bf16_kernel<D, 8, HCA>), grid, dim3(512), 0, a.stream, a, p);
   if (p.splits > 1) {
     constexpr int HPW = 256 / (D / 4);
     hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(unsigned(p.rows * ((a.H + HPW - 1) / HPW))), dim3(256),
@@ -741,8 +747,8 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p) {
   if (p.rows == 0) return hipSuccess;
   ProfScope prof(a.hca ? "hca_attend" : "csa_attend", a.stream);
   if (a.bf16) {
-    if (a.d == 128) launch_bf16<128>(a, p);
-    else launch_bf16<64>(a, p);
+    if (a.d == 128) a.hca ? launch_bf16<128, true>(a, p) : launch_bf16<128, false>(a, p);
+    else a.hca ? launch_bf16<64, true>(a, p) : launch_bf16<64, false>(a, p);
   } else {
     dim3 grid(unsigned(p.groups * p.group_stride)), block(kThreads);
     if (a.d == 128) hipLaunchKernelGGL(attend_f32_kernel<128>, grid, block, 0, a.stream, a, p);
