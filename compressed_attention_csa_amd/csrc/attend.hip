@@ -186,12 +186,12 @@ __device__ __forceinline__ bool decode_block(const AttendPlan& p, int64_t& hg, i
 constexpr int kTB = 32;           // slots per tile
 constexpr int kMaxTable = 3072;   // selected-entry slots of one CSA split (top_k + window bound)
 
-template <int D>
+template <int D, int NB>
 struct LdsB {
-  uint4 k[2][kTB * D / 8];  // K rows, 16-byte chunks swizzled for row-wise reads
-  uint4 v[2][kTB * D / 8];  // V rows, swizzled for transposing reads
-  float bias[2][kTB];      // 0 for a live slot, -inf for a skipped one
-  int32_t src[kMaxTable];   // selected compressed entry of each CSA slot of the split, -1 if skipped
+  uint4 k[NB][kTB * D / 8];  // K rows, 16-byte chunks swizzled for row-wise reads
+  uint4 v[NB][kTB * D / 8];  // V rows, swizzled for transposing reads
+  uint32_t live[NB][kTB];    // all ones for a live slot, 0 for a skipped one
+  int32_t src[kMaxTable];    // selected compressed entry of each CSA slot of the split, -1 if skipped
 };
 
 // K chunk position: 16 lanes reading one chunk of 16 consecutive rows, and 16
@@ -202,15 +202,22 @@ __device__ __forceinline__ int k_pos(int sl, int ch) {
   return sl * 8 + (ch ^ ((sl & 7) ^ ((sl >> 3) & 1)));
 }
 // V chunk position: the transposing read of 4 consecutive rows x 2 adjacent
-// chunks by 16 lanes hits distinct 8-byte bank pairs.
+// chunks by 16 lanes hits distinct 8-byte bank pairs, and the next 16 lanes
+// (the next 4 rows) the other half of the banks.
 template <int CPR>
 __device__ __forceinline__ int v_pos(int sl, int ch) {
-  return sl * CPR + (ch ^ (2 * (sl & 3)));
+  if (CPR == 16) return sl * 16 + (ch ^ (2 * (sl & 3)) ^ (8 * ((sl >> 2) & 1)));
+  return sl * CPR + (ch ^ (2 * ((sl & 3) ^ ((sl >> 2) & 1))));
 }
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 
-template <int D, int NW, bool HCA>
+// x where mask is all ones, -inf where it is 0 (one bitfield select).
+__device__ __forceinline__ float mask_or_neg_inf(float x, uint32_t mask) {
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & mask) | (~mask & 0xff800000u));
+}
+
+template <int D, int NW, bool HCA, int PAIR>
 __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
   constexpr int kT = NW * 64;
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
@@ -219,7 +226,8 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
   constexpr int SETS = CPT >= 4 ? 2 : 4;         // tiles in flight in registers
   constexpr int KS = D / 32;                     // k-steps of the QK product
   constexpr int DVT = D / 16;                    // 16-column tiles of the output
-  __shared__ LdsB<D> L;
+  constexpr int NB = 2 * PAIR;                   // LDS tile buffers
+  __shared__ LdsB<D, NB> L;
   const int64_t r = div64(blockIdx.x, p.splits), s = blockIdx.x - r * p.splits;
   const RowSlots x = row_slots(a, p, r, s);
   if (s >= x.S) return;
@@ -260,8 +268,25 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
     uint32_t lv;
   };
   // Loads tile t of the split (slots beyond the split or skipped read the query row).
+  const int64_t cmp_end = x.hi < nsel ? x.hi : nsel;  // end of the compressed slots of the split
   auto fetch = [&](Pre& P, int t) __attribute__((always_inline)) {
     const int64_t t0 = x.lo + int64_t(t) * kTB;
+    // HCA tile of consecutive live compressed rows (all but the split's last
+    // tiles): one base address for the workgroup.
+    if (HCA && t0 + kTB <= cmp_end) {
+      const bf16_t* kb = kc + t0 * D;
+      const bf16_t* vb = vc + t0 * D;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int id = (tid + c * kT) % CT;
+        const uint4 kw = *reinterpret_cast<const uint4*>(kb + id * 8);
+        const uint4 vw = *reinterpret_cast<const uint4*>(vb + id * 8);
+        P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y; P.k[4 * c + 2] = kw.z; P.k[4 * c + 3] = kw.w;
+        P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y; P.v[4 * c + 2] = vw.z; P.v[4 * c + 3] = vw.w;
+      }
+      P.lv = (1u << CPT) - 1;
+      return;
+    }
     uint32_t lv = 0;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -301,7 +326,7 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
       if (id < CT) {
         L.k[buf][k_pos<CPR>(sl, ch)] = make_uint4(P.k[4 * c], P.k[4 * c + 1], P.k[4 * c + 2], P.k[4 * c + 3]);
         L.v[buf][v_pos<CPR>(sl, ch)] = make_uint4(P.v[4 * c], P.v[4 * c + 1], P.v[4 * c + 2], P.v[4 * c + 3]);
-        if (ch == 0) L.bias[buf][sl] = ((P.lv >> c) & 1u) ? 0.0f : -INFINITY;
+        if (ch == 0) L.live[buf][sl] = ((P.lv >> c) & 1u) ? 0xffffffffu : 0u;
       }
     }
   };
@@ -310,12 +335,16 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
   f32x4_t o[DVT];
 #pragma unroll
   for (int v = 0; v < DVT; ++v) o[v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float mrun = -INFINITY, lpart = 0.0f;
+  // Softmax reference of this lane's head (log2 units; equal in the 4 lanes of
+  // a head): the running maximum as of the last rescale.  Weights are formed
+  // against it as long as no score exceeds it by more than kSlack, so most tiles
+  // need neither a cross-lane reduction nor a rescale of O.
+  constexpr float kSlack = 8.0f;
+  float mref = -INFINITY, lpart = 0.0f;
 
-  // S^T = K Q^T (lane: head h0 + col, slots 16cg + 4g + j), online softmax in
-  // log2 units, then O^T += V^T P^T with P as a bf16 hi + lo pair.
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-    f32x4_t sc[2];
+  // S^T = K Q^T (lane: head h0 + col, slots 16cg + 4g + j), weights in log2
+  // units, then O^T += V^T P^T with P as a bf16 hi + lo pair.
+  auto qk = [&](int buf, f32x4_t (&sc)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int cg = 0; cg < 2; ++cg) {
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -326,81 +355,138 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
       }
       sc[cg] = acc;
     }
-    float tmax = -INFINITY;
+  };
+  // A operand of V^T for output columns 16v..16v+15: lane (g, col) needs
+  // V[slot][16v + col] for the slots 4g..4g+3 and 16+4g..16+4g+3; a
+  // transposing read of 4 rows returns them.
+  auto vfrag = [&](int buf, int v) __attribute__((always_inline)) {
+    const int vr0 = 4 * g + col / 4, half = col & 1;
+    const int ch = 2 * v + (col & 3) / 2;
+    const short* b0 = reinterpret_cast<const short*>(&L.v[buf][v_pos<CPR>(vr0, ch)]) + 4 * half;
+    const short* b1 = reinterpret_cast<const short*>(&L.v[buf][v_pos<CPR>(vr0 + 16, ch)]) + 4 * half;
+    const v4s_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b0));
+    const v4s_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b1));
+    uint4 w;
+    __builtin_memcpy(&w.x, &t0, 8);
+    __builtin_memcpy(&w.z, &t1, 8);
+    return u32x4_as_bf16x8(w);
+  };
+  // One group of PAIR staged tiles (buffers b0, b0+1): the scores of all of
+  // them, one reference check for the group, then weights and O^T updates.
+  // A tile past the split was staged with every slot skipped, so it adds
+  // nothing and needs no branch.
+  auto compute = [&](int b0) __attribute__((always_inline)) {
+    f32x4_t sc[PAIR][2];
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg)
+    for (int i = 0; i < PAIR; ++i) qk(b0 + i, sc[i]);
+    // Paired tiles read the first tile's V^T operands while the products run;
+    // single tiles read them just before use (fewer registers, for occupancy).
+    bf16x8_t va[DVT];
+    if (PAIR == 2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = fmaf(sc[cg][j], sl2, L.bias[buf][cg * 16 + 4 * g + j]);
-        sc[cg][j] = v;
-        tmax = fmaxf(tmax, v);
+      for (int v = 0; v < DVT; ++v) va[v] = vfrag(b0, v);
+    }
+    // u = score - reference (log2 units); skipped slots get -inf (a bit
+    // select with the slot's mask, which also holds while the reference is
+    // -inf).
+    float u[PAIR][2][4];
+    float umax = -INFINITY;
+    const float nref = -mref;
+#pragma unroll
+    for (int i = 0; i < PAIR; ++i)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        const uint4 lm = *reinterpret_cast<const uint4*>(&L.live[b0 + i][cg * 16 + 4 * g]);
+        const uint32_t lmv[4] = {lm.x, lm.y, lm.z, lm.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u[i][cg][j] = mask_or_neg_inf(fmaf(sc[i][cg][j], sl2, nref), lmv[j]);
+          umax = fmaxf(umax, u[i][cg][j]);
+        }
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(mrun, tmax);
-    // With no live slot yet everything below is zero: subtract 0 instead of -inf.
-    const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float corr = __builtin_amdgcn_exp2f(mrun - msafe);
-    mrun = mnew;
-    float psum = 0.0f;
-    uint32_t phi[4], plo[4];
+    // A live score above reference + kSlack (or a live slot while there is no
+    // reference yet: u = +inf) moves the reference to the running maximum (a
+    // wave-uniform branch).
+    if (__builtin_expect(__ballot(umax > kSlack) != 0, 0)) {
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg)
+      for (int i = 0; i < PAIR; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        // hardware 2^x (results below the normal range flush to 0, far below
-        // what a softmax weight next to the running max can matter)
-        const f32x2_t pp = {__builtin_amdgcn_exp2f(sc[cg][j] - msafe),
-                            __builtin_amdgcn_exp2f(sc[cg][j + 1] - msafe)};
-        psum += pp[0] + pp[1];
-        // P = hi + lo, both bf16 (hardware round-to-nearest-even conversions).
-        const uint32_t hi = bf16x2_bits(pp);
-        const f32x2_t back = {u32_as_f32(hi << 16), u32_as_f32(hi & 0xffff0000u)};
-        phi[cg * 2 + j / 2] = hi;
-        plo[cg * 2 + j / 2] = bf16x2_bits(pp - back);
-      }
-    lpart = lpart * corr + psum;
-    // The running max rarely moves after the first tiles: skip the rescale then
-    // (a wave-uniform branch).
-    if (__builtin_expect(__ballot(corr != 1.0f) != 0, 0)) {
+        for (int cg = 0; cg < 2; ++cg) {
+          const uint4 lm = *reinterpret_cast<const uint4*>(&L.live[b0 + i][cg * 16 + 4 * g]);
+          const uint32_t lmv[4] = {lm.x, lm.y, lm.z, lm.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            u[i][cg][j] = mask_or_neg_inf(sc[i][cg][j] * sl2, lmv[j]);
+            tmax = fmaxf(tmax, u[i][cg][j]);
+          }
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(mref, tmax);
+      // With no live slot yet everything is zero: subtract 0 instead of -inf.
+      const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
+      const float corr = exp2f(mref - msafe);
+      mref = mnew;
+      lpart *= corr;
 #pragma unroll
       for (int v = 0; v < DVT; ++v)
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[v][j] *= corr;
-    }
-    const bf16x8_t pb_hi = u32x4_as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
-    const bf16x8_t pb_lo = u32x4_as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
-    // A operand of V^T: lane (g, col) needs V[slot][16v + col] for the slots
-    // 4g..4g+3 and 16+4g..16+4g+3; a transposing read of 4 rows returns them.
-    const int vr0 = 4 * g + col / 4, half = col & 1;
 #pragma unroll
-    for (int v = 0; v < DVT; ++v) {
-      const int ch = 2 * v + (col & 3) / 2;
-      const short* b0 = reinterpret_cast<const short*>(&L.v[buf][v_pos<CPR>(vr0, ch)]) + 4 * half;
-      const short* b1 = reinterpret_cast<const short*>(&L.v[buf][v_pos<CPR>(vr0 + 16, ch)]) + 4 * half;
-      const v4s_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b0));
-      const v4s_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b1));
-      uint4 w;
-      __builtin_memcpy(&w.x, &t0, 8);
-      __builtin_memcpy(&w.z, &t1, 8);
-      const bf16x8_t va = u32x4_as_bf16x8(w);
-      f32x4_t acc = o[v];
-      acc = mfma16x16x32(va, pb_hi, acc);
-      acc = mfma16x16x32(va, pb_lo, acc);
-      o[v] = acc;
+      for (int i = 0; i < PAIR; ++i)
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) u[i][cg][j] -= msafe;
+    }
+#pragma unroll
+    for (int i = 0; i < PAIR; ++i) {
+      f32x2_t ps = {0.0f, 0.0f};
+      uint32_t phi[4], plo[4];
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          // hardware 2^x (results below the normal range flush to 0, far below
+          // what a weight within 2^8 of the reference can matter)
+          const f32x2_t pp = {__builtin_amdgcn_exp2f(u[i][cg][j]), __builtin_amdgcn_exp2f(u[i][cg][j + 1])};
+          ps = (cg == 0 && j == 0) ? pp : ps + pp;
+          // P = hi + lo, both bf16 (hardware round-to-nearest-even conversions).
+          const uint32_t hi = bf16x2_bits(pp);
+          const f32x2_t back = {u32_as_f32(hi << 16), u32_as_f32(hi & 0xffff0000u)};
+          phi[cg * 2 + j / 2] = hi;
+          plo[cg * 2 + j / 2] = bf16x2_bits(pp - back);
+        }
+      lpart += ps[0] + ps[1];
+      const bf16x8_t pb_hi = u32x4_as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
+      const bf16x8_t pb_lo = u32x4_as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
+      if (PAIR == 1 || i == 1) {
+#pragma unroll
+        for (int v = 0; v < DVT; ++v) va[v] = vfrag(b0 + i, v);
+      }
+      // Eight independent accumulators: the hi pass, then the lo pass.
+#pragma unroll
+      for (int v = 0; v < DVT; ++v) o[v] = mfma16x16x32(va[v], pb_hi, o[v]);
+#pragma unroll
+      for (int v = 0; v < DVT; ++v) o[v] = mfma16x16x32(va[v], pb_lo, o[v]);
     }
   };
 
   const int nt = int((x.hi - x.lo + kTB - 1) / kTB);
-  // Tile t goes to buffer t&1, last read for tile t-2: every wave passed the
-  // barrier of tile t-1 only after finishing that.  Tiles past the split are
-  // staged and fetched like the others (from the query row) so that every
-  // thread issues the same loads; only their math is skipped.
-  auto step = [&](Pre& P, int t) __attribute__((always_inline)) {
-    stage(P, t & 1);
+  // PAIR tiles are staged per barrier, into buffers PAIR * (group & 1) + i;
+  // a buffer is last read for the group two before: every wave passed the
+  // barrier of the group in between only after finishing that.  Tiles past
+  // the split are staged and fetched like the others (from the query row) so
+  // that every thread issues the same loads; only their math is skipped.
+  auto step = [&](Pre& P0, Pre& P1, int t) __attribute__((always_inline)) {
+    const int b0 = PAIR * ((t / PAIR) & 1);
+    stage(P0, b0);
+    if (PAIR == 2) stage(P1, b0 + 1);
     __syncthreads();
-    fetch(P, t + SETS);
-    if (has && t < nt) compute(t & 1);
+    fetch(P0, t + SETS);
+    if (PAIR == 2) fetch(P1, t + 1 + SETS);
+    if (has && t < nt) compute(b0);
   };
   Pre P0, P1, P2, P3;
   fetch(P0, 0);
@@ -410,11 +496,16 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
     fetch(P3, 3);
   }
   for (int t0 = 0; t0 < nt; t0 += SETS) {
-    step(P0, t0);
-    step(P1, t0 + 1);
-    if (SETS == 4) {
-      step(P2, t0 + 2);
-      step(P3, t0 + 3);
+    if (PAIR == 2) {
+      step(P0, P1, t0);
+      if (SETS == 4) step(P2, P3, t0 + 2);
+    } else {
+      step(P0, P0, t0);
+      step(P1, P1, t0 + 1);
+      if (SETS == 4) {
+        step(P2, P2, t0 + 2);
+        step(P3, P3, t0 + 3);
+      }
     }
   }
 
@@ -438,7 +529,7 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
             make_float4(o[v][0] * inv, o[v][1] * inv, o[v][2] * inv, o[v][3] * inv);
       }
     }
-    if (a.lse && g == 0) a.lse[r * H + h] = lt > 0.0f ? (mrun + log2f(lt)) * kLn2 : -INFINITY;
+    if (a.lse && g == 0) a.lse[r * H + h] = lt > 0.0f ? (mref + log2f(lt)) * kLn2 : -INFINITY;
     return;
   }
   // Partials for the merge kernel: un-normalised O, running max (log2 units), sum.
@@ -448,79 +539,71 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
 #pragma unroll
   for (int v = 0; v < DVT; ++v)
     *reinterpret_cast<float4*>(part + v * 16 + 4 * g) = make_float4(o[v][0], o[v][1], o[v][2], o[v][3]);
-  if (g == 0) *reinterpret_cast<float2*>(ml) = make_float2(mrun, lt);
+  if (g == 0) *reinterpret_cast<float2*>(ml) = make_float2(mref, lt);
 }
 
-// Log-sum-exp merge of the split partials of one row and HPW heads: every
-// thread owns one 16-byte column chunk of one head and keeps eight splits'
-// loads in flight.
+// Log-sum-exp merge of the split partials: one thread per (row, head, 16-byte
+// column chunk).  The (max, sum) pairs and partial rows of up to 16 splits are
+// loaded together, so every load of a thread is in flight at once; longer rows
+// fold further groups of 16 in with an online rescale.
 template <int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, AttendPlan p) {
-  constexpr int CPH = D / 4;        // float4 chunks per head
-  constexpr int HPW = 256 / CPH;    // heads per workgroup
-  __shared__ float2 mls[kMaxSplits][HPW];
-  __shared__ float f[kMaxSplits][HPW];
-  __shared__ float lse_s[HPW];
-  const int hgs = (a.H + HPW - 1) / HPW;
-  const int64_t r = blockIdx.x / hgs;
-  const int h_begin = int(blockIdx.x % hgs) * HPW;
+  constexpr int CPH = D / 4;  // float4 chunks per head
+  constexpr int G = 16;       // splits per load group
+  const int H = a.H;
+  const int64_t gi = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (gi >= p.rows * H * CPH) return;
+  const int cc = int(gi % CPH) * 4;
+  const int64_t rh = gi / CPH;
+  const int64_t r = div64(rh, H);
+  const int h = int(rh - r * H);
   const RowSlots x = row_slots(a, p, r, 0);
   if (x.S <= 1) return;  // written directly by the attention kernel
   const int S = int(x.S);
-  const int H = a.H, tid = threadIdx.x;
-  const int nh = (H - h_begin) < HPW ? (H - h_begin) : HPW;
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
-  const float* part = reinterpret_cast<const float*>(ws + p.off_part) + r * p.splits * int64_t(H) * D;
-  const float* ml = reinterpret_cast<const float*>(ws + p.off_ml) + r * p.splits * int64_t(H) * 2;
-  for (int i = tid; i < S * nh; i += 256) {
-    const int sp = i / nh, hl = i % nh;
-    mls[sp][hl] = *reinterpret_cast<const float2*>(ml + (int64_t(sp) * H + h_begin + hl) * 2);
-  }
-  __syncthreads();
-  if (tid < nh) {
-    float mx = -INFINITY;
-    for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, mls[sp][tid].x);
-    const float ms = (mx == -INFINITY) ? 0.0f : mx;
-    float Lsum = 0.0f;
-    for (int sp = 0; sp < S; ++sp) Lsum = fmaf(exp2f(mls[sp][tid].x - ms), mls[sp][tid].y, Lsum);
-    const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-    for (int sp = 0; sp < S; ++sp) f[sp][tid] = exp2f(mls[sp][tid].x - ms) * inv;
-    lse_s[tid] = Lsum > 0.0f ? (mx + log2f(Lsum)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-  const int hl = tid / CPH, cc = (tid % CPH) * 4;
-  if (hl < nh) {
-    const float* src = part + int64_t(h_begin + hl) * D + cc;
-    const int64_t stride = int64_t(H) * D;
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    int sp = 0;
-    for (; sp + 8 <= S; sp += 8) {
-      float4 v[8];
+  const float* part = reinterpret_cast<const float*>(ws + p.off_part) + (r * p.splits * H + h) * int64_t(D) + cc;
+  const float* ml = reinterpret_cast<const float*>(ws + p.off_ml) + (r * p.splits * H + h) * 2;
+  const int64_t pstride = int64_t(H) * D, mstride = int64_t(H) * 2;
+  float M = -INFINITY, Lsum = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s0 = 0; s0 < S; s0 += G) {
+    float2 m2[G];
+    float4 v[G];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(src + (sp + u) * stride);
+    for (int u = 0; u < G; ++u) {
+      const int sp = (s0 + u) < S ? s0 + u : S - 1;  // clamped: every load is issued
+      m2[u] = *reinterpret_cast<const float2*>(ml + sp * mstride);
+      v[u] = *reinterpret_cast<const float4*>(part + sp * pstride);
+    }
+    float mc = M;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = f[sp + u][hl];
-        acc.x = fmaf(w, v[u].x, acc.x); acc.y = fmaf(w, v[u].y, acc.y);
-        acc.z = fmaf(w, v[u].z, acc.z); acc.w = fmaf(w, v[u].w, acc.w);
-      }
+    for (int u = 0; u < G; ++u)
+      if (s0 + u < S) mc = fmaxf(mc, m2[u].x);
+    // With no live slot so far everything is zero: subtract 0 instead of -inf.
+    const float ms = (mc == -INFINITY) ? 0.0f : mc;
+    const float corr = exp2f(M - ms);
+    Lsum *= corr;
+    acc.x *= corr; acc.y *= corr; acc.z *= corr; acc.w *= corr;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const float w = (s0 + u < S) ? exp2f(m2[u].x - ms) : 0.0f;
+      Lsum = fmaf(w, m2[u].y, Lsum);
+      acc.x = fmaf(w, v[u].x, acc.x); acc.y = fmaf(w, v[u].y, acc.y);
+      acc.z = fmaf(w, v[u].z, acc.z); acc.w = fmaf(w, v[u].w, acc.w);
     }
-    for (; sp < S; ++sp) {
-      const float4 v = *reinterpret_cast<const float4*>(src + sp * stride);
-      const float w = f[sp][hl];
-      acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
-    }
-    const int64_t oi = (r * H + h_begin + hl) * int64_t(D) + cc;
-    if (a.out_bf16) {
-      const uint32_t w0 = uint32_t(f32_to_bf16(acc.x)) | (uint32_t(f32_to_bf16(acc.y)) << 16);
-      const uint32_t w1 = uint32_t(f32_to_bf16(acc.z)) | (uint32_t(f32_to_bf16(acc.w)) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + oi) = make_uint2(w0, w1);
-    } else {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) = acc;
-    }
+    M = mc;
   }
-  if (a.lse && tid < nh) a.lse[r * H + h_begin + tid] = lse_s[tid];
+  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
+  const int64_t oi = rh * D + cc;
+  if (a.out_bf16) {
+    const uint32_t w0 = uint32_t(f32_to_bf16(acc.x)) | (uint32_t(f32_to_bf16(acc.y)) << 16);
+    const uint32_t w1 = uint32_t(f32_to_bf16(acc.z)) | (uint32_t(f32_to_bf16(acc.w)) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + oi) = make_uint2(w0, w1);
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) = acc;
+  }
+  if (a.lse && cc == 0) a.lse[rh] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------- fp32 kernel
@@ -729,17 +812,25 @@ int64_t attend_grid(const AttendPlan& p, bool bf16) {
   return bf16 ? p.rows * p.splits : p.groups * p.group_stride;
 }
 
+template <int D, bool HCA, int PAIR>
+static void launch_bf16_nw(const AttendArgs& a, const AttendPlan& p, dim3 grid) {
+  const int nw = (a.H + 15) / 16;
+  if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2, HCA, PAIR>), grid, dim3(128), 0, a.stream, a, p);
+  else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4, HCA, PAIR>), grid, dim3(256), 0, a.stream, a, p);
+  else hipLaunchKernelGGL((attend_bf16_kernel<D, 8, HCA, PAIR>), grid, dim3(512), 0, a.stream, a, p);
+}
+
 template <int D, bool HCA>
 static void launch_bf16(const AttendArgs& a, const AttendPlan& p) {
   const dim3 grid(unsigned(p.rows * p.splits));
-  const int nw = (a.H + 15) / 16;
-  if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2, HCA>), grid, dim3(128), 0, a.stream, a, p);
-  else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4, HCA>), grid, dim3(256), 0, a.stream, a, p);
-  else hipLaunchKernelGGL((attend_bf16_kernel<D, 8, HCA>), grid, dim3(512), 0, a.stream, a, p);
+  // Split rows (decode) have one workgroup per CU: stage tiles in pairs.  Many
+  // unsplit rows (prefill) keep the smaller LDS footprint for occupancy.
+  if (p.splits > 1) launch_bf16_nw<D, HCA, 2>(a, p, grid);
+  else launch_bf16_nw<D, HCA, 1>(a, p, grid);
   if (p.splits > 1) {
-    constexpr int HPW = 256 / (D / 4);
-    hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(unsigned(p.rows * ((a.H + HPW - 1) / HPW))), dim3(256),
-                       0, a.stream, a, p);
+    const int64_t threads = p.rows * a.H * (D / 4);
+    hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
+                       a.stream, a, p);
   }
 }
 
