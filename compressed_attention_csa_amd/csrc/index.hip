@@ -20,7 +20,7 @@
 //     the last WG then rescores exactly those slices and adds the dropped
 //     entries above the threshold before selecting again, so the result is
 //     exact for any input; on typical inputs no slice needs it.
-// Output order is deterministic (slice order, then a fixed order within the slice).
+// Output order is deterministic (a fixed order of the candidates).
 // bf16 / e4m3 keys are scored with 16x16x32 bf16 MFMA (query heads as rows,
 // entries as columns; e4m3 codes are widened exactly to bf16 in registers),
 // with 8 groups of 16 keys in flight per wave; fp32 keys use fp32 FMA with one
@@ -493,7 +493,6 @@ __device__ int64_t emit_get(int64_t n, uint64_t T, Get get, int64_t from, Dst ds
   return done - from;
 }
 
-constexpr int kKeysPerThread = kMaxSlice / kThreads;  // 16
 constexpr int kCandPerThread = 16;                    // last-WG register capacity
 
 struct LdsIdx {
@@ -505,7 +504,8 @@ struct LdsIdx {
 };
 static_assert(kBins == kMaxSlice, "the key buffer doubles as the histogram");
 
-template <int KK>
+// KPT: slice keys per thread (slice <= KPT * kThreads).
+template <int KK, int KPT>
 __global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPlan p, int64_t row0) {
   __shared__ LdsIdx L;
   const int64_t lr = div64(blockIdx.x, p.slices);  // row within this launch
@@ -518,9 +518,9 @@ __global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPl
 
   score_slice<KK>(a, ri, L.keys, L.q);
   const uint32_t base = uint32_t(ri.lo);
-  uint64_t v[kKeysPerThread];  // thread tid: slice elements tid + 256 u
+  uint64_t v[KPT];  // thread tid: slice elements tid + 256 u
 #pragma unroll
-  for (int u = 0; u < kKeysPerThread; ++u) {
+  for (int u = 0; u < KPT; ++u) {
     const int64_t x = tid + int64_t(u) * kThreads;
     v[u] = x < n ? rank_key(L.keys[x], base + uint32_t(x)) : 0ull;
   }
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPl
   if (in_regs) {
 #pragma unroll
     for (int u = 0; u < kCandPerThread; ++u) {
-      const int64_t g = int64_t(tid) * kCandPerThread + u;  // thread-major: candidate order
+      const int64_t g = int64_t(u) * kThreads + tid;  // element order: coalesced loads
       c[u] = g < total ? get_c(g) : 0ull;
     }
     T = select_rel(c, ri.kk, L.keys, L.sel);
@@ -647,6 +647,16 @@ IndexPlan plan_index(int B, int64_t T, int H_I, int64_t N_alloc, int top_k, int 
   return p;
 }
 
+// Registers sized to the slice: 2, 4, 8 or 16 keys per thread.
+template <int KK>
+static void launch_kpt(const IndexArgs& a, const IndexPlan& p, int64_t row0, dim3 grid, dim3 block) {
+  const int64_t kpt = (p.slice + kThreads - 1) / kThreads;
+  if (kpt <= 2) hipLaunchKernelGGL((idx_topk_kernel<KK, 2>), grid, block, 0, a.stream, a, p, row0);
+  else if (kpt <= 4) hipLaunchKernelGGL((idx_topk_kernel<KK, 4>), grid, block, 0, a.stream, a, p, row0);
+  else if (kpt <= 8) hipLaunchKernelGGL((idx_topk_kernel<KK, 8>), grid, block, 0, a.stream, a, p, row0);
+  else hipLaunchKernelGGL((idx_topk_kernel<KK, 16>), grid, block, 0, a.stream, a, p, row0);
+}
+
 hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p) {
   if (p.rows == 0) return hipSuccess;
   if (p.prefill) return launch_index_prefill(a, p);
@@ -655,12 +665,9 @@ hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p) {
     const int64_t nr = (p.rows - row0) < p.chunk_rows ? (p.rows - row0) : p.chunk_rows;
     const dim3 grid(unsigned(nr * p.slices));
     ProfScope prof("index_topk", a.stream);
-    if (a.key_kind == kKeyF32)
-      hipLaunchKernelGGL(idx_topk_kernel<kKeyF32>, grid, block, 0, a.stream, a, p, row0);
-    else if (a.key_kind == kKeyBF16)
-      hipLaunchKernelGGL(idx_topk_kernel<kKeyBF16>, grid, block, 0, a.stream, a, p, row0);
-    else
-      hipLaunchKernelGGL(idx_topk_kernel<kKeyE4M3>, grid, block, 0, a.stream, a, p, row0);
+    if (a.key_kind == kKeyF32) launch_kpt<kKeyF32>(a, p, row0, grid, block);
+    else if (a.key_kind == kKeyBF16) launch_kpt<kKeyBF16>(a, p, row0, grid, block);
+    else launch_kpt<kKeyE4M3>(a, p, row0, grid, block);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
