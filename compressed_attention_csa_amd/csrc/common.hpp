@@ -92,6 +92,13 @@ __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t packed, uint32_t& lo, 
   hi = (f32_as_u32(b[0]) >> 16) | (f32_as_u32(b[1]) & 0xffff0000u);
 }
 
+// Two e4m3fn codes (the low or the high 16 bits of packed) widened exactly to
+// a bf16 pair: every e4m3 value is a bf16 value, and a scale of 1 leaves it be.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t packed) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, HIGH));
+}
+
 // ---------------------------------------------------------------- ordering keys
 
 // Order-preserving image of a binary32 score: a > b  <=>  key(a) > key(b).

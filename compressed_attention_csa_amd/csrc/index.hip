@@ -103,6 +103,148 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* s_
 
 // ---------------------------------------------------------------- scoring
 
+// Sum of x over the four 16-lane rows of the wave, in every lane (two lane
+// swaps; no LDS round trip).
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(f32_as_u32(x), f32_as_u32(x), false, false);
+  const float y = u32_as_f32(a[0]) + u32_as_f32(a[1]);  // x[l] + x[l ^ 32]
+  const auto b = __builtin_amdgcn_permlane16_swap(f32_as_u32(y), f32_as_u32(y), false, false);
+  return u32_as_f32(b[0]) + u32_as_f32(b[1]);            // y[l] + y[l ^ 16]
+}
+
+// bf16 / e4m3 keys on 16x16x32 MFMA: query heads are the rows of A (zero past
+// H_I), 16 keys are the columns of B, so lane (g, col) ends with heads
+// 4g..4g+3 of key col.  Each wave takes groups of 16 keys; the loads of one
+// round (8 groups, 4 for 64-dim bf16 keys) are in flight while the previous
+// round is scored.
+// Loads are unconditional (groups past the slice re-read its last key), so
+// the compiler's wait counts stay exact.
+template <int KK, int DI>
+__device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowInfo& ri, uint32_t* keys,
+                                                 int64_t qrow) {
+  constexpr int CW = KK == kKeyBF16 ? 2 * DI / 16 : DI / 16;  // dwords of key per lane
+  constexpr int U = CW > 4 ? kUnroll / 2 : kUnroll;             // groups per round and wave
+  typedef uint32_t kregs_t __attribute__((ext_vector_type(U * CW)));
+  typedef float sregs_t __attribute__((ext_vector_type(U)));
+  struct Round {
+    kregs_t k;
+    sregs_t sc;
+  };
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
+  const int64_t n = ri.hi - ri.lo;
+  const int H_I = a.H_I;
+  const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q_idx) + qrow * DI;
+  // A operands: row = head col (zero past H_I), k-slots 8g..8g+7.  For 64 dims
+  // the k-slots of the two products map to dims 16g..16g+7 and 16g+8..16g+15,
+  // so a lane reads 16 contiguous dims of its key.
+  bf16x8_t qa0, qa1;
+  {
+    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
+    if (col < H_I) {
+      if (DI == 64) {
+        v0 = *reinterpret_cast<const uint4*>(q + col * 64 + 16 * g);
+        v1 = *reinterpret_cast<const uint4*>(q + col * 64 + 16 * g + 8);
+      } else {
+        v0 = *reinterpret_cast<const uint4*>(q + col * 32 + 8 * g);
+      }
+    }
+    qa0 = u32x4_as_bf16x8(v0);
+    qa1 = u32x4_as_bf16x8(v1);
+  }
+  float wr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = 4 * g + j;
+    wr[j] = (h < H_I) ? (a.w ? a.w[qrow + h] : 1.0f) : 0.0f;
+  }
+  const int64_t kb = ri.b * a.N_alloc + ri.lo;
+  const int64_t ngroups = (n + 15) / 16;
+  constexpr int RS = kWaves * U;  // groups per round
+  const int nr = int((ngroups + RS - 1) / RS);
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_idx) + kb * DI * (KK == kKeyBF16 ? 2 : 1);
+  const float* sbase = KK == kKeyE4M3 ? a.k_scale + kb : nullptr;
+  const uint32_t last = uint32_t(n - 1);
+  auto load = [&](Round& R, int rr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t e = uint32_t((int64_t(rr) * RS + u * kWaves + wid) * 16 + col);
+      const uint32_t ec = e < last ? e : last;
+      if (KK == kKeyBF16) {
+        const uint8_t* kp = kbase + ec * (DI * 2);
+        const uint4 x0 = *reinterpret_cast<const uint4*>(kp + (DI == 64 ? 32 : 16) * g);
+        R.k[CW * u] = x0.x; R.k[CW * u + 1] = x0.y; R.k[CW * u + 2] = x0.z; R.k[CW * u + 3] = x0.w;
+        if (DI == 64) {
+          const uint4 x1 = *reinterpret_cast<const uint4*>(kp + 32 * g + 16);
+          R.k[CW * u + 4] = x1.x; R.k[CW * u + 5] = x1.y; R.k[CW * u + 6] = x1.z; R.k[CW * u + 7] = x1.w;
+        }
+      } else {
+        const uint8_t* kp = kbase + ec * DI;
+        if (DI == 64) {
+          const uint4 x0 = *reinterpret_cast<const uint4*>(kp + 16 * g);
+          R.k[CW * u] = x0.x; R.k[CW * u + 1] = x0.y; R.k[CW * u + 2] = x0.z; R.k[CW * u + 3] = x0.w;
+        } else {
+          const uint2 x0 = *reinterpret_cast<const uint2*>(kp + 8 * g);
+          R.k[CW * u] = x0.x; R.k[CW * u + 1] = x0.y;
+        }
+        R.sc[u] = sbase[ec];
+      }
+    }
+  };
+  auto score = [&](const Round& R, int rr) __attribute__((always_inline)) {
+    f32x4_t acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint4 b0, b1 = make_uint4(0, 0, 0, 0);
+      if (KK == kKeyBF16) {
+        b0 = make_uint4(R.k[CW * u], R.k[CW * u + 1], R.k[CW * u + 2], R.k[CW * u + 3]);
+        if (DI == 64) b1 = make_uint4(R.k[CW * u + 4], R.k[CW * u + 5], R.k[CW * u + 6], R.k[CW * u + 7]);
+      } else {
+        // e4m3 codes widen exactly to bf16 (scale 1).
+        b0.x = e4m3x2_to_bf16x2<false>(R.k[CW * u]);
+        b0.y = e4m3x2_to_bf16x2<true>(R.k[CW * u]);
+        b0.z = e4m3x2_to_bf16x2<false>(R.k[CW * u + 1]);
+        b0.w = e4m3x2_to_bf16x2<true>(R.k[CW * u + 1]);
+        if (DI == 64) {
+          b1.x = e4m3x2_to_bf16x2<false>(R.k[CW * u + 2]);
+          b1.y = e4m3x2_to_bf16x2<true>(R.k[CW * u + 2]);
+          b1.z = e4m3x2_to_bf16x2<false>(R.k[CW * u + 3]);
+          b1.w = e4m3x2_to_bf16x2<true>(R.k[CW * u + 3]);
+        }
+      }
+      f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+      c = mfma16x16x32(qa0, u32x4_as_bf16x8(b0), c);
+      if (DI == 64) c = mfma16x16x32(qa1, u32x4_as_bf16x8(b1), c);
+      acc[u] = c;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float part = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // ReLU as an integer max: negative floats have negative bit patterns.
+        const float rl = u32_as_f32(uint32_t(max(int32_t(f32_as_u32(acc[u][j])), 0)));
+        part = fmaf(wr[j], rl, part);
+      }
+      part = sum_rows4(part);
+      if (KK == kKeyE4M3) part *= R.sc[u];
+      const int64_t e = (int64_t(rr) * RS + u * kWaves + wid) * 16 + col;
+      if (g == 0 && e < n) keys[e] = score_key(part);
+    }
+  };
+  if (nr > 0) {
+    Round R0, R1;
+    load(R0, 0);
+    for (int rr = 0; rr < nr; rr += 2) {
+      load(R1, rr + 1);
+      score(R0, rr);
+      if (rr + 1 >= nr) break;
+      load(R0, rr + 2);
+      score(R1, rr + 1);
+    }
+  }
+  __syncthreads();
+}
+
 // Scores of entries [lo, hi) of row ri into keys[0 .. hi-lo).
 template <int KK>
 __device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* keys, float* s_q) {
@@ -135,91 +277,10 @@ __device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* key
     }
     __syncthreads();
     return;
+  } else if (d_I == 64) {
+    score_slice_mfma<KK, 64>(a, ri, keys, qrow);
   } else {
-    const int lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
-    const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q_idx) + qrow * d_I;
-    // A operands: row = head col (zero past H_I), k-slots 8g..8g+7.  For d_I = 64
-    // the k-slots of the two products map to dims 16g..16g+7 and 16g+8..16g+15,
-    // so a lane reads 16 contiguous dims of its key.
-    bf16x8_t qa0, qa1;
-    {
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-      if (col < H_I) {
-        if (d_I == 64) {
-          v0 = *reinterpret_cast<const uint4*>(q + col * 64 + 16 * g);
-          v1 = *reinterpret_cast<const uint4*>(q + col * 64 + 16 * g + 8);
-        } else {
-          v0 = *reinterpret_cast<const uint4*>(q + col * 32 + 8 * g);
-        }
-      }
-      qa0 = u32x4_as_bf16x8(v0);
-      qa1 = u32x4_as_bf16x8(v1);
-    }
-    float wr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int h = 4 * g + j;
-      wr[j] = (h < H_I) ? (a.w ? a.w[qrow + h] : 1.0f) : 0.0f;
-    }
-    const int64_t kb = ri.b * a.N_alloc + ri.lo;
-    const int64_t ngroups = (n + 15) / 16;
-    for (int64_t g0 = wid; g0 < ngroups; g0 += kWaves * kUnroll) {
-      uint4 k0[kUnroll], k1[kUnroll];
-      float ksc[kUnroll];
-      // Issue every load of this round first.
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t e = (g0 + int64_t(u) * kWaves) * 16 + col;
-        k0[u] = make_uint4(0, 0, 0, 0);
-        k1[u] = make_uint4(0, 0, 0, 0);
-        ksc[u] = 1.0f;
-        if (e < n) {
-          if (KK == kKeyBF16) {
-            const bf16_t* kp = reinterpret_cast<const bf16_t*>(a.k_idx) + (kb + e) * d_I;
-            if (d_I == 64) {
-              k0[u] = *reinterpret_cast<const uint4*>(kp + 16 * g);
-              k1[u] = *reinterpret_cast<const uint4*>(kp + 16 * g + 8);
-            } else {
-              k0[u] = *reinterpret_cast<const uint4*>(kp + 8 * g);
-            }
-          } else {
-            const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k_idx) + (kb + e) * d_I;
-            if (d_I == 64) {
-              k0[u] = *reinterpret_cast<const uint4*>(kp + 16 * g);
-            } else {
-              const uint2 r2 = *reinterpret_cast<const uint2*>(kp + 8 * g);
-              k0[u] = make_uint4(r2.x, r2.y, 0, 0);
-            }
-            ksc[u] = a.k_scale[kb + e];
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t e = (g0 + int64_t(u) * kWaves) * 16 + col;
-        uint4 b0 = k0[u], b1 = k1[u];
-        if (KK == kKeyE4M3) {
-          const uint4 raw = k0[u];
-          e4m3x4_to_bf16x4(raw.x, b0.x, b0.y);
-          e4m3x4_to_bf16x4(raw.y, b0.z, b0.w);
-          if (d_I == 64) {
-            e4m3x4_to_bf16x4(raw.z, b1.x, b1.y);
-            e4m3x4_to_bf16x4(raw.w, b1.z, b1.w);
-          }
-        }
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = mfma16x16x32(qa0, u32x4_as_bf16x8(b0), acc);
-        if (d_I == 64) acc = mfma16x16x32(qa1, u32x4_as_bf16x8(b1), acc);
-        float part = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) part = fmaf(wr[j], fmaxf(acc[j], 0.0f), part);
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        if (KK == kKeyE4M3) part *= ksc[u];
-        if (e < n && g == 0) keys[e] = score_key(part);
-      }
-    }
-    __syncthreads();
+    score_slice_mfma<KK, 32>(a, ri, keys, qrow);
   }
 }
 
@@ -505,8 +566,10 @@ struct LdsIdx {
 static_assert(kBins == kMaxSlice, "the key buffer doubles as the histogram");
 
 // KPT: slice keys per thread (slice <= KPT * kThreads).
+// (At most 256 registers, so that two workgroups share a CU.)
 template <int KK, int KPT>
-__global__ __launch_bounds__(kThreads) void idx_topk_kernel(IndexArgs a, IndexPlan p, int64_t row0) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void idx_topk_kernel(
+    IndexArgs a, IndexPlan p, int64_t row0) {
   __shared__ LdsIdx L;
   const int64_t lr = div64(blockIdx.x, p.slices);  // row within this launch
   const int64_t r = row0 + lr;

@@ -196,6 +196,37 @@ def test_index_topk_all_scores_equal():
     np.testing.assert_array_equal(np.sort(out[0, 0].cpu().numpy()), np.arange(k))
 
 
+@pytest.mark.parametrize("d_I", [64, 32])
+def test_index_topk_every_e4m3_code_scores_exactly(d_I):
+    """Entry j of the fp8 key cache holds code j in one dimension and +0 in the
+    others (NaN codes replaced by +0); every head's query picks that dimension
+    with +1 (sequence 0) or -1 (sequence 1), so the score is 8 * ReLU(+-value),
+    exact in binary32.  With k = 256 every entry is selected and every score
+    must equal the oracle's bit for bit: a code the kernel widens wrongly
+    (subnormals, the sign, the largest exponents) shows up here."""
+    N, H_I, m = 256, 8, 4
+    code = np.arange(256, dtype=np.uint8)
+    code[(code & 0x7F) == 0x7F] = 0
+    codes = np.zeros((2, N, d_I), dtype=np.uint8)
+    codes[:, :, 5] = code
+    scale = np.ones((2, N), dtype=np.float32)
+    q = torch.zeros((2, 1, H_I, d_I), dtype=torch.bfloat16)
+    q[0, 0, :, 5] = 1.0
+    q[1, 0, :, 5] = -1.0
+    out_idx = torch.empty((2, 1, N), dtype=torch.int32, device=DEV)
+    out_score = torch.empty((2, 1, N), dtype=torch.float32, device=DEV)
+    say("index_topk every e4m3 code, d_I", d_I)
+    csa.csa_index_topk(q.to(DEV), None, torch.from_numpy(codes).to(DEV), torch.from_numpy(scale).to(DEV),
+                       4 * N - 1, m, N, out_idx, out_score)
+    torch.cuda.synchronize()
+    stored = formats.e4m3_decode(codes) * scale[:, :, None]
+    for b in range(2):
+        ref = method.index_scores(f64(q[b]), None, stored[b], 4 * N - 1, m)[0]
+        idx = out_idx[b, 0].cpu().numpy()
+        np.testing.assert_array_equal(np.sort(idx), np.arange(N))
+        np.testing.assert_array_equal(out_score[b, 0].cpu().numpy().astype(np.float64), ref[idx])
+
+
 # ----------------------------------------------------------------------------- attention
 
 
