@@ -292,6 +292,7 @@ __device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* key
 
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
+constexpr int kRelBins = 1024;  // bins of the range-relative first pass
 
 struct SelLds {
   uint32_t scan[kWaves];
@@ -363,9 +364,9 @@ __device__ __forceinline__ uint64_t select_regs(const uint64_t (&v)[KPT], int64_
   return prefix;  // remaining low bits zero
 }
 
-// The same threshold with a first pass whose bins span only the occupied range
-// of the keys' upper halves (min .. max), which usually leaves a handful of
-// keys in the bin of the need-th key.  Those are then ranked exactly against
+// The same threshold with a first pass whose 1024 bins span only the occupied
+// range of the keys' upper halves (min .. max), which usually leaves a handful
+// of keys in the bin of the need-th key.  Those are then ranked exactly against
 // each other in LDS; finer radix passes follow only if the bin is crowded.
 template <int KPT>
 __device__ __forceinline__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t need, uint32_t* hist, SelLds& S) {
@@ -384,7 +385,7 @@ __device__ __forceinline__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t
     S.lo[wid] = lo;
     S.hi[wid] = hi;
   }
-  for (int x = tid; x < kBins; x += kThreads) hist[x] = 0;
+  for (int x = tid; x < kRelBins; x += kThreads) hist[x] = 0;
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
@@ -392,14 +393,14 @@ __device__ __forceinline__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t
     hi = max(hi, S.hi[w]);
   }
   int sh = 0;
-  while ((hi >> sh) - (lo >> sh) >= uint32_t(kBins)) ++sh;
+  while ((hi >> sh) - (lo >> sh) >= uint32_t(kRelBins)) ++sh;
   const uint32_t base = lo >> sh;
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
-    if (v[u] != 0) atomicAdd(&hist[((uint32_t(v[u] >> 32) >> sh) - base) & (kBins - 1)], 1u);
+    if (v[u] != 0) atomicAdd(&hist[((uint32_t(v[u] >> 32) >> sh) - base) & (kRelBins - 1)], 1u);
   __syncthreads();
   uint32_t dstar, above, in_digit;
-  pick_digit(hist, kBins, need, S, dstar, above, in_digit);
+  pick_digit(hist, kRelBins, need, S, dstar, above, in_digit);
   const int hi_bit = 32 + sh;
   const uint64_t top = uint64_t(base + dstar);
   const uint64_t prefix = top << hi_bit;
