@@ -289,14 +289,15 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   uint4 pre0 = make_uint4(0, 0, 0, 0), pre1 = make_uint4(0, 0, 0, 0);
   float psc = 1.0f;
   const int id0 = tid % CHUNKS, id1 = (tid + kThreads) % CHUNKS;
+  int ss = 1;  // entry stride of the sweep (the sample stride in the sampling pass)
   auto chunk_ptr = [&](int t, int id) {
-    const int ge = min(t * kTileE + id / CPG, cmax - 1);
+    const int ge = min((t * kTileE + id / CPG) * ss, cmax - 1);
     return reinterpret_cast<const uint4*>(kbytes + int64_t(ge) * (DI * KB) + (id % CPG) * 16);
   };
   auto fetch = [&](int t) {
     pre0 = *chunk_ptr(t, id0);
     if (LOADS > 1) pre1 = *chunk_ptr(t, id1);
-    if (KK == kKeyE4M3) psc = a.k_scale[b * a.N_alloc + min(t * kTileE + (tid & (kTileE - 1)), cmax - 1)];
+    if (KK == kKeyE4M3) psc = a.k_scale[b * a.N_alloc + min((t * kTileE + (tid & (kTileE - 1))) * ss, cmax - 1)];
   };
   // Writes the prefetched chunks to LDS buffer `buf`; fp8 keys are widened to
   // bf16 here, once per workgroup, rather than by every wave that reads them.
@@ -388,63 +389,123 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     __builtin_amdgcn_wave_barrier();
   };
 
-  if (ntiles > 0) {
-    fetch(0);
-    stage(0);
-    fetch(ntiles > 1 ? 1 : 0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const int e0 = t * kTileE;
-    // Tile t+1 (loaded during the previous tile) goes to the other buffer, which
-    // every wave finished reading before the last barrier; tile t+2 then stays
-    // in flight for the whole of this tile.
-    if (t + 1 < ntiles) stage(cur ^ 1);
-    fetch(t + 2 < ntiles ? t + 2 : ntiles - 1);
-    // All B operands of the tile are read up front, so the LDS latency is paid
-    // once per tile rather than once per group.
-    uint4 bo0[GROUPS], bo1[GROUPS];
-#pragma unroll
-    for (int gi = 0; gi < GROUPS; ++gi) operands(cur, gi, bo0[gi], bo1[gi]);
-    f32x4_t acc[2], nxt[2];
-    products(bo0[0], bo1[0], acc);
-    const int lim = cq - e0 - col;  // entry 16*gi + col of the tile is visible iff 16*gi < lim
-#pragma unroll
-    for (int gi = 0; gi < GROUPS; ++gi) {
-      if (gi + 1 < GROUPS) products(bo0[gi + 1], bo1[gi + 1], nxt);
-      const int e = gi * 16 + col;
-      float s = 0.0f;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * hf + j], relu(acc[hf][j]), s);
-      if (KK == kKeyE4M3) s *= L.scale[cur][e];
-      // The screen admits every entry whose rank key can exceed tau (and a few
-      // equal-score ones that cannot); the exact test runs when staged entries
-      // are drained, so the per-pair cost here is two compares.
-      const bool screen = 16 * gi < lim && !(s < tau_s);
-      const uint64_t m = __ballot(screen);
-      if (m) {
-        const uint32_t mg = uint32_t(m >> (16 * g)) & 0xffffu;
-        if (screen) mystg[scnt + __popc(mg & below_g)] = (uint64_t(__float_as_uint(s)) << 32) | uint32_t(e0 + e);
-        scnt += __popc(mg);
-      }
-      if (gi + 1 < GROUPS) {
-        acc[0] = nxt[0];
-        acc[1] = nxt[1];
+  // Sampling pass.  With many more visible entries than k, a first sweep over
+  // every ss-th entry (about 2048 of them) finds, per query, the r-th best
+  // sampled score, r = 3 * ceil(need / ss) + 8.  The full sweep then starts
+  // with that score as its threshold, which prunes about all but r * ss
+  // entries (near 3k) from the start instead of admitting every entry until
+  // the buffer first fills.  The pruning is checked afterwards: a query whose
+  // full sweep kept fewer than need candidates (possible only when more than r
+  // of the sampled entries rank among its true top-k) is swept again with no
+  // threshold, so the result stays exact for any input.
+  const bool sampling = a.top_k > 0 && cmax >= 16 * a.top_k && cmax >= 32 * kTileE;
+  int sstride = 2;
+  while (sampling && int64_t(sstride) * 2048 < cmax) sstride *= 2;
+  bool active = true;  // this lane's query takes part in the current pass
+  bool pruned = false; // this lane's query started the full sweep above zero
+#pragma unroll 1
+  for (int pass = sampling ? 0 : 1; pass < 3; ++pass) {
+    if (pass == 2) {
+      const bool redo = qvalid && pruned && cnt < need_l;
+      if (!__syncthreads_or(redo)) break;
+      active = redo;
+      if (redo) {
+        tau = 0ull;
+        tau_s = key_score(0u);
+        cnt = 0;
+        top_hi = 0u;
       }
     }
-    // Staging areas that cannot take another tile are drained.
-#pragma unroll 1
-    for (int q = 0; q < kPrefillQPW; ++q)
-      if (__builtin_amdgcn_readlane(scnt, 16 * q) > kStage - kTileE) drain(q);
+    ss = pass == 0 ? sstride : 1;
+    const int ntp = pass == 0 ? ((cmax + ss - 1) / ss + kTileE - 1) / kTileE : ntiles;
+    const int cqv = pass == 0 ? (cq + ss - 1) / ss : cq;
+    if (ntp > 0) {
+      fetch(0);
+      stage(0);
+      fetch(ntp > 1 ? 1 : 0);
+    }
     __syncthreads();
-  }
+
+    for (int t = 0; t < ntp; ++t) {
+      const int cur = t & 1;
+      const int e0 = t * kTileE;
+      // Tile t+1 (loaded during the previous tile) goes to the other buffer, which
+      // every wave finished reading before the last barrier; tile t+2 then stays
+      // in flight for the whole of this tile.
+      if (t + 1 < ntp) stage(cur ^ 1);
+      fetch(t + 2 < ntp ? t + 2 : ntp - 1);
+      // All B operands of the tile are read up front, so the LDS latency is paid
+      // once per tile rather than once per group.
+      uint4 bo0[GROUPS], bo1[GROUPS];
+  #pragma unroll
+      for (int gi = 0; gi < GROUPS; ++gi) operands(cur, gi, bo0[gi], bo1[gi]);
+      f32x4_t acc[2], nxt[2];
+      products(bo0[0], bo1[0], acc);
+      const int lim = cqv - e0 - col;  // entry 16*gi + col of the tile is visible iff 16*gi < lim
+  #pragma unroll
+      for (int gi = 0; gi < GROUPS; ++gi) {
+        if (gi + 1 < GROUPS) products(bo0[gi + 1], bo1[gi + 1], nxt);
+        const int e = gi * 16 + col;
+        float s = 0.0f;
+  #pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * hf + j], relu(acc[hf][j]), s);
+        if (KK == kKeyE4M3) s *= L.scale[cur][e];
+        // The screen admits every entry whose rank key can exceed tau (and a few
+        // equal-score ones that cannot); the exact test runs when staged entries
+        // are drained, so the per-pair cost here is two compares.
+        const bool screen = 16 * gi < lim && !(s < tau_s) && active;
+        const uint64_t m = __ballot(screen);
+        if (m) {
+          const uint32_t mg = uint32_t(m >> (16 * g)) & 0xffffu;
+          if (screen) mystg[scnt + __popc(mg & below_g)] = (uint64_t(__float_as_uint(s)) << 32) | uint32_t(e0 + e);
+          scnt += __popc(mg);
+        }
+        if (gi + 1 < GROUPS) {
+          acc[0] = nxt[0];
+          acc[1] = nxt[1];
+        }
+      }
+      // Staging areas that cannot take another tile are drained.
+  #pragma unroll 1
+      for (int q = 0; q < kPrefillQPW; ++q)
+        if (__builtin_amdgcn_readlane(scnt, 16 * q) > kStage - kTileE) drain(q);
+      __syncthreads();
+    }
+  #pragma unroll 1
+    for (int q = 0; q < kPrefillQPW; ++q)
+      if (__builtin_amdgcn_readlane(scnt, 16 * q) > 0) drain(q);
+    if (pass == 0) {
+      // Starting threshold of each query: the r-th best sampled rank key with
+      // its index half cleared (so every entry with that score passes).
+      wait_mem();  // every drain of this wave has reached the buffers
+      uint64_t t0k = 0ull;
 #pragma unroll 1
-  for (int q = 0; q < kPrefillQPW; ++q)
-    if (__builtin_amdgcn_readlane(scnt, 16 * q) > 0) drain(q);
+      for (int q = 0; q < kPrefillQPW; ++q) {
+        const int n = __builtin_amdgcn_readlane(cnt, 16 * q);
+        const int need = __shfl(need_l, 16 * q);
+        const int r = 3 * ((need + ss - 1) / ss) + 8;
+        const int cqq = __shfl(cq, 16 * q);
+        uint64_t T = 0ull;
+        if (need > 0 && cqq >= 16 * need && n >= r) {
+          const uint64_t tq = shfl64(tau, 16 * q);
+          const uint32_t tp = __builtin_amdgcn_readlane(top_hi, 16 * q);
+          int kept;
+          T = wave_threshold(bufs + (rowbase + qw0 + q) * cap, n, r, true, 0, tq, tp, L.hist[wid], kept) &
+              0xffffffff00000000ull;
+        }
+        if (g == q) t0k = T;
+      }
+      tau = t0k;
+      tau_s = key_score(uint32_t(t0k >> 32));  // t0k = 0: NaN, admits everything
+      pruned = t0k != 0ull;
+      cnt = 0;
+      scnt = 0;
+      top_hi = 0u;
+      __syncthreads();  // the tiles and staging areas are reused by the next pass
+    }
+  }
 
   // ---- final exact selection for each query of this wave
   wait_mem();  // every drain of this wave has reached the buffers

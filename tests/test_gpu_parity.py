@@ -196,6 +196,28 @@ def test_index_topk_all_scores_equal():
     np.testing.assert_array_equal(np.sort(out[0, 0].cpu().numpy()), np.arange(k))
 
 
+def test_index_topk_prefill_sampled_threshold_falls_back():
+    """Prefill rows whose best entries all sit at multiples of 32 (the sample
+    stride of a 40000-entry sweep): the threshold taken from the sampled
+    entries then prunes away most of the true top-k, and the kernel must notice
+    and sweep those queries again without a threshold."""
+    B, T, H_I, d_I, N, m, k = 1, 70, 8, 64, 40000, 4, 64
+    t0 = 4 * N - T
+    q = gen("smp_q", (B, T, H_I, d_I), "f32", seed=3).abs().to(torch.bfloat16)
+    keys = gen("smp_k", (B, N, d_I), "f32", seed=4)
+    keys[:, ::32, :] = 3.0 + 0.3 * keys[:, ::32, :]
+    keys = keys.to(torch.bfloat16)
+    out_idx = torch.full((B, T, k), 12345, dtype=torch.int32, device=DEV)
+    out_score = torch.empty((B, T, k), dtype=torch.float32, device=DEV)
+    say("index_topk prefill, winners on the sample grid")
+    csa.csa_index_topk(q.to(DEV), None, keys.to(DEV), None, t0, m, k, out_idx, out_score)
+    torch.cuda.synchronize()
+    scores = method.index_scores(f64(q[0]), None, f64(keys[0]), t0, m)
+    idx = out_idx[0].cpu().numpy()
+    check_topk_rows(idx, out_score[0].cpu().numpy(), scores, k)
+    assert np.all(idx % 32 == 0), "winners are the entries on the sample grid"
+
+
 @pytest.mark.parametrize("d_I", [64, 32])
 def test_index_topk_every_e4m3_code_scores_exactly(d_I):
     """Entry j of the fp8 key cache holds code j in one dimension and +0 in the
