@@ -36,6 +36,8 @@
 // 5k/4 candidates, and the buffer is compacted in order.  Everything dropped ranks below at least k
 // candidates already kept, so the final exact selection over the buffer is the
 // exact top-k; the output lists the winners by increasing entry index.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.h"
 
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   const bool sampling = a.top_k > 0 && cmax >= 16 * a.top_k && cmax >= 32 * kTileE;
   int sstride = 2;
   while (sampling && int64_t(sstride) * 2048 < cmax) sstride *= 2;
-  bool active = true;  // this lane's query takes part in the current pass
+  bool active = qvalid;  // this lane's query takes part in the current pass
   bool pruned = false; // this lane's query started the full sweep above zero
 #pragma unroll 1
   for (int pass = sampling ? 0 : 1; pass < 3; ++pass) {
@@ -419,6 +421,11 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     ss = pass == 0 ? sstride : 1;
     const int ntp = pass == 0 ? ((cmax + ss - 1) / ss + kTileE - 1) / kTileE : ntiles;
     const int cqv = pass == 0 ? (cq + ss - 1) / ss : cq;
+    // Tiles every query of the workgroup sees in full need no visibility test
+    // (its first query sees the fewest entries).
+    const int64_t cfirst64 = (a.t0 + i0 + 1) / a.m < a.N_alloc ? (a.t0 + i0 + 1) / a.m : a.N_alloc;
+    const int cfull = pass == 0 ? (int(cfirst64) + ss - 1) / ss : int(cfirst64);
+    const uint64_t act_mask = __ballot(active);
     if (ntp > 0) {
       fetch(0);
       stage(0);
@@ -439,34 +446,43 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
       uint4 bo0[GROUPS], bo1[GROUPS];
   #pragma unroll
       for (int gi = 0; gi < GROUPS; ++gi) operands(cur, gi, bo0[gi], bo1[gi]);
-      f32x4_t acc[2], nxt[2];
-      products(bo0[0], bo1[0], acc);
       const int lim = cqv - e0 - col;  // entry 16*gi + col of the tile is visible iff 16*gi < lim
+      // The groups of the tile; FULL: every query of the workgroup sees the
+      // whole tile, so the visibility test is left out.
+      auto groups = [&](auto full_c) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_c)::value;
+        f32x4_t acc[2], nxt[2];
+        products(bo0[0], bo1[0], acc);
   #pragma unroll
-      for (int gi = 0; gi < GROUPS; ++gi) {
-        if (gi + 1 < GROUPS) products(bo0[gi + 1], bo1[gi + 1], nxt);
-        const int e = gi * 16 + col;
-        float s = 0.0f;
+        for (int gi = 0; gi < GROUPS; ++gi) {
+          if (gi + 1 < GROUPS) products(bo0[gi + 1], bo1[gi + 1], nxt);
+          const int e = gi * 16 + col;
+          float s = 0.0f;
   #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+          for (int hf = 0; hf < 2; ++hf)
   #pragma unroll
-          for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * hf + j], relu(acc[hf][j]), s);
-        if (KK == kKeyE4M3) s *= L.scale[cur][e];
-        // The screen admits every entry whose rank key can exceed tau (and a few
-        // equal-score ones that cannot); the exact test runs when staged entries
-        // are drained, so the per-pair cost here is two compares.
-        const bool screen = 16 * gi < lim && !(s < tau_s) && active;
-        const uint64_t m = __ballot(screen);
-        if (m) {
-          const uint32_t mg = uint32_t(m >> (16 * g)) & 0xffffu;
-          if (screen) mystg[scnt + __popc(mg & below_g)] = (uint64_t(__float_as_uint(s)) << 32) | uint32_t(e0 + e);
-          scnt += __popc(mg);
+            for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * hf + j], relu(acc[hf][j]), s);
+          if (KK == kKeyE4M3) s *= L.scale[cur][e];
+          // The screen admits every entry whose rank key can exceed tau (and a
+          // few equal-score ones that cannot); the exact test runs when staged
+          // entries are drained.  Ballots of the compares themselves: each is
+          // one compare into a lane mask.
+          uint64_t m = __ballot(!(s < tau_s)) & act_mask;
+          if (!FULL) m &= __ballot(16 * gi < lim);
+          if (m) {
+            const uint32_t mg = uint32_t(m >> (16 * g)) & 0xffffu;
+            if ((m >> lane) & 1ull)
+              mystg[scnt + __popc(mg & below_g)] = (uint64_t(__float_as_uint(s)) << 32) | uint32_t(e0 + e);
+            scnt += __popc(mg);
+          }
+          if (gi + 1 < GROUPS) {
+            acc[0] = nxt[0];
+            acc[1] = nxt[1];
+          }
         }
-        if (gi + 1 < GROUPS) {
-          acc[0] = nxt[0];
-          acc[1] = nxt[1];
-        }
-      }
+      };
+      if (e0 + kTileE <= cfull) groups(std::integral_constant<bool, true>());
+      else groups(std::integral_constant<bool, false>());
       // Staging areas that cannot take another tile are drained.
   #pragma unroll 1
       for (int q = 0; q < kPrefillQPW; ++q)
