@@ -59,10 +59,15 @@ __device__ __forceinline__ RowInfo row_info(const IndexArgs& a, const IndexPlan&
   int64_t hi = ri.lo + p.slice;
   ri.hi = hi < ri.c ? hi : ri.c;
   if (ri.hi < ri.lo) ri.hi = ri.lo;
-  // Local candidates per slice: about 4x the slice's expected share of winners.
-  int64_t share = div64(ri.kk + ri.S - 1, ri.S);
-  int64_t kl = ((4 * share + 31) / 32) * 32;
-  if (kl < 32) kl = 32;
+  // Local candidates per slice: the slice's expected share of winners plus
+  // four standard deviations of that count (about sqrt(share)) and a margin,
+  // rounded up to 8.  A slice holding more winners is caught by its
+  // certificate and rescored.
+  const int64_t share = div64(ri.kk + ri.S - 1, ri.S);
+  int64_t sd = 1;
+  while (sd * sd < share) ++sd;
+  int64_t kl = ((share + 4 * sd + 4 + 7) / 8) * 8;
+  if (kl < 16) kl = 16;
   if (kl > p.slice) kl = p.slice;
   ri.kloc = kl;
   return ri;
