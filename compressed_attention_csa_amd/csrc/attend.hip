@@ -759,12 +759,14 @@ AttendPlan plan_attend(bool bf16, int B, int64_t T, int H, int d, int64_t max_en
   };
   if (bf16) {
     // Every head of a row in one workgroup; split the slots until there are
-    // about 256 workgroups, keeping at least 4 tiles of 32 per split.
+    // about 256 workgroups, keeping at least 4 tiles of 32 per split (2 with
+    // at most 64 heads, whose split partials are half the size to merge).
     p.groups = 1;
     int64_t splits = 1;
     if (p.rows > 0 && p.rows < 256) {
       splits = (256 + p.rows - 1) / p.rows;
-      const int64_t max_splits = (p.slots + 4 * kTB - 1) / (4 * kTB);
+      const int64_t min_slots = (H > 64 ? 4 : 2) * kTB;
+      const int64_t max_splits = (p.slots + min_slots - 1) / min_slots;
       if (splits > max_splits) splits = max_splits;
       if (splits > kMaxSplits) splits = kMaxSplits;
       if (splits < 1) splits = 1;
