@@ -344,6 +344,10 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     }
   };
 
+  // Buffer size at which a drain compacts, and the number of keys a compaction
+  // keeps at least (k, or r in the sampling pass).
+  int cap_pass = cap;
+  int target_l = need_l;
   // Moves the keys staged for query q of this wave into its workspace buffer.
   // When they would not fit, the buffer is first compacted: tau rises to a bin
   // edge that keeps between k and 5k/4 of its keys, and staged keys that do not
@@ -353,10 +357,10 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     int n = __builtin_amdgcn_readlane(cnt, 16 * q);
     uint64_t tq = shfl64(tau, 16 * q);
     uint64_t* buf = bufs + (rowbase + qw0 + q) * cap;
-    if (n + ns > cap) {  // then n > cap - kStage >= 5k/4 >= need
+    if (n + ns > cap_pass) {  // then n > cap_pass - kStage >= 5/4 of the target
       wait_mem();  // earlier drains of this wave have reached the buffer
       const uint32_t tp = __builtin_amdgcn_readlane(top_hi, 16 * q);
-      const int need = __shfl(need_l, 16 * q);
+      const int need = __shfl(target_l, 16 * q);
       int kept;
       const uint64_t T = wave_threshold(buf, n, need, false, need + need / 4, tq, tp, L.hist[wid], kept);
       n = wave_compact(buf, n, T);
@@ -392,17 +396,27 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   };
 
   // Sampling pass.  With many more visible entries than k, a first sweep over
-  // every ss-th entry (about 2048 of them) finds, per query, the r-th best
-  // sampled score, r = 3 * ceil(need / ss) + 8.  The full sweep then starts
-  // with that score as its threshold, which prunes about all but r * ss
-  // entries (near 3k) from the start instead of admitting every entry until
-  // the buffer first fills.  The pruning is checked afterwards: a query whose
+  // every ss-th entry (about 8192 of them) finds, per query, the r-th best
+  // sampled score.  The full sweep then starts with that score as its
+  // threshold, which prunes about all but r * ss entries (a little over 2k)
+  // from the start instead of admitting every entry until the buffer first
+  // fills.  The pruning is checked afterwards: a query whose
   // full sweep kept fewer than need candidates (possible only when more than r
   // of the sampled entries rank among its true top-k) is swept again with no
   // threshold, so the result stays exact for any input.
-  const bool sampling = a.top_k > 0 && cmax >= 16 * a.top_k && cmax >= 32 * kTileE;
+  const bool sampling = a.top_k > 0 && cmax >= 16 * a.top_k && cmax >= 64 * kTileE;
   int sstride = 2;
-  while (sampling && int64_t(sstride) * 2048 < cmax) sstride *= 2;
+  while (sampling && int64_t(sstride) * 8192 < cmax) sstride *= 2;
+  // r = lambda + 6 * ceil(sqrt(lambda)) + 8 sampled keys above the starting
+  // threshold, lambda = ceil(need / ss) being the expected number of sampled
+  // entries among the query's true top-need.
+  int r_l = 0;
+  {
+    const int lam = (need_l + sstride - 1) / sstride;
+    int sq = 0;
+    while (sq * sq < lam) ++sq;
+    r_l = lam + 6 * sq + 8;
+  }
   bool active = qvalid;  // this lane's query takes part in the current pass
   bool pruned = false; // this lane's query started the full sweep above zero
 #pragma unroll 1
@@ -419,6 +433,10 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
       }
     }
     ss = pass == 0 ? sstride : 1;
+    // The sampling pass compacts early, to about r keys, so that its threshold
+    // rises fast; the full sweeps keep at least k.
+    cap_pass = pass == 0 ? min(cap, max(1024, 8 * int(wave_max_u32(uint32_t(r_l))))) : cap;
+    target_l = pass == 0 ? min(r_l, max(need_l, 1)) : need_l;
     const int ntp = pass == 0 ? ((cmax + ss - 1) / ss + kTileE - 1) / kTileE : ntiles;
     const int cqv = pass == 0 ? (cq + ss - 1) / ss : cq;
     // Tiles every query of the workgroup sees in full need no visibility test
@@ -501,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
       for (int q = 0; q < kPrefillQPW; ++q) {
         const int n = __builtin_amdgcn_readlane(cnt, 16 * q);
         const int need = __shfl(need_l, 16 * q);
-        const int r = 3 * ((need + ss - 1) / ss) + 8;
+        const int r = __shfl(r_l, 16 * q);
         const int cqq = __shfl(cq, 16 * q);
         uint64_t T = 0ull;
         if (need > 0 && cqq >= 16 * need && n >= r) {
