@@ -6,9 +6,9 @@ context (4 sequences, 128 query heads, e4m3 indexer keys, top-1024 + 128-token
 window): one step = csa_index_topk + csa_attend for one new query token per
 sequence, with every input already resident in HBM.  ``value`` is decode
 query-tokens/s.  The same line carries "legs" for the HCA dense decode at 1M,
-the CSA chunked prefill at 1M (which also compresses the chunk's new blocks)
-and the Flash-like CSA decode at 128K, so that every step of the path is
-measured.
+the CSA chunked prefill at 1M (which also compresses the chunk's new blocks),
+the Flash-like CSA decode at 128K and the HCA chunked prefill at 1M, so that
+every step of the path is measured.
 
 Decode steps are measured cache-cold: each step reads its own replica of the
 caches, and the replicas together are at least twice the 256 MB Infinity
@@ -199,10 +199,51 @@ class PrefillCSA:
                 "queries": wl.B * wl.T}
 
 
+class PrefillHCA:
+    """HCA chunked prefill: compress the chunk's new heavy blocks, then dense attention
+    of every new query over the visible heavy entries and its window."""
+
+    dominant = "hca_attend"
+
+    def __init__(self, wl, seed, replicas):
+        import torch
+        import compressed_attention_csa_amd as csa
+        import inputgen
+        self.wl, self.csa = wl, csa
+        dev = "cuda"
+        B, n, d, N = wl.B, wl.n, wl.d, wl.N_h
+        self.q = inputgen.normal("q", (B, wl.T, wl.H, d), seed, "bf16", device=dev)
+        self.z = inputgen.normal("z_hca", (wl.m_heavy,), seed, "f32", std=0.5, device=dev)
+        self.raw = {name: inputgen.normal(name, (B, n, d), seed, "bf16", device=dev)
+                    for name in ("k_raw", "v_raw")}
+        self.cmp = {name: torch.empty((B, N, d), dtype=torch.bfloat16, device=dev) for name in self.raw}
+        for name, out in self.cmp.items():  # the prior context, compressed before the step
+            csa.csa_compress(self.raw[name], self.z, wl.m_heavy, out, entry_begin=0,
+                             entry_end=wl.cmp_begin)
+        self.out = torch.empty((B, wl.T, wl.H, d), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, r):
+        wl, csa = self.wl, self.csa
+        for name, out in self.cmp.items():
+            csa.csa_compress(self.raw[name], self.z, wl.m_heavy, out, entry_begin=wl.cmp_begin,
+                             entry_end=wl.N_h)
+        csa.hca_attend(self.q, self.cmp["k_raw"], self.cmp["v_raw"], wl.m_heavy, self.raw["k_raw"],
+                       self.raw["v_raw"], wl.t0, wl.W, wl.scale, self.out)
+
+    def algorithmic(self):
+        wl = self.wl
+        slots = sum(min(wl.N_h, (wl.t0 + i + 1) // wl.m_heavy) + min(wl.W, wl.t0 + i + 1)
+                    for i in range(wl.T))
+        flops = 4 * wl.B * wl.H * wl.d * slots
+        return {"bytes": None, "flops": flops, "dominant_flops": flops, "queries": wl.B * wl.T}
+
+
 KINDS = {"csa_decode_pro_1m": DecodeCSA, "csa_decode_flash_128k": DecodeCSA,
-         "hca_decode_1m": DecodeHCA, "csa_prefill_chunk_1m": PrefillCSA}
+         "hca_decode_1m": DecodeHCA, "csa_prefill_chunk_1m": PrefillCSA,
+         "hca_prefill_chunk_1m": PrefillHCA}
 REPLICAS = {"csa_decode_pro_1m": 8, "csa_decode_flash_128k": 16, "hca_decode_1m": 8,
-            "csa_prefill_chunk_1m": 1}
+            "csa_prefill_chunk_1m": 1, "hca_prefill_chunk_1m": 1}
 
 
 # ----------------------------------------------------------------------------- timing
@@ -404,7 +445,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="csa_decode_pro_1m")
-    ap.add_argument("--legs", default="hca_decode_1m,csa_prefill_chunk_1m,csa_decode_flash_128k",
+    ap.add_argument("--legs", default="hca_decode_1m,csa_prefill_chunk_1m,csa_decode_flash_128k,"
+                    "hca_prefill_chunk_1m",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
@@ -436,7 +478,7 @@ def main():
     head = time_workload(args.workload, args.seed, args.steps, args.warmup, graph=not args.no_graph)
     legs = {}
     for name in [x for x in args.legs.split(",") if x]:
-        steps = 5 if name == "csa_prefill_chunk_1m" else args.steps
+        steps = 5 if name in ("csa_prefill_chunk_1m", "hca_prefill_chunk_1m") else args.steps
         r = time_workload(name, args.seed, steps, min(args.warmup, 3) if steps < 10 else args.warmup,
                           graph=not args.no_graph)
         s = summarize(r)

@@ -82,6 +82,10 @@ WORKLOADS = {
     # HCA dense decode at 1M context.
     "hca_decode_1m": Workload("hca_decode_1m", B=16, n=1048576, T=1, t0=1048575, H=128, d=128,
                               m_heavy=128, W=128, csa=False, hca=True),
+    # HCA chunked prefill: the same 8192-token chunk, dense over the heavy entries.
+    "hca_prefill_chunk_1m": Workload("hca_prefill_chunk_1m", B=1, n=1048576, T=8192,
+                                     t0=1040384, H=64, d=128, m_heavy=128, W=128, csa=False,
+                                     hca=True, cmp_begin=1040384 // 128),
     # CSA chunked prefill: 8192 new tokens at the end of a 1M context.
     "csa_prefill_chunk_1m": Workload("csa_prefill_chunk_1m", B=1, n=1048576, T=8192,
                                      t0=1040384, H=64, d=128, H_I=8, d_I=64, m=4, k=1024,

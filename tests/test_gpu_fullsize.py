@@ -276,3 +276,41 @@ def test_csa_prefill_chunk_full_size():
                                          wl.scale)
         check_attention(f64(out[0, i:i + 1]), f64(lse[0, i:i + 1]), o_ref, l_ref, "bf16", what=f"{name} row {i}")
     say("  attention rows ok")
+
+
+# ----------------------------------------------------------------------------- HCA prefill
+
+
+def test_hca_prefill_chunk_full_size():
+    name = "hca_prefill_chunk_1m"
+    wl = inputgen.WORKLOADS[name]
+    say("full-size", name)
+    n, Nh, d, mh, W, T = wl.n, wl.N_h, wl.d, wl.m_heavy, wl.W, wl.T
+    P = bench.PrefillHCA(wl, SEED, 1)
+    P.step(0)
+    torch.cuda.synchronize()
+    z64 = f64(inputgen.normal("z_hca", (mh,), SEED, "f32", std=0.5, device=DEV))
+    for nm, sd in (("k_raw", 1), ("v_raw", 2)):
+        check_cache_samples(P.cmp[nm], P.raw[nm], z64, mh, "bf16", count=64, seed=sd)
+        tail = P.cmp[nm][:, wl.cmp_begin:]
+        check_cache_samples(tail, P.raw[nm][:, wl.cmp_begin * mh:], z64, mh, "bf16", count=64, seed=sd + 10)
+    say("  compressor samples ok")
+
+    # every query of the chunk on oracle-compressed heavy entries; sampled rows checked
+    ek = oracle_compress(P.raw["k_raw"][0], z64, mh, "bf16")["values"]
+    ev = oracle_compress(P.raw["v_raw"][0], z64, mh, "bf16")["values"]
+    out = torch.empty((1, T, wl.H, d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((1, T, wl.H), dtype=torch.float32, device=DEV)
+    csa.hca_attend(P.q, bf16_dev(ek)[None], bf16_dev(ev)[None], mh, P.raw["k_raw"], P.raw["v_raw"],
+                   wl.t0, W, wl.scale, out, lse)
+    torch.cuda.synchronize()
+    q64 = f64(P.q[0])
+    for i in [0, 1, 127, 128, 4095, 5000, T - 2, T - 1]:
+        t = wl.t0 + i
+        win = method.window_positions(t, W)
+        kr = f64(P.raw["k_raw"][0, int(win[0]):int(win[-1]) + 1])
+        vr = f64(P.raw["v_raw"][0, int(win[0]):int(win[-1]) + 1])
+        o_ref, l_ref = method.hca_attend(q64[i:i + 1], ek, ev, mh, kr, vr, int(win[0]), t, W, wl.scale)
+        check_attention(f64(out[0, i:i + 1]), f64(lse[0, i:i + 1]), o_ref, l_ref, "bf16",
+                        what=f"{name} row {i}")
+    say("  attention rows ok")
