@@ -22,6 +22,8 @@
 // (16 significant bits).  fp32 path: fp32 FMA with one slot per lane.
 // With several splits, each writes (O, max, sum) partials and the last split of
 // the (row, head group) to finish merges them (log-sum-exp).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.h"
 
@@ -542,6 +544,338 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
   if (g == 0) *reinterpret_cast<float2*>(ml) = make_float2(mref, lt);
 }
 
+// ---------------------------------------------------------------- HCA prefill kernel
+//
+// Consecutive query tokens of one sequence see the same heavy entries except
+// at most the newest one (a heavy block completes every m' positions) and
+// windows that overlap in all but a few positions.  A workgroup therefore takes
+// QT consecutive tokens and every head: wave w owns 16 heads and RB of the
+// tokens, so each K/V tile staged in LDS, and each MFMA operand read from it,
+// serves RB query rows.  The slots are the heavy entries visible to the last
+// token of the workgroup, then the union of the windows of its tokens.  Only
+// the last heavy tile and the window tiles need a per-token visibility test: a
+// range test on the slot's coordinate (entry index or position).
+
+// Rows are padded (K by one 16-byte chunk, V by two) instead of swizzled: the
+// row reads of K by 16 lanes and the transposing reads of V by 32 lanes hit
+// distinct banks, and every read address of a lane is one base plus a
+// constant, so the compiler folds the offsets into the instructions.
+template <int D>
+struct LdsM {
+  static constexpr int KS = D / 8 + 1;  // K row stride in chunks
+  static constexpr int VS = D / 8 + 2;  // V row stride in chunks
+  uint4 k[2][kTB * KS];
+  uint4 v[2][kTB * VS];
+};
+
+template <int D, int NW, int RB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1))) void hca_multi_kernel(AttendArgs a, int64_t groups_per_seq) {
+  constexpr int kT = NW * 64;
+  constexpr int CPR = D / 8;
+  constexpr int CT = kTB * CPR;
+  constexpr int CPT = CT >= kT ? CT / kT : 1;
+  constexpr int KS = D / 32;
+  constexpr int DVT = D / 16;
+  __shared__ LdsM<D> L;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, col = lane & 15;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H, HW = H / 16;
+  const int QT = RB * (NW / HW);
+  const int64_t T = a.T;
+  const int64_t b = blockIdx.x / groups_per_seq;
+  const int64_t i0 = (blockIdx.x - b * groups_per_seq) * QT;  // first token of the workgroup
+  const int64_t ilast = (i0 + QT < T ? i0 + QT : T) - 1;
+  const int h0 = (wid % HW) * 16;
+  const int64_t iw = i0 + (wid / HW) * RB;  // first token of this wave
+
+  // Visibility of the wave's tokens: heavy entries [0, c), positions [wl, t].
+  int64_t tr[RB], cr[RB], wlr[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t i = iw + rb < ilast ? iw + rb : ilast;
+    tr[rb] = a.t0 + i;
+    const int64_t c = div64(tr[rb] + 1, a.m);
+    cr[rb] = c < a.N_alloc ? c : a.N_alloc;
+    const int64_t ws = tr[rb] - a.window + 1;
+    wlr[rb] = a.window == 0 ? tr[rb] + 1 : (ws > 0 ? ws : 0);
+  }
+  // Slots of the workgroup: heavy tiles, then the windows' union.
+  const int64_t t_first = a.t0 + i0, t_last = a.t0 + ilast;
+  const int64_t cl = div64(t_last + 1, a.m);
+  const int64_t c_max = cl < a.N_alloc ? cl : a.N_alloc;
+  const int64_t wlo0 = t_first - a.window + 1;
+  const int64_t wlo = wlo0 > 0 ? wlo0 : 0;
+  const int64_t whi = a.window == 0 ? wlo : t_last + 1;
+  const int nht = int((c_max + kTB - 1) / kTB);
+  const int nt = nht + int((whi - wlo + kTB - 1) / kTB);
+  const int64_t wdelta = wlo - int64_t(nht) * kTB;  // window tile t starts at position t * kTB + wdelta
+
+  const bf16_t* qbase = reinterpret_cast<const bf16_t*>(a.q) + (b * T) * int64_t(H) * D;
+  const bf16_t* qrow = qbase + i0 * int64_t(H) * D;  // a safe address for skipped slots
+  bf16x8_t qb[RB][KS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t i = iw + rb < ilast ? iw + rb : ilast;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      qb[rb][kk] = u32x4_as_bf16x8(
+          *reinterpret_cast<const uint4*>(qbase + (i * H + h0 + col) * int64_t(D) + 32 * kk + 8 * g));
+  }
+
+  const bf16_t* kc = reinterpret_cast<const bf16_t*>(a.k_cmp) + b * a.N_alloc * D;
+  const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.v_cmp) + b * a.N_alloc * D;
+  const bf16_t* kr = reinterpret_cast<const bf16_t*>(a.k_raw) + (b * a.n_raw - a.raw_base) * D;
+  const bf16_t* vr = reinterpret_cast<const bf16_t*>(a.v_raw) + (b * a.n_raw - a.raw_base) * D;
+  typedef uint32_t chunks_t __attribute__((ext_vector_type(4 * CPT)));
+  struct Pre {
+    chunks_t k, v;
+  };
+  // Loads tile t (tiles past the end, and slots past the heavy or window
+  // range, read the query row; their math is masked or skipped).  Written
+  // without branches, so that the tile loop body stays one basic block.
+  auto fetch = [&](Pre& P, int t) __attribute__((always_inline)) {
+    // Wave-uniform choices as masks rather than branches.
+    const int64_t win = -int64_t(t >= nht);  // all ones for a window tile
+    const int64_t past = -int64_t(t >= nt);
+    const bf16_t* kb = reinterpret_cast<const bf16_t*>((reinterpret_cast<intptr_t>(kc) & ~win) |
+                                                       (reinterpret_cast<intptr_t>(kr) & win));
+    const bf16_t* vb = reinterpret_cast<const bf16_t*>((reinterpret_cast<intptr_t>(vc) & ~win) |
+                                                       (reinterpret_cast<intptr_t>(vr) & win));
+    const int64_t r0 = int64_t(t) * kTB + (wdelta & win);
+    const int64_t lim = ((c_max & ~win) | (whi & win)) & ~past;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int id = (tid + c * kT) % CT, sl = id / CPR, ch = id % CPR;
+      const int64_t row = r0 + sl;
+      const bool ok = row < lim;
+      const bf16_t* kp = ok ? kb + row * D : qrow;
+      const bf16_t* vp = ok ? vb + row * D : qrow;
+      const uint4 kw = *reinterpret_cast<const uint4*>(kp + ch * 8);
+      const uint4 vw = *reinterpret_cast<const uint4*>(vp + ch * 8);
+      P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y; P.k[4 * c + 2] = kw.z; P.k[4 * c + 3] = kw.w;
+      P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y; P.v[4 * c + 2] = vw.z; P.v[4 * c + 3] = vw.w;
+    }
+  };
+  auto stage = [&](const Pre& P, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int id = tid + c * kT, sl = (id % CT) / CPR, ch = id % CPR;
+      if (CT >= kT || id < CT) {
+        L.k[buf][sl * LdsM<D>::KS + ch] = make_uint4(P.k[4 * c], P.k[4 * c + 1], P.k[4 * c + 2], P.k[4 * c + 3]);
+        L.v[buf][sl * LdsM<D>::VS + ch] = make_uint4(P.v[4 * c], P.v[4 * c + 1], P.v[4 * c + 2], P.v[4 * c + 3]);
+      }
+    }
+  };
+
+  const float sl2 = a.scale * kLog2e;
+  f32x4_t o[RB][DVT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int v = 0; v < DVT; ++v) o[rb][v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // Per-row softmax reference (log2 units) and partial sum, as in the kernel
+  // above: the reference moves only when a score exceeds it by kSlack.
+  constexpr float kSlack = 8.0f;
+  float mref[RB], lpart[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    mref[rb] = -INFINITY;
+    lpart[rb] = 0.0f;
+  }
+
+  auto vfrag = [&](int buf, int v) __attribute__((always_inline)) {
+    const int vr0 = 4 * g + col / 4, half = col & 1;
+    const int ch = 2 * v + (col & 3) / 2;
+    const short* b0 = reinterpret_cast<const short*>(&L.v[buf][vr0 * LdsM<D>::VS + ch]) + 4 * half;
+    const short* b1 = reinterpret_cast<const short*>(&L.v[buf][(vr0 + 16) * LdsM<D>::VS + ch]) + 4 * half;
+    const v4s_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b0));
+    const v4s_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b1));
+    uint4 w;
+    __builtin_memcpy(&w.x, &t0, 8);
+    __builtin_memcpy(&w.z, &t1, 8);
+    return u32x4_as_bf16x8(w);
+  };
+  // Per tile: S^T = K Q^T, the weights, then O^T += V^T P^T.  Each K and
+  // each V operand read from LDS serves every row block of the wave.
+  float u[RB][2][4];        // score - reference (log2 units), -inf if not visible
+  uint32_t vmask[RB];       // visibility bits of a masked tile (bit 4 cg + j: slot 16 cg + 4 g + j)
+  bf16x8_t ph[RB], pl[RB];  // weights as bf16 hi + lo
+  // S^T = K Q^T of the tile in buffer buf; the 2 RB accumulators are
+  // independent, so consecutive MFMAs never wait for each other.
+  auto qk = [&](int buf, f32x4_t (&sc)[RB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sc[rb][0] = sc[rb][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        const bf16x8_t kv = u32x4_as_bf16x8(L.k[buf][(cg * 16 + col) * LdsM<D>::KS + 4 * kk + g]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sc[rb][cg] = mfma16x16x32(kv, qb[rb][kk], sc[rb][cg]);
+      }
+  };
+  // Scores and u of tile t; returns whether some row's reference must move
+  // (a visible score above reference + kSlack, or the first visible one).
+  auto scores = [&](int buf, int t, auto full_c) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_c)::value;
+    f32x4_t sc[RB][2];
+    qk(buf, sc);
+    const bool heavy = t < nht;
+    const int64_t cb = heavy ? int64_t(t) * kTB : wlo + int64_t(t - nht) * kTB;  // slot 0's coordinate
+    float umax = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      uint32_t vm = 0xffu;
+      if (!FULL) {
+        int64_t lo = heavy ? 0 : wlr[rb], hi = heavy ? cr[rb] : tr[rb] + 1;
+        lo -= cb;
+        hi -= cb;
+        const int vl = int(lo < 0 ? 0 : (lo > kTB ? kTB : lo));
+        const int vh = int(hi < 0 ? 0 : (hi > kTB ? kTB : hi));
+        vm = 0;
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            vm |= uint32_t(uint32_t(16 * cg + 4 * g + j - vl) < uint32_t(vh - vl)) << (4 * cg + j);
+        vmask[rb] = vm;
+      }
+      const float nref = -mref[rb];
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = fmaf(sc[rb][cg][j], sl2, nref);
+          u[rb][cg][j] = FULL ? x : (((vm >> (4 * cg + j)) & 1u) ? x : -INFINITY);
+          umax = fmaxf(umax, u[rb][cg][j]);
+        }
+    }
+    return __ballot(umax > kSlack) != 0;
+  };
+  // Slow path of the lazy reference: the scores are recomputed (rather than
+  // kept in registers), every row's reference moves to its running maximum,
+  // O and the partial sum are rescaled, u is recomputed.
+  auto rescale = [&](int buf, bool full) __attribute__((always_inline)) {
+    f32x4_t sc[RB][2];
+    qk(buf, sc);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = sc[rb][cg][j] * sl2;
+          u[rb][cg][j] = (full || ((vmask[rb] >> (4 * cg + j)) & 1u)) ? x : -INFINITY;
+          tmax = fmaxf(tmax, u[rb][cg][j]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(mref[rb], tmax);
+      // With no visible slot yet everything is zero: subtract 0, not -inf.
+      const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
+      const float corr = exp2f(mref[rb] - msafe);
+      mref[rb] = mnew;
+      lpart[rb] *= corr;
+#pragma unroll
+      for (int v = 0; v < DVT; ++v)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[rb][v][j] *= corr;
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[rb][cg][j] -= msafe;
+    }
+  };
+  // Weights 2^u as bf16 hi + lo pairs (hardware exp2 and round-to-nearest
+  // conversions) and their sums.
+  auto weights = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x2_t ps = {0.0f, 0.0f};
+      uint32_t whi[4], wlo[4];
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          const f32x2_t pp = {__builtin_amdgcn_exp2f(u[rb][cg][j]), __builtin_amdgcn_exp2f(u[rb][cg][j + 1])};
+          ps = (cg == 0 && j == 0) ? pp : ps + pp;
+          const uint32_t hi = bf16x2_bits(pp);
+          const f32x2_t back = {u32_as_f32(hi << 16), u32_as_f32(hi & 0xffff0000u)};
+          whi[cg * 2 + j / 2] = hi;
+          wlo[cg * 2 + j / 2] = bf16x2_bits(pp - back);
+        }
+      lpart[rb] += ps[0] + ps[1];
+      ph[rb] = u32x4_as_bf16x8(make_uint4(whi[0], whi[1], whi[2], whi[3]));
+      pl[rb] = u32x4_as_bf16x8(make_uint4(wlo[0], wlo[1], wlo[2], wlo[3]));
+    }
+  };
+  // O^T += V^T P^T (V^T operands va): every hi product, then every lo
+  // product, so that the two updates of one accumulator are RB * DVT MFMAs
+  // apart.
+  auto products = [&](const bf16x8_t (&va)[DVT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int v = 0; v < DVT; ++v) o[rb][v] = mfma16x16x32(va[v], ph[rb], o[rb][v]);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int v = 0; v < DVT; ++v) o[rb][v] = mfma16x16x32(va[v], pl[rb], o[rb][v]);
+  };
+
+  // Two LDS buffers and one tile in flight in registers: tile t + 1 loads
+  // while tile t computes.  Buffer t & 1 is rewritten at tile t + 2, after
+  // every wave passed the barrier of tile t + 1 and hence finished tile t.
+  // Tiles [0, nfull) are visible to every token of the workgroup and run
+  // without visibility tests; the rest (the newest heavy tile, the windows)
+  // test each slot.
+  const int64_t cf = div64(t_first + 1, a.m);
+  const int nfull = int((cf < a.N_alloc ? cf : a.N_alloc) / kTB);
+  Pre P;
+  fetch(P, 0);
+  auto tile = [&](int t, auto full_c) __attribute__((always_inline)) {
+    const int buf = t & 1;
+    stage(P, buf);
+    __syncthreads();
+    fetch(P, t + 1);
+    bf16x8_t va[DVT];  // V^T operands, read early
+#pragma unroll
+    for (int v = 0; v < DVT; ++v) va[v] = vfrag(buf, v);
+    if (__builtin_expect(scores(buf, t, full_c), 0)) rescale(buf, decltype(full_c)::value);
+    weights();
+    products(va);
+  };
+  int t = 0;
+  for (; t < nfull; ++t) tile(t, std::true_type{});
+  for (; t < nt; ++t) tile(t, std::false_type{});
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float lt = lpart[rb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int64_t i = iw + rb;
+    if (i > ilast) continue;
+    const int64_t row = b * T + i;
+    const int h = h0 + col;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+#pragma unroll
+    for (int v = 0; v < DVT; ++v) {
+      const int64_t oi = (row * H + h) * int64_t(D) + v * 16 + 4 * g;
+      if (a.out_bf16) {
+        const uint32_t w0 = uint32_t(f32_to_bf16(o[rb][v][0] * inv)) | (uint32_t(f32_to_bf16(o[rb][v][1] * inv)) << 16);
+        const uint32_t w1 = uint32_t(f32_to_bf16(o[rb][v][2] * inv)) | (uint32_t(f32_to_bf16(o[rb][v][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(a.out) + oi) = make_uint2(w0, w1);
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) =
+            make_float4(o[rb][v][0] * inv, o[rb][v][1] * inv, o[rb][v][2] * inv, o[rb][v][3] * inv);
+      }
+    }
+    if (a.lse && g == 0) a.lse[row * H + h] = lt > 0.0f ? (mref[rb] + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
 // Log-sum-exp merge of the split partials: one thread per (row, head, 16-byte
 // column chunk).  The (max, sum) pairs and partial rows of up to 16 splits are
 // loaded together, so every load of a thread is in flight at once; longer rows
@@ -836,9 +1170,34 @@ static void launch_bf16(const AttendArgs& a, const AttendPlan& p) {
   }
 }
 
+// HCA prefill: QT = RB * NW / (H / 16) consecutive tokens per workgroup.
+template <int D, int NW, int RB>
+static bool launch_hca_multi(const AttendArgs& a) {
+  const int HW = a.H / 16;
+  if (HW > NW || NW % HW != 0) return false;
+  const int QT = RB * (NW / HW);
+  const int64_t gps = (a.T + QT - 1) / QT;
+  hipLaunchKernelGGL((hca_multi_kernel<D, NW, RB>), dim3(unsigned(int64_t(a.B) * gps)), dim3(NW * 64), 0,
+                     a.stream, a, gps);
+  return true;
+}
+
+template <int D>
+static bool hca_multi(const AttendArgs& a) {
+  if (a.H <= 64) return launch_hca_multi<D, 8, 2>(a);
+  return launch_hca_multi<D, 8, 2>(a);
+}
+
+// Rows per sequence from which HCA uses the multi-token kernel (when the rows
+// are numerous enough not to need slot splits).
+constexpr int64_t kHcaMultiMinT = 16;
+
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p) {
   if (p.rows == 0) return hipSuccess;
   ProfScope prof(a.hca ? "hca_attend" : "csa_attend", a.stream);
+  if (a.bf16 && a.hca && p.splits == 1 && a.T >= kHcaMultiMinT &&
+      (a.d == 128 ? hca_multi<128>(a) : hca_multi<64>(a)))
+    return hipGetLastError();
   if (a.bf16) {
     if (a.d == 128) a.hca ? launch_bf16<128, true>(a, p) : launch_bf16<128, false>(a, p);
     else a.hca ? launch_bf16<64, true>(a, p) : launch_bf16<64, false>(a, p);

@@ -290,6 +290,14 @@ ATTEND_CASES = [
     ("hca-short", "bf16", 3, 1, 64, 128, 200, 128, 0, 128, 128 * 200 - 1, "bf16"),
     ("hca-prefill", "bf16", 1, 40, 64, 128, 10, 128, 0, 128, 300, "f32"),
     ("hca-f32", "f32", 1, 33, 8, 64, 32, 128, 0, 128, 4000, "f32"),
+    # many consecutive query tokens per sequence (multi-token HCA kernel): heavy
+    # blocks completing inside the chunk, ragged token counts, capped entries
+    ("hca-prefill-multi", "bf16", 2, 301, 64, 128, 40, 128, 0, 128, 4000, "f32"),
+    ("hca-prefill-multi-h128-d64", "bf16", 1, 263, 128, 64, 30, 128, 0, 100, 3700, "bf16"),
+    ("hca-prefill-multi-h16", "bf16", 1, 259, 16, 128, 64, 128, 0, 128, 100, "f32"),
+    ("hca-prefill-multi-h32-nowin", "bf16", 1, 300, 32, 128, 20, 128, 0, 0, 2000, "f32"),
+    ("hca-prefill-multi-empty-rows", "bf16", 1, 300, 64, 128, 8, 128, 0, 0, 0, "f32"),
+    ("hca-prefill-multi-w1", "bf16", 1, 290, 48, 128, 16, 128, 0, 1, 1000, "f32"),
 ]
 
 
