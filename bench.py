@@ -7,8 +7,10 @@ window): one step = csa_index_topk + csa_attend for one new query token per
 sequence, with every input already resident in HBM.  ``value`` is decode
 query-tokens/s.  The same line carries "legs" for the HCA dense decode at 1M,
 the CSA chunked prefill at 1M (which also compresses the chunk's new blocks),
-the Flash-like CSA decode at 128K and the HCA chunked prefill at 1M, so that
-every step of the path is measured.
+the Flash-like CSA decode at 128K, the HCA chunked prefill at 1M and the
+Pro-like decode with state-cache maintenance (csa_append of the new token's
+K, V and indexer-key rows before the step), so that every step of the path is
+measured.
 
 Decode steps are measured cache-cold: each step reads its own replica of the
 caches, and the replicas together are at least twice the 256 MB Infinity
@@ -45,11 +47,15 @@ def log(*a):
 
 
 class DecodeCSA:
-    """CSA decode step: index + top-k over all compressed entries, then attention."""
+    """CSA decode step: index + top-k over all compressed entries, then attention.
+
+    With ``state`` the step first appends the new token's K, V and indexer-key
+    rows to the state-cache rings (compressing the block the token completes)
+    and the attention reads its window from the K / V rings."""
 
     dominant = "index_topk"
 
-    def __init__(self, wl, seed, replicas):
+    def __init__(self, wl, seed, replicas, state=False):
         import torch
         import compressed_attention_csa_amd as csa
         import inputgen
@@ -61,9 +67,18 @@ class DecodeCSA:
         self.q_idx = inputgen.normal("q_idx", (B, 1, wl.H_I, dI), seed, "bf16", device=dev)
         self.w = inputgen.normal("w", (B, 1, wl.H_I), seed, "f32", device=dev)
         z = inputgen.normal("z_csa", (wl.m,), seed, "f32", std=0.5, device=dev)
-        caches = {}
+        self.z, self.state = z, state
+        R = W + wl.m  # state-cache ring rows
+        caches, self.new = {}, {}
         for name, dim in (("k_raw", d), ("v_raw", d), ("k_idx_raw", dI)):
             raw = inputgen.normal(name, (B, n, dim), seed, "bf16", device=dev)
+            if state:  # the newest R positions, as the appends of earlier steps left them
+                ring = torch.empty((B, 2 * R, dim), dtype=torch.bfloat16, device=dev)
+                rows = torch.arange(n - R, n, device=dev) % R
+                ring[:, rows] = raw[:, n - R:]
+                ring[:, rows + R] = raw[:, n - R:]
+                caches["ring_" + name] = ring
+                self.new[name] = raw[:, n - 1:].contiguous()
             if name == "k_idx_raw":
                 if e4m3:
                     out = torch.empty((B, N, dI), dtype=torch.uint8, device=dev)
@@ -90,9 +105,19 @@ class DecodeCSA:
 
     def step(self, r):
         wl, csa, c = self.wl, self.csa, self.reps[r % len(self.reps)]
+        if self.state:
+            csa.csa_append(self.new["k_raw"], c["ring_k_raw"], wl.t0, self.z, wl.m, c["k_cmp"])
+            csa.csa_append(self.new["v_raw"], c["ring_v_raw"], wl.t0, self.z, wl.m, c["v_cmp"])
+            csa.csa_append(self.new["k_idx_raw"], c["ring_k_idx_raw"], wl.t0, self.z, wl.m, c["k_idx"],
+                           c["k_scale"])
         csa.csa_index_topk(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, self.idx)
-        csa.csa_attend(self.q, c["k_cmp"], c["v_cmp"], wl.m, self.idx, c["k_win"], c["v_win"], wl.t0,
-                       wl.W, wl.scale, self.out, raw_base=self.raw_base)
+        if self.state:
+            kr, base = csa.ring_window(c["ring_k_raw"], wl.t0 - wl.W + 1)
+            csa.csa_attend(self.q, c["k_cmp"], c["v_cmp"], wl.m, self.idx, kr, c["ring_v_raw"], wl.t0,
+                           wl.W, wl.scale, self.out, raw_base=base)
+        else:
+            csa.csa_attend(self.q, c["k_cmp"], c["v_cmp"], wl.m, self.idx, c["k_win"], c["v_win"], wl.t0,
+                           wl.W, wl.scale, self.out, raw_base=self.raw_base)
 
     def algorithmic(self):
         wl = self.wl
@@ -105,7 +130,11 @@ class DecodeCSA:
         q = wl.B * wl.H * wl.d * 2
         o = wl.B * wl.H * wl.d * 4
         flops = 2 * wl.B * wl.N_c * wl.H_I * wl.d_I + 4 * wl.B * wl.H * wl.d * (wl.k + wl.W)
-        return {"bytes": keys + qi + idx + gathered + window + q + o, "flops": flops,
+        state = 0
+        if self.state:  # new rows read, written twice; the completed block read, its entry written
+            row = wl.B * (2 * wl.d + wl.d_I) * 2
+            state = 3 * row + wl.m * row + wl.B * (2 * wl.d * 2 + wl.d_I * kb)
+        return {"bytes": keys + qi + idx + gathered + window + q + o + state, "flops": flops,
                 "dominant_bytes": keys + qi, "queries": wl.B}
 
 
@@ -253,11 +282,12 @@ def time_workload(name, seed, steps, warmup, graph=True):
     import torch
     import compressed_attention_csa_amd as csa
     import inputgen
-    wl = inputgen.WORKLOADS[name]
-    R = REPLICAS[name]
+    base, _, variant = name.partition("+")  # "+state": the decode step also maintains the state cache
+    wl = inputgen.WORKLOADS[base]
+    R = REPLICAS[base]
     log(f"[bench] {name}: setting up ({R} replica(s))")
     t = time.time()
-    w = KINDS[name](wl, seed, R)
+    w = KINDS[base](wl, seed, R, state=True) if variant == "state" else KINDS[base](wl, seed, R)
     log(f"[bench] {name}: setup {time.time() - t:.1f}s; warmup {warmup}")
     for i in range(max(warmup, R)):
         w.step(i)
@@ -446,7 +476,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="csa_decode_pro_1m")
     ap.add_argument("--legs", default="hca_decode_1m,csa_prefill_chunk_1m,csa_decode_flash_128k,"
-                    "hca_prefill_chunk_1m",
+                    "hca_prefill_chunk_1m,csa_decode_pro_1m+state",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")

@@ -38,6 +38,8 @@ SIGNATURES = {
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_compress": (_i32, [_vp, _i32, _i32, _i64, _i32, _i64, _vp, _i32, _i64, _i64, _i64, _vp,
                             _i32, _vp, _vp]),
+    "csa_append": (_i32, [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _i32, _i64, _vp, _i32,
+                          _vp, _vp]),
     "csa_index_topk_workspace": (_sz, [_i32, _i64, _i32, _i32, _i64, _i32, _i32]),
     "csa_index_topk": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i32, _i32, _i64, _i64,
                               _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
@@ -134,6 +136,23 @@ def csa_compress(x, logits, m, out, out_scale=None, raw_base=0, entry_begin=0, e
                             entry_end, N_alloc, _ptr(out), _dt(out), _ptr(out_scale), _stream(x))
     _check("csa_compress", st)
     return out
+
+
+def csa_append(x_new, ring, t0, logits, m, out, out_scale=None):
+    """Append rows for positions t0 .. t0 + T_new - 1 to the mirrored ring
+    [B, 2R, d] and compress the blocks they complete into ``out``."""
+    B, T_new, d = x_new.shape
+    R = ring.shape[1] // 2
+    st = lib().csa_append(_ptr(x_new), _dt(x_new), B, T_new, d, t0, _ptr(ring), R, _ptr(logits), m,
+                          out.shape[1], _ptr(out), _dt(out), _ptr(out_scale), _stream(x_new))
+    _check("csa_append", st)
+    return out
+
+
+def ring_window(ring, s):
+    """(raw rows, raw_base) that present positions s .. s + R - 1 of a mirrored ring."""
+    R = ring.shape[1] // 2
+    return ring, s - s % R
 
 
 def index_topk_workspace_bytes(B, T, H_I, d_I, N_alloc, top_k, k_dt) -> int:

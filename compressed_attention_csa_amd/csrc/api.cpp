@@ -148,6 +148,47 @@ csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw,
   return hip_status(csa::launch_compress(a), "compress launch");
 }
 
+csa_status_t csa_append(const void* x_new, csa_dtype_t dt, int B, int T_new, int d, int64_t t0,
+                        void* ring, int64_t R, const float* logits, int m, int64_t N_alloc, void* out,
+                        csa_dtype_t out_dt, float* out_scale, csa_stream_t stream) {
+  REQUIRE_PTR(x_new);
+  REQUIRE_PTR(ring);
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(out);
+  REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_E_DTYPE, "dt must be CSA_F32 or CSA_BF16");
+  REQUIRE(out_dt == CSA_F32 || out_dt == CSA_BF16 || out_dt == CSA_FP8_E4M3, CSA_E_DTYPE,
+          "unknown out_dt %d", int(out_dt));
+  if (out_dt == CSA_FP8_E4M3) REQUIRE_PTR(out_scale);
+  else REQUIRE(out_scale == nullptr, CSA_E_DTYPE, "out_scale must be NULL unless out_dt is CSA_FP8_E4M3");
+  REQUIRE(B >= 1 && B <= 65535, CSA_E_SHAPE, "B=%d out of range [1, 65535]", B);
+  REQUIRE(d >= 8 && d <= 512 && d % 8 == 0, CSA_E_SHAPE, "d=%d must be a multiple of 8 in [8, 512]", d);
+  REQUIRE(out_dt != CSA_FP8_E4M3 || (d >= 16 && (d & (d - 1)) == 0), CSA_E_SHAPE,
+          "fp8 output needs d a power of two >= 16, got %d", d);
+  REQUIRE(m >= 1 && m <= 128, CSA_E_SHAPE, "m=%d out of range [1, 128]", m);
+  REQUIRE(T_new >= 0 && T_new <= 4096, CSA_E_SHAPE, "T_new=%d out of range [0, 4096]", T_new);
+  REQUIRE(t0 >= 0 && N_alloc >= 0, CSA_E_SHAPE, "t0 / N_alloc must be >= 0");
+  REQUIRE(R >= 1 && R <= (int64_t(1) << 24), CSA_E_SHAPE, "R=%lld out of range [1, 2^24]", (long long)R);
+  REQUIRE(R >= int64_t(m) + T_new - 1, CSA_E_SHAPE,
+          "R=%lld must hold a block and the new rows: R >= m + T_new - 1 = %d", (long long)R, m + T_new - 1);
+  REQUIRE_ALIGN(x_new);
+  REQUIRE_ALIGN(ring);
+  REQUIRE_ALIGN(logits);
+  REQUIRE_ALIGN(out);
+  REQUIRE(out_scale == nullptr || aligned16(out_scale), CSA_E_ALIGN, "out_scale is not 16-byte aligned");
+  if (T_new == 0) return CSA_OK;
+  // Blocks completed by the new rows: (j + 1) m - 1 in [t0, t0 + T_new - 1].
+  const int64_t j_lo = t0 / m;
+  int64_t j_hi = (t0 + T_new) / m;
+  if (j_hi > N_alloc) j_hi = N_alloc;
+  if (j_hi < j_lo) j_hi = j_lo;
+  // Their positions are R consecutive ring rows from (j_lo m) % R on.
+  const int64_t p_lo = j_lo * m;
+  csa::CompressArgs a{ring, dt == CSA_BF16, B, 2 * R, d, p_lo - p_lo % R, logits, m, j_lo, j_hi, N_alloc,
+                      out, out_dt == CSA_F32 ? 0 : (out_dt == CSA_BF16 ? 1 : 2), out_scale,
+                      reinterpret_cast<hipStream_t>(stream)};
+  return hip_status(csa::launch_append(a, x_new, t0, T_new, R), "append launch");
+}
+
 size_t csa_index_topk_workspace(int B, int64_t T, int H_I, int d_I, int64_t N_alloc, int top_k,
                                 csa_dtype_t k_dt) {
   (void)d_I;

@@ -40,16 +40,44 @@ struct Row8<bf16_t> {
   }
 };
 
+// The new rows of an append (state-cache ring, see csa_append): workgroups
+// past the compression ones copy them into both ring rows of their position,
+// and the compression reads positions >= t0 from them instead of the ring, so
+// that one launch does both without ordering the two.
+struct AppendTail {
+  const void* x_new;  // [B, T_new, d]
+  int64_t t0;
+  int T_new;
+  int64_t R;
+  int cmp_blocks;     // workgroups (per sequence) that compress
+};
+
 // OUT: 0 = fp32, 1 = bf16, 2 = e4m3 + per-entry fp32 scale.
-template <typename TIn, int OUT>
+template <typename TIn, int OUT, bool APPEND>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
     const TIn* __restrict__ x, int64_t n_raw, int d, int64_t raw_base,
     const float* __restrict__ logits, int m, int64_t entry_begin, int64_t n_ent, int64_t N_alloc,
-    void* __restrict__ out, float* __restrict__ out_scale) {
+    void* __restrict__ out, float* __restrict__ out_scale, AppendTail at) {
   __shared__ double alpha[128];
   __shared__ float zmax_s;
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
+  const TIn* xn = reinterpret_cast<const TIn*>(at.x_new) + int64_t(b) * at.T_new * d;
+  if (APPEND && int(blockIdx.x) >= at.cmp_blocks) {
+    // Copy: one thread per 16-byte chunk of a new row, written to rows
+    // p % R and p % R + R of the (writable) ring x.
+    constexpr int EPC = 16 / sizeof(TIn);  // elements per chunk
+    const int cpr = d / EPC;
+    const int64_t gi = int64_t(int(blockIdx.x) - at.cmp_blocks) * kThreads + tid;
+    if (gi >= int64_t(at.T_new) * cpr) return;
+    const int i = int(gi / cpr), c = int(gi - int64_t(i) * cpr);
+    const int64_t slot = (at.t0 + i) % at.R;
+    TIn* ring = const_cast<TIn*>(x) + int64_t(b) * n_raw * d + c * EPC;
+    const uint4 v = *reinterpret_cast<const uint4*>(xn + int64_t(i) * d + c * EPC);
+    *reinterpret_cast<uint4*>(ring + slot * d) = v;
+    *reinterpret_cast<uint4*>(ring + (slot + at.R) * d) = v;
+    return;
+  }
 
   // Slot weights: softmax of the logits, in fp64.
   if (tid < kWave) {
@@ -82,7 +110,9 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 #pragma unroll 8
     for (int s = 0; s < m; ++s) {
       double v[8];
-      Row8<TIn>::load(src + int64_t(s) * d, v);
+      const TIn* rp = src + int64_t(s) * d;
+      if (APPEND && j * m + s >= at.t0) rp = xn + (j * m + s - at.t0) * d + seg * 8;
+      Row8<TIn>::load(rp, v);
       const double a = alpha[s];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fma(a, v[i], acc[i]);
@@ -131,31 +161,45 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   }
 }
 
-template <typename TIn, int OUT>
-hipError_t launch(const CompressArgs& a) {
+template <typename TIn, int OUT, bool APPEND>
+hipError_t launch(const CompressArgs& a, const AppendTail& at) {
   const int tpe = a.d / 8;
   const int epb = kThreads / tpe;
   const int64_t n_ent = a.entry_end - a.entry_begin;
-  dim3 grid(unsigned((n_ent + epb - 1) / epb), unsigned(a.B));
-  ProfScope prof("compress", a.stream);
-  hipLaunchKernelGGL((compress_kernel<TIn, OUT>), grid, dim3(kThreads), 0, a.stream,
+  AppendTail t = at;
+  t.cmp_blocks = int((n_ent + epb - 1) / epb);
+  int64_t blocks = t.cmp_blocks;
+  if (APPEND) blocks += (int64_t(t.T_new) * (a.d * int64_t(sizeof(TIn)) / 16) + kThreads - 1) / kThreads;
+  dim3 grid(unsigned(blocks), unsigned(a.B));
+  ProfScope prof(APPEND ? "append" : "compress", a.stream);
+  hipLaunchKernelGGL((compress_kernel<TIn, OUT, APPEND>), grid, dim3(kThreads), 0, a.stream,
                      reinterpret_cast<const TIn*>(a.x), a.n_raw, a.d, a.raw_base, a.logits, a.m,
-                     a.entry_begin, n_ent, a.N_alloc, a.out, a.out_scale);
+                     a.entry_begin, n_ent, a.N_alloc, a.out, a.out_scale, t);
   return hipGetLastError();
+}
+
+template <bool APPEND>
+hipError_t dispatch(const CompressArgs& a, const AppendTail& t) {
+  if (a.x_bf16) {
+    if (a.out_kind == 0) return launch<bf16_t, 0, APPEND>(a, t);
+    if (a.out_kind == 1) return launch<bf16_t, 1, APPEND>(a, t);
+    return launch<bf16_t, 2, APPEND>(a, t);
+  }
+  if (a.out_kind == 0) return launch<float, 0, APPEND>(a, t);
+  if (a.out_kind == 1) return launch<float, 1, APPEND>(a, t);
+  return launch<float, 2, APPEND>(a, t);
 }
 
 }  // namespace
 
 hipError_t launch_compress(const CompressArgs& a) {
   if (a.entry_end <= a.entry_begin) return hipSuccess;
-  if (a.x_bf16) {
-    if (a.out_kind == 0) return launch<bf16_t, 0>(a);
-    if (a.out_kind == 1) return launch<bf16_t, 1>(a);
-    return launch<bf16_t, 2>(a);
-  }
-  if (a.out_kind == 0) return launch<float, 0>(a);
-  if (a.out_kind == 1) return launch<float, 1>(a);
-  return launch<float, 2>(a);
+  return dispatch<false>(a, AppendTail{a.x, 0, 0, 1, 0});
+}
+
+hipError_t launch_append(const CompressArgs& a, const void* x_new, int64_t t0, int T_new, int64_t R) {
+  if (T_new <= 0) return hipSuccess;
+  return dispatch<true>(a, AppendTail{x_new, t0, T_new, R, 0});
 }
 
 }  // namespace csa

@@ -38,6 +38,12 @@ struct CompressArgs {
 };
 hipError_t launch_compress(const CompressArgs& a);
 
+// State-cache append in one launch: the rows x_new [B, T_new, d] of positions
+// t0 .. t0 + T_new - 1 go to rows p % R and p % R + R of the ring a.x
+// [B, 2R, d], and entries [a.entry_begin, a.entry_end) are compressed (from
+// the ring with a.raw_base / a.n_raw = 2R, or from x_new for positions >= t0).
+hipError_t launch_append(const CompressArgs& a, const void* x_new, int64_t t0, int T_new, int64_t R);
+
 // ------------------------------------------------------------------ indexer + top-k
 
 enum KeyKind { kKeyF32 = 0, kKeyBF16 = 1, kKeyE4M3 = 2 };

@@ -5,6 +5,8 @@
  * transformer layer:
  *
  *   csa_compress    block KV compressor (CSA block m = 4, HCA block m' = 128)
+ *   csa_append      decode-time state cache: ring of raw rows + compression of
+ *                   the blocks each new token completes
  *   csa_index_topk  Lightning-Indexer scores of compressed entries + per-query top-k
  *   csa_attend      attention over the selected compressed entries and the raw
  *                   sliding window, under one softmax
@@ -111,6 +113,37 @@ csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw,
                           int64_t raw_base, const float* logits, int m, int64_t entry_begin,
                           int64_t entry_end, int64_t N_alloc, void* out, csa_dtype_t out_dt,
                           float* out_scale, csa_stream_t stream);
+
+/*
+ * csa_append -- decode-time state cache: append raw rows and compress the
+ * blocks they complete.
+ *
+ * [digest] 七: besides the compressed cache there is a state cache for the
+ * sliding-window rows and for the tokens of a block that is not complete yet.
+ * Here it is a ring of R rows per sequence kept twice ("mirrored"): position p
+ * lives in rows p % R and p % R + R of ring, so the newest R positions are
+ * always R consecutive rows.  Readers take the ring as ordinary raw rows:
+ * positions s .. s + L - 1 (L <= R, all among the newest R) are the rows
+ * starting at s % R, i.e. pass x / k_raw / v_raw = ring, n_raw = 2R and
+ * raw_base = s - s % R to csa_compress, csa_attend or hca_attend.
+ *
+ *   x_new   [B, T_new, d] of dt (CSA_F32 | CSA_BF16): the rows of positions
+ *           t0 .. t0 + T_new - 1 (0 <= T_new <= 4096; 0 is a no-op).
+ *   ring    [B, 2R, d] of dt, updated in place.  It must already hold the
+ *           positions t0 - R + T_new .. t0 - 1 (those >= 0) from earlier calls.
+ *   R       ring rows, 1 <= R <= 2^24 and R >= m + T_new - 1 (so that every
+ *           completed block is still in the ring); R >= W + T_new keeps a
+ *           window of W rows readable after the call.
+ *   logits, m, out, out_dt, out_scale, N_alloc: as in csa_compress.  Every
+ *           block j < N_alloc that the new rows complete, t0 <= (j+1) m - 1 <=
+ *           t0 + T_new - 1, is written to out[b, j] with the same arithmetic
+ *           (and hence the same bits) as csa_compress over the full history.
+ *   d       as in csa_compress.
+ * Calls for one ring must be ordered on one stream.  No workspace.
+ */
+csa_status_t csa_append(const void* x_new, csa_dtype_t dt, int B, int T_new, int d, int64_t t0,
+                        void* ring, int64_t R, const float* logits, int m, int64_t N_alloc,
+                        void* out, csa_dtype_t out_dt, float* out_scale, csa_stream_t stream);
 
 /*
  * csa_index_topk -- Lightning-Indexer scores and per-query top-k selection.

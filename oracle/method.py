@@ -83,6 +83,28 @@ def compress_exact(x, z, m: int, entry_begin: int = 0, entry_end: int | None = N
     return np.einsum("s,jsd->jd", alpha, blocks)
 
 
+def state_ring(history, t_end: int, R: int) -> np.ndarray:
+    """The state cache after positions 0 .. t_end were appended one by one.
+
+    [digest] section 七 keeps the window rows and the rows of the block that is
+    not complete yet in a state cache next to the compressed cache.  Reading
+    taken here: a ring of R rows kept twice, position p written to rows p % R
+    and p % R + R, so that the newest R positions are R consecutive rows.
+    Returns [2R, d] float64; rows never written are NaN.
+    """
+    history = np.asarray(history, dtype=np.float64)
+    ring = np.full((2 * R, history.shape[1]), np.nan)
+    for p in range(t_end + 1):
+        ring[p % R] = history[p]
+        ring[p % R + R] = history[p]
+    return ring
+
+
+def completed_blocks(t0: int, T_new: int, m: int, N_alloc: int) -> range:
+    """Blocks j < N_alloc whose last position (j+1) m - 1 lies in [t0, t0 + T_new - 1]."""
+    return range(t0 // m, min(N_alloc, (t0 + T_new) // m))
+
+
 def store(sums: np.ndarray, dtype: str):
     """Round exact entries once to the storage type.
 

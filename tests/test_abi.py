@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
         assert n in csa.SIGNATURES, n
@@ -72,6 +72,36 @@ def test_compress_validation(L):
     assert compress(L, out=MIS) == E_ALIGN
     compress(L, x=None)
     assert L.csa_last_error() == b"x is NULL"
+
+
+def append(L, x=P, dt=BF16, B=2, T_new=1, d=128, t0=100, ring=P, R=132, logits=P, m=4, N=64, out=P,
+           out_dt=BF16, scale=None):
+    return L.csa_append(x, dt, B, T_new, d, t0, ring, R, logits, m, N, out, out_dt, scale, None)
+
+
+def test_append_validation(L):
+    """Every check fires before any HIP call (no GPU is touched here)."""
+    assert append(L, x=None) == E_NULL
+    assert append(L, ring=None) == E_NULL
+    assert append(L, logits=None) == E_NULL
+    assert append(L, out=None) == E_NULL
+    assert append(L, dt=FP8) == E_DTYPE
+    assert append(L, out_dt=FP8) == E_NULL            # fp8 needs a scale buffer
+    assert append(L, scale=P) == E_DTYPE
+    assert append(L, B=0) == E_SHAPE
+    assert append(L, T_new=-1) == E_SHAPE
+    assert append(L, T_new=4097, R=5000) == E_SHAPE
+    assert append(L, d=12) == E_SHAPE
+    assert append(L, m=0) == E_SHAPE
+    assert append(L, t0=-1) == E_SHAPE
+    assert append(L, R=0) == E_SHAPE
+    assert append(L, m=128, R=127) == E_SHAPE         # a block must fit in the ring
+    assert append(L, m=4, T_new=10, R=12) == E_SHAPE  # R >= m + T_new - 1
+    assert append(L, ring=MIS) == E_ALIGN
+    assert append(L, x=MIS) == E_ALIGN
+    assert append(L, T_new=0) == OK                   # nothing to do, nothing enqueued
+    append(L, R=2)
+    assert b"R=2" in L.csa_last_error()
 
 
 def index(L, q=P, q_dt=BF16, w=P, k=P, k_dt=BF16, ks=None, B=4, T=1, H_I=8, d_I=64, N=1024, t0=4095,

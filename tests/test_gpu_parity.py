@@ -87,6 +87,112 @@ def test_compress(case):
             assert (out[b, :eb] == 7.0).all() and (out[b, ee:] == 7.0).all()
 
 
+# ----------------------------------------------------------------------------- state cache (append)
+
+APPEND_CASES = [
+    # x_dt, out_dt, B, d, m, R, positions, pattern of rows per call
+    ("bf16", "bf16", 2, 128, 4, 132, 701, [1]),
+    ("bf16", "e4m3", 3, 64, 4, 132, 530, [1, 1, 3, 1, 2, 7, 1]),
+    ("bf16", "bf16", 2, 128, 128, 256, 1100, [1] * 9 + [100]),
+    ("f32", "f32", 1, 32, 5, 12, 301, [1, 2, 8, 1]),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[f"{c[0]}-{c[1]}-m{c[4]}-R{c[5]}" for c in APPEND_CASES])
+def test_append_builds_the_caches_of_the_full_history(case):
+    """Rows appended token by token (and in small chunks) leave the ring holding
+    the newest R positions bit-exactly, and the compressed cache equal to the
+    oracle's compression of the whole history (same criteria as csa_compress)."""
+    x_dt, out_dt, B, d, m, R, n, pattern = case
+    say("append", case)
+    hist = gen("app_x", (B, n, d), x_dt, seed=n + d)
+    z = gen("app_z", (m,), "f32", seed=m, std=0.5).to(DEV)
+    N = n // m + 3  # a few entries past the history stay untouched
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.uint8}[out_dt]
+    sentinel = 0x55 if out_dt == "e4m3" else 7.0
+    out = torch.full((B, N, d), sentinel, dtype=tdt, device=DEV)
+    scale = torch.full((B, N), 7.0, device=DEV) if out_dt == "e4m3" else None
+    ring = torch.zeros((B, 2 * R, d), dtype=hist.dtype, device=DEV)
+    hd = hist.to(DEV)
+    t, k = 0, 0
+    while t < n:
+        T_new = min(pattern[k % len(pattern)], n - t)
+        k += 1
+        csa.csa_append(hd[:, t:t + T_new].contiguous(), ring, t, z, m, out, scale)
+        t += T_new
+    torch.cuda.synchronize()
+    z64 = f64(z)
+    n_ent = n // m
+    for b in range(B):
+        # the ring rows the oracle's state cache holds (the newest R positions), bit-exact
+        exp_ring = method.state_ring(f64(hist[b]), n - 1, R)
+        held = ~np.isnan(exp_ring).any(axis=1)
+        assert held.sum() == 2 * min(R, n)
+        got_ring = f64(ring[b])
+        np.testing.assert_array_equal(got_ring[held], exp_ring[held])
+        sums = method.compress_exact(f64(hist[b]), z64, m, 0, n_ent)
+        if out_dt == "bf16":
+            diff = ulp_diff_bf16(bf16_bits(out[b, :n_ent]), formats.f64_to_bf16_bits(sums))
+            assert diff.max() <= 1
+            assert (diff == 0).mean() >= 0.9999
+        elif out_dt == "f32":
+            np.testing.assert_allclose(f64(out[b, :n_ent]), formats.round_to_f32(sums), rtol=1e-6, atol=0)
+        else:
+            n_bad = check_e4m3(out[b, :n_ent].cpu().numpy(), scale[b, :n_ent].cpu().numpy(),
+                               sums.astype(np.float32))
+            assert n_bad <= max(2, sums.size // 10000)
+            assert (scale[b, n_ent:] == 7.0).all()
+        rest = out[b, n_ent:]
+        assert (rest == sentinel).all(), "entries of incomplete blocks must stay untouched"
+
+
+def test_decode_reads_its_window_from_the_ring():
+    """A CSA and an HCA decode step whose window comes from the state ring equal
+    the oracle over the full history."""
+    B, d, H, W, n = 2, 128, 64, 128, 4099
+    say("append+decode", B, n)
+    hist_k = gen("ad_k", (B, n, d), "bf16", seed=1)
+    hist_v = gen("ad_v", (B, n, d), "bf16", seed=2)
+    q = gen("ad_q", (B, 1, H, d), "bf16", seed=3)
+    scale = 1.0 / math.sqrt(d)
+    t0 = n - 1
+    for m, k in ((4, 256), (128, 0)):
+        R = W + m
+        z = gen("ad_z", (m,), "f32", seed=m, std=0.5).to(DEV)
+        N = n // m
+        kc = torch.empty((B, N, d), dtype=torch.bfloat16, device=DEV)
+        vc = torch.empty_like(kc)
+        rk = torch.zeros((B, 2 * R, d), dtype=torch.bfloat16, device=DEV)
+        rv = torch.zeros_like(rk)
+        hk, hv = hist_k.to(DEV), hist_v.to(DEV)
+        for t in range(n):  # one token per decode step
+            csa.csa_append(hk[:, t:t + 1].contiguous(), rk, t, z, m, kc)
+            csa.csa_append(hv[:, t:t + 1].contiguous(), rv, t, z, m, vc)
+        s = t0 - W + 1
+        raw, base = csa.ring_window(rk, s)
+        out = torch.empty((B, 1, H, d), dtype=torch.float32, device=DEV)
+        lse = torch.empty((B, 1, H), dtype=torch.float32, device=DEV)
+        z64 = f64(z)
+        ek = [method.store(method.compress_exact(f64(hist_k[b]), z64, m), "bf16")["values"] for b in range(B)]
+        ev = [method.store(method.compress_exact(f64(hist_v[b]), z64, m), "bf16")["values"] for b in range(B)]
+        if m == 4:
+            idx = np.stack([np.random.default_rng(b).choice(N, k, replace=False) for b in range(B)])
+            idx = idx.astype(np.int32).reshape(B, 1, k)
+            csa.csa_attend(q.to(DEV), kc, vc, m, torch.from_numpy(idx).to(DEV), raw, rv, t0, W, scale, out,
+                           lse, raw_base=base)
+        else:
+            csa.hca_attend(q.to(DEV), kc, vc, m, raw, rv, t0, W, scale, out, lse, raw_base=base)
+        torch.cuda.synchronize()
+        for b in range(B):
+            if m == 4:
+                o_ref, l_ref = method.csa_attend(f64(q[b]), ek[b], ev[b], idx[b], f64(hist_k[b]), f64(hist_v[b]),
+                                                 0, t0, W, m, scale)
+            else:
+                o_ref, l_ref = method.hca_attend(f64(q[b]), ek[b], ev[b], m, f64(hist_k[b]), f64(hist_v[b]),
+                                                 0, t0, W, scale)
+            check_attention(f64(out[b]), f64(lse[b]), o_ref, l_ref, "bf16", what=f"ring m={m} b={b}")
+
+
 # ----------------------------------------------------------------------------- indexer + top-k
 
 

@@ -75,6 +75,48 @@ def test_compress_matches_brute_force():
     np.testing.assert_allclose(got, exp, rtol=1e-14, atol=1e-15)
 
 
+@pytest.mark.parametrize("R", [5, 8, 13])
+def test_state_ring_holds_the_newest_R_positions_as_consecutive_rows(R):
+    """Every window of <= R newest positions is a contiguous row range of the
+    mirrored ring, starting at row s % R; rows of older positions are gone."""
+    rng = np.random.default_rng(R)
+    hist = rng.standard_normal((40, 3))
+    for t_end in (0, R - 2, R - 1, R, 2 * R + 3, 39):
+        if t_end < 0:
+            continue
+        ring = method.state_ring(hist, t_end, R)
+        lo = max(0, t_end - R + 1)
+        for s in range(lo, t_end + 1):
+            L = t_end - s + 1
+            np.testing.assert_array_equal(ring[s % R: s % R + L], hist[s: t_end + 1])
+        held = {tuple(r) for r in ring if not np.isnan(r).any()}
+        assert held == {tuple(hist[p]) for p in range(lo, t_end + 1)}
+
+
+def test_compressing_from_the_ring_equals_compressing_the_history():
+    """Blocks completed by each append, compressed from the ring view, are the
+    entries of the full history; the completed-block ranges tile the entries."""
+    rng = np.random.default_rng(3)
+    m, R, N = 4, 11, 25
+    hist = rng.standard_normal((103, 6))
+    z = rng.standard_normal(m) * 0.5
+    full = method.compress_exact(hist, z, m, 0, N)
+    seen, t = [], 0
+    for T_new in [1, 1, 3, 2, 8, 1] * 20:
+        if t >= len(hist):
+            break
+        T_new = min(T_new, len(hist) - t, R - m + 1)
+        ring = method.state_ring(hist, t + T_new - 1, R)
+        blocks = method.completed_blocks(t, T_new, m, N)
+        if len(blocks):
+            p_lo = blocks.start * m
+            got = method.compress_exact(ring, z, m, blocks.start, blocks.stop, raw_base=p_lo - p_lo % R)
+            np.testing.assert_allclose(got, full[blocks.start:blocks.stop], rtol=1e-15, atol=0)
+            seen.extend(blocks)
+        t += T_new
+    assert seen == list(range(min(N, len(hist) // m)))
+
+
 def test_store_rounds_once():
     s = rnd(11, 10, 64)
     np.testing.assert_array_equal(method.store(s, "bf16")["values"], formats.round_to_bf16(s))
