@@ -362,7 +362,7 @@ def roofline(res):
     dom_ms = res.get("dominant_ms")
     if dom_ms is None:
         return None
-    key = f"{res['dominant']}@{res['workload']}"
+    key = f"{res['dominant']}@{res['workload'].partition('+')[0]}"
     traffic = load_traffic(key)
     if "dominant_bytes" in alg:
         achieved = alg["dominant_bytes"] / (dom_ms * 1e-3) / 1e9
