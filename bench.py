@@ -9,8 +9,8 @@ query-tokens/s.  The same line carries "legs" for the HCA dense decode at 1M,
 the CSA chunked prefill at 1M (which also compresses the chunk's new blocks),
 the Flash-like CSA decode at 128K, the HCA chunked prefill at 1M and the
 Pro-like decode with state-cache maintenance (csa_append of the new token's
-K, V and indexer-key rows before the step), so that every step of the path is
-measured.
+K, V and indexer-key rows before the step) and the HCA decode over fp8-e4m3
+heavy caches, so that every step of the path is measured.
 
 Decode steps are measured cache-cold: each step reads its own replica of the
 caches, and the replicas together are at least twice the 256 MB Infinity
@@ -55,7 +55,9 @@ class DecodeCSA:
 
     dominant = "index_topk"
 
-    def __init__(self, wl, seed, replicas, state=False):
+    def __init__(self, wl, seed, replicas, variant=""):
+        assert variant in ("", "state"), variant
+        state = variant == "state"
         import torch
         import compressed_attention_csa_amd as csa
         import inputgen
@@ -139,13 +141,18 @@ class DecodeCSA:
 
 
 class DecodeHCA:
+    """HCA decode step: dense attention over every heavy entry plus the window.
+    Variant ``fp8kv``: the heavy K / V caches are e4m3 codes with per-entry
+    scales (as csa_compress writes them)."""
+
     dominant = "hca_attend"
 
-    def __init__(self, wl, seed, replicas):
+    def __init__(self, wl, seed, replicas, variant=""):
         import torch
         import compressed_attention_csa_amd as csa
         import inputgen
-        self.wl, self.csa = wl, csa
+        assert variant in ("", "fp8kv"), variant
+        self.wl, self.csa, self.kv8 = wl, csa, variant == "fp8kv"
         dev = "cuda"
         B, n, d, Nh, W = wl.B, wl.n, wl.d, wl.N_h, wl.W
         self.q = inputgen.normal("q", (B, 1, wl.H, d), seed, "bf16", device=dev)
@@ -153,9 +160,16 @@ class DecodeHCA:
         caches = {}
         for name in ("k_raw", "v_raw"):
             raw = inputgen.normal(name, (B, n, d), seed, "bf16", device=dev)
-            out = torch.empty((B, Nh, d), dtype=torch.bfloat16, device=dev)
-            csa.csa_compress(raw, z, wl.m_heavy, out)
-            caches[name.replace("_raw", "_cmp")] = out
+            key = name.replace("_raw", "_cmp")
+            if self.kv8:
+                out = torch.empty((B, Nh, d), dtype=torch.uint8, device=dev)
+                sc = torch.empty((B, Nh), device=dev)
+                csa.csa_compress(raw, z, wl.m_heavy, out, sc)
+                caches[key.replace("_cmp", "_scale")] = sc
+            else:
+                out = torch.empty((B, Nh, d), dtype=torch.bfloat16, device=dev)
+                csa.csa_compress(raw, z, wl.m_heavy, out)
+            caches[key] = out
             caches[name.replace("_raw", "_win")] = raw[:, n - W:].contiguous()
             del raw
         torch.cuda.synchronize()
@@ -167,11 +181,12 @@ class DecodeHCA:
     def step(self, r):
         wl, c = self.wl, self.reps[r % len(self.reps)]
         self.csa.hca_attend(self.q, c["k_cmp"], c["v_cmp"], wl.m_heavy, c["k_win"], c["v_win"], wl.t0,
-                            wl.W, wl.scale, self.out, raw_base=self.raw_base)
+                            wl.W, wl.scale, self.out, raw_base=self.raw_base, k_scale=c.get("k_scale"),
+                            v_scale=c.get("v_scale"))
 
     def algorithmic(self):
         wl = self.wl
-        kv = wl.B * wl.N_h * wl.d * 2 * 2
+        kv = wl.B * wl.N_h * (wl.d + 4) * 2 if self.kv8 else wl.B * wl.N_h * wl.d * 2 * 2
         window = wl.B * wl.W * wl.d * 2 * 2
         q = wl.B * wl.H * wl.d * 2
         o = wl.B * wl.H * wl.d * 4
@@ -287,7 +302,7 @@ def time_workload(name, seed, steps, warmup, graph=True):
     R = REPLICAS[base]
     log(f"[bench] {name}: setting up ({R} replica(s))")
     t = time.time()
-    w = KINDS[base](wl, seed, R, state=True) if variant == "state" else KINDS[base](wl, seed, R)
+    w = KINDS[base](wl, seed, R, **({"variant": variant} if variant else {}))
     log(f"[bench] {name}: setup {time.time() - t:.1f}s; warmup {warmup}")
     for i in range(max(warmup, R)):
         w.step(i)
@@ -362,7 +377,7 @@ def roofline(res):
     dom_ms = res.get("dominant_ms")
     if dom_ms is None:
         return None
-    key = f"{res['dominant']}@{res['workload'].partition('+')[0]}"
+    key = f"{res['dominant']}@{res['workload']}"
     traffic = load_traffic(key)
     if "dominant_bytes" in alg:
         achieved = alg["dominant_bytes"] / (dom_ms * 1e-3) / 1e9
@@ -476,7 +491,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="csa_decode_pro_1m")
     ap.add_argument("--legs", default="hca_decode_1m,csa_prefill_chunk_1m,csa_decode_flash_128k,"
-                    "hca_prefill_chunk_1m,csa_decode_pro_1m+state",
+                    "hca_prefill_chunk_1m,csa_decode_pro_1m+state,hca_decode_1m+fp8kv",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")

@@ -44,11 +44,12 @@ SIGNATURES = {
     "csa_index_topk": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i32, _i32, _i64, _i64,
                               _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "csa_attend_workspace": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
-    "csa_attend": (_i32, [_vp, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64, _i64, _i32,
-                          _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "csa_attend": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64,
+                          _i64, _i32, _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz,
+                          _vp]),
     "hca_attend_workspace": (_sz, [_i32, _i64, _i32, _i32, _i64, _i32, _i32]),
-    "hca_attend": (_i32, [_vp, _i32, _vp, _vp, _i64, _i32, _vp, _vp, _i64, _i64, _i32, _i64,
-                          _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "hca_attend": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _vp, _i64, _i64,
+                          _i32, _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
     "csa_profile_enable": (_i32, [_i32]),
     "csa_profile_report": (_i32, [ctypes.c_char_p, _sz]),
 }
@@ -175,13 +176,15 @@ def csa_index_topk(q_idx, w, k_idx, k_scale, t0, m, top_k, out_idx, out_score=No
 
 
 def csa_attend(q, k_cmp, v_cmp, m, idx, k_raw, v_raw, t0, window, scale, out, lse=None,
-               raw_base=0, workspace_tensor=None):
+               raw_base=0, workspace_tensor=None, k_scale=None, v_scale=None):
+    """k_cmp / v_cmp of dtype uint8 are e4m3 caches with per-entry k_scale / v_scale."""
     B, T, H, d = q.shape
     N_alloc = k_cmp.shape[1]
     top_k = 0 if idx is None else idx.shape[-1]
     need = int(lib().csa_attend_workspace(B, T, H, d, top_k, window))
     ws = workspace_tensor if workspace_tensor is not None else workspace(need, q.device, "attend")
-    st = lib().csa_attend(_ptr(q), _dt(q), _ptr(k_cmp), _ptr(v_cmp), N_alloc, m, _ptr(idx), top_k,
+    st = lib().csa_attend(_ptr(q), _dt(q), _ptr(k_cmp), _ptr(v_cmp), _dt(k_cmp), _ptr(k_scale),
+                          _ptr(v_scale), N_alloc, m, _ptr(idx), top_k,
                           _ptr(k_raw), _ptr(v_raw), raw_base, k_raw.shape[1], B, T, H, d, t0,
                           window, float(scale), _ptr(out), _dt(out), _ptr(lse), _ptr(ws),
                           0 if ws is None else ws.numel(), _stream(q))
@@ -190,12 +193,14 @@ def csa_attend(q, k_cmp, v_cmp, m, idx, k_raw, v_raw, t0, window, scale, out, ls
 
 
 def hca_attend(q, k_cmp, v_cmp, m_heavy, k_raw, v_raw, t0, window, scale, out, lse=None,
-               raw_base=0, workspace_tensor=None):
+               raw_base=0, workspace_tensor=None, k_scale=None, v_scale=None):
+    """k_cmp / v_cmp of dtype uint8 are e4m3 caches with per-entry k_scale / v_scale."""
     B, T, H, d = q.shape
     N_alloc = k_cmp.shape[1]
     need = int(lib().hca_attend_workspace(B, T, H, d, N_alloc, m_heavy, window))
     ws = workspace_tensor if workspace_tensor is not None else workspace(need, q.device, "attend")
-    st = lib().hca_attend(_ptr(q), _dt(q), _ptr(k_cmp), _ptr(v_cmp), N_alloc, m_heavy,
+    st = lib().hca_attend(_ptr(q), _dt(q), _ptr(k_cmp), _ptr(v_cmp), _dt(k_cmp), _ptr(k_scale),
+                          _ptr(v_scale), N_alloc, m_heavy,
                           _ptr(k_raw), _ptr(v_raw), raw_base, k_raw.shape[1], B, T, H, d, t0,
                           window, float(scale), _ptr(out), _dt(out), _ptr(lse), _ptr(ws),
                           0 if ws is None else ws.numel(), _stream(q))

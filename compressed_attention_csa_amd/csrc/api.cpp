@@ -254,7 +254,8 @@ size_t hca_attend_workspace(int B, int64_t T, int H, int d, int64_t N_alloc, int
 }
 
 static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const void* k_cmp,
-                                const void* v_cmp, int64_t N_alloc, int m, const int32_t* idx,
+                                const void* v_cmp, csa_dtype_t kv_dt, const float* k_scale,
+                                const float* v_scale, int64_t N_alloc, int m, const int32_t* idx,
                                 int top_k, const void* k_raw, const void* v_raw, int64_t raw_base,
                                 int64_t n_raw, int B, int64_t T, int H, int d, int64_t t0,
                                 int window, float scale, void* out, csa_dtype_t out_dt, float* lse,
@@ -262,6 +263,17 @@ static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const v
   csa_status_t st = check_attend_common(q, dt, k_cmp, v_cmp, N_alloc, m, k_raw, v_raw, raw_base,
                                         n_raw, B, T, H, d, t0, window, out, out_dt, lse);
   if (st != CSA_OK) return st;
+  const bool kv8 = kv_dt == CSA_FP8_E4M3;
+  REQUIRE(kv_dt == dt || (kv8 && dt == CSA_BF16), CSA_E_DTYPE,
+          "kv_dt must equal dt, or be CSA_FP8_E4M3 with dt == CSA_BF16");
+  if (kv8) {
+    REQUIRE_PTR(k_scale);
+    REQUIRE_PTR(v_scale);
+    REQUIRE(aligned16(k_scale) && aligned16(v_scale), CSA_E_ALIGN, "k_scale / v_scale are not 16-byte aligned");
+  } else {
+    REQUIRE(k_scale == nullptr && v_scale == nullptr, CSA_E_DTYPE,
+            "k_scale / v_scale must be NULL unless kv_dt is CSA_FP8_E4M3");
+  }
   if (!hca) {
     REQUIRE(top_k >= 0 && top_k <= 2048, CSA_E_SHAPE, "top_k=%d out of range [0, 2048]", top_k);
     REQUIRE(top_k == 0 || idx != nullptr, CSA_E_NULL, "idx is NULL");
@@ -274,29 +286,31 @@ static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const v
   REQUIRE(workspace_bytes >= p.ws_bytes, CSA_E_WORKSPACE, "workspace has %zu bytes, needs %zu",
           workspace_bytes, p.ws_bytes);
   REQUIRE(workspace == nullptr || aligned16(workspace), CSA_E_ALIGN, "workspace is not 16-byte aligned");
-  csa::AttendArgs a{hca, dt == CSA_BF16, q, k_cmp, v_cmp, N_alloc, m, hca ? nullptr : idx,
+  csa::AttendArgs a{hca, dt == CSA_BF16, q, k_cmp, v_cmp, kv8, k_scale, v_scale, N_alloc, m, hca ? nullptr : idx,
                     hca ? 0 : top_k, k_raw, v_raw, raw_base, n_raw, B, T, H, d, t0, window, scale,
                     out, out_dt == CSA_BF16, lse, workspace, reinterpret_cast<hipStream_t>(stream)};
   return hip_status(csa::launch_attend(a, p), hca ? "hca_attend launch" : "csa_attend launch");
 }
 
 csa_status_t csa_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
+                        csa_dtype_t kv_dt, const float* k_scale, const float* v_scale,
                         int64_t N_alloc, int m, const int32_t* idx, int top_k, const void* k_raw,
                         const void* v_raw, int64_t raw_base, int64_t n_raw, int B, int64_t T,
                         int H, int d, int64_t t0, int window, float scale, void* out,
                         csa_dtype_t out_dt, float* lse, void* workspace, size_t workspace_bytes,
                         csa_stream_t stream) {
-  return attend_impl(false, q, dt, k_cmp, v_cmp, N_alloc, m, idx, top_k, k_raw, v_raw, raw_base,
+  return attend_impl(false, q, dt, k_cmp, v_cmp, kv_dt, k_scale, v_scale, N_alloc, m, idx, top_k, k_raw, v_raw, raw_base,
                      n_raw, B, T, H, d, t0, window, scale, out, out_dt, lse, workspace,
                      workspace_bytes, stream);
 }
 
 csa_status_t hca_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
+                        csa_dtype_t kv_dt, const float* k_scale, const float* v_scale,
                         int64_t N_alloc, int m_heavy, const void* k_raw, const void* v_raw,
                         int64_t raw_base, int64_t n_raw, int B, int64_t T, int H, int d,
                         int64_t t0, int window, float scale, void* out, csa_dtype_t out_dt,
                         float* lse, void* workspace, size_t workspace_bytes, csa_stream_t stream) {
-  return attend_impl(true, q, dt, k_cmp, v_cmp, N_alloc, m_heavy, nullptr, 0, k_raw, v_raw,
+  return attend_impl(true, q, dt, k_cmp, v_cmp, kv_dt, k_scale, v_scale, N_alloc, m_heavy, nullptr, 0, k_raw, v_raw,
                      raw_base, n_raw, B, T, H, d, t0, window, scale, out, out_dt, lse, workspace,
                      workspace_bytes, stream);
 }

@@ -193,6 +193,8 @@ struct LdsB {
   uint4 k[NB][kTB * D / 8];  // K rows, 16-byte chunks swizzled for row-wise reads
   uint4 v[NB][kTB * D / 8];  // V rows, swizzled for transposing reads
   uint32_t live[NB][kTB];    // all ones for a live slot, 0 for a skipped one
+  float ksc[NB][kTB];        // fp8 caches: per-slot score factor (K scale * scale * log2 e)
+  float vsc[NB][kTB];        // fp8 caches: per-slot V scale
   int32_t src[kMaxTable];    // selected compressed entry of each CSA slot of the split, -1 if skipped
 };
 
@@ -219,7 +221,11 @@ __device__ __forceinline__ float mask_or_neg_inf(float x, uint32_t mask) {
   return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & mask) | (~mask & 0xff800000u));
 }
 
-template <int D, int NW, bool HCA, int PAIR>
+// KV8: the compressed caches hold e4m3 codes with one fp32 scale per entry
+// (K and V each).  The codes are widened exactly to bf16 when a tile is
+// staged; the K scale joins the per-slot score factor and the V scale the
+// slot's weight in O^T += V^T P^T (not in the softmax sum).
+template <int D, int NW, bool HCA, int PAIR, bool KV8>
 __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
   constexpr int kT = NW * 64;
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
@@ -260,14 +266,21 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
 
   const bf16_t* kc = reinterpret_cast<const bf16_t*>(a.k_cmp) + x.b * a.N_alloc * D;
   const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.v_cmp) + x.b * a.N_alloc * D;
+  const uint8_t* kc8 = reinterpret_cast<const uint8_t*>(a.k_cmp) + x.b * a.N_alloc * D;
+  const uint8_t* vc8 = reinterpret_cast<const uint8_t*>(a.v_cmp) + x.b * a.N_alloc * D;
+  const float* ksp = a.k_scale + x.b * a.N_alloc;
+  const float* vsp = a.v_scale + x.b * a.N_alloc;
   const bf16_t* kr = reinterpret_cast<const bf16_t*>(a.k_raw) + (x.b * a.n_raw - a.raw_base) * D;
   const bf16_t* vr = reinterpret_cast<const bf16_t*>(a.v_raw) + (x.b * a.n_raw - a.raw_base) * D;
+  const float sl2 = a.scale * kLog2e;
   // Registers of one tile in flight (vectors rather than arrays, so that they
-  // stay in registers).
+  // stay in registers).  With KV8, a chunk of a compressed row holds 8 codes
+  // in its first two words (bit c of f8) until it is staged.
   typedef uint32_t chunks_t __attribute__((ext_vector_type(4 * CPT)));
   struct Pre {
     chunks_t k, v;
-    uint32_t lv;
+    uint32_t lv, f8;
+    float ks, vs;  // KV8: scales of slot tid of the tile (threads tid < kTB)
   };
   // Loads tile t of the split (slots beyond the split or skipped read the query row).
   const int64_t cmp_end = x.hi < nsel ? x.hi : nsel;  // end of the compressed slots of the split
@@ -281,30 +294,44 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int id = (tid + c * kT) % CT;
-        const uint4 kw = *reinterpret_cast<const uint4*>(kb + id * 8);
-        const uint4 vw = *reinterpret_cast<const uint4*>(vb + id * 8);
-        P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y; P.k[4 * c + 2] = kw.z; P.k[4 * c + 3] = kw.w;
-        P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y; P.v[4 * c + 2] = vw.z; P.v[4 * c + 3] = vw.w;
+        if (KV8) {
+          const uint2 kw = *reinterpret_cast<const uint2*>(kc8 + t0 * D + id * 8);
+          const uint2 vw = *reinterpret_cast<const uint2*>(vc8 + t0 * D + id * 8);
+          P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y;
+          P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y;
+        } else {
+          const uint4 kw = *reinterpret_cast<const uint4*>(kb + id * 8);
+          const uint4 vw = *reinterpret_cast<const uint4*>(vb + id * 8);
+          P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y; P.k[4 * c + 2] = kw.z; P.k[4 * c + 3] = kw.w;
+          P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y; P.v[4 * c + 2] = vw.z; P.v[4 * c + 3] = vw.w;
+        }
       }
       P.lv = (1u << CPT) - 1;
+      P.f8 = KV8 ? (1u << CPT) - 1 : 0u;
+      if (KV8 && tid < kTB) {
+        P.ks = ksp[t0 + tid];
+        P.vs = vsp[t0 + tid];
+      }
       return;
     }
-    uint32_t lv = 0;
+    uint32_t lv = 0, f8 = 0;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int id = (tid + c * kT) % CT, sl = id / CPR, ch = id % CPR;
       const int64_t slot = t0 + sl;
       const bf16_t* kp = qrow;
       const bf16_t* vp = qrow;
-      bool live = false;
+      bool live = false, cmp8 = false;
+      int64_t j = 0;
       if (slot < x.hi) {
         if (slot < nsel) {
-          int64_t j = slot;
+          j = slot;
           if (!HCA) j = L.src[slot - x.lo];
           if (j >= 0) {
             kp = kc + j * D;
             vp = vc + j * D;
             live = true;
+            cmp8 = KV8;
           }
         } else {
           const int64_t pos = x.wstart + (slot - nsel);
@@ -313,27 +340,54 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
           live = true;
         }
       }
-      const uint4 kw = *reinterpret_cast<const uint4*>(kp + ch * 8);
-      const uint4 vw = *reinterpret_cast<const uint4*>(vp + ch * 8);
-      P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y; P.k[4 * c + 2] = kw.z; P.k[4 * c + 3] = kw.w;
-      P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y; P.v[4 * c + 2] = vw.z; P.v[4 * c + 3] = vw.w;
+      if (KV8 && cmp8) {
+        const uint2 kw = *reinterpret_cast<const uint2*>(kc8 + j * D + ch * 8);
+        const uint2 vw = *reinterpret_cast<const uint2*>(vc8 + j * D + ch * 8);
+        P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y;
+        P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y;
+      } else {
+        const uint4 kw = *reinterpret_cast<const uint4*>(kp + ch * 8);
+        const uint4 vw = *reinterpret_cast<const uint4*>(vp + ch * 8);
+        P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y; P.k[4 * c + 2] = kw.z; P.k[4 * c + 3] = kw.w;
+        P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y; P.v[4 * c + 2] = vw.z; P.v[4 * c + 3] = vw.w;
+      }
       lv |= uint32_t(live) << c;
+      f8 |= uint32_t(cmp8) << c;
     }
     P.lv = lv;
+    P.f8 = f8;
+    if (KV8 && tid < kTB) {  // the scales of slot t0 + tid (1 for window and skipped slots)
+      const int64_t slot = t0 + tid;
+      int64_t j = -1;
+      if (slot < x.hi && slot < nsel) j = HCA ? slot : int64_t(L.src[slot - x.lo]);
+      P.ks = j >= 0 ? ksp[j] : 1.0f;
+      P.vs = j >= 0 ? vsp[j] : 1.0f;
+    }
   };
   auto stage = [&](const Pre& P, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int id = tid + c * kT, sl = (id % CT) / CPR, ch = id % CPR;
       if (id < CT) {
-        L.k[buf][k_pos<CPR>(sl, ch)] = make_uint4(P.k[4 * c], P.k[4 * c + 1], P.k[4 * c + 2], P.k[4 * c + 3]);
-        L.v[buf][v_pos<CPR>(sl, ch)] = make_uint4(P.v[4 * c], P.v[4 * c + 1], P.v[4 * c + 2], P.v[4 * c + 3]);
+        uint4 kw = make_uint4(P.k[4 * c], P.k[4 * c + 1], P.k[4 * c + 2], P.k[4 * c + 3]);
+        uint4 vw = make_uint4(P.v[4 * c], P.v[4 * c + 1], P.v[4 * c + 2], P.v[4 * c + 3]);
+        if (KV8 && ((P.f8 >> c) & 1u)) {
+          kw = make_uint4(e4m3x2_to_bf16x2<false>(P.k[4 * c]), e4m3x2_to_bf16x2<true>(P.k[4 * c]),
+                          e4m3x2_to_bf16x2<false>(P.k[4 * c + 1]), e4m3x2_to_bf16x2<true>(P.k[4 * c + 1]));
+          vw = make_uint4(e4m3x2_to_bf16x2<false>(P.v[4 * c]), e4m3x2_to_bf16x2<true>(P.v[4 * c]),
+                          e4m3x2_to_bf16x2<false>(P.v[4 * c + 1]), e4m3x2_to_bf16x2<true>(P.v[4 * c + 1]));
+        }
+        L.k[buf][k_pos<CPR>(sl, ch)] = kw;
+        L.v[buf][v_pos<CPR>(sl, ch)] = vw;
         if (ch == 0) L.live[buf][sl] = ((P.lv >> c) & 1u) ? 0xffffffffu : 0u;
       }
     }
+    if (KV8 && tid < kTB) {
+      L.ksc[buf][tid] = P.ks * sl2;
+      L.vsc[buf][tid] = P.vs;
+    }
   };
 
-  const float sl2 = a.scale * kLog2e;
   f32x4_t o[DVT];
 #pragma unroll
   for (int v = 0; v < DVT; ++v) o[v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -400,9 +454,12 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
       for (int cg = 0; cg < 2; ++cg) {
         const uint4 lm = *reinterpret_cast<const uint4*>(&L.live[b0 + i][cg * 16 + 4 * g]);
         const uint32_t lmv[4] = {lm.x, lm.y, lm.z, lm.w};
+        float4 kf = make_float4(sl2, sl2, sl2, sl2);
+        if (KV8) kf = *reinterpret_cast<const float4*>(&L.ksc[b0 + i][cg * 16 + 4 * g]);
+        const float kfv[4] = {kf.x, kf.y, kf.z, kf.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          u[i][cg][j] = mask_or_neg_inf(fmaf(sc[i][cg][j], sl2, nref), lmv[j]);
+          u[i][cg][j] = mask_or_neg_inf(fmaf(sc[i][cg][j], kfv[j], nref), lmv[j]);
           umax = fmaxf(umax, u[i][cg][j]);
         }
       }
@@ -417,9 +474,12 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
         for (int cg = 0; cg < 2; ++cg) {
           const uint4 lm = *reinterpret_cast<const uint4*>(&L.live[b0 + i][cg * 16 + 4 * g]);
           const uint32_t lmv[4] = {lm.x, lm.y, lm.z, lm.w};
+          float4 kf = make_float4(sl2, sl2, sl2, sl2);
+          if (KV8) kf = *reinterpret_cast<const float4*>(&L.ksc[b0 + i][cg * 16 + 4 * g]);
+          const float kfv[4] = {kf.x, kf.y, kf.z, kf.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            u[i][cg][j] = mask_or_neg_inf(sc[i][cg][j] * sl2, lmv[j]);
+            u[i][cg][j] = mask_or_neg_inf(sc[i][cg][j] * kfv[j], lmv[j]);
             tmax = fmaxf(tmax, u[i][cg][j]);
           }
         }
@@ -447,19 +507,24 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
       f32x2_t ps = {0.0f, 0.0f};
       uint32_t phi[4], plo[4];
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg)
+      for (int cg = 0; cg < 2; ++cg) {
+        float4 vf = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        if (KV8) vf = *reinterpret_cast<const float4*>(&L.vsc[b0 + i][cg * 16 + 4 * g]);
+        const float vfv[4] = {vf.x, vf.y, vf.z, vf.w};
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {
           // hardware 2^x (results below the normal range flush to 0, far below
           // what a weight within 2^8 of the reference can matter)
-          const f32x2_t pp = {__builtin_amdgcn_exp2f(u[i][cg][j]), __builtin_amdgcn_exp2f(u[i][cg][j + 1])};
+          f32x2_t pp = {__builtin_amdgcn_exp2f(u[i][cg][j]), __builtin_amdgcn_exp2f(u[i][cg][j + 1])};
           ps = (cg == 0 && j == 0) ? pp : ps + pp;
+          if (KV8) pp = f32x2_t{pp[0] * vfv[j], pp[1] * vfv[j + 1]};  // the slot's V scale
           // P = hi + lo, both bf16 (hardware round-to-nearest-even conversions).
           const uint32_t hi = bf16x2_bits(pp);
           const f32x2_t back = {u32_as_f32(hi << 16), u32_as_f32(hi & 0xffff0000u)};
           phi[cg * 2 + j / 2] = hi;
           plo[cg * 2 + j / 2] = bf16x2_bits(pp - back);
         }
+      }
       lpart += ps[0] + ps[1];
       const bf16x8_t pb_hi = u32x4_as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
       const bf16x8_t pb_lo = u32x4_as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
@@ -490,25 +555,12 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
     if (PAIR == 2) fetch(P1, t + 1 + SETS);
     if (has && t < nt) compute(b0);
   };
-  Pre P0, P1, P2, P3;
-  fetch(P0, 0);
-  fetch(P1, 1);
-  if (SETS == 4) {
-    fetch(P2, 2);
-    fetch(P3, 3);
-  }
+  Pre P[SETS];
+#pragma unroll
+  for (int i = 0; i < SETS; ++i) fetch(P[i], i);
   for (int t0 = 0; t0 < nt; t0 += SETS) {
-    if (PAIR == 2) {
-      step(P0, P1, t0);
-      if (SETS == 4) step(P2, P3, t0 + 2);
-    } else {
-      step(P0, P0, t0);
-      step(P1, P1, t0 + 1);
-      if (SETS == 4) {
-        step(P2, P2, t0 + 2);
-        step(P3, P3, t0 + 3);
-      }
-    }
+#pragma unroll
+    for (int i = 0; i < SETS; i += PAIR) step(P[i], P[i + PAIR - 1], t0 + i);
   }
 
   // Per-head totals; lane (g, col) holds head h0 + col, columns 16v + 4g + j.
@@ -566,9 +618,13 @@ struct LdsM {
   static constexpr int VS = D / 8 + 2;  // V row stride in chunks
   uint4 k[2][kTB * KS];
   uint4 v[2][kTB * VS];
+  float ksc[2][kTB];  // fp8 caches: per-slot score factor (K scale * scale * log2 e)
+  float vsc[2][kTB];  // fp8 caches: per-slot V scale
 };
 
-template <int D, int NW, int RB>
+// KV8 as in attend_bf16_kernel: heavy tiles hold e4m3 codes (widened when
+// staged) with per-entry K and V scales; window tiles are bf16.
+template <int D, int NW, int RB, bool KV8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1))) void hca_multi_kernel(AttendArgs a, int64_t groups_per_seq) {
   constexpr int kT = NW * 64;
   constexpr int CPR = D / 8;
@@ -626,14 +682,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
   const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.v_cmp) + b * a.N_alloc * D;
   const bf16_t* kr = reinterpret_cast<const bf16_t*>(a.k_raw) + (b * a.n_raw - a.raw_base) * D;
   const bf16_t* vr = reinterpret_cast<const bf16_t*>(a.v_raw) + (b * a.n_raw - a.raw_base) * D;
+  const uint8_t* kc8 = reinterpret_cast<const uint8_t*>(a.k_cmp) + b * a.N_alloc * D;
+  const uint8_t* vc8 = reinterpret_cast<const uint8_t*>(a.v_cmp) + b * a.N_alloc * D;
+  const float* ksp = a.k_scale + b * a.N_alloc;
+  const float* vsp = a.v_scale + b * a.N_alloc;
+  const float sl2 = a.scale * kLog2e;
   typedef uint32_t chunks_t __attribute__((ext_vector_type(4 * CPT)));
   struct Pre {
     chunks_t k, v;
+    bool f8;        // a heavy tile of e4m3 codes (two words per chunk)
+    float ks, vs;   // its scales of slot tid (threads tid < kTB)
   };
   // Loads tile t (tiles past the end, and slots past the heavy or window
   // range, read the query row; their math is masked or skipped).  Written
   // without branches, so that the tile loop body stays one basic block.
   auto fetch = [&](Pre& P, int t) __attribute__((always_inline)) {
+    P.f8 = KV8 && t < nht;
+    if (KV8 && t < nht) {
+      const int64_t r0 = int64_t(t) * kTB;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int id = (tid + c * kT) % CT, sl = id / CPR, ch = id % CPR;
+        const int64_t row = r0 + sl < c_max ? r0 + sl : c_max - 1;  // past the end: re-read the last entry
+        const uint2 kw = *reinterpret_cast<const uint2*>(kc8 + row * D + ch * 8);
+        const uint2 vw = *reinterpret_cast<const uint2*>(vc8 + row * D + ch * 8);
+        P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y;
+        P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y;
+      }
+      if (tid < kTB) {
+        const int64_t row = r0 + tid < c_max ? r0 + tid : c_max - 1;
+        P.ks = ksp[row];
+        P.vs = vsp[row];
+      }
+      return;
+    }
     // Wave-uniform choices as masks rather than branches.
     const int64_t win = -int64_t(t >= nht);  // all ones for a window tile
     const int64_t past = -int64_t(t >= nt);
@@ -655,19 +737,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
       P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y; P.k[4 * c + 2] = kw.z; P.k[4 * c + 3] = kw.w;
       P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y; P.v[4 * c + 2] = vw.z; P.v[4 * c + 3] = vw.w;
     }
+    if (KV8) {
+      P.ks = 1.0f;
+      P.vs = 1.0f;
+    }
   };
   auto stage = [&](const Pre& P, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int id = tid + c * kT, sl = (id % CT) / CPR, ch = id % CPR;
       if (CT >= kT || id < CT) {
-        L.k[buf][sl * LdsM<D>::KS + ch] = make_uint4(P.k[4 * c], P.k[4 * c + 1], P.k[4 * c + 2], P.k[4 * c + 3]);
-        L.v[buf][sl * LdsM<D>::VS + ch] = make_uint4(P.v[4 * c], P.v[4 * c + 1], P.v[4 * c + 2], P.v[4 * c + 3]);
+        uint4 kw = make_uint4(P.k[4 * c], P.k[4 * c + 1], P.k[4 * c + 2], P.k[4 * c + 3]);
+        uint4 vw = make_uint4(P.v[4 * c], P.v[4 * c + 1], P.v[4 * c + 2], P.v[4 * c + 3]);
+        if (KV8 && P.f8) {
+          kw = make_uint4(e4m3x2_to_bf16x2<false>(P.k[4 * c]), e4m3x2_to_bf16x2<true>(P.k[4 * c]),
+                          e4m3x2_to_bf16x2<false>(P.k[4 * c + 1]), e4m3x2_to_bf16x2<true>(P.k[4 * c + 1]));
+          vw = make_uint4(e4m3x2_to_bf16x2<false>(P.v[4 * c]), e4m3x2_to_bf16x2<true>(P.v[4 * c]),
+                          e4m3x2_to_bf16x2<false>(P.v[4 * c + 1]), e4m3x2_to_bf16x2<true>(P.v[4 * c + 1]));
+        }
+        L.k[buf][sl * LdsM<D>::KS + ch] = kw;
+        L.v[buf][sl * LdsM<D>::VS + ch] = vw;
       }
+    }
+    if (KV8 && tid < kTB) {
+      L.ksc[buf][tid] = P.ks * sl2;
+      L.vsc[buf][tid] = P.vs;
     }
   };
 
-  const float sl2 = a.scale * kLog2e;
   f32x4_t o[RB][DVT];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -720,6 +817,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
     constexpr bool FULL = decltype(full_c)::value;
     f32x4_t sc[RB][2];
     qk(buf, sc);
+    f32x4_t kf[2];  // per-slot score factors (fp8 caches)
+    if (KV8)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) kf[cg] = *reinterpret_cast<const f32x4_t*>(&L.ksc[buf][cg * 16 + 4 * g]);
     const bool heavy = t < nht;
     const int64_t cb = heavy ? int64_t(t) * kTB : wlo + int64_t(t - nht) * kTB;  // slot 0's coordinate
     float umax = -INFINITY;
@@ -745,7 +846,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
       for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float x = fmaf(sc[rb][cg][j], sl2, nref);
+          const float x = fmaf(sc[rb][cg][j], KV8 ? kf[cg][j] : sl2, nref);
           u[rb][cg][j] = FULL ? x : (((vm >> (4 * cg + j)) & 1u) ? x : -INFINITY);
           umax = fmaxf(umax, u[rb][cg][j]);
         }
@@ -758,6 +859,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
   auto rescale = [&](int buf, bool full) __attribute__((always_inline)) {
     f32x4_t sc[RB][2];
     qk(buf, sc);
+    f32x4_t kf[2];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg)
+      kf[cg] = KV8 ? *reinterpret_cast<const f32x4_t*>(&L.ksc[buf][cg * 16 + 4 * g])
+                   : f32x4_t{sl2, sl2, sl2, sl2};
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float tmax = -INFINITY;
@@ -765,7 +871,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
       for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float x = sc[rb][cg][j] * sl2;
+          const float x = sc[rb][cg][j] * kf[cg][j];
           u[rb][cg][j] = (full || ((vmask[rb] >> (4 * cg + j)) & 1u)) ? x : -INFINITY;
           tmax = fmaxf(tmax, u[rb][cg][j]);
         }
@@ -789,7 +895,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
   };
   // Weights 2^u as bf16 hi + lo pairs (hardware exp2 and round-to-nearest
   // conversions) and their sums.
-  auto weights = [&]() __attribute__((always_inline)) {
+  auto weights = [&](int buf) __attribute__((always_inline)) {
+    f32x4_t vf[2];  // per-slot V scales (fp8 caches)
+    if (KV8)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) vf[cg] = *reinterpret_cast<const f32x4_t*>(&L.vsc[buf][cg * 16 + 4 * g]);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       f32x2_t ps = {0.0f, 0.0f};
@@ -798,8 +908,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
       for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {
-          const f32x2_t pp = {__builtin_amdgcn_exp2f(u[rb][cg][j]), __builtin_amdgcn_exp2f(u[rb][cg][j + 1])};
+          f32x2_t pp = {__builtin_amdgcn_exp2f(u[rb][cg][j]), __builtin_amdgcn_exp2f(u[rb][cg][j + 1])};
           ps = (cg == 0 && j == 0) ? pp : ps + pp;
+          if (KV8) pp = f32x2_t{pp[0] * vf[cg][j], pp[1] * vf[cg][j + 1]};  // the slot's V scale
           const uint32_t hi = bf16x2_bits(pp);
           const f32x2_t back = {u32_as_f32(hi << 16), u32_as_f32(hi & 0xffff0000u)};
           whi[cg * 2 + j / 2] = hi;
@@ -843,7 +954,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
 #pragma unroll
     for (int v = 0; v < DVT; ++v) va[v] = vfrag(buf, v);
     if (__builtin_expect(scores(buf, t, full_c), 0)) rescale(buf, decltype(full_c)::value);
-    weights();
+    weights(buf);
     products(va);
   };
   int t = 0;
@@ -1148,12 +1259,12 @@ int64_t attend_grid(const AttendPlan& p, bool bf16) {
   return bf16 ? p.rows * p.splits : p.groups * p.group_stride;
 }
 
-template <int D, bool HCA, int PAIR>
+template <int D, bool HCA, int PAIR, bool KV8>
 static void launch_bf16_nw(const AttendArgs& a, const AttendPlan& p, dim3 grid) {
   const int nw = (a.H + 15) / 16;
-  if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2, HCA, PAIR>), grid, dim3(128), 0, a.stream, a, p);
-  else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4, HCA, PAIR>), grid, dim3(256), 0, a.stream, a, p);
-  else hipLaunchKernelGGL((attend_bf16_kernel<D, 8, HCA, PAIR>), grid, dim3(512), 0, a.stream, a, p);
+  if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2, HCA, PAIR, KV8>), grid, dim3(128), 0, a.stream, a, p);
+  else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4, HCA, PAIR, KV8>), grid, dim3(256), 0, a.stream, a, p);
+  else hipLaunchKernelGGL((attend_bf16_kernel<D, 8, HCA, PAIR, KV8>), grid, dim3(512), 0, a.stream, a, p);
 }
 
 template <int D, bool HCA>
@@ -1161,8 +1272,8 @@ static void launch_bf16(const AttendArgs& a, const AttendPlan& p) {
   const dim3 grid(unsigned(p.rows * p.splits));
   // Split rows (decode) have one workgroup per CU: stage tiles in pairs.  Many
   // unsplit rows (prefill) keep the smaller LDS footprint for occupancy.
-  if (p.splits > 1) launch_bf16_nw<D, HCA, 2>(a, p, grid);
-  else launch_bf16_nw<D, HCA, 1>(a, p, grid);
+  if (p.splits > 1) a.kv8 ? launch_bf16_nw<D, HCA, 2, true>(a, p, grid) : launch_bf16_nw<D, HCA, 2, false>(a, p, grid);
+  else a.kv8 ? launch_bf16_nw<D, HCA, 1, true>(a, p, grid) : launch_bf16_nw<D, HCA, 1, false>(a, p, grid);
   if (p.splits > 1) {
     const int64_t threads = p.rows * a.H * (D / 4);
     hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
@@ -1177,8 +1288,9 @@ static bool launch_hca_multi(const AttendArgs& a) {
   if (HW > NW || NW % HW != 0) return false;
   const int QT = RB * (NW / HW);
   const int64_t gps = (a.T + QT - 1) / QT;
-  hipLaunchKernelGGL((hca_multi_kernel<D, NW, RB>), dim3(unsigned(int64_t(a.B) * gps)), dim3(NW * 64), 0,
-                     a.stream, a, gps);
+  const dim3 grid(unsigned(int64_t(a.B) * gps)), block(NW * 64);
+  if (a.kv8) hipLaunchKernelGGL((hca_multi_kernel<D, NW, RB, true>), grid, block, 0, a.stream, a, gps);
+  else hipLaunchKernelGGL((hca_multi_kernel<D, NW, RB, false>), grid, block, 0, a.stream, a, gps);
   return true;
 }
 

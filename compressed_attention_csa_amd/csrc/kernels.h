@@ -111,6 +111,9 @@ struct AttendArgs {
   const void* q;   // [B, T, H, d]
   const void* k_cmp;
   const void* v_cmp;  // [B, N_alloc, d]
+  bool kv8;           // k_cmp / v_cmp hold e4m3 codes with per-entry scales
+  const float* k_scale;
+  const float* v_scale;  // [B, N_alloc] (kv8 only)
   int64_t N_alloc;
   int m;  // block size for visibility (CSA m or HCA m_heavy)
   const int32_t* idx;

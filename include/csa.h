@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum {
   CSA_F32 = 0,      /* IEEE binary32 */
@@ -191,7 +191,13 @@ csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w,
  * Listed indices that are negative, >= N_alloc or not yet visible
  * (j >= (t+1)/m) are skipped; a repeated index counts once per listing.
  *
- *   q        [B, T, H, d] of dt;  k_cmp, v_cmp [B, N_alloc, d] of dt
+ *   q        [B, T, H, d] of dt;  k_cmp, v_cmp [B, N_alloc, d] of kv_dt
+ *   kv_dt    dt, or CSA_FP8_E4M3 (dt == CSA_BF16 only) for compressed caches of
+ *            e4m3 codes with one fp32 scale per entry, as csa_compress writes
+ *            them ([summary] 五: low-precision KV caches): the entry is
+ *            code * scale.  k_scale, v_scale [B, N_alloc] fp32, 16-byte
+ *            aligned, required iff kv_dt == CSA_FP8_E4M3 (else NULL).  The raw
+ *            window rows stay of dt.
  *   idx      [B, T, top_k] int32 (top_k may be 0: window only)
  *   k_raw, v_raw [B, n_raw, d] of dt for positions raw_base ..; every window
  *            position of every query must be inside (else CSA_E_SHAPE).
@@ -203,6 +209,7 @@ csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w,
  */
 size_t csa_attend_workspace(int B, int64_t T, int H, int d, int top_k, int window);
 csa_status_t csa_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
+                        csa_dtype_t kv_dt, const float* k_scale, const float* v_scale,
                         int64_t N_alloc, int m, const int32_t* idx, int top_k, const void* k_raw,
                         const void* v_raw, int64_t raw_base, int64_t n_raw, int B, int64_t T,
                         int H, int d, int64_t t0, int window, float scale, void* out,
@@ -215,11 +222,12 @@ csa_status_t csa_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const 
  * [digest] 三 and [book] 4: HCA folds every m' tokens and attends densely to all
  * n/m' heavy entries (no top-k), plus the window.  E(t) = {heavy entries
  * j < min(N_alloc, (t+1)/m_heavy)} plus the raw window; the formulas, layouts,
- * dtypes and limits are those of csa_attend.
+ * dtypes (kv_dt, k_scale, v_scale included) and limits are those of csa_attend.
  */
 size_t hca_attend_workspace(int B, int64_t T, int H, int d, int64_t N_alloc, int m_heavy,
                             int window);
 csa_status_t hca_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
+                        csa_dtype_t kv_dt, const float* k_scale, const float* v_scale,
                         int64_t N_alloc, int m_heavy, const void* k_raw, const void* v_raw,
                         int64_t raw_base, int64_t n_raw, int B, int64_t T, int H, int d,
                         int64_t t0, int window, float scale, void* out, csa_dtype_t out_dt,

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported_and_bound(L):
     for n in names:
         assert hasattr(L, n), n
         assert n in csa.SIGNATURES, n
-    assert L.csa_abi_version() == 1
+    assert L.csa_abi_version() == 2
     for s, name in enumerate(csa.STATUS):
         assert L.csa_status_string(s).decode() == name
 
@@ -135,22 +135,30 @@ def test_index_validation(L):
     assert index(L, w=MIS) == E_ALIGN
 
 
-def attend(L, hca=False, q=P, dt=BF16, kc=P, vc=P, N=256, m=4, idx=P, top_k=64, kr=P, vr=P,
-           raw_base=0, n_raw=1024, B=2, T=1, H=64, d=128, t0=1023, W=128, out=P, out_dt=F32,
-           lse=None, ws=P, ws_bytes=None):
+def attend(L, hca=False, q=P, dt=BF16, kc=P, vc=P, kv_dt=None, ks=None, vs=None, N=256, m=4, idx=P,
+           top_k=64, kr=P, vr=P, raw_base=0, n_raw=1024, B=2, T=1, H=64, d=128, t0=1023, W=128, out=P,
+           out_dt=F32, lse=None, ws=P, ws_bytes=None):
+    kv_dt = dt if kv_dt is None else kv_dt
     if hca:
         if ws_bytes is None:
             ws_bytes = L.hca_attend_workspace(B, T, H, d, N, m, W)
-        return L.hca_attend(q, dt, kc, vc, N, m, kr, vr, raw_base, n_raw, B, T, H, d, t0, W, 0.1,
-                            out, out_dt, lse, ws, ws_bytes, None)
+        return L.hca_attend(q, dt, kc, vc, kv_dt, ks, vs, N, m, kr, vr, raw_base, n_raw, B, T, H, d, t0,
+                            W, 0.1, out, out_dt, lse, ws, ws_bytes, None)
     if ws_bytes is None:
         ws_bytes = L.csa_attend_workspace(B, T, H, d, top_k, W)
-    return L.csa_attend(q, dt, kc, vc, N, m, idx, top_k, kr, vr, raw_base, n_raw, B, T, H, d, t0, W,
-                        0.1, out, out_dt, lse, ws, ws_bytes, None)
+    return L.csa_attend(q, dt, kc, vc, kv_dt, ks, vs, N, m, idx, top_k, kr, vr, raw_base, n_raw, B, T, H,
+                        d, t0, W, 0.1, out, out_dt, lse, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("hca", [False, True])
 def test_attend_validation(L, hca):
+    # fp8 compressed caches: bf16 queries only, both scales, aligned
+    assert attend(L, hca, kv_dt=FP8) == E_NULL
+    assert attend(L, hca, kv_dt=FP8, ks=P) == E_NULL
+    assert attend(L, hca, kv_dt=FP8, ks=P, vs=MIS) == E_ALIGN
+    assert attend(L, hca, dt=F32, kv_dt=FP8, ks=P, vs=P, H=8) == E_DTYPE
+    assert attend(L, hca, kv_dt=F32) == E_DTYPE
+    assert attend(L, hca, ks=P) == E_DTYPE            # scales only with fp8 caches
     assert attend(L, hca, q=None) == E_NULL
     assert attend(L, hca, vr=None) == E_NULL
     assert attend(L, hca, dt=FP8) == E_DTYPE

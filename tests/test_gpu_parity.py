@@ -441,6 +441,53 @@ def test_attend(case):
                         out_bf16=(out_dt == "bf16"))
 
 
+FP8_KV_CASES = [
+    # name, B, T, H, d, N, m, k, W, t0
+    ("csa-decode", 2, 1, 128, 128, 3000, 4, 1024, 128, 4 * 3000 - 1),
+    ("csa-prefill", 1, 37, 64, 128, 300, 4, 64, 128, 1100),
+    ("csa-d64", 2, 20, 16, 64, 100, 4, 40, 0, 60),
+    ("hca-decode", 2, 1, 128, 128, 2000, 128, 0, 128, 128 * 2000 - 1),
+    ("hca-prefill-multi", 2, 301, 64, 128, 40, 128, 0, 128, 4000),
+    ("hca-prefill-multi-d64", 1, 263, 32, 64, 30, 128, 0, 100, 3700),
+]
+
+
+@pytest.mark.parametrize("case", FP8_KV_CASES, ids=[c[0] for c in FP8_KV_CASES])
+def test_attend_with_fp8_compressed_caches(case):
+    """Compressed K and V stored as e4m3 codes with one fp32 scale per entry (the
+    oracle's quantiser); the oracle attends over the stored values code * scale."""
+    name, B, T, H, d, N, m, k, W, t0 = case
+    say("attend fp8 kv", case)
+    hca = name.startswith("hca")
+    n_raw = t0 + T + 3
+    q = gen("f8_q", (B, T, H, d), "bf16", seed=H + T)
+    kq = formats.e4m3_quantize_rows(gen("f8_kc", (B, N, d), "f32", seed=N, std=0.6).numpy())
+    vq = formats.e4m3_quantize_rows(gen("f8_vc", (B, N, d), "f32", seed=N + 1, std=0.6).numpy())
+    kc, ks, kv64 = torch.from_numpy(kq[0]).to(DEV), torch.from_numpy(kq[1]).to(DEV), kq[2]
+    vc, vs, vv64 = torch.from_numpy(vq[0]).to(DEV), torch.from_numpy(vq[1]).to(DEV), vq[2]
+    kr = gen("f8_kr", (B, n_raw, d), "bf16", seed=7)
+    vr = gen("f8_vr", (B, n_raw, d), "bf16", seed=8)
+    scale = 1.0 / math.sqrt(d)
+    out = torch.full((B, T, H, d), 9.0, device=DEV)
+    lse = torch.full((B, T, H), 9.0, device=DEV)
+    if hca:
+        csa.hca_attend(q.to(DEV), kc, vc, m, kr.to(DEV), vr.to(DEV), t0, W, scale, out, lse,
+                       k_scale=ks, v_scale=vs)
+    else:
+        idx = make_idx(B, T, k, t0, m, N, seed=N + k)
+        csa.csa_attend(q.to(DEV), kc, vc, m, torch.from_numpy(idx).to(DEV), kr.to(DEV), vr.to(DEV), t0, W,
+                       scale, out, lse, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    for b in range(B):
+        if hca:
+            o_ref, l_ref = method.hca_attend(f64(q[b]), kv64[b], vv64[b], m, f64(kr[b]), f64(vr[b]), 0, t0, W,
+                                             scale)
+        else:
+            o_ref, l_ref = method.csa_attend(f64(q[b]), kv64[b], vv64[b], idx[b], f64(kr[b]), f64(vr[b]), 0,
+                                             t0, W, m, scale)
+        check_attention(f64(out[b]), f64(lse[b]), o_ref, l_ref, "bf16", what=f"fp8 kv {name} b={b}")
+
+
 def test_attend_is_deterministic_and_consistent_across_splits():
     """Same call twice: identical bits.  Decode rows (split) equal the same rows
     computed inside a prefill call (unsplit), within tolerance."""
