@@ -209,6 +209,49 @@ def test_hca_decode_full_size():
     say("  attention rows ok")
 
 
+def test_hca_decode_fp8_caches_full_size():
+    """The fp8 variant of the HCA decode leg: e4m3 heavy caches as the bench builds
+    them (sampled entries against the oracle's quantiser), then whole decode rows of
+    two sequences on oracle-quantised caches against the oracle over code * scale."""
+    name = "hca_decode_1m"
+    wl = inputgen.WORKLOADS[name]
+    say("full-size fp8 caches", name)
+    B, n, Nh, d, mh, W = wl.B, wl.n, wl.N_h, wl.d, wl.m_heavy, wl.W
+    P = bench.DecodeHCA(wl, SEED, 1, variant="fp8kv")
+    P.step(0)
+    torch.cuda.synchronize()
+    c = P.reps[0]
+    z64 = f64(inputgen.normal("z_hca", (mh,), SEED, "f32", std=0.5, device=DEV))
+    raw = {nm: inputgen.normal(nm, (B, n, d), SEED, "bf16", device=DEV) for nm in ("k_raw", "v_raw")}
+    check_cache_samples(c["k_cmp"], raw["k_raw"], z64, mh, "e4m3", scale=c["k_scale"], count=64)
+    check_cache_samples(c["v_cmp"], raw["v_raw"], z64, mh, "e4m3", scale=c["v_scale"], count=64, seed=2)
+    say("  compressor samples ok")
+    checked = [0, B - 1]
+    kc = torch.zeros((B, Nh, d), dtype=torch.uint8, device=DEV)
+    vc = torch.zeros((B, Nh, d), dtype=torch.uint8, device=DEV)
+    ks = torch.ones((B, Nh), device=DEV)
+    vs = torch.ones((B, Nh), device=DEV)
+    ref = {}
+    for b in checked:
+        sk = oracle_compress(raw["k_raw"][b], z64, mh, "e4m3")
+        sv = oracle_compress(raw["v_raw"][b], z64, mh, "e4m3")
+        kc[b], ks[b] = torch.from_numpy(sk["codes"]).to(DEV), torch.from_numpy(sk["scale"]).to(DEV)
+        vc[b], vs[b] = torch.from_numpy(sv["codes"]).to(DEV), torch.from_numpy(sv["scale"]).to(DEV)
+        ref[b] = (sk["values"], sv["values"])
+    kw, vw = window_dev(raw["k_raw"], n, W), window_dev(raw["v_raw"], n, W)
+    out = torch.empty((B, 1, wl.H, d), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, 1, wl.H), dtype=torch.float32, device=DEV)
+    csa.hca_attend(P.q, kc, vc, mh, kw, vw, wl.t0, W, wl.scale, out, lse, raw_base=n - W, k_scale=ks,
+                   v_scale=vs)
+    torch.cuda.synchronize()
+    q64 = f64(P.q)
+    for b in checked:
+        o_ref, l_ref = method.hca_attend(q64[b], ref[b][0], ref[b][1], mh, f64(kw[b]), f64(vw[b]),
+                                         n - W, wl.t0, W, wl.scale)
+        check_attention(f64(out[b]), f64(lse[b]), o_ref, l_ref, "bf16", what=f"{name} fp8 b={b}")
+    say("  attention rows ok")
+
+
 # ----------------------------------------------------------------------------- CSA prefill
 
 
