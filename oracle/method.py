@@ -83,6 +83,35 @@ def compress_exact(x, z, m: int, entry_begin: int = 0, entry_end: int | None = N
     return np.einsum("s,jsd->jd", alpha, blocks)
 
 
+def compress_overlap(x, z, m: int, o: int, entry_begin: int = 0, entry_end: int | None = None,
+                     raw_base: int = 0) -> np.ndarray:
+    """Overlapping, position-weighted blocks (a method variant), exact in fp64.
+
+    [summary] section 2.1 says the CSA compressor weights positions and lets
+    blocks overlap so that no boundary loses context, without a formula.
+    Reading taken: entry j folds the m + o rows of positions j*m - o .. j*m + m - 1
+    (its own block and the last o rows of the previous one) with the weights
+    softmax(z), z holding one logit per slot (m + o of them).  Slots before
+    position 0 do not exist; the first entries take the softmax over the slots
+    that do.  The entry still ends at position j*m + m - 1, so visibility is
+    unchanged, and o = 0 is compress_exact.  ``x`` holds positions raw_base ..
+    raw_base + len(x) - 1.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    assert z.shape == (m + o,)
+    if entry_end is None:
+        entry_end = (raw_base + x.shape[0]) // m
+    out = np.zeros((max(0, entry_end - entry_begin), x.shape[1]))
+    for j in range(entry_begin, entry_end):
+        pos = np.arange(j * m - o, j * m + m)
+        ok = pos >= 0
+        assert pos[ok][0] >= raw_base and pos[-1] < raw_base + x.shape[0], "rows outside x"
+        w = compressor_weights(z[ok])
+        out[j - entry_begin] = w @ x[pos[ok] - raw_base]
+    return out
+
+
 def state_ring(history, t_end: int, R: int) -> np.ndarray:
     """The state cache after positions 0 .. t_end were appended one by one.
 

@@ -75,6 +75,48 @@ def test_compress_matches_brute_force():
     np.testing.assert_allclose(got, exp, rtol=1e-14, atol=1e-15)
 
 
+def test_overlap_zero_is_the_plain_compressor():
+    x, z = rnd(31, 50, 6), rnd(32, 4) * 0.5
+    np.testing.assert_allclose(method.compress_overlap(x, z, 4, 0), method.compress_exact(x, z, 4), rtol=1e-14,
+                               atol=1e-15)
+
+
+def test_overlap_brute_force_and_first_entries():
+    """Direct fsum over the m + o rows; the first entries renormalise over the
+    slots at positions >= 0."""
+    m, o = 4, 3
+    x, z = rnd(33, 29, 5), rnd(34, m + o) * 0.7
+    got = method.compress_overlap(x, z, m, o)
+    for j in range(len(got)):
+        rows = [(s, j * m - o + s) for s in range(m + o) if j * m - o + s >= 0]
+        e = [math.exp(z[s]) for s, _ in rows]
+        tot = math.fsum(e)
+        for c in range(x.shape[1]):
+            exp = math.fsum(e[i] / tot * x[p, c] for i, (_, p) in enumerate(rows))
+            assert abs(got[j, c] - exp) <= 1e-13 * (1 + abs(exp))
+
+
+def test_overlap_slot_order_and_uniform_weights():
+    """A dominant first logit picks the oldest overlapped row j*m - o (the offset
+    runs backwards); uniform logits average the m + o rows."""
+    m, o = 4, 2
+    x = rnd(35, 40, 3)
+    z = np.full(m + o, -60.0)
+    z[0] = 0.0
+    got = method.compress_overlap(x, z, m, o, entry_begin=1)
+    np.testing.assert_allclose(got, x[[j * m - o for j in range(1, 10)]], rtol=0, atol=1e-20)
+    u = method.compress_overlap(x, np.zeros(m + o), m, o, entry_begin=1)
+    np.testing.assert_allclose(u, [x[j * m - o: j * m + m].mean(axis=0) for j in range(1, 10)], rtol=1e-14)
+
+
+def test_overlap_subrange_with_raw_base_matches_full():
+    m, o = 4, 4
+    x, z = rnd(36, 64, 5), rnd(37, m + o)
+    full = method.compress_overlap(x, z, m, o)
+    part = method.compress_overlap(x[16:], z, m, o, entry_begin=5, entry_end=16, raw_base=16)
+    np.testing.assert_array_equal(part, full[5:16])
+
+
 @pytest.mark.parametrize("R", [5, 8, 13])
 def test_state_ring_holds_the_newest_R_positions_as_consecutive_rows(R):
     """Every window of <= R newest positions is a contiguous row range of the
