@@ -36,10 +36,10 @@ SIGNATURES = {
     "csa_abi_version": (_i32, []),
     "csa_status_string": (ctypes.c_char_p, [_i32]),
     "csa_last_error": (ctypes.c_char_p, []),
-    "csa_compress": (_i32, [_vp, _i32, _i32, _i64, _i32, _i64, _vp, _i32, _i64, _i64, _i64, _vp,
-                            _i32, _vp, _vp]),
-    "csa_append": (_i32, [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _i32, _i64, _vp, _i32,
-                          _vp, _vp]),
+    "csa_compress": (_i32, [_vp, _i32, _i32, _i64, _i32, _i64, _vp, _i32, _i32, _i64, _i64, _i64,
+                            _vp, _i32, _vp, _vp]),
+    "csa_append": (_i32, [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _i32, _i32, _i64, _vp,
+                          _i32, _vp, _vp]),
     "csa_index_topk_workspace": (_sz, [_i32, _i64, _i32, _i32, _i64, _i32, _i32]),
     "csa_index_topk": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i32, _i32, _i64, _i64,
                               _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
@@ -128,24 +128,27 @@ def workspace(nbytes: int, device, key: str = "default") -> torch.Tensor | None:
     return ws
 
 
-def csa_compress(x, logits, m, out, out_scale=None, raw_base=0, entry_begin=0, entry_end=None):
+def csa_compress(x, logits, m, out, out_scale=None, raw_base=0, entry_begin=0, entry_end=None,
+                 overlap=0):
+    """``logits`` holds m + overlap slot logits (overlap > 0: the overlapping variant)."""
     B, n_raw, d = x.shape
     N_alloc = out.shape[1]
     if entry_end is None:
         entry_end = min(N_alloc, (raw_base + n_raw) // m)
-    st = lib().csa_compress(_ptr(x), _dt(x), B, n_raw, d, raw_base, _ptr(logits), m, entry_begin,
-                            entry_end, N_alloc, _ptr(out), _dt(out), _ptr(out_scale), _stream(x))
+    st = lib().csa_compress(_ptr(x), _dt(x), B, n_raw, d, raw_base, _ptr(logits), m, overlap,
+                            entry_begin, entry_end, N_alloc, _ptr(out), _dt(out), _ptr(out_scale),
+                            _stream(x))
     _check("csa_compress", st)
     return out
 
 
-def csa_append(x_new, ring, t0, logits, m, out, out_scale=None):
+def csa_append(x_new, ring, t0, logits, m, out, out_scale=None, overlap=0):
     """Append rows for positions t0 .. t0 + T_new - 1 to the mirrored ring
     [B, 2R, d] and compress the blocks they complete into ``out``."""
     B, T_new, d = x_new.shape
     R = ring.shape[1] // 2
     st = lib().csa_append(_ptr(x_new), _dt(x_new), B, T_new, d, t0, _ptr(ring), R, _ptr(logits), m,
-                          out.shape[1], _ptr(out), _dt(out), _ptr(out_scale), _stream(x_new))
+                          overlap, out.shape[1], _ptr(out), _dt(out), _ptr(out_scale), _stream(x_new))
     _check("csa_append", st)
     return out
 

@@ -111,9 +111,9 @@ const char* csa_status_string(int s) {
 const char* csa_last_error(void) { return g_last_error.c_str(); }
 
 csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw, int d,
-                          int64_t raw_base, const float* logits, int m, int64_t entry_begin,
-                          int64_t entry_end, int64_t N_alloc, void* out, csa_dtype_t out_dt,
-                          float* out_scale, csa_stream_t stream) {
+                          int64_t raw_base, const float* logits, int m, int overlap,
+                          int64_t entry_begin, int64_t entry_end, int64_t N_alloc, void* out,
+                          csa_dtype_t out_dt, float* out_scale, csa_stream_t stream) {
   REQUIRE_PTR(x);
   REQUIRE_PTR(logits);
   REQUIRE_PTR(out);
@@ -127,14 +127,17 @@ csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw,
   REQUIRE(out_dt != CSA_FP8_E4M3 || (d >= 16 && (d & (d - 1)) == 0), CSA_E_SHAPE,
           "fp8 output needs d a power of two >= 16, got %d", d);
   REQUIRE(m >= 1 && m <= 128, CSA_E_SHAPE, "m=%d out of range [1, 128]", m);
+  REQUIRE(overlap >= 0 && m + overlap <= 128, CSA_E_SHAPE, "overlap=%d: need 0 <= overlap and m + overlap <= 128",
+          overlap);
   REQUIRE(n_raw >= 0 && raw_base >= 0, CSA_E_SHAPE, "n_raw / raw_base must be >= 0");
   REQUIRE(0 <= entry_begin && entry_begin <= entry_end && entry_end <= N_alloc, CSA_E_SHAPE,
           "need 0 <= entry_begin <= entry_end <= N_alloc");
   if (entry_end > entry_begin) {
-    REQUIRE(entry_begin * m >= raw_base && entry_end * m <= raw_base + n_raw, CSA_E_SHAPE,
-            "blocks [%lld, %lld) * m are not inside the raw rows [%lld, %lld)",
-            (long long)entry_begin, (long long)entry_end, (long long)raw_base,
-            (long long)(raw_base + n_raw));
+    const int64_t first = entry_begin * m - overlap > 0 ? entry_begin * m - overlap : 0;
+    REQUIRE(first >= raw_base && entry_end * m <= raw_base + n_raw, CSA_E_SHAPE,
+            "the rows of blocks [%lld, %lld) (positions %lld .. %lld) are not inside the raw rows [%lld, %lld)",
+            (long long)entry_begin, (long long)entry_end, (long long)first, (long long)(entry_end * m - 1),
+            (long long)raw_base, (long long)(raw_base + n_raw));
     REQUIRE((entry_end - entry_begin) / (256 / (d / 8)) < kMaxGrid, CSA_E_SHAPE, "too many entries");
   }
   REQUIRE_ALIGN(x);
@@ -142,15 +145,15 @@ csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw,
   REQUIRE_ALIGN(out);
   REQUIRE(out_scale == nullptr || aligned16(out_scale), CSA_E_ALIGN, "out_scale is not 16-byte aligned");
   csa::CompressArgs a{x,     x_dt == CSA_BF16, B,         n_raw,    d,
-                      raw_base, logits, m, entry_begin, entry_end, N_alloc,
+                      raw_base, logits, m, overlap, entry_begin, entry_end, N_alloc,
                       out,   out_dt == CSA_F32 ? 0 : (out_dt == CSA_BF16 ? 1 : 2), out_scale,
                       reinterpret_cast<hipStream_t>(stream)};
   return hip_status(csa::launch_compress(a), "compress launch");
 }
 
 csa_status_t csa_append(const void* x_new, csa_dtype_t dt, int B, int T_new, int d, int64_t t0,
-                        void* ring, int64_t R, const float* logits, int m, int64_t N_alloc, void* out,
-                        csa_dtype_t out_dt, float* out_scale, csa_stream_t stream) {
+                        void* ring, int64_t R, const float* logits, int m, int overlap, int64_t N_alloc,
+                        void* out, csa_dtype_t out_dt, float* out_scale, csa_stream_t stream) {
   REQUIRE_PTR(x_new);
   REQUIRE_PTR(ring);
   REQUIRE_PTR(logits);
@@ -165,11 +168,14 @@ csa_status_t csa_append(const void* x_new, csa_dtype_t dt, int B, int T_new, int
   REQUIRE(out_dt != CSA_FP8_E4M3 || (d >= 16 && (d & (d - 1)) == 0), CSA_E_SHAPE,
           "fp8 output needs d a power of two >= 16, got %d", d);
   REQUIRE(m >= 1 && m <= 128, CSA_E_SHAPE, "m=%d out of range [1, 128]", m);
+  REQUIRE(overlap >= 0 && m + overlap <= 128, CSA_E_SHAPE, "overlap=%d: need 0 <= overlap and m + overlap <= 128",
+          overlap);
   REQUIRE(T_new >= 0 && T_new <= 4096, CSA_E_SHAPE, "T_new=%d out of range [0, 4096]", T_new);
   REQUIRE(t0 >= 0 && N_alloc >= 0, CSA_E_SHAPE, "t0 / N_alloc must be >= 0");
   REQUIRE(R >= 1 && R <= (int64_t(1) << 24), CSA_E_SHAPE, "R=%lld out of range [1, 2^24]", (long long)R);
-  REQUIRE(R >= int64_t(m) + T_new - 1, CSA_E_SHAPE,
-          "R=%lld must hold a block and the new rows: R >= m + T_new - 1 = %d", (long long)R, m + T_new - 1);
+  REQUIRE(R >= int64_t(m) + overlap + T_new - 1, CSA_E_SHAPE,
+          "R=%lld must hold a block and the new rows: R >= m + overlap + T_new - 1 = %d", (long long)R,
+          m + overlap + T_new - 1);
   REQUIRE_ALIGN(x_new);
   REQUIRE_ALIGN(ring);
   REQUIRE_ALIGN(logits);
@@ -181,9 +187,10 @@ csa_status_t csa_append(const void* x_new, csa_dtype_t dt, int B, int T_new, int
   int64_t j_hi = (t0 + T_new) / m;
   if (j_hi > N_alloc) j_hi = N_alloc;
   if (j_hi < j_lo) j_hi = j_lo;
-  // Their positions are R consecutive ring rows from (j_lo m) % R on.
-  const int64_t p_lo = j_lo * m;
-  csa::CompressArgs a{ring, dt == CSA_BF16, B, 2 * R, d, p_lo - p_lo % R, logits, m, j_lo, j_hi, N_alloc,
+  // Their rows (positions j_lo m - overlap .. , those >= 0) are consecutive
+  // ring rows from p_lo % R on.
+  const int64_t p_lo = j_lo * m - overlap > 0 ? j_lo * m - overlap : 0;
+  csa::CompressArgs a{ring, dt == CSA_BF16, B, 2 * R, d, p_lo - p_lo % R, logits, m, overlap, j_lo, j_hi, N_alloc,
                       out, out_dt == CSA_F32 ? 0 : (out_dt == CSA_BF16 ? 1 : 2), out_scale,
                       reinterpret_cast<hipStream_t>(stream)};
   return hip_status(csa::launch_append(a, x_new, t0, T_new, R), "append launch");

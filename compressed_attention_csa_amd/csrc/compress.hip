@@ -53,10 +53,13 @@ struct AppendTail {
 };
 
 // OUT: 0 = fp32, 1 = bf16, 2 = e4m3 + per-entry fp32 scale.
+// Overlap o > 0 (a method variant): entry j folds the m + o rows of positions
+// j*m - o .. j*m + m - 1 with the softmax of m + o logits; the first entries,
+// whose leading slots fall before position 0, renormalise over the rest.
 template <typename TIn, int OUT, bool APPEND>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
     const TIn* __restrict__ x, int64_t n_raw, int d, int64_t raw_base,
-    const float* __restrict__ logits, int m, int64_t entry_begin, int64_t n_ent, int64_t N_alloc,
+    const float* __restrict__ logits, int m, int o, int64_t entry_begin, int64_t n_ent, int64_t N_alloc,
     void* __restrict__ out, float* __restrict__ out_scale, AppendTail at) {
   __shared__ double alpha[128];
   __shared__ float zmax_s;
@@ -80,19 +83,20 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   }
 
   // Slot weights: softmax of the logits, in fp64.
+  const int ms = m + o;  // slots per entry
   if (tid < kWave) {
     float v = -INFINITY;
-    for (int s = tid; s < m; s += kWave) v = fmaxf(v, logits[s]);
+    for (int s = tid; s < ms; s += kWave) v = fmaxf(v, logits[s]);
     v = wave_max(v);
     if (tid == 0) zmax_s = v;
   }
   __syncthreads();
-  for (int s = tid; s < m; s += kThreads) alpha[s] = exp(double(logits[s]) - double(zmax_s));
+  for (int s = tid; s < ms; s += kThreads) alpha[s] = exp(double(logits[s]) - double(zmax_s));
   __syncthreads();
   double total = 0.0;
-  for (int s = 0; s < m; ++s) total += alpha[s];
+  for (int s = 0; s < ms; ++s) total += alpha[s];
   __syncthreads();
-  for (int s = tid; s < m; s += kThreads) alpha[s] = alpha[s] / total;
+  for (int s = tid; s < ms; s += kThreads) alpha[s] = alpha[s] / total;
   __syncthreads();
 
   const int tpe = d >> 3;  // threads per entry, 8 columns each
@@ -106,17 +110,25 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0;
   if (valid) {
-    const TIn* src = x + (int64_t(b) * n_raw + (j * m - raw_base)) * d + seg * 8;
+    const TIn* xb = x + int64_t(b) * n_raw * d + seg * 8;
+    const int64_t p0 = j * m - o;  // position of slot 0
+    double wsum = 0.0;             // weight of the slots at positions >= 0
 #pragma unroll 8
-    for (int s = 0; s < m; ++s) {
+    for (int s = 0; s < ms; ++s) {
+      const int64_t pos = p0 + s;
+      if (pos < 0) continue;
       double v[8];
-      const TIn* rp = src + int64_t(s) * d;
-      if (APPEND && j * m + s >= at.t0) rp = xn + (j * m + s - at.t0) * d + seg * 8;
+      const TIn* rp = xb + (pos - raw_base) * d;
+      if (APPEND && pos >= at.t0) rp = xn + (pos - at.t0) * d + seg * 8;
       Row8<TIn>::load(rp, v);
       const double a = alpha[s];
+      wsum += a;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fma(a, v[i], acc[i]);
     }
+    if (p0 < 0)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] /= wsum;
   }
 
   const int64_t orow = int64_t(b) * N_alloc + j;
@@ -173,7 +185,7 @@ hipError_t launch(const CompressArgs& a, const AppendTail& at) {
   dim3 grid(unsigned(blocks), unsigned(a.B));
   ProfScope prof(APPEND ? "append" : "compress", a.stream);
   hipLaunchKernelGGL((compress_kernel<TIn, OUT, APPEND>), grid, dim3(kThreads), 0, a.stream,
-                     reinterpret_cast<const TIn*>(a.x), a.n_raw, a.d, a.raw_base, a.logits, a.m,
+                     reinterpret_cast<const TIn*>(a.x), a.n_raw, a.d, a.raw_base, a.logits, a.m, a.overlap,
                      a.entry_begin, n_ent, a.N_alloc, a.out, a.out_scale, t);
   return hipGetLastError();
 }

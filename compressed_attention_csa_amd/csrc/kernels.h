@@ -28,8 +28,9 @@ struct CompressArgs {
   int64_t n_raw;
   int d;
   int64_t raw_base;
-  const float* logits;
+  const float* logits;  // m + overlap slot logits
   int m;
+  int overlap;          // rows of the previous block folded into each entry (0: none)
   int64_t entry_begin, entry_end, N_alloc;
   void* out;
   int out_kind;  // 0 fp32, 1 bf16, 2 e4m3 + scale

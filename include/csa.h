@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum {
   CSA_F32 = 0,      /* IEEE binary32 */
@@ -95,11 +95,18 @@ const char* csa_last_error(void);
  *
  *   x          [B, n_raw, d] of x_dt (CSA_F32 | CSA_BF16): raw rows for the
  *              positions raw_base .. raw_base + n_raw - 1.
- *   logits     [m] fp32, device.  1 <= m <= 128.
+ *   logits     [m + overlap] fp32, device.  1 <= m, m + overlap <= 128.
+ *   overlap    0 for the blocks above.  overlap = o > 0 is a method variant
+ *              ([summary] 2.1: position weighting and overlapping blocks, no
+ *              formula): entry j folds the m + o rows of positions
+ *              j*m - o .. j*m + m - 1 with alpha = softmax(logits) over the
+ *              m + o slots; slots before position 0 are left out and the
+ *              first entries renormalise over the rest.  An entry still ends
+ *              at position j*m + m - 1 (its visibility is unchanged).
  *   entries    [entry_begin, entry_end) of each sequence are written; every
  *              covered position must lie inside x:
- *              raw_base <= entry_begin*m and entry_end*m <= raw_base + n_raw,
- *              0 <= entry_begin <= entry_end <= N_alloc.
+ *              raw_base <= max(0, entry_begin*m - overlap) and
+ *              entry_end*m <= raw_base + n_raw, 0 <= entry_begin <= entry_end <= N_alloc.
  *   out        [B, N_alloc, d] of out_dt: CSA_F32 | CSA_BF16 (sum rounded once,
  *              nearest-even), or CSA_FP8_E4M3 (bytes) with out_scale.
  *   out_scale  [B, N_alloc] fp32, required iff out_dt == CSA_FP8_E4M3, else
@@ -110,9 +117,9 @@ const char* csa_last_error(void);
  * An empty entry range is a no-op.  No workspace.
  */
 csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw, int d,
-                          int64_t raw_base, const float* logits, int m, int64_t entry_begin,
-                          int64_t entry_end, int64_t N_alloc, void* out, csa_dtype_t out_dt,
-                          float* out_scale, csa_stream_t stream);
+                          int64_t raw_base, const float* logits, int m, int overlap,
+                          int64_t entry_begin, int64_t entry_end, int64_t N_alloc, void* out,
+                          csa_dtype_t out_dt, float* out_scale, csa_stream_t stream);
 
 /*
  * csa_append -- decode-time state cache: append raw rows and compress the
@@ -131,10 +138,10 @@ csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw,
  *           t0 .. t0 + T_new - 1 (0 <= T_new <= 4096; 0 is a no-op).
  *   ring    [B, 2R, d] of dt, updated in place.  It must already hold the
  *           positions t0 - R + T_new .. t0 - 1 (those >= 0) from earlier calls.
- *   R       ring rows, 1 <= R <= 2^24 and R >= m + T_new - 1 (so that every
- *           completed block is still in the ring); R >= W + T_new keeps a
- *           window of W rows readable after the call.
- *   logits, m, out, out_dt, out_scale, N_alloc: as in csa_compress.  Every
+ *   R       ring rows, 1 <= R <= 2^24 and R >= m + overlap + T_new - 1 (so
+ *           that the rows of every completed block are still in the ring);
+ *           R >= W + T_new keeps a window of W rows readable after the call.
+ *   logits, m, overlap, out, out_dt, out_scale, N_alloc: as in csa_compress.  Every
  *           block j < N_alloc that the new rows complete, t0 <= (j+1) m - 1 <=
  *           t0 + T_new - 1, is written to out[b, j] with the same arithmetic
  *           (and hence the same bits) as csa_compress over the full history.
@@ -142,8 +149,9 @@ csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw,
  * Calls for one ring must be ordered on one stream.  No workspace.
  */
 csa_status_t csa_append(const void* x_new, csa_dtype_t dt, int B, int T_new, int d, int64_t t0,
-                        void* ring, int64_t R, const float* logits, int m, int64_t N_alloc,
-                        void* out, csa_dtype_t out_dt, float* out_scale, csa_stream_t stream);
+                        void* ring, int64_t R, const float* logits, int m, int overlap,
+                        int64_t N_alloc, void* out, csa_dtype_t out_dt, float* out_scale,
+                        csa_stream_t stream);
 
 /*
  * csa_index_topk -- Lightning-Indexer scores and per-query top-k selection.

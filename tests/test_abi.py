@@ -41,14 +41,15 @@ def test_every_declared_symbol_is_exported_and_bound(L):
     for n in names:
         assert hasattr(L, n), n
         assert n in csa.SIGNATURES, n
-    assert L.csa_abi_version() == 2
+    assert L.csa_abi_version() == 3
     for s, name in enumerate(csa.STATUS):
         assert L.csa_status_string(s).decode() == name
 
 
 def compress(L, x=P, x_dt=BF16, B=1, n_raw=64, d=128, raw_base=0, logits=P, m=4, eb=0, ee=16,
-             N=16, out=P, out_dt=BF16, scale=None):
-    return L.csa_compress(x, x_dt, B, n_raw, d, raw_base, logits, m, eb, ee, N, out, out_dt, scale, None)
+             N=16, out=P, out_dt=BF16, scale=None, overlap=0):
+    return L.csa_compress(x, x_dt, B, n_raw, d, raw_base, logits, m, overlap, eb, ee, N, out, out_dt, scale,
+                          None)
 
 
 def test_compress_validation(L):
@@ -67,6 +68,9 @@ def test_compress_validation(L):
     assert compress(L, eb=5, ee=4) == E_SHAPE
     assert compress(L, n_raw=63) == E_SHAPE           # last block not inside x
     assert compress(L, raw_base=4) == E_SHAPE         # first block before raw_base
+    assert compress(L, overlap=-1) == E_SHAPE
+    assert compress(L, m=100, overlap=29) == E_SHAPE  # m + overlap <= 128 logits
+    assert compress(L, eb=2, raw_base=8, n_raw=56, overlap=1) == E_SHAPE  # overlap row 7 before raw_base
     assert compress(L, B=0) == E_SHAPE
     assert compress(L, x=MIS) == E_ALIGN
     assert compress(L, out=MIS) == E_ALIGN
@@ -75,8 +79,8 @@ def test_compress_validation(L):
 
 
 def append(L, x=P, dt=BF16, B=2, T_new=1, d=128, t0=100, ring=P, R=132, logits=P, m=4, N=64, out=P,
-           out_dt=BF16, scale=None):
-    return L.csa_append(x, dt, B, T_new, d, t0, ring, R, logits, m, N, out, out_dt, scale, None)
+           out_dt=BF16, scale=None, overlap=0):
+    return L.csa_append(x, dt, B, T_new, d, t0, ring, R, logits, m, overlap, N, out, out_dt, scale, None)
 
 
 def test_append_validation(L):
@@ -97,6 +101,7 @@ def test_append_validation(L):
     assert append(L, R=0) == E_SHAPE
     assert append(L, m=128, R=127) == E_SHAPE         # a block must fit in the ring
     assert append(L, m=4, T_new=10, R=12) == E_SHAPE  # R >= m + T_new - 1
+    assert append(L, m=4, T_new=1, R=5, overlap=2) == E_SHAPE  # R >= m + overlap + T_new - 1
     assert append(L, ring=MIS) == E_ALIGN
     assert append(L, x=MIS) == E_ALIGN
     assert append(L, T_new=0) == OK                   # nothing to do, nothing enqueued

@@ -87,26 +87,68 @@ def test_compress(case):
             assert (out[b, :eb] == 7.0).all() and (out[b, ee:] == 7.0).all()
 
 
-# ----------------------------------------------------------------------------- state cache (append)
-
-APPEND_CASES = [
-    # x_dt, out_dt, B, d, m, R, positions, pattern of rows per call
-    ("bf16", "bf16", 2, 128, 4, 132, 701, [1]),
-    ("bf16", "e4m3", 3, 64, 4, 132, 530, [1, 1, 3, 1, 2, 7, 1]),
-    ("bf16", "bf16", 2, 128, 128, 256, 1100, [1] * 9 + [100]),
-    ("f32", "f32", 1, 32, 5, 12, 301, [1, 2, 8, 1]),
+OVERLAP_CASES = [
+    # x_dt, out_dt, m, overlap, d, n_raw, raw_base, entry_begin, entry_end, N
+    ("bf16", "bf16", 4, 2, 128, 400, 0, 0, 100, 100),
+    ("bf16", "e4m3", 4, 4, 64, 300, 40, 11, 70, 80),
+    ("f32", "f32", 5, 3, 32, 203, 0, 0, 40, 41),
+    ("bf16", "bf16", 64, 64, 128, 1024, 0, 0, 16, 16),
 ]
 
 
-@pytest.mark.parametrize("case", APPEND_CASES, ids=[f"{c[0]}-{c[1]}-m{c[4]}-R{c[5]}" for c in APPEND_CASES])
+@pytest.mark.parametrize("case", OVERLAP_CASES, ids=[f"{c[0]}-{c[1]}-m{c[2]}-o{c[3]}" for c in OVERLAP_CASES])
+def test_compress_with_overlapping_blocks(case):
+    """The overlapping variant (m + o slots per entry, first entries renormalised)
+    against the oracle's compress_overlap, with the csa_compress criteria."""
+    x_dt, out_dt, m, o, d, n_raw, raw_base, eb, ee, N = case
+    say("compress overlap", case)
+    B = 2
+    x = gen("ov_x", (B, n_raw, d), x_dt, seed=n_raw + d + o)
+    z = gen("ov_z", (m + o,), "f32", seed=m + o, std=0.5)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.uint8}[out_dt]
+    sentinel = 0x55 if out_dt == "e4m3" else 7.0
+    out = torch.full((B, N, d), sentinel, dtype=tdt, device=DEV)
+    scale = torch.full((B, N), 7.0, device=DEV) if out_dt == "e4m3" else None
+    csa.csa_compress(x.to(DEV), z.to(DEV), m, out, scale, raw_base=raw_base, entry_begin=eb, entry_end=ee,
+                     overlap=o)
+    torch.cuda.synchronize()
+    for b in range(B):
+        sums = method.compress_overlap(f64(x[b]), f64(z), m, o, eb, ee, raw_base)
+        if out_dt == "bf16":
+            diff = ulp_diff_bf16(bf16_bits(out[b, eb:ee]), formats.f64_to_bf16_bits(sums))
+            assert diff.max() <= 1
+            assert (diff == 0).mean() >= 0.999
+        elif out_dt == "f32":
+            np.testing.assert_allclose(f64(out[b, eb:ee]), formats.round_to_f32(sums), rtol=1e-6, atol=0)
+        else:
+            n_bad = check_e4m3(out[b, eb:ee].cpu().numpy(), scale[b, eb:ee].cpu().numpy(), sums.astype(np.float32))
+            assert n_bad <= max(2, sums.size // 10000)
+        assert (out[b, :eb] == sentinel).all() and (out[b, ee:] == sentinel).all()
+
+
+# ----------------------------------------------------------------------------- state cache (append)
+
+APPEND_CASES = [
+    # x_dt, out_dt, B, d, m, R, positions, pattern of rows per call, overlap
+    ("bf16", "bf16", 2, 128, 4, 132, 701, [1], 0),
+    ("bf16", "e4m3", 3, 64, 4, 132, 530, [1, 1, 3, 1, 2, 7, 1], 0),
+    ("bf16", "bf16", 2, 128, 128, 256, 1100, [1] * 9 + [100], 0),
+    ("f32", "f32", 1, 32, 5, 12, 301, [1, 2, 8, 1], 0),
+    ("bf16", "bf16", 2, 64, 4, 134, 403, [1, 1, 5, 1, 3], 2),
+    ("f32", "f32", 1, 32, 5, 17, 120, [1, 2, 8, 1], 3),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES,
+                         ids=[f"{c[0]}-{c[1]}-m{c[4]}-R{c[5]}-o{c[8]}" for c in APPEND_CASES])
 def test_append_builds_the_caches_of_the_full_history(case):
     """Rows appended token by token (and in small chunks) leave the ring holding
     the newest R positions bit-exactly, and the compressed cache equal to the
     oracle's compression of the whole history (same criteria as csa_compress)."""
-    x_dt, out_dt, B, d, m, R, n, pattern = case
+    x_dt, out_dt, B, d, m, R, n, pattern, o = case
     say("append", case)
     hist = gen("app_x", (B, n, d), x_dt, seed=n + d)
-    z = gen("app_z", (m,), "f32", seed=m, std=0.5).to(DEV)
+    z = gen("app_z", (m + o,), "f32", seed=m, std=0.5).to(DEV)
     N = n // m + 3  # a few entries past the history stay untouched
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.uint8}[out_dt]
     sentinel = 0x55 if out_dt == "e4m3" else 7.0
@@ -118,7 +160,7 @@ def test_append_builds_the_caches_of_the_full_history(case):
     while t < n:
         T_new = min(pattern[k % len(pattern)], n - t)
         k += 1
-        csa.csa_append(hd[:, t:t + T_new].contiguous(), ring, t, z, m, out, scale)
+        csa.csa_append(hd[:, t:t + T_new].contiguous(), ring, t, z, m, out, scale, overlap=o)
         t += T_new
     torch.cuda.synchronize()
     z64 = f64(z)
@@ -130,7 +172,8 @@ def test_append_builds_the_caches_of_the_full_history(case):
         assert held.sum() == 2 * min(R, n)
         got_ring = f64(ring[b])
         np.testing.assert_array_equal(got_ring[held], exp_ring[held])
-        sums = method.compress_exact(f64(hist[b]), z64, m, 0, n_ent)
+        sums = method.compress_overlap(f64(hist[b]), z64, m, o, 0, n_ent) if o else \
+            method.compress_exact(f64(hist[b]), z64, m, 0, n_ent)
         if out_dt == "bf16":
             diff = ulp_diff_bf16(bf16_bits(out[b, :n_ent]), formats.f64_to_bf16_bits(sums))
             assert diff.max() <= 1
