@@ -38,6 +38,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
   } while (0)
 
 #define REQUIRE_PTR(p) REQUIRE((p) != nullptr, CSA_E_NULL, "%s is NULL", #p)
+// A pointer to an array with no elements may be NULL.
+#define REQUIRE_PTR_IF(p, nonempty) REQUIRE((p) != nullptr || !(nonempty), CSA_E_NULL, "%s is NULL", #p)
 #define REQUIRE_ALIGN(p) REQUIRE(aligned16(p), CSA_E_ALIGN, "%s is not 16-byte aligned", #p)
 
 constexpr int64_t kMaxEntries = int64_t(1) << 22;  // indexer entries per sequence
@@ -48,12 +50,12 @@ csa_status_t check_attend_common(const void* q, csa_dtype_t dt, const void* k_cm
                                  const void* v_raw, int64_t raw_base, int64_t n_raw, int B,
                                  int64_t T, int H, int d, int64_t t0, int window, void* out,
                                  csa_dtype_t out_dt, const float* lse) {
-  REQUIRE_PTR(q);
-  REQUIRE_PTR(k_cmp);
-  REQUIRE_PTR(v_cmp);
-  REQUIRE_PTR(k_raw);
-  REQUIRE_PTR(v_raw);
-  REQUIRE_PTR(out);
+  REQUIRE_PTR_IF(q, T > 0);
+  REQUIRE_PTR_IF(k_cmp, N_alloc > 0);
+  REQUIRE_PTR_IF(v_cmp, N_alloc > 0);
+  REQUIRE_PTR_IF(k_raw, n_raw > 0);
+  REQUIRE_PTR_IF(v_raw, n_raw > 0);
+  REQUIRE_PTR_IF(out, T > 0);
   REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_E_DTYPE, "dt must be CSA_F32 or CSA_BF16");
   REQUIRE(out_dt == CSA_F32 || out_dt == CSA_BF16, CSA_E_DTYPE, "out_dt must be CSA_F32 or CSA_BF16");
   REQUIRE(B >= 1 && B <= 65535, CSA_E_SHAPE, "B=%d out of range [1, 65535]", B);
@@ -114,13 +116,13 @@ csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw,
                           int64_t raw_base, const float* logits, int m, int overlap,
                           int64_t entry_begin, int64_t entry_end, int64_t N_alloc, void* out,
                           csa_dtype_t out_dt, float* out_scale, csa_stream_t stream) {
-  REQUIRE_PTR(x);
+  REQUIRE_PTR_IF(x, n_raw > 0);
   REQUIRE_PTR(logits);
-  REQUIRE_PTR(out);
+  REQUIRE_PTR_IF(out, N_alloc > 0);
   REQUIRE(x_dt == CSA_F32 || x_dt == CSA_BF16, CSA_E_DTYPE, "x_dt must be CSA_F32 or CSA_BF16");
   REQUIRE(out_dt == CSA_F32 || out_dt == CSA_BF16 || out_dt == CSA_FP8_E4M3, CSA_E_DTYPE,
           "unknown out_dt %d", int(out_dt));
-  if (out_dt == CSA_FP8_E4M3) REQUIRE_PTR(out_scale);
+  if (out_dt == CSA_FP8_E4M3) REQUIRE_PTR_IF(out_scale, N_alloc > 0);
   else REQUIRE(out_scale == nullptr, CSA_E_DTYPE, "out_scale must be NULL unless out_dt is CSA_FP8_E4M3");
   REQUIRE(B >= 1 && B <= 65535, CSA_E_SHAPE, "B=%d out of range [1, 65535]", B);
   REQUIRE(d >= 8 && d <= 512 && d % 8 == 0, CSA_E_SHAPE, "d=%d must be a multiple of 8 in [8, 512]", d);
@@ -154,14 +156,14 @@ csa_status_t csa_compress(const void* x, csa_dtype_t x_dt, int B, int64_t n_raw,
 csa_status_t csa_append(const void* x_new, csa_dtype_t dt, int B, int T_new, int d, int64_t t0,
                         void* ring, int64_t R, const float* logits, int m, int overlap, int64_t N_alloc,
                         void* out, csa_dtype_t out_dt, float* out_scale, csa_stream_t stream) {
-  REQUIRE_PTR(x_new);
+  REQUIRE_PTR_IF(x_new, T_new > 0);
   REQUIRE_PTR(ring);
   REQUIRE_PTR(logits);
-  REQUIRE_PTR(out);
+  REQUIRE_PTR_IF(out, N_alloc > 0);
   REQUIRE(dt == CSA_F32 || dt == CSA_BF16, CSA_E_DTYPE, "dt must be CSA_F32 or CSA_BF16");
   REQUIRE(out_dt == CSA_F32 || out_dt == CSA_BF16 || out_dt == CSA_FP8_E4M3, CSA_E_DTYPE,
           "unknown out_dt %d", int(out_dt));
-  if (out_dt == CSA_FP8_E4M3) REQUIRE_PTR(out_scale);
+  if (out_dt == CSA_FP8_E4M3) REQUIRE_PTR_IF(out_scale, N_alloc > 0);
   else REQUIRE(out_scale == nullptr, CSA_E_DTYPE, "out_scale must be NULL unless out_dt is CSA_FP8_E4M3");
   REQUIRE(B >= 1 && B <= 65535, CSA_E_SHAPE, "B=%d out of range [1, 65535]", B);
   REQUIRE(d >= 8 && d <= 512 && d % 8 == 0, CSA_E_SHAPE, "d=%d must be a multiple of 8 in [8, 512]", d);
@@ -209,13 +211,13 @@ csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w,
                             int d_I, int64_t N_alloc, int64_t t0, int m, int top_k,
                             int32_t* out_idx, float* out_score, void* workspace,
                             size_t workspace_bytes, csa_stream_t stream) {
-  REQUIRE_PTR(q_idx);
-  REQUIRE_PTR(k_idx);
-  REQUIRE_PTR(out_idx);
+  REQUIRE_PTR_IF(q_idx, T > 0);
+  REQUIRE_PTR_IF(k_idx, N_alloc > 0);
+  REQUIRE_PTR_IF(out_idx, T > 0 && top_k > 0);
   const bool ok_dt = (q_dt == CSA_F32 && k_dt == CSA_F32) || (q_dt == CSA_BF16 && k_dt == CSA_BF16) ||
                      (q_dt == CSA_BF16 && k_dt == CSA_FP8_E4M3);
   REQUIRE(ok_dt, CSA_E_DTYPE, "unsupported (q_dt, k_dt) = (%d, %d)", int(q_dt), int(k_dt));
-  if (k_dt == CSA_FP8_E4M3) REQUIRE_PTR(k_scale);
+  if (k_dt == CSA_FP8_E4M3) REQUIRE_PTR_IF(k_scale, N_alloc > 0);
   else REQUIRE(k_scale == nullptr, CSA_E_DTYPE, "k_scale must be NULL unless k_dt is CSA_FP8_E4M3");
   REQUIRE(B >= 1 && B <= 65535, CSA_E_SHAPE, "B=%d out of range [1, 65535]", B);
   REQUIRE(T >= 0, CSA_E_SHAPE, "T < 0");
@@ -274,8 +276,8 @@ static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const v
   REQUIRE(kv_dt == dt || (kv8 && dt == CSA_BF16), CSA_E_DTYPE,
           "kv_dt must equal dt, or be CSA_FP8_E4M3 with dt == CSA_BF16");
   if (kv8) {
-    REQUIRE_PTR(k_scale);
-    REQUIRE_PTR(v_scale);
+    REQUIRE_PTR_IF(k_scale, N_alloc > 0);
+    REQUIRE_PTR_IF(v_scale, N_alloc > 0);
     REQUIRE(aligned16(k_scale) && aligned16(v_scale), CSA_E_ALIGN, "k_scale / v_scale are not 16-byte aligned");
   } else {
     REQUIRE(k_scale == nullptr && v_scale == nullptr, CSA_E_DTYPE,
@@ -283,7 +285,7 @@ static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const v
   }
   if (!hca) {
     REQUIRE(top_k >= 0 && top_k <= 2048, CSA_E_SHAPE, "top_k=%d out of range [0, 2048]", top_k);
-    REQUIRE(top_k == 0 || idx != nullptr, CSA_E_NULL, "idx is NULL");
+    REQUIRE(top_k == 0 || T == 0 || idx != nullptr, CSA_E_NULL, "idx is NULL");
     REQUIRE(idx == nullptr || aligned16(idx), CSA_E_ALIGN, "idx is not 16-byte aligned");
   }
   const csa::AttendPlan p =

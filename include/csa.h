@@ -23,7 +23,8 @@
  * Conventions for every call
  *   - Tensor arguments are DEVICE pointers to row-major arrays whose innermost
  *     dimension is contiguous, with the shapes given below; base addresses must
- *     be 16-byte aligned.  Sizes are element counts.
+ *     be 16-byte aligned.  Sizes are element counts.  A pointer to an array
+ *     with no elements (T = 0, N_alloc = 0, T_new = 0, ...) may be NULL.
  *   - B sequences in a call share the context length and query positions.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL means the null
  *     stream) and is asynchronous: a call never synchronises and never allocates

@@ -193,6 +193,17 @@ def test_attend_validation(L, hca):
     assert attend(L, hca, ws=None, **big) == E_WS
 
 
+def test_null_pointers_are_allowed_for_empty_arrays(L):
+    """Arrays with no elements may be NULL; such calls succeed and enqueue nothing
+    (no GPU is touched here)."""
+    assert attend(L, False, q=None, out=None, idx=None, T=0) == OK
+    assert attend(L, True, q=None, out=None, T=0) == OK
+    assert index(L, q=None, out=None, T=0) == OK
+    assert compress(L, x=None, n_raw=0, eb=0, ee=0) == OK
+    assert append(L, x=None, T_new=0) == OK
+    assert attend(L, True, q=None) == E_NULL          # but not when the array has elements
+
+
 def test_last_error_is_thread_local_and_descriptive(L):
     msgs = {}
 

@@ -447,6 +447,9 @@ ATTEND_CASES = [
     ("hca-prefill-multi-h32-nowin", "bf16", 1, 300, 32, 128, 20, 128, 0, 0, 2000, "f32"),
     ("hca-prefill-multi-empty-rows", "bf16", 1, 300, 64, 128, 8, 128, 0, 0, 0, "f32"),
     ("hca-prefill-multi-w1", "bf16", 1, 290, 48, 128, 16, 128, 0, 1, 1000, "f32"),
+    # the limits: top_k 2048 and a 1024-token window
+    ("csa-max-k-window", "bf16", 1, 1, 64, 128, 4000, 4, 2048, 1024, 4 * 4000 - 1, "f32"),
+    ("hca-prefill-multi-w1024", "bf16", 1, 260, 64, 128, 40, 128, 0, 1024, 4000, "f32"),
 ]
 
 
@@ -529,6 +532,55 @@ def test_attend_with_fp8_compressed_caches(case):
             o_ref, l_ref = method.csa_attend(f64(q[b]), kv64[b], vv64[b], idx[b], f64(kr[b]), f64(vr[b]), 0,
                                              t0, W, m, scale)
         check_attention(f64(out[b]), f64(lse[b]), o_ref, l_ref, "bf16", what=f"fp8 kv {name} b={b}")
+
+
+def test_empty_calls_enqueue_nothing():
+    """T = 0 queries, an empty entry range and T_new = 0 rows succeed and leave
+    every output untouched.  (Zero-length views keep a valid base pointer.)"""
+    say("empty calls")
+    B, H, d, N = 2, 64, 128, 64
+    empty = lambda shape, dt: torch.zeros((shape[0], 1) + tuple(shape[2:]), dtype=dt, device=DEV)[:, :0]
+    q = empty((B, 0, H, d), torch.bfloat16)
+    kc = torch.zeros((B, N, d), dtype=torch.bfloat16, device=DEV)
+    raw = torch.zeros((B, 300, d), dtype=torch.bfloat16, device=DEV)
+    out = empty((B, 0, H, d), torch.float32)
+    csa.hca_attend(q, kc, kc, 4, raw, raw, 10, 128, 0.1, out)
+    csa.csa_attend(q, kc, kc, 4, empty((B, 0, 8), torch.int32), raw, raw, 10, 128, 0.1, out)
+    csa.csa_index_topk(empty((B, 0, 8, 64), torch.bfloat16), None,
+                       torch.zeros((B, N, 64), dtype=torch.bfloat16, device=DEV), None, 10, 4, 8,
+                       empty((B, 0, 8), torch.int32))
+    cache = torch.full((B, N, d), 7.0, device=DEV)
+    z = torch.zeros(4, device=DEV)
+    csa.csa_compress(raw.float(), z, 4, cache, entry_begin=5, entry_end=5)
+    ring = torch.full((B, 2 * 8, d), 3.0, device=DEV)
+    csa.csa_append(empty((B, 0, d), torch.float32), ring, 17, z, 4, cache)
+    torch.cuda.synchronize()
+    assert (cache == 7.0).all() and (ring == 3.0).all()
+
+
+def test_append_of_the_largest_chunk():
+    """4096 rows in one call (the limit): ring and compressed entries as from the
+    full history, with the blocks before the chunk completed by an earlier call."""
+    B, d, m, R = 2, 64, 4, 4096 + 4 - 1 + 5
+    say("append max chunk", R)
+    n = 4096 + 6
+    hist = gen("app_big", (B, n, d), "bf16", seed=5)
+    z = gen("app_big_z", (m,), "f32", seed=6, std=0.5).to(DEV)
+    out = torch.full((B, n // m + 1, d), 7.0, dtype=torch.bfloat16, device=DEV)
+    ring = torch.zeros((B, 2 * R, d), dtype=torch.bfloat16, device=DEV)
+    hd = hist.to(DEV)
+    csa.csa_append(hd[:, :6].contiguous(), ring, 0, z, m, out)
+    csa.csa_append(hd[:, 6:].contiguous(), ring, 6, z, m, out)
+    torch.cuda.synchronize()
+    z64 = f64(z)
+    for b in range(B):
+        exp_ring = method.state_ring(f64(hist[b]), n - 1, R)
+        held = ~np.isnan(exp_ring).any(axis=1)
+        np.testing.assert_array_equal(f64(ring[b])[held], exp_ring[held])
+        sums = method.compress_exact(f64(hist[b]), z64, m, 0, n // m)
+        diff = ulp_diff_bf16(bf16_bits(out[b, :n // m]), formats.f64_to_bf16_bits(sums))
+        assert diff.max() <= 1
+        assert (f64(out[b, n // m:]) == 7.0).all()
 
 
 def test_attend_is_deterministic_and_consistent_across_splits():
