@@ -510,8 +510,9 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 10}))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the path shards by sequence or by entry range, see DESIGN.md).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path would "
+              "shard by sequence or by compressed-entry range, with no multi-GPU code here).",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

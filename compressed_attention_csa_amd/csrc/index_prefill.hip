@@ -23,19 +23,21 @@
 //
 // Exact top-k.  Each query keeps a candidate buffer in the workspace and a
 // threshold tau (a 64-bit rank key: score, then lower index first).  A binary32
-// compare against tau's score screens every pair; pairs that pass it are
-// appended as (score, entry) with wave ballots, in entry order, to a small LDS
-// staging area (so the scoring loop issues no global stores, whose pending
-// completion would otherwise make every wait also drain the key prefetch).
-// Rank keys are formed, and tested exactly against tau, when a staging area
-// is drained.  A
-// staging area that cannot take another tile is drained to the buffer between
-// tiles.  When the buffer cannot take it, a histogram pass over the keys
+// compare against tau's score screens every pair; the pairs that pass it are
+// appended as (score, entry | query << 30), in entry order, to one LDS staging
+// area per wave shared by its 4 queries: the compare is the write mask and the
+// slot is the running count plus the lane's rank in the mask (so the scoring
+// loop issues no global stores, whose pending completion would otherwise make
+// every wait also drain the key prefetch).  Rank keys are formed, and tested
+// exactly against their query's tau, when the staging area is drained to the
+// query buffers, between tiles once it cannot take another tile.  When a
+// buffer cannot take its query's staged pairs, a histogram pass over the keys
 // relative to tau (bins spanning tau .. the largest key appended) and, if
 // needed, finer radix passes raise tau to a bin edge that keeps between k and
-// 5k/4 candidates, and the buffer is compacted in order.  Everything dropped ranks below at least k
-// candidates already kept, so the final exact selection over the buffer is the
-// exact top-k; the output lists the winners by increasing entry index.
+// 5k/4 candidates, and the buffer is compacted in order.  Everything dropped
+// ranks below at least k candidates already kept, so the final exact selection
+// over the buffer is the exact top-k; the output lists the winners by
+// increasing entry index.
 #include <type_traits>
 
 #include "common.hpp"
@@ -50,13 +52,14 @@ constexpr int kTileE = 128;  // entries per LDS tile
 constexpr int kHBits = 9;    // histogram digit
 constexpr int kHBins = 1 << kHBits;
 constexpr int kBatch = 8;    // buffer keys per lane per batch of loads
-constexpr int kStage = 384;  // LDS staging slots per query
+constexpr int kStage = 384 * kPrefillQPW;  // LDS staging slots per wave
+constexpr uint32_t kTagShift = 30;          // staged entry: index | query << 30
 
 struct LdsPrefill {
   uint4 tile[2][kTileE * 8];  // up to 128 B per entry, two buffers
   float scale[2][kTileE];
   uint32_t hist[kWaves][kHBins];
-  uint64_t stg[kWaves][kPrefillQPW][kStage];  // appended keys not yet in the workspace
+  uint64_t stg[kWaves][kStage];  // appended (score, entry) pairs not yet in the workspace
 };
 
 // LDS position (in 16-byte chunks) of chunk c of entry e, for cpe = 4 or 8
@@ -265,10 +268,13 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   for (int h = 0; h < 8; ++h)
     wv[h] = (qvalid && h < H_I) ? (a.w ? a.w[(rowbase + iq) * H_I + h] : 1.0f) : 0.0f;
   uint64_t tau = 0ull;             // every key appended from now on is > tau
-  float tau_s = key_score(0u);     // screening score of tau (NaN: admits everything)
+  bool active = qvalid;            // this lane's query takes part in the current pass
+  // Screening score of tau: NaN admits everything, +inf (a lane whose query
+  // takes no part in the current pass) all but NaN scores, which the drain drops.
+  float tau_s = qvalid ? key_score(0u) : INFINITY;
   uint32_t top_hi = 0u;            // largest upper key half in the query's buffer
   int cnt = 0;                     // keys in the query's workspace buffer
-  int scnt = 0;                    // keys staged in LDS for the query
+  int scnt = 0;                    // pairs staged in LDS by the wave (all its queries)
 
   // Entries visible to the last query of this workgroup bound the sweep.
   const int64_t ilast = (i0 + kPrefillQPB < a.T ? i0 + kPrefillQPB : a.T) - 1;
@@ -278,8 +284,8 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   const int ntiles = (cmax + kTileE - 1) / kTileE;
   uint64_t* bufs = reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(a.ws) + p.off_cand);
   const int cap = int(p.cap);
-  uint64_t* mystg = L.stg[wid][g];
-  const uint32_t below_g = uint32_t(below >> (16 * g));  // lanes of this group before this one
+  uint64_t* const stg = L.stg[wid];
+  const uint32_t coltag = uint32_t(col) | (uint32_t(g) << kTagShift);  // staged entry, less e0 + 16 gi
 
   const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(a.k_idx) + b * a.N_alloc * int64_t(DI * KB);
   // Tile prefetch registers (at most two 16-byte chunks per thread).  Every
@@ -348,50 +354,85 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   // keeps at least (k, or r in the sampling pass).
   int cap_pass = cap;
   int target_l = need_l;
-  // Moves the keys staged for query q of this wave into its workspace buffer.
-  // When they would not fit, the buffer is first compacted: tau rises to a bin
-  // edge that keeps between k and 5k/4 of its keys, and staged keys that do not
-  // exceed the new tau are dropped as well.
-  auto drain = [&](int q) {
-    const int ns = __builtin_amdgcn_readlane(scnt, 16 * q);
-    int n = __builtin_amdgcn_readlane(cnt, 16 * q);
-    uint64_t tq = shfl64(tau, 16 * q);
-    uint64_t* buf = bufs + (rowbase + qw0 + q) * cap;
-    if (n + ns > cap_pass) {  // then n > cap_pass - kStage >= 5/4 of the target
-      wait_mem();  // earlier drains of this wave have reached the buffer
-      const uint32_t tp = __builtin_amdgcn_readlane(top_hi, 16 * q);
-      const int need = __shfl(target_l, 16 * q);
-      int kept;
-      const uint64_t T = wave_threshold(buf, n, need, false, need + need / 4, tq, tp, L.hist[wid], kept);
-      n = wave_compact(buf, n, T);
-      tq = T > tq ? T : tq;
-    }
-    // Staged entries are (score bits, entry) pairs; their rank keys are formed
-    // here, and only keys above the (possibly raised) threshold are kept.
-    const uint64_t* st = L.stg[wid][q];
-    uint32_t km = 0u;
+  // Moves every pair staged by this wave into the workspace buffer of its
+  // query.  A buffer that cannot take its query's staged pairs is first
+  // compacted: tau rises to a bin edge that keeps between k and 5k/4 of its
+  // keys, and staged pairs that do not exceed the new tau are dropped as well.
+  auto drain = [&]() {
+    const int ns = scnt;
+    // Pairs staged per query (held by the lanes of the query's group).
+    int my_ns = 0;
     for (int x0 = 0; x0 < ns; x0 += kWave) {
       const int x = x0 + lane;
-      const uint64_t sv = x < ns ? st[x] : 0ull;
-      const uint64_t v = rank_key(score_key(__uint_as_float(uint32_t(sv >> 32))), uint32_t(sv));
-      const bool keep = x < ns && v > tq;
-      const uint64_t m = __ballot(keep);
-      if (keep) {
-        buf[n + __popcll(m & below)] = v;
-        km = max(km, uint32_t(v >> 32));
-      }
-      n += __popcll(m);
-    }
-    km = wave_max_u32(km);
-    if (g == q) {
-      cnt = n;
-      scnt = 0;
-      top_hi = max(top_hi, km);
-      if (tq > tau) {
-        tau = tq;
-        tau_s = key_score(uint32_t(tq >> 32));
+      const uint32_t tag = x < ns ? uint32_t(stg[x]) >> kTagShift : 4u;
+#pragma unroll
+      for (int q = 0; q < kPrefillQPW; ++q) {
+        const int c = __popcll(__ballot(tag == uint32_t(q)));
+        if (g == q) my_ns += c;
       }
     }
+#pragma unroll 1
+    for (int q = 0; q < kPrefillQPW; ++q) {
+      const int n = __builtin_amdgcn_readlane(cnt, 16 * q);
+      const int need = __builtin_amdgcn_readlane(target_l, 16 * q);
+      // A buffer of at most 5/4 of the target takes a full staging area
+      // without compaction (the capacity is at least 5/4 of any target plus
+      // kStage), so it is compacted only above that.
+      if (n + __builtin_amdgcn_readlane(my_ns, 16 * q) > cap_pass && n > need + need / 4) {
+        wait_mem();  // earlier drains of this wave have reached the buffer
+        uint64_t* buf = bufs + (rowbase + qw0 + q) * cap;
+        const uint64_t tq = shfl64(tau, 16 * q);
+        const uint32_t tp = __builtin_amdgcn_readlane(top_hi, 16 * q);
+        int kept;
+        const uint64_t T = wave_threshold(buf, n, need, false, need + need / 4, tq, tp, L.hist[wid], kept);
+        const int n2 = wave_compact(buf, n, T);
+        if (g == q) {
+          cnt = n2;
+          if (T > tau) {
+            tau = T;
+            tau_s = key_score(uint32_t(T >> 32));
+          }
+        }
+      }
+    }
+    // Rank keys are formed here, and only keys above their query's (possibly
+    // raised) tau are kept.
+    int nq[kPrefillQPW];
+    uint32_t kmq[kPrefillQPW];
+#pragma unroll
+    for (int q = 0; q < kPrefillQPW; ++q) {
+      nq[q] = __builtin_amdgcn_readlane(cnt, 16 * q);
+      kmq[q] = 0u;
+    }
+    for (int x0 = 0; x0 < ns; x0 += kWave) {
+      const int x = x0 + lane;
+      const uint64_t sv = x < ns ? stg[x] : 0ull;
+      const uint32_t tag = uint32_t(sv) >> kTagShift;
+      const uint64_t tq = shfl64(tau, 16 * int(tag));
+      const bool act = __shfl(int(active), 16 * int(tag)) != 0;  // NaN scores of inactive queries
+      const uint64_t v = rank_key(score_key(__uint_as_float(uint32_t(sv >> 32))),
+                                  uint32_t(sv) & ((1u << kTagShift) - 1u));
+      const bool keep = x < ns && act && v > tq;
+      int pos = 0;
+#pragma unroll
+      for (int q = 0; q < kPrefillQPW; ++q) {
+        const bool mine = tag == uint32_t(q);
+        const uint64_t bq = __ballot(keep && mine);
+        if (mine) pos = nq[q] + __popcll(bq & below);
+        if (keep && mine) kmq[q] = max(kmq[q], uint32_t(v >> 32));
+        nq[q] += __popcll(bq);
+      }
+      if (keep) bufs[(rowbase + qw0 + int(tag)) * cap + pos] = v;
+    }
+#pragma unroll
+    for (int q = 0; q < kPrefillQPW; ++q) {
+      const uint32_t km = wave_max_u32(kmq[q]);
+      if (g == q) {
+        cnt = nq[q];
+        top_hi = max(top_hi, km);
+      }
+    }
+    scnt = 0;
     __builtin_amdgcn_wave_barrier();
   };
 
@@ -417,7 +458,6 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     while (sq * sq < lam) ++sq;
     r_l = lam + 6 * sq + 8;
   }
-  bool active = qvalid;  // this lane's query takes part in the current pass
   bool pruned = false; // this lane's query started the full sweep above zero
 #pragma unroll 1
   for (int pass = sampling ? 0 : 1; pass < 3; ++pass) {
@@ -425,6 +465,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
       const bool redo = qvalid && pruned && cnt < need_l;
       if (!__syncthreads_or(redo)) break;
       active = redo;
+      tau_s = INFINITY;
       if (redo) {
         tau = 0ull;
         tau_s = key_score(0u);
@@ -443,7 +484,6 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     // (its first query sees the fewest entries).
     const int64_t cfirst64 = (a.t0 + i0 + 1) / a.m < a.N_alloc ? (a.t0 + i0 + 1) / a.m : a.N_alloc;
     const int cfull = pass == 0 ? (int(cfirst64) + ss - 1) / ss : int(cfirst64);
-    const uint64_t act_mask = __ballot(active);
     if (ntp > 0) {
       fetch(0);
       stage(0);
@@ -483,15 +523,19 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
           if (KK == kKeyE4M3) s *= L.scale[cur][e];
           // The screen admits every entry whose rank key can exceed tau (and a
           // few equal-score ones that cannot); the exact test runs when staged
-          // entries are drained.  Ballots of the compares themselves: each is
-          // one compare into a lane mask.
-          uint64_t m = __ballot(!(s < tau_s)) & act_mask;
-          if (!FULL) m &= __ballot(16 * gi < lim);
+          // entries are drained.  The passing lanes write their pairs to
+          // consecutive staging slots in lane order.  (In full tiles the
+          // compare alone is the write mask.)
+          bool pass = !(s < tau_s);
+          if (!FULL) pass = pass && 16 * gi < lim;
+          const uint64_t m = __ballot(pass);
           if (m) {
-            const uint32_t mg = uint32_t(m >> (16 * g)) & 0xffffu;
-            if ((m >> lane) & 1ull)
-              mystg[scnt + __popc(mg & below_g)] = (uint64_t(__float_as_uint(s)) << 32) | uint32_t(e0 + e);
-            scnt += __popc(mg);
+            if (pass) {
+              const uint32_t pos = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo(uint32_t(m), uint32_t(scnt)));
+              stg[pos] = (uint64_t(__float_as_uint(s)) << 32) | (uint32_t(e0 + 16 * gi) + coltag);
+            }
+            scnt += __popcll(m);
           }
           if (gi + 1 < GROUPS) {
             acc[0] = nxt[0];
@@ -501,15 +545,11 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
       };
       if (e0 + kTileE <= cfull) groups(std::integral_constant<bool, true>());
       else groups(std::integral_constant<bool, false>());
-      // Staging areas that cannot take another tile are drained.
-  #pragma unroll 1
-      for (int q = 0; q < kPrefillQPW; ++q)
-        if (__builtin_amdgcn_readlane(scnt, 16 * q) > kStage - kTileE) drain(q);
+      // The staging area is drained when it cannot take another tile.
+      if (scnt > kStage - kTileE * kPrefillQPW) drain();
       __syncthreads();
     }
-  #pragma unroll 1
-    for (int q = 0; q < kPrefillQPW; ++q)
-      if (__builtin_amdgcn_readlane(scnt, 16 * q) > 0) drain(q);
+    if (scnt > 0) drain();
     if (pass == 0) {
       // Starting threshold of each query: the r-th best sampled rank key with
       // its index half cleared (so every entry with that score passes).
@@ -532,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
         if (g == q) t0k = T;
       }
       tau = t0k;
-      tau_s = key_score(uint32_t(t0k >> 32));  // t0k = 0: NaN, admits everything
+      tau_s = active ? key_score(uint32_t(t0k >> 32)) : INFINITY;  // t0k = 0: NaN, admits everything
       pruned = t0k != 0ull;
       cnt = 0;
       scnt = 0;

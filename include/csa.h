@@ -72,7 +72,7 @@ typedef enum {
   CSA_E_DTYPE = 3,       /* unsupported dtype or dtype combination */
   CSA_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   CSA_E_WORKSPACE = 5,   /* workspace NULL or smaller than *_workspace() */
-  CSA_E_UNSUPPORTED = 6, /* valid request this build does not implement */
+  CSA_E_UNSUPPORTED = 6, /* valid request the library does not implement */
   CSA_E_HIP = 7          /* a HIP runtime call failed */
 } csa_status_t;
 
