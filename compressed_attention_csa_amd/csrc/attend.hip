@@ -618,12 +618,24 @@ struct LdsM {
   static constexpr int VS = D / 8 + 2;  // V row stride in chunks
   uint4 k[2][kTB * KS];
   uint4 v[2][kTB * VS];
-  float ksc[2][kTB];  // fp8 caches: per-slot score factor (K scale * scale * log2 e)
-  float vsc[2][kTB];  // fp8 caches: per-slot V scale
+  uint4 vh[2][kTB * VS];  // bf16 caches: the V tile as binary16
+  alignas(8) uint8_t vflag[2][8];  // per wave, staged |V|: bit 0, one != 0; bit 1, one >= 2^-10; bit 2, one > 65280
+  float ksc[2][kTB];      // fp8 caches: per-slot score factor (K scale * scale * log2 e)
+  float vsc[2][kTB];      // fp8 caches: per-slot V scale
 };
 
 // KV8 as in attend_bf16_kernel: heavy tiles hold e4m3 codes (widened when
 // staged) with per-entry K and V scales; window tiles are bf16.
+//
+// Binary16 weights (bf16 caches).  Every bf16 value of magnitude 0 or in
+// [2^-14, 65280] is a binary16 value, so a V tile in that range is staged a
+// second time as binary16, exactly.  Such a tile enters O^T += V^T P^T with P
+// rounded once to binary16 (11 significant bits, relative error at most
+// 2^-11 per weight): one product per operand pair instead of the bf16 hi + lo
+// pair.  A tile whose largest |V| exceeds 65280 (it would overflow), or is
+// nonzero and below 2^-10 (so that values losing bits as binary16 subnormals,
+// by at most 2^-25 each, could matter next to the output), ends the binary16
+// run: it and every later tile of the workgroup take the hi + lo path.
 template <int D, int NW, int RB, bool KV8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1))) void hca_multi_kernel(AttendArgs a, int64_t groups_per_seq) {
   constexpr int kT = NW * 64;
@@ -632,6 +644,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
   constexpr int CPT = CT >= kT ? CT / kT : 1;
   constexpr int KS = D / 32;
   constexpr int DVT = D / 16;
+  constexpr bool F16 = !KV8;  // binary16 path available
+  static_assert(NW <= 8, "one V range flag per wave");
   __shared__ LdsM<D> L;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, col = lane & 15;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -742,7 +756,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
       P.vs = 1.0f;
     }
   };
-  auto stage = [&](const Pre& P, int buf) __attribute__((always_inline)) {
+  typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+  auto stage = [&](const Pre& P, int buf, auto w16_c) __attribute__((always_inline)) {
+    constexpr bool W16 = F16 && decltype(w16_c)::value;
+    u16x2_t vmax = {0, 0};  // largest |V| bit patterns of the staged chunks
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int id = tid + c * kT, sl = (id % CT) / CPR, ch = id % CPR;
@@ -757,7 +774,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
         }
         L.k[buf][sl * LdsM<D>::KS + ch] = kw;
         L.v[buf][sl * LdsM<D>::VS + ch] = vw;
+        if (W16) {
+          L.vh[buf][sl * LdsM<D>::VS + ch] = make_uint4(bf16x2_to_f16x2(vw.x), bf16x2_to_f16x2(vw.y),
+                                                        bf16x2_to_f16x2(vw.z), bf16x2_to_f16x2(vw.w));
+          auto mag = [](uint32_t w) {
+            const uint32_t m = w & 0x7fff7fffu;
+            u16x2_t r;
+            __builtin_memcpy(&r, &m, 4);
+            return r;
+          };
+          vmax = __builtin_elementwise_max(vmax, __builtin_elementwise_max(mag(vw.x), mag(vw.y)));
+          vmax = __builtin_elementwise_max(vmax, __builtin_elementwise_max(mag(vw.z), mag(vw.w)));
+        }
       }
+    }
+    if (W16) {
+      const uint32_t mx = vmax[0] > vmax[1] ? vmax[0] : vmax[1];
+      const bool big = __ballot(mx >= 0x3A80u) != 0;  // 2^-10
+      const bool ovf = __ballot(mx > 0x477Fu) != 0;   // 65280
+      const bool nz = __ballot(mx != 0u) != 0;
+      if (lane == 0) L.vflag[buf][wid] = uint8_t((ovf ? 4u : 0u) | (big ? 2u : 0u) | (nz ? 1u : 0u));
     }
     if (KV8 && tid < kTB) {
       L.ksc[buf][tid] = P.ks * sl2;
@@ -780,23 +816,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
     lpart[rb] = 0.0f;
   }
 
-  auto vfrag = [&](int buf, int v) __attribute__((always_inline)) {
+  // V^T operand v of a 16-bit V tile (bf16 or binary16 bits).
+  auto vfrag_bits = [&](const uint4* vt, int v) __attribute__((always_inline)) {
     const int vr0 = 4 * g + col / 4, half = col & 1;
     const int ch = 2 * v + (col & 3) / 2;
-    const short* b0 = reinterpret_cast<const short*>(&L.v[buf][vr0 * LdsM<D>::VS + ch]) + 4 * half;
-    const short* b1 = reinterpret_cast<const short*>(&L.v[buf][(vr0 + 16) * LdsM<D>::VS + ch]) + 4 * half;
+    const short* b0 = reinterpret_cast<const short*>(&vt[vr0 * LdsM<D>::VS + ch]) + 4 * half;
+    const short* b1 = reinterpret_cast<const short*>(&vt[(vr0 + 16) * LdsM<D>::VS + ch]) + 4 * half;
     const v4s_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b0));
     const v4s_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(b1));
     uint4 w;
     __builtin_memcpy(&w.x, &t0, 8);
     __builtin_memcpy(&w.z, &t1, 8);
-    return u32x4_as_bf16x8(w);
+    return w;
   };
   // Per tile: S^T = K Q^T, the weights, then O^T += V^T P^T.  Each K and
   // each V operand read from LDS serves every row block of the wave.
   float u[RB][2][4];        // score - reference (log2 units), -inf if not visible
   uint32_t vmask[RB];       // visibility bits of a masked tile (bit 4 cg + j: slot 16 cg + 4 g + j)
   bf16x8_t ph[RB], pl[RB];  // weights as bf16 hi + lo
+  f16x8_t pw[RB];           // weights as binary16
   // S^T = K Q^T of the tile in buffer buf; the 2 RB accumulators are
   // independent, so consecutive MFMAs never wait for each other.
   auto qk = [&](int buf, f32x4_t (&sc)[RB][2]) __attribute__((always_inline)) {
@@ -921,6 +959,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
       pl[rb] = u32x4_as_bf16x8(make_uint4(wlo[0], wlo[1], wlo[2], wlo[3]));
     }
   };
+  // Weights 2^u as binary16 (one round-to-nearest conversion per pair) and
+  // their sums, for tiles staged as binary16.
+  auto weights16 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x2_t ps = {0.0f, 0.0f};
+      uint32_t w[4];
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+          const f32x2_t pp = {__builtin_amdgcn_exp2f(u[rb][cg][j]), __builtin_amdgcn_exp2f(u[rb][cg][j + 1])};
+          ps = (cg == 0 && j == 0) ? pp : ps + pp;
+          w[cg * 2 + j / 2] = f16x2_bits(pp);
+        }
+      lpart[rb] += ps[0] + ps[1];
+      pw[rb] = u32x4_as_f16x8(make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  };
+  auto products16 = [&](const f16x8_t (&va)[DVT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int v = 0; v < DVT; ++v) o[rb][v] = mfma16x16x32_f16(va[v], pw[rb], o[rb][v]);
+  };
   // O^T += V^T P^T (V^T operands va): every hi product, then every lo
   // product, so that the two updates of one accumulator are RB * DVT MFMAs
   // apart.
@@ -945,21 +1008,89 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
   const int nfull = int((cf < a.N_alloc ? cf : a.N_alloc) / kTB);
   Pre P;
   fetch(P, 0);
-  auto tile = [&](int t, auto full_c) __attribute__((always_inline)) {
+  // Stages tile t (with W16, V also as binary16 and its range flags) and
+  // starts loading tile t + 1.
+  auto head = [&](int t, auto w16_c) __attribute__((always_inline)) {
     const int buf = t & 1;
-    stage(P, buf);
+    stage(P, buf, w16_c);
     __syncthreads();
     fetch(P, t + 1);
-    bf16x8_t va[DVT];  // V^T operands, read early
-#pragma unroll
-    for (int v = 0; v < DVT; ++v) va[v] = vfrag(buf, v);
-    if (__builtin_expect(scores(buf, t, full_c), 0)) rescale(buf, decltype(full_c)::value);
-    weights(buf);
-    products(va);
   };
+  // Whether a staged tile, whose range flags (one byte per wave) are fl, may
+  // take the binary16 path.
+  auto in_range = [&](uint2 fl) __attribute__((always_inline)) {
+    uint32_t f = fl.x | fl.y;
+    f |= f >> 16;
+    f = (f | (f >> 8)) & 0xffu;
+    // In range: no |V| above 65280, and either some |V| >= 2^-10 or all zero
+    // (the flags of the waves or to 0 or 3).  One bit test: a compare pair
+    // here changes the register allocation of the loops enough to spill.
+    f = __builtin_amdgcn_readfirstlane(f);
+    return ((9u >> f) & 1u) != 0u;  // f = 0 or 3
+  };
+  // The math of staged tile t, on the binary16 or the bf16 hi + lo path.
+  // The binary16 path tests the range only once the scores are formed (so
+  // that the flag reads overlap the products) and returns false, before any
+  // weight is added, for a tile outside it; the caller then does the tile
+  // again on the bf16 path (a repeated score pass finds the reference already
+  // moved and changes nothing).
+  auto body = [&](int t, auto full_c, auto w16_c) __attribute__((always_inline)) {
+    constexpr bool W16 = decltype(w16_c)::value;
+    const int buf = t & 1;
+    uint2 fl = make_uint2(0u, 0u);  // range flags, read first: used after the scores
+    if (W16) fl = *reinterpret_cast<const uint2*>(L.vflag[buf]);
+    uint4 vbits[DVT];  // V^T operands, read early
+#pragma unroll
+    for (int v = 0; v < DVT; ++v) vbits[v] = vfrag_bits(W16 ? L.vh[buf] : L.v[buf], v);
+    if (__builtin_expect(scores(buf, t, full_c), 0)) rescale(buf, decltype(full_c)::value);
+    if (W16 && !in_range(fl)) return false;
+    if (W16) {
+      f16x8_t va[DVT];
+#pragma unroll
+      for (int v = 0; v < DVT; ++v) va[v] = u32x4_as_f16x8(vbits[v]);
+      weights16();
+      products16(va);
+    } else {
+      bf16x8_t va[DVT];
+#pragma unroll
+      for (int v = 0; v < DVT; ++v) va[v] = u32x4_as_bf16x8(vbits[v]);
+      weights(buf);
+      products(va);
+    }
+    return true;
+  };
+  // Binary16 tiles first; the first tile outside the binary16 range (already
+  // staged) and every later one take the bf16 loops.  Each loop has one path,
+  // which keeps the register allocation of either (a per-tile choice inside
+  // one loop spills).
   int t = 0;
-  for (; t < nfull; ++t) tile(t, std::true_type{});
-  for (; t < nt; ++t) tile(t, std::false_type{});
+  bool staged = false;  // tile t is staged and its successor is loading
+  if (F16) {
+    for (; t < nfull && !staged; ++t) {
+      head(t, std::true_type{});
+      if (!body(t, std::true_type{}, std::true_type{})) {
+        staged = true;
+        break;
+      }
+    }
+    for (; t < nt && !staged; ++t) {
+      head(t, std::true_type{});
+      if (!body(t, std::false_type{}, std::true_type{})) {
+        staged = true;
+        break;
+      }
+    }
+  }
+  for (; t < nfull; ++t) {
+    if (!staged) head(t, std::false_type{});
+    staged = false;
+    body(t, std::true_type{}, std::false_type{});
+  }
+  for (; t < nt; ++t) {
+    if (!staged) head(t, std::false_type{});
+    staged = false;
+    body(t, std::false_type{}, std::false_type{});
+  }
 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {

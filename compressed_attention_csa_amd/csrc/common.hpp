@@ -59,6 +59,22 @@ __device__ __forceinline__ uint32_t bf16x2_bits(f32x2_t v) {
   return u;
 }
 
+// Two binary32 values to packed IEEE binary16 bits (element 0 in the low
+// half), round to nearest even; magnitudes past the binary16 range give inf.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f16x2_bits(f32x2_t v) {
+  const f16x2_t h = __builtin_convertvector(v, f16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
+// Two packed bf16 values to packed binary16: exact when both magnitudes are 0
+// or lie in [2^-14, 65280] (the binary16 normal range holds every bf16 there).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const f32x2_t f = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  return f16x2_bits(f);
+}
+
 // ---------------------------------------------------------------- fp8 e4m3fn
 
 // Encode a binary32 as e4m3fn, nearest-even.  Magnitudes up to 464 round to at
@@ -125,6 +141,17 @@ __device__ __forceinline__ uint32_t rank_key_idx(uint64_t rk) {
 // 8*(l/16) .. 8*(l/16)+7; C/D lane l holds column l%16, rows 4*(l/16) .. +3.
 __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+// The same product with binary16 operands.
+__device__ __forceinline__ f32x4_t mfma16x16x32_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8_t u32x4_as_f16x8(uint4 v) {
+  f16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
 }
 
 template <typename T>

@@ -487,6 +487,73 @@ def test_attend(case):
                         out_bf16=(out_dt == "bf16"))
 
 
+def test_hca_prefill_many_tiny_weights():
+    """HCA prefill (multi-token kernel) where one entry dominates and thousands
+    of others carry weights 2^-15 .. 2^-23 of it, all with the same V row: their
+    sum moves the output by several percent, so weights lost in rounding (the
+    binary16 weights of bf16 tiles fall below the binary16 normal range here)
+    would show.  Scores follow from one nonzero coordinate: q = (8, 0, ...),
+    k_j = (c_j, 0, ...)."""
+    B, T, H, d, m, N, W = 1, 64, 64, 128, 4, 4000, 128
+    t0 = m * N - T - 1
+    say("hca prefill, many tiny weights", (B, T, H, d, m, N, W, t0))
+    n_raw = t0 + T + 3
+    scale = 1.0 / math.sqrt(d)
+    gamma = 8.0
+    rng = np.random.default_rng(5)
+    # natural-log score gaps of -e*ln2 below the dominant entry, e in 15..23
+    gaps = rng.integers(15, 24, size=N).astype(np.float64)
+    c = formats.bf16_bits_to_f64(formats.f64_to_bf16_bits(-gaps * math.log(2) / (gamma * scale)))
+    c[0] = 0.0
+    q = np.zeros((B, T, H, d))
+    q[..., 0] = gamma
+    kc = np.zeros((B, N, d))
+    kc[0, :, 0] = c
+    vc = np.ones((B, N, d))
+    vc[0, 0] = formats.bf16_bits_to_f64(formats.f64_to_bf16_bits(rng.standard_normal(d)))
+    kr = np.zeros((B, n_raw, d))
+    kr[0, :, 0] = c[1 + np.arange(n_raw) % (N - 1)]
+    vr = np.ones((B, n_raw, d))
+    out = torch.full((B, T, H, d), 9.0, device=DEV)
+    lse = torch.full((B, T, H), 9.0, device=DEV)
+    csa.hca_attend(to_dev_bf16(q), to_dev_bf16(kc), to_dev_bf16(vc), m, to_dev_bf16(kr), to_dev_bf16(vr),
+                   t0, W, scale, out, lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = method.hca_attend(q[0], kc[0], vc[0], m, kr[0], vr[0], 0, t0, W, scale)
+    shift = np.abs(o_ref - vc[0, 0]).max()
+    assert shift > 0.02, shift  # the tiny weights matter
+    check_attention(f64(out[0]), f64(lse[0]), o_ref, l_ref, "bf16", what="tiny weights")
+
+
+def test_hca_prefill_v_outside_binary16_range():
+    """HCA prefill with V tiles the binary16 weight path cannot take: in sequence
+    0 the raw V rows of positions 4100..4109 are scaled by 2^17 (|V| past
+    65280), so the workgroups whose windows hold them switch paths part-way
+    through their sweep and the others never do; sequence 1 has every V value
+    scaled by 2^-12 (largest |V| below 2^-4), so it never takes the binary16
+    path."""
+    B, T, H, d, m, N, W, t0 = 2, 301, 64, 128, 128, 40, 128, 4000
+    say("hca prefill, V outside the binary16 range", (B, T, H, d, m, N, W, t0))
+    n_raw = t0 + T + 3
+    q = gen("rng_q", (B, T, H, d), "bf16", seed=11)
+    kc = gen("rng_kc", (B, N, d), "bf16", seed=12, std=0.6)
+    vc = f64(gen("rng_vc", (B, N, d), "bf16", seed=13, std=0.6))
+    kr = gen("rng_kr", (B, n_raw, d), "bf16", seed=14)
+    vr = f64(gen("rng_vr", (B, n_raw, d), "bf16", seed=15))
+    vr[0, 4100:4110] *= 2.0 ** 17
+    vc[1] *= 2.0 ** -12
+    vr[1] *= 2.0 ** -12
+    scale = 1.0 / math.sqrt(d)
+    out = torch.full((B, T, H, d), 9.0, device=DEV)
+    lse = torch.full((B, T, H), 9.0, device=DEV)
+    csa.hca_attend(q.to(DEV), kc.to(DEV), to_dev_bf16(vc), m, kr.to(DEV), to_dev_bf16(vr), t0, W, scale,
+                   out, lse)
+    torch.cuda.synchronize()
+    for b in range(B):
+        o_ref, l_ref = method.hca_attend(f64(q[b]), f64(kc[b]), vc[b], m, f64(kr[b]), vr[b], 0, t0, W, scale)
+        check_attention(f64(out[b]), f64(lse[b]), o_ref, l_ref, "bf16", what=f"v range b={b}")
+
+
 FP8_KV_CASES = [
     # name, B, T, H, d, N, m, k, W, t0
     ("csa-decode", 2, 1, 128, 128, 3000, 4, 1024, 128, 4 * 3000 - 1),
