@@ -45,16 +45,25 @@ namespace csa {
 
 ProfScope::ProfScope(const char* name, hipStream_t s) : name_(name), stream_(s), start_(nullptr) {
   if (!g_prof.on) return;
-  start_ = g_prof.get();
-  if (start_) hipEventRecord(reinterpret_cast<hipEvent_t>(start_), stream_);
+  hipEvent_t e = g_prof.get();
+  if (!e) return;
+  if (hipEventRecord(e, stream_) != hipSuccess) {  // not timed; the event goes back
+    g_prof.pool.push_back(e);
+    return;
+  }
+  start_ = e;
 }
 
 ProfScope::~ProfScope() {
   if (!start_) return;
+  hipEvent_t a = reinterpret_cast<hipEvent_t>(start_);
   hipEvent_t stop = g_prof.get();
-  if (!stop) return;
-  hipEventRecord(stop, stream_);
-  g_prof.recs.push_back(Rec{name_, reinterpret_cast<hipEvent_t>(start_), stop});
+  if (!stop || hipEventRecord(stop, stream_) != hipSuccess) {  // this launch goes untimed
+    g_prof.pool.push_back(a);
+    if (stop) g_prof.pool.push_back(stop);
+    return;
+  }
+  g_prof.recs.push_back(Rec{name_, a, stop});
 }
 
 }  // namespace csa
