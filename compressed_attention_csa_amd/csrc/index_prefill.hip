@@ -499,11 +499,13 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
       // in flight for the whole of this tile.
       if (t + 1 < ntp) stage(cur ^ 1);
       fetch(t + 2 < ntp ? t + 2 : ntp - 1);
-      // All B operands of the tile are read up front, so the LDS latency is paid
-      // once per tile rather than once per group.
+      // B operands are read two groups ahead of their products: each read has
+      // a group's work to land, and the reads of the 8 waves, which leave the
+      // barrier together, spread over the tile instead of queueing at its start.
+      constexpr int LA = 2;
       uint4 bo0[GROUPS], bo1[GROUPS];
   #pragma unroll
-      for (int gi = 0; gi < GROUPS; ++gi) operands(cur, gi, bo0[gi], bo1[gi]);
+      for (int gi = 0; gi < LA; ++gi) operands(cur, gi, bo0[gi], bo1[gi]);
       const int lim = cqv - e0 - col;  // entry 16*gi + col of the tile is visible iff 16*gi < lim
       // The groups of the tile; FULL: every query of the workgroup sees the
       // whole tile, so the visibility test is left out.
@@ -513,6 +515,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
         products(bo0[0], bo1[0], acc);
   #pragma unroll
         for (int gi = 0; gi < GROUPS; ++gi) {
+          if (gi + LA < GROUPS) operands(cur, gi + LA, bo0[gi + LA], bo1[gi + LA]);
           if (gi + 1 < GROUPS) products(bo0[gi + 1], bo1[gi + 1], nxt);
           const int e = gi * 16 + col;
           float s = 0.0f;
