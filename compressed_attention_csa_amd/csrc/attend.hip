@@ -1039,10 +1039,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
     const int buf = t & 1;
     uint2 fl = make_uint2(0u, 0u);  // range flags, read first: used after the scores
     if (W16) fl = *reinterpret_cast<const uint2*>(L.vflag[buf]);
-    uint4 vbits[DVT];  // V^T operands, read early
+    if (__builtin_expect(scores(buf, t, full_c), 0)) rescale(buf, decltype(full_c)::value);
+    // V^T operands, read after the scores (read before them, the reads of the
+    // 8 waves, which leave the barrier together, queue on LDS).
+    uint4 vbits[DVT];
 #pragma unroll
     for (int v = 0; v < DVT; ++v) vbits[v] = vfrag_bits(W16 ? L.vh[buf] : L.v[buf], v);
-    if (__builtin_expect(scores(buf, t, full_c), 0)) rescale(buf, decltype(full_c)::value);
     if (W16 && !in_range(fl)) return false;
     if (W16) {
       f16x8_t va[DVT];
