@@ -487,16 +487,17 @@ def test_attend(case):
                         out_bf16=(out_dt == "bf16"))
 
 
-def test_hca_prefill_many_tiny_weights():
-    """HCA prefill (multi-token kernel) where one entry dominates and thousands
-    of others carry weights 2^-15 .. 2^-23 of it, all with the same V row: their
-    sum moves the output by several percent, so weights lost in rounding (the
-    binary16 weights of bf16 tiles fall below the binary16 normal range here)
-    would show.  Scores follow from one nonzero coordinate: q = (8, 0, ...),
-    k_j = (c_j, 0, ...)."""
-    B, T, H, d, m, N, W = 1, 64, 64, 128, 4, 4000, 128
+@pytest.mark.parametrize("T", [64, 1], ids=["prefill-multi", "decode"])
+def test_hca_many_tiny_weights(T):
+    """HCA prefill (multi-token kernel) and decode where one entry dominates and
+    thousands of others carry weights 2^-15 .. 2^-23 of it, all with the same V
+    row: their sum moves the output by several percent, so weights lost in
+    rounding (the binary16 weights of bf16 tiles fall below the binary16 normal
+    range here) would show.  Scores follow from one nonzero coordinate:
+    q = (8, 0, ...), k_j = (c_j, 0, ...)."""
+    B, H, d, m, N, W = 1, 64, 128, 4, 4000, 128
     t0 = m * N - T - 1
-    say("hca prefill, many tiny weights", (B, T, H, d, m, N, W, t0))
+    say("hca, many tiny weights", (B, T, H, d, m, N, W, t0))
     n_raw = t0 + T + 3
     scale = 1.0 / math.sqrt(d)
     gamma = 8.0
@@ -525,15 +526,19 @@ def test_hca_prefill_many_tiny_weights():
     check_attention(f64(out[0]), f64(lse[0]), o_ref, l_ref, "bf16", what="tiny weights")
 
 
-def test_hca_prefill_v_outside_binary16_range():
-    """HCA prefill with V tiles the binary16 weight path cannot take: in sequence
-    0 the raw V rows of positions 4100..4109 are scaled by 2^17 (|V| past
-    65280), so the workgroups whose windows hold them switch paths part-way
-    through their sweep and the others never do; sequence 1 has every V value
-    scaled by 2^-12 (largest |V| below 2^-4), so it never takes the binary16
-    path."""
-    B, T, H, d, m, N, W, t0 = 2, 301, 64, 128, 128, 40, 128, 4000
-    say("hca prefill, V outside the binary16 range", (B, T, H, d, m, N, W, t0))
+@pytest.mark.parametrize("T", [301, 1], ids=["prefill-multi", "decode"])
+def test_hca_v_outside_binary16_range(T):
+    """HCA prefill (multi-token kernel) and decode with V values the binary16
+    weight path of the multi-token kernel cannot take: in sequence 0 the raw V
+    rows of positions 4100..4109 (and, in decode, the heavy entries 10..12) are
+    scaled by 2^17 (|V| past 65280), so the prefill sweeps that meet them switch
+    paths part-way and the others stay binary16; sequence 1 has every V value
+    scaled by 2^-12 (largest |V| below 2^-10), so it never takes the binary16
+    path.  (Decode uses bf16 hi + lo weights throughout; the cases check it on
+    the same extremes.)"""
+    B, H, d, m, N, W = 2, 64, 128, 128, 40, 128
+    t0 = 4000 if T > 1 else 4105
+    say("hca, V outside the binary16 range", (B, T, H, d, m, N, W, t0))
     n_raw = t0 + T + 3
     q = gen("rng_q", (B, T, H, d), "bf16", seed=11)
     kc = gen("rng_kc", (B, N, d), "bf16", seed=12, std=0.6)
@@ -541,6 +546,8 @@ def test_hca_prefill_v_outside_binary16_range():
     kr = gen("rng_kr", (B, n_raw, d), "bf16", seed=14)
     vr = f64(gen("rng_vr", (B, n_raw, d), "bf16", seed=15))
     vr[0, 4100:4110] *= 2.0 ** 17
+    if T == 1:  # (in prefill this would end every sweep's binary16 run at its first tile)
+        vc[0, 10:13] *= 2.0 ** 17
     vc[1] *= 2.0 ** -12
     vr[1] *= 2.0 ** -12
     scale = 1.0 / math.sqrt(d)
