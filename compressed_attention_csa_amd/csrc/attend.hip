@@ -608,13 +608,14 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
 // the last heavy tile and the window tiles need a per-token visibility test: a
 // range test on the slot's coordinate (entry index or position).
 
-// Rows are padded (K by one 16-byte chunk, V by two) instead of swizzled: the
-// row reads of K by 16 lanes and the transposing reads of V by 32 lanes hit
-// distinct banks, and every read address of a lane is one base plus a
-// constant, so the compiler folds the offsets into the instructions.
+// Rows are padded by two 16-byte chunks instead of swizzled: the LDS counters
+// show no bank conflicts for the row reads of K, the transposing reads of V
+// and the staging writes (a one-chunk K pad conflicted on a quarter of the LDS
+// cycles), and every read address of a lane is one base plus a constant, so
+// the compiler folds the offsets into the instructions.
 template <int D>
 struct LdsM {
-  static constexpr int KS = D / 8 + 1;  // K row stride in chunks
+  static constexpr int KS = D / 8 + 2;  // K row stride in chunks
   static constexpr int VS = D / 8 + 2;  // V row stride in chunks
   uint4 k[2][kTB * KS];
   uint4 v[2][kTB * VS];
