@@ -52,7 +52,7 @@ constexpr int kTileE = 128;  // entries per LDS tile
 constexpr int kHBits = 9;    // histogram digit
 constexpr int kHBins = 1 << kHBits;
 constexpr int kBatch = 8;    // buffer keys per lane per batch of loads
-constexpr int kStage = 384 * kPrefillQPW;  // LDS staging slots per wave
+constexpr int kStage = kPrefillStage;  // LDS staging slots per wave
 constexpr uint32_t kTagShift = 30;          // staged entry: index | query << 30
 
 struct LdsPrefill {
