@@ -51,13 +51,16 @@ class DecodeCSA:
 
     With ``state`` the step first appends the new token's K, V and indexer-key
     rows to the state-cache rings (compressing the block the token completes)
-    and the attention reads its window from the K / V rings."""
+    and the attention reads its window from the K / V rings.  With ``bf16sel``
+    the selection is the approximate one (top-k of bf16-rounded scores); its
+    recall against the exact selection is reported beside the timing."""
 
     dominant = "index_topk"
 
     def __init__(self, wl, seed, replicas, variant=""):
-        assert variant in ("", "state"), variant
+        assert variant in ("", "state", "bf16sel"), variant
         state = variant == "state"
+        self.bf16sel = variant == "bf16sel"
         import torch
         import compressed_attention_csa_amd as csa
         import inputgen
@@ -112,7 +115,8 @@ class DecodeCSA:
             csa.csa_append(self.new["v_raw"], c["ring_v_raw"], wl.t0, self.z, wl.m, c["v_cmp"])
             csa.csa_append(self.new["k_idx_raw"], c["ring_k_idx_raw"], wl.t0, self.z, wl.m, c["k_idx"],
                            c["k_scale"])
-        csa.csa_index_topk(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, self.idx)
+        csa.csa_index_topk(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, self.idx,
+                           bf16_scores=self.bf16sel)
         if self.state:
             kr, base = csa.ring_window(c["ring_k_raw"], wl.t0 - wl.W + 1)
             csa.csa_attend(self.q, c["k_cmp"], c["v_cmp"], wl.m, self.idx, kr, c["ring_v_raw"], wl.t0,
@@ -120,6 +124,20 @@ class DecodeCSA:
         else:
             csa.csa_attend(self.q, c["k_cmp"], c["v_cmp"], wl.m, self.idx, c["k_win"], c["v_win"], wl.t0,
                            wl.W, wl.scale, self.out, raw_base=self.raw_base)
+
+    def quality(self):
+        """Recall of the approximate selection against the exact one (replica 0)."""
+        if not self.bf16sel:
+            return None
+        wl, csa, torch, c = self.wl, self.csa, self.torch, self.reps[0]
+        sel = {}
+        for approx in (False, True):
+            idx = torch.empty_like(self.idx)
+            csa.csa_index_topk(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, idx,
+                               bf16_scores=approx)
+            sel[approx] = idx.cpu()
+        hits = sum(len(set(sel[True][b, 0].tolist()) & set(sel[False][b, 0].tolist())) for b in range(wl.B))
+        return {"recall_vs_exact": round(hits / (wl.B * wl.k), 5)}
 
     def algorithmic(self):
         wl = self.wl
@@ -351,6 +369,9 @@ def time_workload(name, seed, steps, warmup, graph=True):
     dom = prof.get(w.dominant)
     if dom:
         res["dominant_ms"] = dom["total_ms"] / dom["launches"]
+    q = w.quality() if hasattr(w, "quality") else None
+    if q:
+        res["quality"] = q
     del w, g
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -369,6 +390,7 @@ def summarize(res):
     out.update({"tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
                 "alg_flops": alg["flops"]})
     out["kernel_ms"] = {k: round(v["total_ms"] / v["launches"], 6) for k, v in res["kernels"].items()}
+    out.update(res.get("quality") or {})
     return out
 
 
@@ -491,7 +513,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="csa_decode_pro_1m")
     ap.add_argument("--legs", default="hca_decode_1m,csa_prefill_chunk_1m,csa_decode_flash_128k,"
-                    "hca_prefill_chunk_1m,csa_decode_pro_1m+state,hca_decode_1m+fp8kv",
+                    "hca_prefill_chunk_1m,csa_decode_pro_1m+state,hca_decode_1m+fp8kv,"
+                    "csa_decode_pro_1m+bf16sel",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")

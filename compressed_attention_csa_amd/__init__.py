@@ -10,7 +10,8 @@ Functions (same names and argument order as the C ABI, tensors in place of
 pointers, shapes read from the tensors):
 
     csa_compress(x, logits, m, out, out_scale=None, raw_base=0, entry_begin=0, entry_end=None)
-    csa_index_topk(q_idx, w, k_idx, k_scale, t0, m, top_k, out_idx, out_score=None, workspace=None)
+    csa_index_topk(q_idx, w, k_idx, k_scale, t0, m, top_k, out_idx, out_score=None, workspace=None,
+                   bf16_scores=False)
     csa_attend(q, k_cmp, v_cmp, m, idx, k_raw, v_raw, t0, window, scale, out, lse=None,
                raw_base=0, workspace=None)
     hca_attend(q, k_cmp, v_cmp, m_heavy, k_raw, v_raw, t0, window, scale, out, lse=None,
@@ -43,6 +44,8 @@ SIGNATURES = {
     "csa_index_topk_workspace": (_sz, [_i32, _i64, _i32, _i32, _i64, _i32, _i32]),
     "csa_index_topk": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i32, _i32, _i64, _i64,
                               _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_bf16": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i32, _i32, _i64,
+                                   _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "csa_attend_workspace": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "csa_attend": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64,
                           _i64, _i32, _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz,
@@ -164,17 +167,20 @@ def index_topk_workspace_bytes(B, T, H_I, d_I, N_alloc, top_k, k_dt) -> int:
 
 
 def csa_index_topk(q_idx, w, k_idx, k_scale, t0, m, top_k, out_idx, out_score=None,
-                   workspace_tensor=None):
+                   workspace_tensor=None, bf16_scores=False):
+    """Exact top-k (csa_index_topk); with bf16_scores, csa_index_topk_bf16: the
+    exact top-k of the scores rounded to bf16 (the approximate selector)."""
     B, T, H_I, d_I = q_idx.shape
     N_alloc = k_idx.shape[1]
     k_dt = _dt(k_idx)
     need = index_topk_workspace_bytes(B, T, H_I, d_I, N_alloc, top_k, k_dt)
     ws = workspace_tensor if workspace_tensor is not None else workspace(need, q_idx.device, "index")
-    st = lib().csa_index_topk(_ptr(q_idx), _dt(q_idx), _ptr(w), _ptr(k_idx), k_dt, _ptr(k_scale),
+    name = "csa_index_topk_bf16" if bf16_scores else "csa_index_topk"
+    st = getattr(lib(), name)(_ptr(q_idx), _dt(q_idx), _ptr(w), _ptr(k_idx), k_dt, _ptr(k_scale),
                               B, T, H_I, d_I, N_alloc, t0, m, top_k, _ptr(out_idx),
                               _ptr(out_score), _ptr(ws), 0 if ws is None else ws.numel(),
                               _stream(q_idx))
-    _check("csa_index_topk", st)
+    _check(name, st)
     return out_idx
 
 

@@ -206,11 +206,11 @@ size_t csa_index_topk_workspace(int B, int64_t T, int H_I, int d_I, int64_t N_al
   return csa::plan_index(B, T, H_I, N_alloc, top_k, kind).ws_bytes;
 }
 
-csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w, const void* k_idx,
-                            csa_dtype_t k_dt, const float* k_scale, int B, int64_t T, int H_I,
-                            int d_I, int64_t N_alloc, int64_t t0, int m, int top_k,
-                            int32_t* out_idx, float* out_score, void* workspace,
-                            size_t workspace_bytes, csa_stream_t stream) {
+static csa_status_t index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w, const void* k_idx,
+                               csa_dtype_t k_dt, const float* k_scale, int B, int64_t T, int H_I,
+                               int d_I, int64_t N_alloc, int64_t t0, int m, int top_k,
+                               int32_t* out_idx, float* out_score, void* workspace,
+                               size_t workspace_bytes, csa_stream_t stream, bool bf16_scores) {
   REQUIRE_PTR_IF(q_idx, T > 0);
   REQUIRE_PTR_IF(k_idx, N_alloc > 0);
   REQUIRE_PTR_IF(out_idx, T > 0 && top_k > 0);
@@ -245,8 +245,26 @@ csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w,
   csa::IndexArgs a{q_idx, w, k_idx, k_scale,
                    k_dt == CSA_F32 ? csa::kKeyF32 : (k_dt == CSA_BF16 ? csa::kKeyBF16 : csa::kKeyE4M3),
                    B, T, H_I, d_I, N_alloc, t0, m, top_k, out_idx, out_score, workspace,
-                   reinterpret_cast<hipStream_t>(stream)};
+                   reinterpret_cast<hipStream_t>(stream), bf16_scores};
   return hip_status(csa::launch_index_topk(a, p), "index_topk launch");
+}
+
+csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w, const void* k_idx,
+                            csa_dtype_t k_dt, const float* k_scale, int B, int64_t T, int H_I,
+                            int d_I, int64_t N_alloc, int64_t t0, int m, int top_k,
+                            int32_t* out_idx, float* out_score, void* workspace,
+                            size_t workspace_bytes, csa_stream_t stream) {
+  return index_topk(q_idx, q_dt, w, k_idx, k_dt, k_scale, B, T, H_I, d_I, N_alloc, t0, m, top_k,
+                    out_idx, out_score, workspace, workspace_bytes, stream, false);
+}
+
+csa_status_t csa_index_topk_bf16(const void* q_idx, csa_dtype_t q_dt, const float* w,
+                                 const void* k_idx, csa_dtype_t k_dt, const float* k_scale, int B,
+                                 int64_t T, int H_I, int d_I, int64_t N_alloc, int64_t t0, int m,
+                                 int top_k, int32_t* out_idx, float* out_score, void* workspace,
+                                 size_t workspace_bytes, csa_stream_t stream) {
+  return index_topk(q_idx, q_dt, w, k_idx, k_dt, k_scale, B, T, H_I, d_I, N_alloc, t0, m, top_k,
+                    out_idx, out_score, workspace, workspace_bytes, stream, true);
 }
 
 size_t csa_attend_workspace(int B, int64_t T, int H, int d, int top_k, int window) {

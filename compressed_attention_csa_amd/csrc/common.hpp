@@ -117,6 +117,12 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t packed) {
 
 // ---------------------------------------------------------------- ordering keys
 
+// A binary32 rounded to the nearest bf16 value (ties to even), as binary32.
+__device__ __forceinline__ float round_bf16(float s) {
+  const f32x2_t v = {s, 0.0f};
+  return u32_as_f32(bf16x2_bits(v) << 16);
+}
+
 // Order-preserving image of a binary32 score: a > b  <=>  key(a) > key(b).
 // -0 is folded onto +0 first so that equal scores get equal keys.
 __device__ __forceinline__ uint32_t score_key(float s) {

@@ -232,6 +232,7 @@ __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowIn
       }
       part = sum_rows4(part);
       if (KK == kKeyE4M3) part *= R.sc[u];
+      if (a.bf16_scores) part = round_bf16(part);
       const int64_t e = (int64_t(rr) * RS + u * kWaves + wid) * 16 + col;
       if (g == 0 && e < n) keys[e] = score_key(part);
     }
@@ -278,7 +279,7 @@ __device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* key
         }
         score = fmaf(s_q[16 * 64 + h], fmaxf(dot, 0.0f), score);
       }
-      keys[e] = score_key(score);
+      keys[e] = score_key(a.bf16_scores ? round_bf16(score) : score);
     }
     __syncthreads();
     return;

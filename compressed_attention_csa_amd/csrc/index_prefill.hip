@@ -524,6 +524,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   #pragma unroll
             for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * hf + j], relu(acc[hf][j]), s);
           if (KK == kKeyE4M3) s *= L.scale[cur][e];
+          if (a.bf16_scores) s = round_bf16(s);  // screen and rank the rounded score
           // The screen admits every entry whose rank key can exceed tau (and a
           // few equal-score ones that cannot); the exact test runs when staged
           // entries are drained.  The passing lanes write their pairs to

@@ -64,6 +64,7 @@ struct IndexArgs {
   float* out_score;
   void* ws;
   hipStream_t stream;
+  bool bf16_scores;  // rank scores rounded to bf16 (the approximate selector)
 };
 
 // Workspace layout shared by every call.  The first kHeaderBytes hold control

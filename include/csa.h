@@ -8,6 +8,7 @@
  *   csa_append      decode-time state cache: ring of raw rows + compression of
  *                   the blocks each new token completes
  *   csa_index_topk  Lightning-Indexer scores of compressed entries + per-query top-k
+ *   csa_index_topk_bf16  the same selection on scores rounded to bf16 (approximate)
  *   csa_attend      attention over the selected compressed entries and the raw
  *                   sliding window, under one softmax
  *   hca_attend      dense attention over every visible heavy entry and the window
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef enum {
   CSA_F32 = 0,      /* IEEE binary32 */
@@ -186,6 +187,24 @@ csa_status_t csa_index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w,
                             int d_I, int64_t N_alloc, int64_t t0, int m, int top_k,
                             int32_t* out_idx, float* out_score, void* workspace,
                             size_t workspace_bytes, csa_stream_t stream);
+
+/*
+ * csa_index_topk_bf16 -- the approximate selector: csa_index_topk on scores
+ * rounded to bf16.
+ *
+ * [digest] 七: the indexer's selector may rank bf16 scores, for speed, at a
+ * small loss of recall against the exact selection.  Here each fp32 score
+ * I(t, j) is rounded to the nearest bf16 value (ties to even) and the
+ * selection is the exact top min(top_k, c(t)) of the rounded scores, ties to
+ * the lower j (rounding makes ties common).  out_score holds the rounded
+ * scores.  Arguments, limits, workspace (csa_index_topk_workspace) and errors
+ * are those of csa_index_topk.
+ */
+csa_status_t csa_index_topk_bf16(const void* q_idx, csa_dtype_t q_dt, const float* w,
+                                 const void* k_idx, csa_dtype_t k_dt, const float* k_scale, int B,
+                                 int64_t T, int H_I, int d_I, int64_t N_alloc, int64_t t0, int m,
+                                 int top_k, int32_t* out_idx, float* out_score, void* workspace,
+                                 size_t workspace_bytes, csa_stream_t stream);
 
 /*
  * csa_attend -- CSA core attention: selected compressed entries + raw window.

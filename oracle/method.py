@@ -214,6 +214,21 @@ def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
+def select_topk_bf16(scores: np.ndarray, k: int) -> np.ndarray:
+    """The approximate selector: select_topk on the scores rounded to bf16.
+
+    [digest] section 七 speaks of a selector that ranks bf16 scores at a small
+    loss of recall.  Reading taken: each score, in the binary32 precision the
+    scores are computed in, is rounded once more to the nearest bf16 value
+    (ties to even), and the exact top-k of those rounded values is selected,
+    ties (now frequent) to the lower index.  Invisible entries stay -inf.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    vis = np.isfinite(scores)
+    r = formats.round_to_bf16(formats.round_to_f32(np.where(vis, scores, 0.0)))
+    return select_topk(np.where(vis, r, -np.inf), k)
+
+
 def topk_is_valid(G, scores_row: np.ndarray, k: int, rel_band: float = 1e-5):
     """Check one query's selected set against exact fp64 scores.
 

@@ -37,11 +37,11 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
         assert n in csa.SIGNATURES, n
-    assert L.csa_abi_version() == 3
+    assert L.csa_abi_version() == 4
     for s, name in enumerate(csa.STATUS):
         assert L.csa_status_string(s).decode() == name
 
@@ -110,11 +110,17 @@ def test_append_validation(L):
 
 
 def index(L, q=P, q_dt=BF16, w=P, k=P, k_dt=BF16, ks=None, B=4, T=1, H_I=8, d_I=64, N=1024, t0=4095,
-          m=4, top_k=64, out=P, score=None, ws=P, ws_bytes=None):
+          m=4, top_k=64, out=P, score=None, ws=P, ws_bytes=None, fn="csa_index_topk"):
     if ws_bytes is None:
         ws_bytes = L.csa_index_topk_workspace(B, T, H_I, d_I, N, top_k, k_dt)
-    return L.csa_index_topk(q, q_dt, w, k, k_dt, ks, B, T, H_I, d_I, N, t0, m, top_k, out, score, ws,
-                            ws_bytes, None)
+    return getattr(L, fn)(q, q_dt, w, k, k_dt, ks, B, T, H_I, d_I, N, t0, m, top_k, out, score, ws,
+                          ws_bytes, None)
+
+
+def test_approximate_selector_validates_like_the_exact_one(L):
+    for kw in (dict(q=None), dict(out=None), dict(q_dt=F32), dict(k_dt=FP8), dict(ks=P),
+               dict(top_k=0), dict(top_k=2049), dict(H_I=17), dict(d_I=48), dict(q=MIS)):
+        assert index(L, fn="csa_index_topk_bf16", **kw) == index(L, **kw) != OK, kw
 
 
 def test_index_validation(L):

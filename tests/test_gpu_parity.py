@@ -16,7 +16,7 @@ import torch
 import compressed_attention_csa_amd as csa
 import inputgen
 from oracle import formats, method
-from parity_util import (check_attention, check_e4m3, check_topk_rows, f64, bf16_bits,
+from parity_util import (check_attention, check_bf16_selection_row, check_e4m3, check_topk_rows, f64, bf16_bits,
                          to_dev_bf16, to_dev_f32, ulp_diff_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -292,6 +292,37 @@ def test_index_topk(case):
         scores = method.index_scores(f64(q[b]), None if w is None else f64(w[b]), k64[b], t0, m)
         swaps += check_topk_rows(idx[b], sc[b], scores, k)
     say("  in-band swaps:", swaps)
+
+
+BF16_SEL_CASES = [INDEX_CASES[i] for i in (0, 1, 3, 8, 9, 13)]
+
+
+@pytest.mark.parametrize("case", BF16_SEL_CASES,
+                         ids=[f"{c[0]}-B{c[1]}T{c[2]}-N{c[5]}-k{c[8]}" for c in BF16_SEL_CASES])
+def test_index_topk_bf16_selector(case):
+    """The approximate selector (csa_index_topk_bf16): the exact top-k of the
+    bf16-rounded scores, ties to the lower index, through the decode, prefill
+    and fp32 paths; its recall against the exact top-k is reported."""
+    kind, B, T, H_I, d_I, N, t0, m, k, with_w = case
+    say("index_topk bf16 selector", case)
+    qdt = "f32" if kind == "f32" else "bf16"
+    q = gen("idx_q", (B, T, H_I, d_I), qdt, seed=N + T)
+    w = gen("idx_w", (B, T, H_I), "f32", seed=N + 1) if with_w else None
+    kd, ks, k64 = make_keys(kind, B, N, d_I, seed=N)
+    out_idx = torch.full((B, T, k), 12345, dtype=torch.int32, device=DEV)
+    out_score = torch.full((B, T, k), 5.0, dtype=torch.float32, device=DEV)
+    csa.csa_index_topk(q.to(DEV), None if w is None else w.to(DEV), kd, ks, t0, m, k, out_idx, out_score,
+                       bf16_scores=True)
+    torch.cuda.synchronize()
+    idx, sc = out_idx.cpu().numpy(), out_score.cpu().numpy()
+    total = hits = 0
+    for b in range(B):
+        scores = method.index_scores(f64(q[b]), None if w is None else f64(w[b]), k64[b], t0, m)
+        for i in range(T):
+            kk, h = check_bf16_selection_row(idx[b, i], sc[b, i], scores[i], k)
+            total, hits = total + kk, hits + h
+    say(f"  recall against the exact top-k: {hits / max(total, 1):.4f}")
+    assert hits >= 0.95 * total
 
 
 def test_index_topk_exact_ties_go_to_lower_index():

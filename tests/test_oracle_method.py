@@ -263,6 +263,32 @@ def test_topk_permutation_equivariance():
         assert set(perm[b[i]]) == set(a[i])
 
 
+def test_bf16_selector_hand_example():
+    """Near 1 the bf16 spacing is 2^-7 above and 2^-8 below: 1.003 and 0.999
+    round to 1.0, 1.004 and 1.006 to 1.0078125; the ties at 1.0 go to the lowest
+    index, so the approximate top-4 takes entry 0 where the exact one takes 1."""
+    s = np.array([[1.0, 1.003, 0.999, 2.0, 1.004, 1.006]])
+    assert list(method.select_topk_bf16(s, 4)[0]) == [3, 4, 5, 0]
+    assert list(method.select_topk(s, 4)[0]) == [3, 5, 4, 1]
+
+
+def test_bf16_selector_rounds_ties_to_even():
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd last bit) and 1 + 2^-6 (even):
+    # it rounds up and ties entry 1 (just below 1 + 2^-6), so index 0 wins.
+    s = np.array([[1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6 - 2.0 ** -20]])
+    assert list(method.select_topk_bf16(s, 1)[0]) == [0]
+    # 1 + 2^-8 lies halfway between 1 (even) and 1 + 2^-7: it rounds down.
+    s = np.array([[1 + 2.0 ** -8, 1 + 2.0 ** -7]])
+    assert list(method.select_topk_bf16(s, 1)[0]) == [1]
+
+
+def test_bf16_selector_equals_exact_on_bf16_values_and_keeps_invisible_out():
+    s = formats.round_to_bf16(rnd(23, 4, 300))
+    s[:, 250:] = -np.inf
+    np.testing.assert_array_equal(method.select_topk_bf16(s, 40), method.select_topk(s, 40))
+    assert (method.select_topk_bf16(s, 260)[:, 250:] == -1).all()
+
+
 def test_topk_validity_checker_accepts_oracle_and_rejects_planted_swap():
     s = rnd(22, 1, 200)[0]
     sel = method.select_topk(s[None], 20)[0]
