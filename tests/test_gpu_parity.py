@@ -325,6 +325,38 @@ def test_index_topk_bf16_selector(case):
     assert hits >= 0.95 * total
 
 
+def test_index_topk_bf16_selector_edges():
+    """The approximate selector where rounding decides everything: identical
+    keys (every score ties: the lowest indices win), k above the visible count
+    (everything visible is listed, then -1), and scores that differ only below
+    bf16 resolution (ties again, so the lowest indices win where the exact
+    selection would take the highest scores)."""
+    B, N, d_I = 1, 20000, 64
+    q = gen("bsel_q", (B, 1, 8, d_I), "bf16", seed=31)
+    same = gen("bsel_k", (1, 1, d_I), "bf16", seed=32).expand(B, N, d_I).contiguous()
+    out = torch.empty((B, 1, 700), dtype=torch.int32, device=DEV)
+    csa.csa_index_topk(q.to(DEV), None, same.to(DEV), None, 4 * N - 1, 4, 700, out, bf16_scores=True)
+    few = torch.empty((B, 1, 2048), dtype=torch.int32, device=DEV)
+    csa.csa_index_topk(q.to(DEV), None, same.to(DEV), None, 4 * 1500 - 1, 4, 2048, few, bf16_scores=True)
+    # scores 8 * (1 + (j % 64) * 2^-16): distinct in binary32, all 8.0 in bf16
+    k64 = np.zeros((3000, d_I))
+    k64[:, 0] = 1.0
+    k64[:, 1] = (np.arange(3000) % 64) * 2.0 ** -16
+    qq = np.zeros((1, 1, 8, d_I))
+    qq[..., :2] = 1.0
+    near = torch.empty((1, 1, 64), dtype=torch.int32, device=DEV)
+    csa.csa_index_topk(to_dev_bf16(qq), None, to_dev_bf16(k64[None]), None, 4 * 3000 - 1, 4, 64, near,
+                       bf16_scores=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np.sort(out[0, 0].cpu().numpy()), np.arange(700))
+    got = few[0, 0].cpu().numpy()
+    np.testing.assert_array_equal(np.sort(got[:1500]), np.arange(1500))
+    assert (got[1500:] == -1).all()
+    np.testing.assert_array_equal(np.sort(near[0, 0].cpu().numpy()), np.arange(64))
+    scores = method.index_scores(qq[0], None, k64, 4 * 3000 - 1, 4)
+    check_bf16_selection_row(near[0, 0].cpu().numpy(), None, scores[0], 64)
+
+
 def test_index_topk_exact_ties_go_to_lower_index():
     B, N, d_I, k = 1, 2000, 64, 100
     base = gen("tie_k", (1, 50, d_I), "bf16", seed=3)
