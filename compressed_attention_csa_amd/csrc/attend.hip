@@ -636,7 +636,9 @@ struct LdsM {
 // pair.  A tile whose largest |V| exceeds 65280 (it would overflow), or is
 // nonzero and below 2^-10 (so that values losing bits as binary16 subnormals,
 // by at most 2^-25 each, could matter next to the output), ends the binary16
-// run: it and every later tile of the workgroup take the hi + lo path.
+// run: it and every later tile of the workgroup take the hi + lo path.  Every
+// staged chunk counts, dead slots (which hold query rows) too: their weight is
+// 0, and 0 times an overflowed binary16 value would be NaN.
 template <int D, int NW, int RB, bool KV8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1))) void hca_multi_kernel(AttendArgs a, int64_t groups_per_seq) {
   constexpr int kT = NW * 64;
