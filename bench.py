@@ -426,7 +426,8 @@ def load_traffic(key):
     on the current kernel sources (else null)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        data = json.load(open(p))
+        with open(p) as f:
+            data = json.load(f)
     except (OSError, ValueError):
         return None
     ent = data.get(key)

@@ -54,7 +54,8 @@ BF16_MAX = float(np.ldexp(2.0 - 2.0 ** -7, 127))
 def bf16_bits_to_f64(bits) -> np.ndarray:
     """Decode raw bf16 bit patterns (uint16) to float64 (exact)."""
     u = np.asarray(bits).astype(np.uint32) << np.uint32(16)
-    return u.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # NaN patterns stay NaN; only the warning is silenced
+        return u.view(np.float32).astype(np.float64)
 
 
 def round_to_bf16(v) -> np.ndarray:

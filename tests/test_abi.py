@@ -31,7 +31,8 @@ def L():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     return re.findall(r"^(?:csa_status_t|size_t|int|const char\*)\s+(\w+)\(", text, re.M)
 
 

@@ -5,7 +5,8 @@ import os
 import inputgen
 from oracle import method
 
-G = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")))
+with open(os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")) as _f:
+    G = json.load(_f)
 
 
 def v(key):
