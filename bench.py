@@ -484,8 +484,8 @@ def cpu_baseline(seed):
     with ctx:
         t0 = time.perf_counter()
         while runs < 3 or time.perf_counter() - t0 < CPU_SAMPLE_SECONDS:
-            s = method.index_scores(qi, w, ki, wl.t0, wl.m)
-            sel = method.select_topk(s, wl.k)
+            s, vis = method.index_scores(qi, w, ki, wl.t0, wl.m)
+            sel = method.select_topk(s, vis, wl.k)
             method.csa_attend(q, kc, vc, sel, k_raw, v_raw, 0, wl.t0, wl.W, wl.m, wl.scale)
             runs += 1
         total = time.perf_counter() - t0

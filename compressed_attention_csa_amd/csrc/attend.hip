@@ -377,6 +377,9 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
           vw = make_uint4(e4m3x2_to_bf16x2<false>(P.v[4 * c]), e4m3x2_to_bf16x2<true>(P.v[4 * c]),
                           e4m3x2_to_bf16x2<false>(P.v[4 * c + 1]), e4m3x2_to_bf16x2<true>(P.v[4 * c + 1]));
         }
+        // A skipped slot holds zeros, not the query row it was loaded from: its
+        // weight is 0, and 0 times a NaN or an infinity there would be NaN.
+        if (!((P.lv >> c) & 1u)) kw = vw = make_uint4(0u, 0u, 0u, 0u);
         L.k[buf][k_pos<CPR>(sl, ch)] = kw;
         L.v[buf][v_pos<CPR>(sl, ch)] = vw;
         if (ch == 0) L.live[buf][sl] = ((P.lv >> c) & 1u) ? 0xffffffffu : 0u;
@@ -637,8 +640,11 @@ struct LdsM {
 // nonzero and below 2^-10 (so that values losing bits as binary16 subnormals,
 // by at most 2^-25 each, could matter next to the output), ends the binary16
 // run: it and every later tile of the workgroup take the hi + lo path.  Every
-// staged chunk counts, dead slots (which hold query rows) too: their weight is
-// 0, and 0 times an overflowed binary16 value would be NaN.
+// staged chunk counts, rows a token does not see too: their weight is 0, and 0
+// times an overflowed binary16 value would be NaN.  (Slots outside every
+// range are staged as zeros.)  A NaN or infinity in a K or V row therefore
+// also reaches the tokens of the workgroup that share its tile without seeing
+// it (in the newest heavy tile and the window tiles): 0 times NaN is NaN.
 template <int D, int NW, int RB, bool KV8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1))) void hca_multi_kernel(AttendArgs a, int64_t groups_per_seq) {
   constexpr int kT = NW * 64;
@@ -707,6 +713,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
   typedef uint32_t chunks_t __attribute__((ext_vector_type(4 * CPT)));
   struct Pre {
     chunks_t k, v;
+    uint32_t lv;    // bit c: chunk c holds a row of the slot range (else zeros are staged)
     bool f8;        // a heavy tile of e4m3 codes (two words per chunk)
     float ks, vs;   // its scales of slot tid (threads tid < kTB)
   };
@@ -717,9 +724,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
     P.f8 = KV8 && t < nht;
     if (KV8 && t < nht) {
       const int64_t r0 = int64_t(t) * kTB;
+      uint32_t lv = 0;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int id = (tid + c * kT) % CT, sl = id / CPR, ch = id % CPR;
+        lv |= uint32_t(r0 + sl < c_max) << c;
         const int64_t row = r0 + sl < c_max ? r0 + sl : c_max - 1;  // past the end: re-read the last entry
         const uint2 kw = *reinterpret_cast<const uint2*>(kc8 + row * D + ch * 8);
         const uint2 vw = *reinterpret_cast<const uint2*>(vc8 + row * D + ch * 8);
@@ -731,6 +740,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
         P.ks = ksp[row];
         P.vs = vsp[row];
       }
+      P.lv = lv;
       return;
     }
     // Wave-uniform choices as masks rather than branches.
@@ -742,11 +752,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
                                                        (reinterpret_cast<intptr_t>(vr) & win));
     const int64_t r0 = int64_t(t) * kTB + (wdelta & win);
     const int64_t lim = ((c_max & ~win) | (whi & win)) & ~past;
+    uint32_t lv = 0;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int id = (tid + c * kT) % CT, sl = id / CPR, ch = id % CPR;
       const int64_t row = r0 + sl;
       const bool ok = row < lim;
+      lv |= uint32_t(ok) << c;
       const bf16_t* kp = ok ? kb + row * D : qrow;
       const bf16_t* vp = ok ? vb + row * D : qrow;
       const uint4 kw = *reinterpret_cast<const uint4*>(kp + ch * 8);
@@ -754,6 +766,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
       P.k[4 * c] = kw.x; P.k[4 * c + 1] = kw.y; P.k[4 * c + 2] = kw.z; P.k[4 * c + 3] = kw.w;
       P.v[4 * c] = vw.x; P.v[4 * c + 1] = vw.y; P.v[4 * c + 2] = vw.z; P.v[4 * c + 3] = vw.w;
     }
+    P.lv = lv;
     if (KV8) {
       P.ks = 1.0f;
       P.vs = 1.0f;
@@ -775,6 +788,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
           vw = make_uint4(e4m3x2_to_bf16x2<false>(P.v[4 * c]), e4m3x2_to_bf16x2<true>(P.v[4 * c]),
                           e4m3x2_to_bf16x2<false>(P.v[4 * c + 1]), e4m3x2_to_bf16x2<true>(P.v[4 * c + 1]));
         }
+        // Slots outside the heavy and window ranges hold zeros, not the row
+        // they were loaded from (0 times a NaN there would be NaN).
+        if (!((P.lv >> c) & 1u)) kw = vw = make_uint4(0u, 0u, 0u, 0u);
         L.k[buf][sl * LdsM<D>::KS + ch] = kw;
         L.v[buf][sl * LdsM<D>::VS + ch] = vw;
         if (W16) {

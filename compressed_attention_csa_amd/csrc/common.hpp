@@ -124,10 +124,13 @@ __device__ __forceinline__ float round_bf16(float s) {
 }
 
 // Order-preserving image of a binary32 score: a > b  <=>  key(a) > key(b).
-// -0 is folded onto +0 first so that equal scores get equal keys.
+// -0 is folded onto +0 first so that equal scores get equal keys.  Every NaN,
+// of either sign, maps to the largest key: a NaN score ranks above every
+// number (+inf included), and key_score gives it back as a NaN.
 __device__ __forceinline__ uint32_t score_key(float s) {
-  uint32_t u = f32_as_u32(s + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = f32_as_u32(s + 0.0f);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (s != s) ? 0xffffffffu : k;
 }
 __device__ __forceinline__ float key_score(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -140,6 +143,10 @@ __device__ __forceinline__ uint64_t rank_key(uint32_t key, uint32_t idx) {
 __device__ __forceinline__ uint32_t rank_key_idx(uint64_t rk) {
   return 0xffffffffu - uint32_t(rk & 0xffffffffu);
 }
+
+// The indexer's rectifier max(0, x), propagating NaN of either sign (IEEE
+// 754-2019 maximum; one v_maximum3_f32 on gfx950).  +-0 give +0.
+__device__ __forceinline__ float relu_nan(float x) { return __builtin_elementwise_maximum(x, 0.0f); }
 
 // ---------------------------------------------------------------- MFMA
 

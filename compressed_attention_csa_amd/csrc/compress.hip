@@ -157,8 +157,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
       amax = fmaxf(amax, fabsf(r[i]));
     }
     for (int o = tpe >> 1; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    // fmaxf leaves NaN elements out of amax.  A quotient of 0 (an all-zero row,
+    // or a largest magnitude below 448 * 2^-150, which underflows) takes scale 1.
     float scale = amax / 448.0f;
-    if (amax == 0.0f) scale = 1.0f;
+    if (scale == 0.0f) scale = 1.0f;
     if (valid) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll

@@ -156,11 +156,15 @@ __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowIn
     qa0 = u32x4_as_bf16x8(v0);
     qa1 = u32x4_as_bf16x8(v1);
   }
+  // Rows past H_I hold zeros; they are left out of the head sum rather than
+  // weighted by 0, since their product with an infinite key element is NaN.
   float wr[4];
+  bool hv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = 4 * g + j;
-    wr[j] = (h < H_I) ? (a.w ? a.w[qrow + h] : 1.0f) : 0.0f;
+    hv[j] = h < H_I;
+    wr[j] = hv[j] ? (a.w ? a.w[qrow + h] : 1.0f) : 0.0f;
   }
   const int64_t kb = ri.b * a.N_alloc + ri.lo;
   const int64_t ngroups = (n + 15) / 16;
@@ -226,9 +230,7 @@ __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowIn
       float part = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // ReLU as an integer max: negative floats have negative bit patterns.
-        const float rl = u32_as_f32(uint32_t(max(int32_t(f32_as_u32(acc[u][j])), 0)));
-        part = fmaf(wr[j], rl, part);
+        part = hv[j] ? fmaf(wr[j], relu_nan(acc[u][j]), part) : part;
       }
       part = sum_rows4(part);
       if (KK == kKeyE4M3) part *= R.sc[u];
@@ -277,7 +279,7 @@ __device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* key
           dot = fmaf(qh[4 * v + 2], x.z, dot);
           dot = fmaf(qh[4 * v + 3], x.w, dot);
         }
-        score = fmaf(s_q[16 * 64 + h], fmaxf(dot, 0.0f), score);
+        score = fmaf(s_q[16 * 64 + h], relu_nan(dot), score);
       }
       keys[e] = score_key(a.bf16_scores ? round_bf16(score) : score);
     }

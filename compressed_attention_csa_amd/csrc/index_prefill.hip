@@ -72,12 +72,6 @@ __device__ __forceinline__ int chunk_pos(int e, int c, int cpe) {
   return e * cpe + (c ^ h);
 }
 
-// max(x, 0) as one integer max on the bit pattern: every negative binary32
-// (-0 included) has its sign bit set and maps to +0.  (fmaxf would add a NaN
-// quieting step per call.)
-__device__ __forceinline__ float relu(float x) {
-  return __int_as_float(max(__float_as_int(x), 0));
-}
 
 __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
   const uint32_t lo = __shfl(uint32_t(v), src), hi = __shfl(uint32_t(v >> 32), src);
@@ -218,7 +212,10 @@ __device__ int wave_compact(uint64_t* buf, int n, uint64_t T) {
 
 // ---------------------------------------------------------------- kernel
 
-template <int KK, int DI>
+// FH: all 8 head rows of the products are real heads (H_I == 8).  Otherwise
+// the zero rows past H_I are left out of the head sum (0 times an infinite key
+// element is NaN, which a zero weight would not remove).
+template <int KK, int DI, bool FH>
 __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, IndexPlan p) {
   __shared__ LdsPrefill L;
   constexpr int KB = (KK == kKeyE4M3) ? 1 : 2;  // key bytes per element
@@ -522,7 +519,10 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   #pragma unroll
           for (int hf = 0; hf < 2; ++hf)
   #pragma unroll
-            for (int j = 0; j < 4; ++j) s = fmaf(wv[4 * hf + j], relu(acc[hf][j]), s);
+            for (int j = 0; j < 4; ++j) {
+              const float t = fmaf(wv[4 * hf + j], relu_nan(acc[hf][j]), s);
+              s = (FH || 4 * hf + j < H_I) ? t : s;
+            }
           if (KK == kKeyE4M3) s *= L.scale[cur][e];
           if (a.bf16_scores) s = round_bf16(s);  // screen and rank the rounded score
           // The screen admits every entry whose rank key can exceed tau (and a
@@ -642,12 +642,23 @@ bool prefill_path(int64_t T, int H_I, int key_kind) {
 hipError_t launch_index_prefill(const IndexArgs& a, const IndexPlan& p) {
   const dim3 grid(unsigned((a.T + kPrefillQPB - 1) / kPrefillQPB), unsigned(a.B)), block(kThreads);
   ProfScope prof("index_topk", a.stream);
+  const bool fh = a.H_I == 8;
   if (a.key_kind == kKeyBF16) {
-    if (a.d_I == 64) hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 64>), grid, block, 0, a.stream, a, p);
-    else hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 32>), grid, block, 0, a.stream, a, p);
+    if (a.d_I == 64) {
+      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 64, true>), grid, block, 0, a.stream, a, p);
+      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 64, false>), grid, block, 0, a.stream, a, p);
+    } else {
+      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 32, true>), grid, block, 0, a.stream, a, p);
+      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 32, false>), grid, block, 0, a.stream, a, p);
+    }
   } else {
-    if (a.d_I == 64) hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 64>), grid, block, 0, a.stream, a, p);
-    else hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 32>), grid, block, 0, a.stream, a, p);
+    if (a.d_I == 64) {
+      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 64, true>), grid, block, 0, a.stream, a, p);
+      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 64, false>), grid, block, 0, a.stream, a, p);
+    } else {
+      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 32, true>), grid, block, 0, a.stream, a, p);
+      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 32, false>), grid, block, 0, a.stream, a, p);
+    }
   }
   return hipGetLastError();
 }

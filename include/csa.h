@@ -47,6 +47,26 @@
  *     output type; dot products accumulate in fp32 (bf16 x bf16 products are
  *     exact in fp32); softmax statistics are fp32; the softmax weights enter the
  *     value product as a bf16 hi + lo pair (about 16 significant bits).
+ *   - Non-finite inputs (NaN, +-inf) never change how long a call runs (every
+ *     loop is bounded by the sizes alone) and follow IEEE arithmetic:
+ *       * indexer: the rectifier max(0, x) keeps a NaN of either sign, so a
+ *         NaN in a key row, in a query head or in a weight makes the affected
+ *         scores NaN; an infinity gives +-inf, or NaN through inf - inf or
+ *         0 * inf.  A NaN score ranks above every number (+inf included),
+ *         NaN ties going to the lower index as any tie does, and out_score
+ *         reports it as NaN.  -inf is an ordinary (lowest) score: visibility
+ *         depends on positions only, never on a score's value.
+ *       * attention: a NaN or infinity in q[b,i,h,:] or in a K or V row that
+ *         takes part in query i's softmax makes outputs of that query
+ *         non-finite: a NaN in q[b,i,h,:] the row (i, h); in a K row, every
+ *         head of query i; in column c of a V row, column c of every head of
+ *         query i.  A skipped slot (invalid, invisible or padding index) reads
+ *         nothing.  An infinity may give NaN where exact arithmetic would give
+ *         an infinity.  One exception: in hca_attend over at least 16
+ *         consecutive query tokens per sequence, a non-finite heavy-entry or
+ *         window row also reaches the tokens of the same group of up to 4
+ *         consecutive tokens that share its tile without seeing it (a zero
+ *         weight times NaN is NaN).
  */
 #ifndef CSA_H
 #define CSA_H

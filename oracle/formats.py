@@ -131,16 +131,23 @@ def e4m3_quantize_rows(r32: np.ndarray):
     """Per-row absmax quantisation of binary32 rows to e4m3fn with a binary32 scale.
 
     The decisions are taken in binary32 arithmetic, as the quantiser on the GPU
-    takes them: ``scale = f32(max_i |r_i| / 448)`` (``scale = 1`` for an all-zero
-    row) and ``code_i = e4m3_rne(f32(r_i / scale))``.  Returns
+    takes them: ``scale = f32(max_i |r_i| / 448)``, the maximum taken over the
+    elements that are not NaN, and ``scale = 1`` where that quotient is 0 (an
+    all-zero row, or one whose largest magnitude is below 448 * 2^-150, where
+    the quotient underflows); then ``code_i = e4m3_rne(f32(r_i / scale))``.  A
+    NaN element gets a NaN code; an infinite element makes the scale infinite,
+    so every stored value of its row is NaN (0 * inf or inf / inf).  Returns
     ``(codes uint8 [N, d], scale float32 [N], stored float64 [N, d])`` where
     ``stored = decode(code) * scale`` is exact in float64.
     """
     r32 = np.asarray(r32, dtype=np.float32)
-    amax = np.max(np.abs(r32), axis=-1)
-    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)  # binary32 division
-    scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
-    y = (r32 / scale[..., None]).astype(np.float32)  # binary32 division
+    amax = np.max(np.where(np.isnan(r32), np.float32(0.0), np.abs(r32)), axis=-1)
+    with np.errstate(under="ignore"):
+        scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)  # binary32 division
+    scale = np.where(scale == 0, np.float32(1.0), scale).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        y = (r32 / scale[..., None]).astype(np.float32)  # binary32 division
     codes = e4m3_encode(y.astype(np.float64))
-    stored = e4m3_decode(codes) * scale.astype(np.float64)[..., None]
+    with np.errstate(invalid="ignore"):
+        stored = e4m3_decode(codes) * scale.astype(np.float64)[..., None]
     return codes, scale, stored

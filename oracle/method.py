@@ -169,98 +169,137 @@ def window_positions(t: int, W: int) -> np.ndarray:
 # ----------------------------------------------------------------------------- indexer
 
 
-def index_scores(q_idx, w, k_idx, t0: int, m: int) -> np.ndarray:
-    """Lightning-Indexer scores I[t, j] in fp64; invisible entries are -inf.
+def index_scores(q_idx, w, k_idx, t0: int, m: int):
+    """Lightning-Indexer scores in fp64 and the visible-entry count of every query.
 
     q_idx [T, H_I, d_I], w [T, H_I] (None means all ones), k_idx [N, d_I]
-    (decoded stored values).  Query i sits at position t0 + i.
+    (decoded stored values).  Query i sits at position t0 + i and sees the
+    entries j < visible[i] = min(N, (t0 + i + 1) // m).  For those,
     I(t, j) = sum_h w[t,h] * max(0, q_idx[t,h] . k_idx[j]).
     [digest] sections 三 and 七; [summary] section 2.1.
+
+    Returns (scores [T, N], visible [T]).  Visibility is carried by ``visible``
+    alone: scores[i, j] for j >= visible[i] is NaN and is not a score.
+
+    Non-finite inputs follow IEEE arithmetic: max(0, NaN) is NaN (the rectifier
+    propagates NaN, of either sign), a NaN weight, query or key element makes
+    the score NaN, and an infinity gives +-inf or, through inf - inf or 0 * inf,
+    NaN.  The products and the head sum are written out elementwise, so that no
+    library routine may skip a zero weight.
     """
     q_idx = np.asarray(q_idx, dtype=np.float64)
     k_idx = np.asarray(k_idx, dtype=np.float64)
     T, H_I, _ = q_idx.shape
     N = k_idx.shape[0]
     w = np.ones((T, H_I)) if w is None else np.asarray(w, dtype=np.float64)
-    out = np.full((T, N), -np.inf)
-    for i in range(T):
-        c = visible_entries(t0 + i, m, N)
-        if c == 0:
-            continue
-        dots = q_idx[i] @ k_idx[:c].T  # [H_I, c]
-        out[i, :c] = w[i] @ np.maximum(dots, 0.0)
-    return out
+    out = np.full((T, N), np.nan)
+    visible = np.array([visible_entries(t0 + i, m, N) for i in range(T)], dtype=np.int64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        for i in range(T):
+            c = int(visible[i])
+            if c == 0:
+                continue
+            dots = np.einsum("hd,jd->hj", q_idx[i], k_idx[:c])  # [H_I, c]
+            relu = np.maximum(dots, 0.0)  # np.maximum propagates NaN
+            out[i, :c] = np.sum(w[i][:, None] * relu, axis=0)
+    return out, visible
 
 
-def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
-    """Per query, the min(k, #visible) best visible entries; -1 pads the rest.
+def _rank_order(s, idx):
+    """Indices ``idx`` ordered by the selection's total order on their scores s:
+    NaN first, then decreasing value, then increasing index."""
+    nan = np.isnan(s)
+    return np.lexsort((idx, -np.where(nan, 0.0, s), ~nan))
+
+
+def select_topk(scores: np.ndarray, visible, k: int) -> np.ndarray:
+    """Per query, the min(k, visible) best visible entries; -1 pads the rest.
 
     The decision is taken on the binary32 images of the scores (the precision
-    the GPU selects in), ordered by (score descending, index ascending).  The
-    output lists entries in that order.  [digest] section 三; [book] section 4.
+    the GPU selects in), ordered by score (a NaN score ranks above every
+    number, +inf included), then by lower index.  The output lists entries in
+    that order.  [digest] section 三; [book] section 4.
     """
     T, N = scores.shape
     out = np.full((T, k), -1, dtype=np.int64)
     if k == 0:
         return out
-    s32 = scores.astype(np.float32).astype(np.float64)
+    with np.errstate(over="ignore"):
+        s32 = scores.astype(np.float32).astype(np.float64)
     for i in range(T):
-        vis = np.nonzero(np.isfinite(scores[i]))[0]
-        if vis.size == 0:
+        c = int(visible[i])
+        if c == 0:
             continue
-        order = np.lexsort((vis, -s32[i, vis]))  # primary key: -score, then index
-        kk = min(k, vis.size)
+        vis = np.arange(c)
+        order = _rank_order(s32[i, :c], vis)
+        kk = min(k, c)
         out[i, :kk] = vis[order[:kk]]
     return out
 
 
-def select_topk_bf16(scores: np.ndarray, k: int) -> np.ndarray:
+def select_topk_bf16(scores: np.ndarray, visible, k: int) -> np.ndarray:
     """The approximate selector: select_topk on the scores rounded to bf16.
 
     [digest] section 七 speaks of a selector that ranks bf16 scores at a small
     loss of recall.  Reading taken: each score, in the binary32 precision the
     scores are computed in, is rounded once more to the nearest bf16 value
     (ties to even), and the exact top-k of those rounded values is selected,
-    ties (now frequent) to the lower index.  Invisible entries stay -inf.
+    ties (now frequent) to the lower index.  NaN stays NaN (ranked first).
     """
     scores = np.asarray(scores, dtype=np.float64)
-    vis = np.isfinite(scores)
-    r = formats.round_to_bf16(formats.round_to_f32(np.where(vis, scores, 0.0)))
-    return select_topk(np.where(vis, r, -np.inf), k)
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = formats.round_to_bf16(formats.round_to_f32(scores))
+    return select_topk(r, visible, k)
 
 
-def topk_is_valid(G, scores_row: np.ndarray, k: int, rel_band: float = 1e-5):
+def topk_is_valid(G, scores_row: np.ndarray, visible: int, k: int, rel_band: float = 1e-5):
     """Check one query's selected set against exact fp64 scores.
 
-    Valid iff |G| = kk = min(k, #visible), the members are distinct and
-    visible, every member scores >= s_k - beta and every visible non-member
-    scores <= s_k + beta, where s_k is the kk-th best exact score and
-    beta = rel_band * |s_k|.  Returns (ok, reason, n_in_band_swaps).
+    The query sees entries 0 .. visible-1.  With kk = min(k, visible): valid iff
+    |G| = kk, the members are distinct and visible, and
+      * NaN scores rank first: if there are at least kk of them, G is the kk
+        lowest-indexed NaN entries; otherwise every NaN entry is in G and the
+        rest of G is valid for the remaining places under the band rule;
+      * band rule: every other member scores >= s_k - beta and every visible
+        non-member scores <= s_k + beta, s_k being the kk-th best exact score
+        and beta = rel_band * |s_k| (0 when s_k is infinite: equal infinities
+        tie, and any choice among them is valid).
+    Returns (ok, reason, n_in_band_swaps).
     """
     G = np.asarray(G, dtype=np.int64)
     G = G[G >= 0]
-    vis = np.nonzero(np.isfinite(scores_row))[0]
-    kk = min(k, vis.size)
+    c = int(visible)
+    kk = min(k, c)
     if G.size != kk:
         return False, f"|G|={G.size} expected {kk}", 0
     if np.unique(G).size != G.size:
         return False, "duplicate members", 0
     if kk == 0:
         return True, "", 0
-    if not np.all(np.isfinite(scores_row[G])):
+    if np.any(G >= c):
         return False, "invisible member", 0
-    s_sorted = np.sort(scores_row[vis])[::-1]
-    s_k = s_sorted[kk - 1]
-    beta = rel_band * abs(s_k)
-    inG = np.zeros(scores_row.shape[0], dtype=bool)
+    s = np.asarray(scores_row[:c], dtype=np.float64)
+    nan_idx = np.nonzero(np.isnan(s))[0]
+    inG = np.zeros(c, dtype=bool)
     inG[G] = True
-    if np.any(scores_row[G] < s_k - beta):
+    if nan_idx.size >= kk:
+        ok = np.array_equal(np.sort(G), nan_idx[:kk])
+        return (ok, "" if ok else "not the lowest-indexed NaN-score entries", 0)
+    if not np.all(inG[nan_idx]):
+        return False, "a NaN-score entry is missing", 0
+    rest = np.nonzero(~np.isnan(s))[0]
+    kr = kk - nan_idx.size
+    s_sorted = np.sort(s[rest])[::-1]
+    s_k = s_sorted[kr - 1]
+    beta = rel_band * abs(s_k) if np.isfinite(s_k) else 0.0
+    members = G[~np.isnan(s[G])]
+    if np.any(s[members] < s_k - beta):
         return False, "member below the k-th score band", 0
-    out_vis = vis[~inG[vis]]
-    if out_vis.size and np.any(scores_row[out_vis] > s_k + beta):
+    out_vis = rest[~inG[rest]]
+    if out_vis.size and np.any(s[out_vis] > s_k + beta):
         return False, "non-member above the k-th score band", 0
-    exact = set(vis[np.argsort(-scores_row[vis], kind="stable")[:kk]].tolist())
-    swaps = len(exact.symmetric_difference(set(G.tolist()))) // 2
+    exact = set(rest[np.lexsort((rest, -s[rest]))[:kr]].tolist())
+    swaps = len(exact.symmetric_difference(set(members.tolist()))) // 2
     return True, "", swaps
 
 
@@ -382,12 +421,12 @@ def csa_layer(q, k_raw, v_raw, q_idx, k_idx_raw, w, z, m: int, top_k: int, W: in
     k_c = store(compress_exact(k_raw, z, m), cmp_dtype)
     v_c = store(compress_exact(v_raw, z, m), cmp_dtype)
     ki_c = store(compress_exact(k_idx_raw, z, m), idx_key_dtype)
-    scores = index_scores(q_idx, w, ki_c["values"], t0, m)
-    idx = select_topk(scores, top_k)
+    scores, visible = index_scores(q_idx, w, ki_c["values"], t0, m)
+    idx = select_topk(scores, visible, top_k)
     o, lse = csa_attend(q, k_c["values"], v_c["values"], idx, k_raw, v_raw, 0, t0, W, m, scale)
     assert n >= t0 + q.shape[0]
-    return {"k_cmp": k_c, "v_cmp": v_c, "k_idx": ki_c, "scores": scores, "idx": idx,
-            "o": o, "lse": lse}
+    return {"k_cmp": k_c, "v_cmp": v_c, "k_idx": ki_c, "scores": scores, "visible": visible,
+            "idx": idx, "o": o, "lse": lse}
 
 
 def hca_layer(q, k_raw, v_raw, z, m_heavy: int, W: int, scale: float, t0: int,

@@ -40,9 +40,13 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def to_dev_bf16(x64: np.ndarray, device="cuda") -> torch.Tensor:
-    """bf16 device tensor holding the given (already bf16-representable) values."""
+    """bf16 device tensor holding the given (already bf16-representable) values;
+    a NaN keeps its sign (quiet NaN pattern 0x7fc0 or 0xffc0)."""
+    x64 = np.asarray(x64, np.float64)
     bits = formats.f64_to_bf16_bits(x64)
-    assert np.array_equal(formats.bf16_bits_to_f64(bits), x64), "value not bf16-representable"
+    nan = np.isnan(x64)
+    bits = np.where(nan, np.where(np.signbit(x64), 0xFFC0, 0x7FC0), bits).astype(np.uint16)
+    assert np.array_equal(formats.bf16_bits_to_f64(bits), x64, equal_nan=True), "value not bf16-representable"
     return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
 
 
@@ -111,35 +115,46 @@ def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, what="", out_bf1
     return worst
 
 
-def check_topk_rows(idx_gpu, score_gpu, scores64, k):
-    """Validate every row's selected set; returns the number of in-band swaps."""
+def check_topk_rows(idx_gpu, score_gpu, scores64, visible, k):
+    """Validate every row's selected set; returns the number of in-band swaps.
+
+    visible[i] is the count of entries row i sees (a prefix of the entries)."""
     swaps = 0
     for i in range(idx_gpu.shape[0]):
         row = idx_gpu[i]
-        ok, why, sw = method.topk_is_valid(row, scores64[i], k)
+        c = int(visible[i])
+        ok, why, sw = method.topk_is_valid(row, scores64[i], c, k)
         assert ok, f"row {i}: {why}"
-        kk = min(k, int(np.isfinite(scores64[i]).sum()))
+        kk = min(k, c)
         assert np.all(row[:kk] >= 0) and np.all(row[kk:] == -1), f"row {i}: padding"
         if score_gpu is not None:
             sg = score_gpu[i, :kk].astype(np.float64)
             so = scores64[i, row[:kk]]
-            scale = np.abs(scores64[i][np.isfinite(scores64[i])]).max() if kk else 1.0
-            assert np.all(np.abs(sg - so) <= 1e-5 * np.maximum(np.abs(so), 1e-2 * scale)), \
+            fin = np.isfinite(scores64[i, :c])
+            scale = np.abs(scores64[i, :c][fin]).max() if fin.any() else 1.0
+            nan = np.isnan(so)
+            assert np.all(np.isnan(sg[nan])), f"row {i}: a NaN score reported as a number"
+            same_inf = np.isinf(so) & (sg == so)
+            reg = ~nan & ~np.isinf(so)
+            assert np.all(same_inf | ~np.isinf(so)), f"row {i}: infinite scores"
+            assert np.all(np.abs(sg[reg] - so[reg]) <= 1e-5 * np.maximum(np.abs(so[reg]), 1e-2 * scale)), \
                 f"row {i}: scores"
             assert np.all(np.isneginf(score_gpu[i, kk:]))
         swaps += sw
     return swaps
 
 
-def check_bf16_selection_row(row, score_row, scores64_row, k):
+def check_bf16_selection_row(row, score_row, scores64_row, visible, k):
     """Validate one row of the approximate selector; returns (kk, recall hits)
-    where hits counts members of the exact fp64 top-k."""
-    vis = np.nonzero(np.isfinite(scores64_row))[0]
+    where hits counts members of the exact fp64 top-k.  Finite scores only."""
+    c = int(visible)
+    vis = np.arange(c)
+    assert np.isfinite(scores64_row[:c]).all(), "finite scores expected"
     kk = min(k, vis.size)
     G = row[:kk]
     assert np.all(row[kk:] == -1), "padding"
     assert np.all(G >= 0) and np.unique(G).size == kk, "members"
-    assert np.all(np.isfinite(scores64_row[G])), "invisible member"
+    assert np.all(G < c), "invisible member"
     s32 = formats.round_to_f32(scores64_row[vis])
     r_dn = formats.round_to_bf16(s32 - np.abs(s32) * 2.0 ** -20)
     r_up = formats.round_to_bf16(s32 + np.abs(s32) * 2.0 ** -20)
@@ -159,3 +174,38 @@ def check_bf16_selection_row(row, score_row, scores64_row, k):
     np.testing.assert_array_equal(np.sort(G), exp, err_msg="not the top-k of the rounded scores")
     exact = set(vis[np.lexsort((vis, -scores64_row[vis]))[:kk]].tolist())
     return kk, len(exact & set(G.tolist()))
+
+
+def check_attention_nonfinite(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, what="", loose=None):
+    """Attention outputs where some inputs are NaN or infinite.
+
+    * every element the oracle makes non-finite is non-finite on the GPU (NaN
+      or an infinity: the sides may differ in which, e.g. the GPU's weight
+      w_hi + w_lo times inf with w_lo = 0 is NaN where the fp64 product is inf);
+    * every element the oracle keeps finite is finite on the GPU and within
+      check_attention's row criterion, relative to the largest finite
+      reference element of its (query, head) row;
+    * rows marked in ``loose`` ([T, H] bool) are only held to the first rule:
+      they may come out non-finite where the oracle is finite (a documented
+      case: a non-finite row shares a tile with a token that does not see it).
+    lse: non-finite where the oracle's is; otherwise to 1e-4 + 1e-5 relative.
+    """
+    o_gpu = np.asarray(o_gpu, np.float64)
+    lse_ref = np.asarray(lse_ref, np.float64)
+    T, H = o_ref.shape[:2]
+    loose = np.zeros((T, H), dtype=bool) if loose is None else np.asarray(loose, bool)
+    bad_ref = ~np.isfinite(o_ref)
+    assert np.all(~np.isfinite(o_gpu[bad_ref])), f"{what}: a non-finite reference element came out finite"
+    fin = np.isfinite(o_ref) & ~loose[..., None]
+    assert np.all(np.isfinite(o_gpu[fin])), f"{what}: an element the oracle keeps finite is not"
+    tol = TOL[dtype]
+    ref = np.abs(np.where(fin, o_ref, 0.0)).max(axis=-1, keepdims=True)
+    err = np.abs(np.where(fin, o_gpu - np.where(fin, o_ref, 0.0), 0.0))
+    assert np.all(err <= tol * ref), f"{what}: finite elements differ (worst {float((err / np.maximum(ref, 1e-300)).max()):.3e})"
+    if lse_gpu is not None:
+        lse_gpu = np.asarray(lse_gpu, np.float64)
+        nf = ~np.isfinite(lse_ref)
+        assert np.all(~np.isfinite(lse_gpu[nf])), f"{what}: lse of a non-finite row"
+        ok = ~nf & ~loose
+        dl = np.abs(lse_gpu[ok] - lse_ref[ok])
+        assert np.all(dl <= 1e-4 + 1e-5 * np.abs(lse_ref[ok])), f"{what}: lse"

@@ -128,9 +128,9 @@ def test_csa_decode_full_size(name):
     q_idx64, w64 = f64(P.q_idx), f64(P.w)
     sel = []
     for b in range(B):
-        s64 = method.index_scores(q_idx64[b], w64[b], keys64[b], wl.t0, m)
-        check_topk_rows(idx[b].cpu().numpy(), score[b].cpu().numpy(), s64, k)
-        sel.append(method.select_topk(s64, k)[0])
+        s64, vis = method.index_scores(q_idx64[b], w64[b], keys64[b], wl.t0, m)
+        check_topk_rows(idx[b].cpu().numpy(), score[b].cpu().numpy(), s64, vis, k)
+        sel.append(method.select_topk(s64, vis, k)[0])
     del keys64
     say("  indexer rows ok")
 
@@ -283,9 +283,9 @@ def test_csa_prefill_chunk_full_size():
     idx_h, score_h = idx[0].cpu().numpy(), score[0].cpu().numpy()
     sel = {}
     for i in rows:
-        s64 = method.index_scores(q_idx64[i:i + 1], w64[i:i + 1], keys64, wl.t0 + i, m)
-        check_topk_rows(idx_h[i:i + 1], score_h[i:i + 1], s64, k)
-        sel[i] = method.select_topk(s64, k)[0]
+        s64, vis = method.index_scores(q_idx64[i:i + 1], w64[i:i + 1], keys64, wl.t0 + i, m)
+        check_topk_rows(idx_h[i:i + 1], score_h[i:i + 1], s64, vis, k)
+        sel[i] = method.select_topk(s64, vis, k)[0]
     say("  indexer rows ok")
 
     # attention: sampled rows carry the oracle's selection, the others none

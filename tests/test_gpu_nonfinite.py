@@ -1,0 +1,233 @@
+"""GPU parity with NaN and infinite inputs (through the C ABI).
+
+The contract (include/csa.h): IEEE arithmetic; the indexer's rectifier keeps a
+NaN of either sign; a NaN score ranks above every number, ties to the lower
+index; visibility is positional.  In attention a NaN or infinity reaches the
+outputs of the (query, head) rows that use it; a skipped slot contributes
+nothing.  Each case runs the decode path (rows x slices), the prefill path, or
+one attention kernel, and compares with the oracle on the same inputs.  Every
+kernel loop is bounded by sizes alone, so none of these inputs can make a
+kernel run longer.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import compressed_attention_csa_amd as csa
+import inputgen
+from oracle import formats, method
+from parity_util import check_attention_nonfinite, check_topk_rows, f64, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+NAN = float("nan")
+INF = float("inf")
+
+
+def gen(name, shape, dtype, seed=0, std=1.0):
+    return inputgen.normal(name, shape, seed, dtype, std=std)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_index(q, w, kd, ks, t0, m, k):
+    B, T = q.shape[:2]
+    out_idx = torch.full((B, T, k), 12345, dtype=torch.int32, device=DEV)
+    out_score = torch.full((B, T, k), 5.0, dtype=torch.float32, device=DEV)
+    csa.csa_index_topk(q.to(DEV), None if w is None else w.to(DEV), kd, ks, t0, m, k, out_idx, out_score)
+    torch.cuda.synchronize()
+    return out_idx.cpu().numpy(), out_score.cpu().numpy()
+
+
+@pytest.mark.parametrize("kind", ["bf16", "e4m3"])
+def test_index_decode_nan_inf_keys(kind):
+    """Decode rows over 20000 entries (many slices): NaN key elements of both
+    signs (and a NaN fp8 code / scale), infinite key elements, a weight of -1
+    on one head (so some scores are -inf or NaN through inf - inf), and a query
+    row with a NaN element (every score NaN: the lowest indices win)."""
+    B, N, H_I, d_I, m, k = 3, 20000, 8, 64, 4, 256
+    say("index decode non-finite", kind)
+    q = gen("nf_q", (B, 1, H_I, d_I), "bf16", seed=1)
+    w = gen("nf_w", (B, 1, H_I), "f32", seed=2).abs()
+    w[1, 0, 3] = -1.0
+    q[2, 0, 5, 17] = NAN
+    r = gen("nf_k", (B, N, d_I), "f32", seed=3).numpy().astype(np.float64)
+    nan_rows = [5, 4097, 12345, 19999]
+    if kind == "bf16":
+        k64 = formats.round_to_bf16(r)
+        for b in range(B):
+            k64[b, nan_rows[0], 3] = NAN
+            k64[b, nan_rows[1], 60] = -NAN
+            k64[b, nan_rows[2], 0] = NAN
+            k64[b, 777, 9] = INF
+            k64[b, 15000, 9] = -INF
+            k64[b, 8000, :] = INF
+        kd, ks = to_dev_bf16(k64), None
+    else:
+        codes, scale, k64 = formats.e4m3_quantize_rows(r.astype(np.float32))
+        for b in range(B):
+            codes[b, nan_rows[0], 3] = 0x7F   # NaN code
+            codes[b, nan_rows[1], 60] = 0xFF  # NaN code, negative sign
+            scale[b, nan_rows[2]] = NAN       # NaN scale
+            scale[b, nan_rows[3]] = -NAN
+        k64 = formats.e4m3_decode(codes) * scale[..., None].astype(np.float64)
+        kd, ks = torch.from_numpy(codes).to(DEV), torch.from_numpy(scale).to(DEV)
+    idx, sc = run_index(q, w, kd, ks, 4 * N - 1, m, k)
+    for b in range(B):
+        scores, vis = method.index_scores(f64(q[b]), f64(w[b]), k64[b], 4 * N - 1, m)
+        check_topk_rows(idx[b], sc[b], scores, vis, k)
+        nan_ent = np.nonzero(np.isnan(scores[0, :N]))[0]
+        say(f"  b={b}: NaN scores {nan_ent.size}, -inf {int(np.isneginf(scores[0]).sum())}, "
+            f"+inf {int(np.isposinf(scores[0]).sum())}")
+        assert set(nan_ent[:k].tolist()) <= set(idx[b, 0].tolist())
+    assert np.all(np.sort(idx[2, 0]) == np.arange(k)), "a NaN query: every score ties as NaN"
+
+
+def test_index_prefill_nan_inf():
+    """Prefill rows (70 queries over 40000 entries: the sampled starting
+    threshold is in use): NaN keys on and off the sample grid, infinite key
+    elements, a query with a NaN element and one with a NaN weight."""
+    B, T, H_I, d_I, N, m, k = 1, 70, 8, 64, 40000, 4, 64
+    t0 = 4 * N - T
+    say("index prefill non-finite")
+    q = gen("nfp_q", (B, T, H_I, d_I), "bf16", seed=5)
+    q[0, 10, 2, 7] = NAN
+    w = gen("nfp_w", (B, T, H_I), "f32", seed=6)
+    w[0, 20, 4] = NAN
+    k64 = formats.round_to_bf16(gen("nfp_k", (B, N, d_I), "f32", seed=7).numpy().astype(np.float64))
+    k64[0, 64, 1] = NAN        # on the sample grid (stride 8 here)
+    k64[0, 1001, 2] = -NAN     # off it
+    k64[0, 39000, 0] = NAN     # visible to every query
+    k64[0, 5000, 11] = INF
+    k64[0, 23001, :] = -INF
+    idx, sc = run_index(q, w, to_dev_bf16(k64), None, t0, m, k)
+    scores, vis = method.index_scores(f64(q[0]), f64(w[0]), k64[0], t0, m)
+    check_topk_rows(idx[0], sc[0], scores, vis, k)
+    assert np.all(np.sort(idx[0, 10]) == np.arange(k)) and np.all(np.sort(idx[0, 20]) == np.arange(k))
+    for i in (0, 40, 69):
+        assert {64, 1001, 39000} <= set(idx[0, i].tolist())
+
+
+def _attend(hca, q, kc, vc, idx, kr, vr, t0, W, m, scale, H, d):
+    B, T = q.shape[:2]
+    out = torch.full((B, T, H, d), 9.0, dtype=torch.float32, device=DEV)
+    lse = torch.full((B, T, H), 9.0, device=DEV)
+    if hca:
+        csa.hca_attend(to_dev_bf16(q), to_dev_bf16(kc), to_dev_bf16(vc), m, to_dev_bf16(kr), to_dev_bf16(vr),
+                       t0, W, scale, out, lse)
+    else:
+        csa.csa_attend(to_dev_bf16(q), to_dev_bf16(kc), to_dev_bf16(vc), m, torch.from_numpy(idx).to(DEV),
+                       to_dev_bf16(kr), to_dev_bf16(vr), t0, W, scale, out, lse)
+    torch.cuda.synchronize()
+    return f64(out), f64(lse)
+
+
+def _bf16(name, shape, seed, std=1.0):
+    return f64(gen(name, shape, "bf16", seed=seed, std=std))
+
+
+@pytest.mark.parametrize("T", [1, 40], ids=["decode", "prefill"])
+def test_csa_attend_nan(T):
+    """CSA attention: NaN in one head of a query (head 0, whose values the
+    kernel's skipped slots once loaded), in a selected K row, in one column of
+    a selected V row, an infinity in a window row, and NaN rows nobody selects;
+    40 slots of every row are skipped (index -1)."""
+    B, H, d, N, m, k, W = 2, 64, 128, 3000, 4, 512, 128
+    t0 = 4 * N - T if T == 1 else 4 * N - 300
+    say("csa_attend non-finite T", T)
+    n_raw = t0 + T + 3
+    q = _bf16("nfa_q", (B, T, H, d), 11)
+    kc, vc = _bf16("nfa_kc", (B, N, d), 12, 0.6), _bf16("nfa_vc", (B, N, d), 13, 0.6)
+    kr, vr = _bf16("nfa_kr", (B, n_raw, d), 14), _bf16("nfa_vr", (B, n_raw, d), 15)
+    rng = np.random.default_rng(16)
+    idx = np.full((B, T, k), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(T):
+            c = min(N, (t0 + i + 1) // m)
+            idx[b, i, : k - 40] = rng.choice(c, k - 40, replace=False)
+    q[0, 0, 0, 3] = NAN
+    e_k, e_v = int(idx[1, 0, 5]), int(idx[0, 0, 7])
+    kc[1, e_k, 30] = NAN
+    vc[0, e_v, 77] = -NAN
+    unused = sorted(set(range(N)) - set(idx[0].ravel().tolist()))[:3]
+    for j in unused:
+        kc[0, j, :] = NAN
+        vc[0, j, :] = NAN
+    vr[1, t0 + T - 1, 5] = INF  # the newest position: in the window of the last query only
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _attend(False, q, kc, vc, idx, kr, vr, t0, W, m, scale, H, d)
+    for b in range(B):
+        o_ref, l_ref = method.csa_attend(q[b], kc[b], vc[b], idx[b], kr[b], vr[b], 0, t0, W, m, scale)
+        check_attention_nonfinite(o[b], lse[b], o_ref, l_ref, "bf16", what=f"csa T={T} b={b}")
+        say(f"  b={b}: rows with a non-finite element {int((~np.isfinite(o_ref)).any(-1).sum())} of {T * H}")
+    assert np.isnan(o[0, 0, 0]).all() and np.isfinite(o[0, 0, 1:, :77]).all()
+    assert np.isnan(o[1, 0]).all()
+
+
+@pytest.mark.parametrize("T", [1, 64], ids=["decode", "prefill-multi"])
+def test_hca_attend_nan(T):
+    """HCA attention, decode (split + merge) and the multi-token prefill kernel:
+    NaN in an old heavy entry's K (every token of sequence 0 sees it), NaN in a
+    head of the first token of a workgroup (whose values the kernel's out-of-range
+    slots once loaded), NaN in one V column of a heavy entry and of a window row.
+    In the multi-token kernel a non-finite row also reaches the tokens of the
+    same workgroup that share its tile without seeing it (documented), so those
+    rows are held only to the non-finite rule."""
+    B, H, d, Nh, m, W = 2, 64, 128, 60, 128, 128
+    QT = 2 * (8 // (H // 16))  # tokens per workgroup of the multi-token kernel
+    t0 = 128 * Nh - T if T == 1 else 128 * 40 + 10
+    say("hca_attend non-finite T", T)
+    n_raw = t0 + T + 3
+    q = _bf16("nfh_q", (B, T, H, d), 21)
+    kc, vc = _bf16("nfh_kc", (B, Nh, d), 22, 0.6), _bf16("nfh_vc", (B, Nh, d), 23, 0.6)
+    kr, vr = _bf16("nfh_kr", (B, n_raw, d), 24), _bf16("nfh_vr", (B, n_raw, d), 25)
+    kc[0, 3, 64] = NAN
+    tq = QT if T > 1 else 0
+    q[1, tq, 0, 1] = NAN
+    vc[1, 10, 50] = NAN
+    p = t0 + T // 2
+    vr[1, p, 2] = NAN
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _attend(True, q, kc, vc, None, kr, vr, t0, W, m, scale, H, d)
+    for b in range(B):
+        o_ref, l_ref = method.hca_attend(q[b], kc[b], vc[b], m, kr[b], vr[b], 0, t0, W, scale)
+        loose = np.zeros((T, H), dtype=bool)
+        if b == 1 and T > 1:
+            sees = np.array([(t0 + i) >= p > (t0 + i) - W for i in range(T)])
+            groups = np.arange(T) // QT
+            for gi in np.unique(groups[sees]):
+                loose[(groups == gi) & ~sees] = True
+        check_attention_nonfinite(o[b], lse[b], o_ref, l_ref, "bf16", what=f"hca T={T} b={b}", loose=loose)
+    assert np.isnan(o[0]).all()
+    assert np.isnan(o[1, tq, 0]).all() and np.isfinite(o[1, tq, 1:, 3:50]).all()
+
+
+def test_compress_e4m3_tiny_and_nonfinite_rows():
+    """The fp8 compressor on rows whose absmax quotient underflows (scale 1,
+    not a division by 0), rows with a NaN element (left out of the absmax,
+    coded NaN) and rows with an infinite element (scale inf): codes and scales
+    equal the oracle's quantiser bit for bit.  m = 1, so each entry is its row."""
+    say("compress e4m3 tiny / non-finite rows")
+    d = 16
+    rows = np.zeros((6, d), dtype=np.float32)
+    rows[0, :3] = [2.0 ** -149, -3 * 2.0 ** -149, 2.0 ** -148]
+    rows[1, :2] = [2.0 ** -126, -2.0 ** -130]
+    rows[2] = np.linspace(-3, 5, d)
+    rows[2, 4] = np.nan
+    rows[3] = np.linspace(-1, 1, d)
+    rows[3, 7] = np.inf
+    rows[4] = np.linspace(-7, 2, d)
+    x = torch.from_numpy(rows[None]).to(DEV)
+    z = torch.zeros(1, device=DEV)
+    out = torch.full((1, 6, d), 0x55, dtype=torch.uint8, device=DEV)
+    sc = torch.full((1, 6), 7.0, device=DEV)
+    csa.csa_compress(x, z, 1, out, sc)
+    torch.cuda.synchronize()
+    codes, scale, _ = formats.e4m3_quantize_rows(rows)
+    np.testing.assert_array_equal(out[0].cpu().numpy(), codes)
+    np.testing.assert_array_equal(sc[0].cpu().numpy(), scale)
+    assert scale[0] == 1.0 and scale[5] == 1.0

@@ -289,8 +289,8 @@ def test_index_topk(case):
     sc = out_score.cpu().numpy()
     swaps = 0
     for b in range(B):
-        scores = method.index_scores(f64(q[b]), None if w is None else f64(w[b]), k64[b], t0, m)
-        swaps += check_topk_rows(idx[b], sc[b], scores, k)
+        scores, vis = method.index_scores(f64(q[b]), None if w is None else f64(w[b]), k64[b], t0, m)
+        swaps += check_topk_rows(idx[b], sc[b], scores, vis, k)
     say("  in-band swaps:", swaps)
 
 
@@ -317,9 +317,9 @@ def test_index_topk_bf16_selector(case):
     idx, sc = out_idx.cpu().numpy(), out_score.cpu().numpy()
     total = hits = 0
     for b in range(B):
-        scores = method.index_scores(f64(q[b]), None if w is None else f64(w[b]), k64[b], t0, m)
+        scores, vis = method.index_scores(f64(q[b]), None if w is None else f64(w[b]), k64[b], t0, m)
         for i in range(T):
-            kk, h = check_bf16_selection_row(idx[b, i], sc[b, i], scores[i], k)
+            kk, h = check_bf16_selection_row(idx[b, i], sc[b, i], scores[i], vis[i], k)
             total, hits = total + kk, hits + h
     say(f"  recall against the exact top-k: {hits / max(total, 1):.4f}")
     assert hits >= 0.95 * total
@@ -353,8 +353,8 @@ def test_index_topk_bf16_selector_edges():
     np.testing.assert_array_equal(np.sort(got[:1500]), np.arange(1500))
     assert (got[1500:] == -1).all()
     np.testing.assert_array_equal(np.sort(near[0, 0].cpu().numpy()), np.arange(64))
-    scores = method.index_scores(qq[0], None, k64, 4 * 3000 - 1, 4)
-    check_bf16_selection_row(near[0, 0].cpu().numpy(), None, scores[0], 64)
+    scores, vis = method.index_scores(qq[0], None, k64, 4 * 3000 - 1, 4)
+    check_bf16_selection_row(near[0, 0].cpu().numpy(), None, scores[0], vis[0], 64)
 
 
 def test_index_topk_exact_ties_go_to_lower_index():
@@ -365,8 +365,8 @@ def test_index_topk_exact_ties_go_to_lower_index():
     out = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
     csa.csa_index_topk(q.to(DEV), None, keys.to(DEV).contiguous(), None, 4 * N - 1, 4, k, out)
     torch.cuda.synchronize()
-    scores = method.index_scores(f64(q[0]), None, f64(keys[0]), 4 * N - 1, 4)
-    exp = np.sort(method.select_topk(scores, k)[0])
+    scores, vis = method.index_scores(f64(q[0]), None, f64(keys[0]), 4 * N - 1, 4)
+    exp = np.sort(method.select_topk(scores, vis, k)[0])
     np.testing.assert_array_equal(np.sort(out[0, 0].cpu().numpy()), exp)
 
 
@@ -391,8 +391,8 @@ def test_index_topk_winners_concentrated_in_few_slices(kind):
     csa.csa_index_topk(q.to(DEV), w.to(DEV), kd, ks, 4 * N - 1, 4, k, out, sc)
     torch.cuda.synchronize()
     for b in range(B):
-        scores = method.index_scores(f64(q[b]), f64(w[b]), k64[b], 4 * N - 1, 4)
-        check_topk_rows(out[b].cpu().numpy(), sc[b].cpu().numpy(), scores, k)
+        scores, vis = method.index_scores(f64(q[b]), f64(w[b]), k64[b], 4 * N - 1, 4)
+        check_topk_rows(out[b].cpu().numpy(), sc[b].cpu().numpy(), scores, vis, k)
         assert (out[b, 0].cpu().numpy() >= 5000).mean() > 0.9
 
 
@@ -424,9 +424,9 @@ def test_index_topk_prefill_sampled_threshold_falls_back():
     say("index_topk prefill, winners on the sample grid")
     csa.csa_index_topk(q.to(DEV), None, keys.to(DEV), None, t0, m, k, out_idx, out_score)
     torch.cuda.synchronize()
-    scores = method.index_scores(f64(q[0]), None, f64(keys[0]), t0, m)
+    scores, vis = method.index_scores(f64(q[0]), None, f64(keys[0]), t0, m)
     idx = out_idx[0].cpu().numpy()
-    check_topk_rows(idx, out_score[0].cpu().numpy(), scores, k)
+    check_topk_rows(idx, out_score[0].cpu().numpy(), scores, vis, k)
     assert np.all(idx % 32 == 0), "winners are the entries on the sample grid"
 
 
@@ -455,7 +455,7 @@ def test_index_topk_every_e4m3_code_scores_exactly(d_I):
     torch.cuda.synchronize()
     stored = formats.e4m3_decode(codes) * scale[:, :, None]
     for b in range(2):
-        ref = method.index_scores(f64(q[b]), None, stored[b], 4 * N - 1, m)[0]
+        ref = method.index_scores(f64(q[b]), None, stored[b], 4 * N - 1, m)[0][0]
         idx = out_idx[b, 0].cpu().numpy()
         np.testing.assert_array_equal(np.sort(idx), np.arange(N))
         np.testing.assert_array_equal(out_score[b, 0].cpu().numpy().astype(np.float64), ref[idx])
@@ -794,7 +794,7 @@ def test_tiny_prefill_f32_end_to_end():
                      for i in range(wl.T)])
     mism = np.nonzero(~same)[0]
     for i in mism:
-        ok, why, _ = method.topk_is_valid(g[i], ref["scores"][i], wl.k)
+        ok, why, _ = method.topk_is_valid(g[i], ref["scores"][i], ref["visible"][i], wl.k)
         assert ok, f"row {i}: {why}"
     say("  rows with an in-band set difference:", len(mism))
     assert len(mism) <= wl.T // 100

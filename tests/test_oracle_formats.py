@@ -92,3 +92,28 @@ def test_e4m3_row_quantiser_invariants(seed):
     assert np.all(err <= bound)
     # scale is the binary32 quotient of the row absmax by 448
     np.testing.assert_array_equal(scale[nz], np.max(np.abs(r[nz]), axis=1) / np.float32(448.0))
+
+
+def test_e4m3_row_quantiser_tiny_and_nonfinite_rows():
+    """Rows whose absmax quotient underflows take scale 1 (like an all-zero row)
+    instead of dividing by 0; a NaN element is left out of the absmax and gets
+    the NaN code; an infinite element makes its whole stored row NaN."""
+    sub = np.float32(2.0 ** -149)
+    r = np.array([
+        [sub, -3 * sub, 0.0, 0.0],           # absmax 3 * 2^-149: 3 * 2^-149 / 448 underflows to 0
+        [2.0 ** -120, 1.0, -2.0, 0.5],       # ordinary row
+        [np.nan, 1.0, -448.0 * 2, 0.25],     # NaN element
+        [np.inf, 1.0, 0.0, -1.0],            # infinite element
+    ], dtype=np.float32)
+    codes, scale, stored = formats.e4m3_quantize_rows(r)
+    assert scale[0] == 1.0 and np.all(codes[0] & 0x7F == 0) and np.all(np.isfinite(stored[0]))
+    assert scale[1] == np.float32(2.0) / np.float32(448.0)
+    assert scale[2] == np.float32(896.0) / np.float32(448.0) == 2.0
+    assert codes[2, 0] & 0x7F == 0x7F and np.isnan(stored[2, 0]) and np.all(np.isfinite(stored[2, 1:]))
+    np.testing.assert_array_equal(stored[2, 1:], [1.0, -896.0, 0.25])
+    assert np.isposinf(scale[3]) and np.all(np.isnan(stored[3]))
+    # torch's own e4m3 conversion agrees on the codes of the finite rows
+    y = (r[:3] / scale[:3, None]).astype(np.float32)
+    fin = ~np.isnan(y)
+    exp = torch.from_numpy(np.where(fin, y, 0)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes[:3][fin], exp[fin])

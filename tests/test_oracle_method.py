@@ -192,7 +192,8 @@ def test_single_head_unit_weight_positive_dots_is_a_matrix_product():
     rng = np.random.default_rng(12)
     q = np.abs(rng.standard_normal((9, 1, 16)))
     k = np.abs(rng.standard_normal((30, 16)))
-    s = method.index_scores(q, None, k, t0=119, m=4)  # position >= 119: all 30 visible
+    s, vis = method.index_scores(q, None, k, t0=119, m=4)  # position >= 119: all 30 visible
+    assert (vis == 30).all()
     np.testing.assert_allclose(s, q[:, 0, :] @ k.T, rtol=1e-14)
 
 
@@ -201,33 +202,38 @@ def test_scores_sign_scaling_and_zero_head():
     q = rng.standard_normal((5, 3, 8))
     k = rng.standard_normal((20, 8))
     w = rng.standard_normal((5, 3))
-    s = method.index_scores(q, w, k, 100, 4)
-    np.testing.assert_allclose(method.index_scores(q, 2.5 * w, k, 100, 4), 2.5 * s, rtol=1e-14)
-    np.testing.assert_allclose(method.index_scores(0.5 * q, w, k, 100, 4), 0.5 * s, rtol=1e-14)
+    s = method.index_scores(q, w, k, 100, 4)[0]
+    np.testing.assert_allclose(method.index_scores(q, 2.5 * w, k, 100, 4)[0], 2.5 * s, rtol=1e-14)
+    np.testing.assert_allclose(method.index_scores(0.5 * q, w, k, 100, 4)[0], 0.5 * s, rtol=1e-14)
     # one head with w = -1: score = -ReLU(q.k)
-    s1 = method.index_scores(q[:, :1], -np.ones((5, 1)), k, 100, 4)
+    s1 = method.index_scores(q[:, :1], -np.ones((5, 1)), k, 100, 4)[0]
     np.testing.assert_allclose(s1, -np.maximum(q[:, 0] @ k.T, 0), rtol=1e-14)
     # a head with zero weight contributes nothing
     w0 = w.copy()
     w0[:, 2] = 0
-    np.testing.assert_allclose(method.index_scores(q, w0, k, 100, 4),
-                               method.index_scores(q[:, :2], w[:, :2], k, 100, 4), rtol=1e-14)
+    np.testing.assert_allclose(method.index_scores(q, w0, k, 100, 4)[0],
+                               method.index_scores(q[:, :2], w[:, :2], k, 100, 4)[0], rtol=1e-14)
 
 
 def test_scores_visibility_mask():
     q = rnd(14, 6, 2, 4)
     k = rnd(15, 10, 4)
-    s = method.index_scores(q, None, k, t0=2, m=4)  # positions 2..7
+    s, vis = method.index_scores(q, None, k, t0=2, m=4)  # positions 2..7
     for i in range(6):
         c = (2 + i + 1) // 4
-        assert np.all(np.isfinite(s[i, :c])) and np.all(np.isneginf(s[i, c:]))
+        assert vis[i] == c
+        assert np.all(np.isfinite(s[i, :c])) and np.all(np.isnan(s[i, c:]))
+    # the selection never reaches past the visible count, whatever the other values hold
+    sel = method.select_topk(np.zeros((6, 10)), vis, 3)
+    for i in range(6):
+        assert list(sel[i]) == list(range(min(3, vis[i]))) + [-1] * (3 - min(3, vis[i]))
 
 
 def test_scores_match_brute_force():
     q = rnd(16, 4, 3, 5)
     k = rnd(17, 12, 5)
     w = rnd(18, 4, 3)
-    s = method.index_scores(q, w, k, t0=47, m=4)  # (47+1)//4 = 12: all entries visible
+    s, _ = method.index_scores(q, w, k, t0=47, m=4)  # (47+1)//4 = 12: all entries visible
     for i in range(4):
         for j in range(12):
             assert math.isclose(s[i, j], brute.score(q[i].tolist(), w[i].tolist(), k[j].tolist()),
@@ -239,17 +245,17 @@ def test_scores_match_brute_force():
 
 def test_topk_matches_torch_topk_on_distinct_scores():
     s = rnd(19, 7, 300)
-    got = method.select_topk(s, 25)
+    got = method.select_topk(s, [300] * 7, 25)
     exp = torch.topk(torch.from_numpy(s), 25, dim=1).indices.numpy()
     for i in range(7):
         assert set(got[i]) == set(exp[i])
 
 
 def test_topk_short_list_pads_and_ties_go_low():
-    s = np.full((2, 10), -np.inf)
+    s = np.full((2, 10), np.nan)
     s[0, :6] = [1.0, 3.0, 3.0, 2.0, 3.0, 0.5]
     s[1, :3] = [0.0, 0.0, 0.0]
-    got = method.select_topk(s, 4)
+    got = method.select_topk(s, [6, 3], 4)
     assert list(got[0]) == [1, 2, 4, 3]  # three-way tie at 3.0 ordered by index
     assert list(got[1]) == [0, 1, 2, -1]
 
@@ -257,8 +263,8 @@ def test_topk_short_list_pads_and_ties_go_low():
 def test_topk_permutation_equivariance():
     s = rnd(20, 3, 50)
     perm = np.random.default_rng(21).permutation(50)
-    a = method.select_topk(s, 10)
-    b = method.select_topk(s[:, perm], 10)
+    a = method.select_topk(s, [50] * 3, 10)
+    b = method.select_topk(s[:, perm], [50] * 3, 10)
     for i in range(3):
         assert set(perm[b[i]]) == set(a[i])
 
@@ -268,47 +274,164 @@ def test_bf16_selector_hand_example():
     round to 1.0, 1.004 and 1.006 to 1.0078125; the ties at 1.0 go to the lowest
     index, so the approximate top-4 takes entry 0 where the exact one takes 1."""
     s = np.array([[1.0, 1.003, 0.999, 2.0, 1.004, 1.006]])
-    assert list(method.select_topk_bf16(s, 4)[0]) == [3, 4, 5, 0]
-    assert list(method.select_topk(s, 4)[0]) == [3, 5, 4, 1]
+    assert list(method.select_topk_bf16(s, [6], 4)[0]) == [3, 4, 5, 0]
+    assert list(method.select_topk(s, [6], 4)[0]) == [3, 5, 4, 1]
 
 
 def test_bf16_selector_rounds_ties_to_even():
     # 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd last bit) and 1 + 2^-6 (even):
     # it rounds up and ties entry 1 (just below 1 + 2^-6), so index 0 wins.
     s = np.array([[1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6 - 2.0 ** -20]])
-    assert list(method.select_topk_bf16(s, 1)[0]) == [0]
+    assert list(method.select_topk_bf16(s, [2], 1)[0]) == [0]
     # 1 + 2^-8 lies halfway between 1 (even) and 1 + 2^-7: it rounds down.
     s = np.array([[1 + 2.0 ** -8, 1 + 2.0 ** -7]])
-    assert list(method.select_topk_bf16(s, 1)[0]) == [1]
+    assert list(method.select_topk_bf16(s, [2], 1)[0]) == [1]
 
 
 def test_bf16_selector_equals_exact_on_bf16_values_and_keeps_invisible_out():
     s = formats.round_to_bf16(rnd(23, 4, 300))
-    s[:, 250:] = -np.inf
-    np.testing.assert_array_equal(method.select_topk_bf16(s, 40), method.select_topk(s, 40))
-    assert (method.select_topk_bf16(s, 260)[:, 250:] == -1).all()
+    s[:, 250:] = np.nan  # not visible: never selected, even though NaN would rank first
+    vis = [250] * 4
+    np.testing.assert_array_equal(method.select_topk_bf16(s, vis, 40), method.select_topk(s, vis, 40))
+    assert (method.select_topk_bf16(s, vis, 260)[:, 250:] == -1).all()
 
 
 def test_topk_validity_checker_accepts_oracle_and_rejects_planted_swap():
     s = rnd(22, 1, 200)[0]
-    sel = method.select_topk(s[None], 20)[0]
-    ok, _, swaps = method.topk_is_valid(sel, s, 20)
+    sel = method.select_topk(s[None], [200], 20)[0]
+    ok, _, swaps = method.topk_is_valid(sel, s, 200, 20)
     assert ok and swaps == 0
     order = np.argsort(-s)
     bad = sel.copy()
     bad[np.where(bad == order[19])[0][0]] = order[40]  # swap the 20th for the 41st
-    assert not method.topk_is_valid(bad, s, 20)[0]
-    assert not method.topk_is_valid(sel[:19], s, 20)[0]
+    assert not method.topk_is_valid(bad, s, 200, 20)[0]
+    assert not method.topk_is_valid(sel[:19], s, 200, 20)[0]
     dup = sel.copy()
     dup[0] = dup[1]
-    assert not method.topk_is_valid(dup, s, 20)[0]
+    assert not method.topk_is_valid(dup, s, 200, 20)[0]
+    # a member past the visible count is rejected
+    assert not method.topk_is_valid(sel, s, int(sel.max()), 20)[0]
     # members inside the tie band are accepted
     s2 = s.copy()
     s2[order[20]] = s2[order[19]] * (1 - 1e-7)
     swapped = sel.copy()
     swapped[np.where(swapped == order[19])[0][0]] = order[20]
-    ok, _, swaps = method.topk_is_valid(swapped, s2, 20)
+    ok, _, swaps = method.topk_is_valid(swapped, s2, 200, 20)
     assert ok and swaps == 1
+
+
+# ----------------------------------------------------------------------------- non-finite inputs
+#
+# Contract: IEEE arithmetic throughout; the rectifier propagates NaN of either
+# sign; a NaN score ranks above every number (+inf included), ties by lower
+# index; visibility is positional only, never inferred from a score's value.
+
+
+def test_topk_order_with_nan_and_infinities_equals_torch_stable_sort():
+    """torch's CPU sort puts NaN above +inf (descending) and keeps equal keys in
+    index order when stable: the selection's total order, from a library."""
+    rng = np.random.default_rng(31)
+    for trial in range(20):
+        s = rng.standard_normal((1, 64))
+        s[0, rng.choice(64, 5, replace=False)] = np.nan
+        s[0, rng.choice(64, 3, replace=False)] = np.inf
+        s[0, rng.choice(64, 3, replace=False)] = -np.inf
+        s[0, 10:14] = s[0, 9]  # a run of equal finite values (ties by index)
+        k = int(rng.integers(1, 64))
+        got = method.select_topk(s, [64], k)[0]
+        exp = torch.sort(torch.from_numpy(s[0]), descending=True, stable=True).indices[:k].numpy()
+        np.testing.assert_array_equal(got, exp)
+
+
+def test_scores_with_nan_and_infinities_follow_ieee():
+    q = np.ones((1, 2, 4))
+    k = np.ones((6, 4))
+    k[1, 2] = np.nan          # NaN key element: NaN score whatever the weights
+    k[2, 0] = -np.nan         # NaN of negative sign: still NaN (the rectifier keeps it)
+    k[3, 1] = np.inf          # dot +inf in both heads
+    k[4, :] = -1.0            # dots -4: rectified to 0
+    w = np.array([[1.0, 0.0]])  # a zero weight times NaN or inf is still NaN
+    s, vis = method.index_scores(q, w, k, t0=23, m=4)
+    assert vis[0] == 6
+    assert np.isnan(s[0, 1]) and np.isnan(s[0, 2])
+    assert np.isnan(s[0, 3])  # 1 * inf + 0 * inf = inf + NaN
+    assert s[0, 4] == 0.0 and s[0, 0] == 4.0 and s[0, 5] == 4.0
+    w2 = np.array([[1.0, 1.0]])
+    s2, _ = method.index_scores(q, w2, k, t0=23, m=4)
+    assert s2[0, 3] == np.inf
+    w3 = np.array([[1.0, -1.0]])
+    s3, _ = method.index_scores(q, w3, k, t0=23, m=4)
+    assert np.isnan(s3[0, 3])  # inf - inf
+    w4 = np.array([[-1.0, -1.0]])
+    s4, _ = method.index_scores(q, w4, k, t0=23, m=4)
+    assert s4[0, 3] == -np.inf and s4[0, 0] == -8.0
+    # a NaN in one head of the query, or in a weight, makes every score of that query NaN
+    qn = q.copy()
+    qn[0, 1, 3] = np.nan
+    assert np.isnan(method.index_scores(qn, w2, k, 23, 4)[0]).all()
+    assert np.isnan(method.index_scores(q, np.array([[np.nan, 1.0]]), k, 23, 4)[0]).all()
+
+
+def test_nan_scores_are_selected_first_and_reported_valid():
+    s = np.array([[0.5, np.nan, 2.0, -np.inf, np.nan, np.inf, 1.0, np.nan]])
+    assert list(method.select_topk(s, [8], 5)[0]) == [1, 4, 7, 5, 2]
+    assert list(method.select_topk(s, [8], 2)[0]) == [1, 4]  # NaN ties: lower index first
+    assert list(method.select_topk(s, [5], 8)[0]) == [1, 4, 2, 0, 3, -1, -1, -1]
+    row = s[0]
+    assert method.topk_is_valid([1, 4, 7, 5, 2], row, 8, 5)[0]
+    assert method.topk_is_valid([2, 5, 7, 4, 1], row, 8, 5)[0]  # any order
+    assert not method.topk_is_valid([1, 4, 5, 2, 6], row, 8, 5)[0]  # a NaN entry left out
+    assert not method.topk_is_valid([1, 7], row, 8, 2)[0]  # NaN ties go to the lower index
+    assert method.topk_is_valid([1, 4], row, 8, 2)[0]
+    # equal infinities tie: either one may be chosen
+    s5 = np.array([np.inf, 1.0, np.inf, 0.0])
+    assert method.topk_is_valid([0], s5, 4, 1)[0] and method.topk_is_valid([2], s5, 4, 1)[0]
+    assert not method.topk_is_valid([1], s5, 4, 1)[0]
+    # -inf scores are visible entries like any other
+    s6 = np.array([-np.inf, -np.inf, 3.0])
+    assert list(method.select_topk(s6[None], [3], 3)[0]) == [2, 0, 1]
+    assert method.topk_is_valid([2, 1, 0], s6, 3, 3)[0]
+
+
+def test_attention_propagates_nan_to_exactly_the_rows_it_touches():
+    rng = np.random.default_rng(32)
+    H, d, N, W, m = 4, 8, 10, 3, 4
+    q = rng.standard_normal((2, H, d))
+    kc, vc = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    kr, vr = rng.standard_normal((60, d)), rng.standard_normal((60, d))
+    idx = np.array([[0, 2, 5], [1, 3, 7]])
+    t0 = 40
+    base, _ = method.csa_attend(q, kc, vc, idx, kr, vr, 0, t0, W, m, 0.3)
+    assert np.isfinite(base).all()
+    qn = q.copy()
+    qn[0, 2, 5] = np.nan  # query 0, head 2
+    o, lse = method.csa_attend(qn, kc, vc, idx, kr, vr, 0, t0, W, m, 0.3)
+    assert np.isnan(o[0, 2]).all() and np.isnan(lse[0, 2])
+    mask = np.ones_like(o, dtype=bool)
+    mask[0, 2] = False
+    np.testing.assert_array_equal(o[mask], base[mask])
+    kn = kc.copy()
+    kn[5, 1] = np.nan  # entry 5: selected by query 0 only
+    o, lse = method.csa_attend(q, kn, vc, idx, kr, vr, 0, t0, W, m, 0.3)
+    assert np.isnan(o[0]).all() and np.isnan(lse[0]).all()
+    np.testing.assert_array_equal(o[1], base[1])
+    vn = vc.copy()
+    vn[7, 6] = -np.nan  # entry 7, column 6: selected by query 1 only
+    o, _ = method.csa_attend(q, kc, vn, idx, kr, vr, 0, t0, W, m, 0.3)
+    assert np.isnan(o[1, :, 6]).all()
+    cols = np.arange(d) != 6
+    np.testing.assert_array_equal(o[1][:, cols], base[1][:, cols])
+    np.testing.assert_array_equal(o[0], base[0])
+    vi = vc.copy()
+    vi[2, 0] = np.inf  # entry 2 (query 0), column 0: a positive weight times inf
+    o, _ = method.csa_attend(q, kc, vi, idx, kr, vr, 0, t0, W, m, 0.3)
+    assert np.isposinf(o[0, :, 0]).all()
+    np.testing.assert_array_equal(o[1], base[1])
+    # an unselected or invisible entry's NaN reaches nothing
+    kn2 = kc.copy()
+    kn2[9] = np.nan
+    o, _ = method.csa_attend(q, kn2, vc, idx, kr, vr, 0, t0, W, m, 0.3)
+    np.testing.assert_array_equal(o, base)
 
 
 # ----------------------------------------------------------------------------- attention
