@@ -1448,7 +1448,6 @@ static bool launch_hca_multi(const AttendArgs& a) {
 
 template <int D>
 static bool hca_multi(const AttendArgs& a) {
-  if (a.H <= 64) return launch_hca_multi<D, 8, 2>(a);
   return launch_hca_multi<D, 8, 2>(a);
 }
 

@@ -12,10 +12,12 @@
 // that all ranks are distinct.
 //   * A row with a single slice is finished by its WG: an LDS radix select
 //     finds the threshold of the kk best and the winners are written.
-//   * A longer row: every WG writes its exact local top-K_loc (K_loc about 4x
-//     the slice's expected share of the row's winners) plus a certificate,
-//     the threshold below which it dropped entries.  The last WG of the row
-//     to arrive radix-selects the row's kk best among all candidates.  A slice
+//   * A longer row: every WG writes its exact local top-K_loc in decreasing
+//     order (K_loc: the slice's expected share of the row's winners plus four
+//     standard deviations, and enough for the slices together to hold kk when
+//     the last one is short) plus a certificate, the key below which it
+//     dropped entries.  The last WG of the row to arrive loads every list and
+//     certificate in one batch and radix-selects the row's kk best.  A slice
 //     whose certificate lies above that threshold may have dropped a winner;
 //     the last WG then rescores exactly those slices and adds the dropped
 //     entries above the threshold before selecting again, so the result is
@@ -66,7 +68,15 @@ __device__ __forceinline__ RowInfo row_info(const IndexArgs& a, const IndexPlan&
   const int64_t share = div64(ri.kk + ri.S - 1, ri.S);
   int64_t sd = 1;
   while (sd * sd < share) ++sd;
-  int64_t kl = ((share + 4 * sd + 4 + 7) / 8) * 8;
+  int64_t kl = share + 4 * sd + 4;
+  // Every slice lists at least min(kl, its size) entries; together they must
+  // reach kk even when the last slice is short.
+  if (ri.S > 1) {
+    const int64_t last_n = ri.c - (ri.S - 1) * p.slice;
+    const int64_t need = div64(ri.kk - (last_n < ri.kk ? last_n : ri.kk) + ri.S - 2, ri.S - 1);
+    if (kl < need) kl = need;
+  }
+  kl = ((kl + 7) / 8) * 8;
   if (kl < 16) kl = 16;
   if (kl > p.slice) kl = p.slice;
   ri.kloc = kl;
@@ -426,6 +436,7 @@ __device__ __forceinline__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t
   if (uint32_t(tid) < in_digit) {
     const uint64_t key = S.list[tid];
     int64_t gt = 0;
+#pragma unroll 8
     for (uint32_t j = 0; j < in_digit; ++j) gt += S.list[j] > key;
     if (gt == need - 1) S.res = key;
   }
@@ -463,22 +474,19 @@ __device__ uint64_t select_get(int64_t n, int64_t need, Get get, uint32_t* hist,
   return prefix;
 }
 
-// The same threshold when `need` is small next to the key count.  In every
-// wave, the ceil(need/4)-th largest of the lanes' maxima is found by ranking
-// the 64 maxima against each other; the smallest of those four values is a
-// lower bound of T (need distinct threads hold a key at or above it).  The
-// keys at or above it, usually a few more than need, are then ranked exactly
-// against each other in LDS.  Falls back to select_rel when more than
-// one key per thread passes the bound.
-// scratch: 2 * kThreads uint64 of LDS, free on entry.
+// A lower bound of the need-th largest key, found without ranking the keys:
+// in every wave, the ceil(need/4)-th largest of the lanes' maxima (the 64
+// maxima ranked against each other in LDS); the smallest of the four is the
+// bound (need distinct threads hold a key at or above it).  Returns 0 (no
+// bound) when a wave has fewer non-empty lanes than its share, or when need
+// exceeds 4 * 64.  scratch: kThreads uint64 of LDS, free on entry.
 template <int KPT>
-__device__ __forceinline__ uint64_t select_small(const uint64_t (&v)[KPT], int64_t need, uint64_t* scratch, uint32_t* hist,
-                                 SelLds& S) {
+__device__ __forceinline__ uint64_t lane_max_bound(const uint64_t (&v)[KPT], int64_t need, uint64_t* scratch,
+                                                   SelLds& S) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int jw = int((need + kWaves - 1) / kWaves);  // share of each wave
-  if (jw > kWave) return select_rel(v, need, hist, S);
+  if (jw > kWave) return 0ull;
   uint64_t* tmax = scratch;
-  uint64_t* cand = scratch + kThreads;
   uint64_t mx = 0;
 #pragma unroll
   for (int u = 0; u < KPT; ++u) mx = v[u] > mx ? v[u] : mx;
@@ -488,6 +496,7 @@ __device__ __forceinline__ uint64_t select_small(const uint64_t (&v)[KPT], int64
   if (mx != 0) {
     const uint64_t* wt = tmax + wid * kWave;
     int above = 0;
+#pragma unroll
     for (int t = 0; t < kWave; t += 2) {
       const uint4 w = *reinterpret_cast<const uint4*>(&wt[t]);
       above += ((uint64_t(w.y) << 32 | w.x) > mx) + ((uint64_t(w.w) << 32 | w.z) > mx);
@@ -498,29 +507,8 @@ __device__ __forceinline__ uint64_t select_small(const uint64_t (&v)[KPT], int64
   uint64_t B = S.wb[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) B = S.wb[w] < B ? S.wb[w] : B;
-  int cnt = 0;
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) cnt += (v[u] != 0 && v[u] >= B) ? 1 : 0;
-  const uint32_t inc = block_inclusive_sum(uint32_t(cnt), S.scan);
-  if (tid == kThreads - 1) S.misc[3] = inc;
   __syncthreads();
-  const uint32_t m = S.misc[3];
-  if (m > uint32_t(kThreads)) return select_rel(v, need, hist, S);
-  uint32_t pos = inc - uint32_t(cnt);
-#pragma unroll
-  for (int u = 0; u < KPT; ++u)
-    if (v[u] != 0 && v[u] >= B) cand[pos++] = v[u];
-  __syncthreads();
-  if (uint32_t(tid) < m) {
-    const uint64_t key = cand[tid];
-    int above = 0;
-    for (uint32_t j = 0; j < m; ++j) above += cand[j] > key;
-    if (above == need - 1) S.res = key;
-  }
-  __syncthreads();
-  const uint64_t T = S.res;
-  __syncthreads();
-  return T;
+  return B;
 }
 
 __device__ __forceinline__ void write_out(const IndexArgs& a, int64_t r, int64_t slot, uint64_t v) {
@@ -546,6 +534,49 @@ __device__ __forceinline__ void emit_regs(const uint64_t (&v)[KPT], uint64_t T, 
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
     if (v[u] != 0 && v[u] >= T) dst(pos++, v[u]);
+}
+
+// Exact top-kl of a slice's keys (kl < number of keys), written to
+// dst[0 .. kl) in decreasing order with device-scope stores; returns the
+// kl-th key: every key not written ranks below it.  The keys at or above
+// lane_max_bound (usually a few more than kl) are ranked exactly against each
+// other in LDS, and each writes itself at its rank; when more than kThreads
+// keys reach the bound, a radix select finds the threshold instead and the
+// winners are written in thread order.
+template <int KPT>
+__device__ uint64_t local_topk(const uint64_t (&v)[KPT], int kl, uint64_t* dst, uint64_t* scratch, uint32_t* hist,
+                               SelLds& S) {
+  const int tid = threadIdx.x;
+  const uint64_t B = lane_max_bound(v, kl, scratch, S);
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) cnt += (v[u] != 0 && v[u] >= B) ? 1 : 0;
+  const uint32_t inc = block_inclusive_sum(uint32_t(cnt), S.scan);
+  if (tid == kThreads - 1) S.misc[3] = inc;
+  __syncthreads();
+  const uint32_t m = S.misc[3];
+  if (m > uint32_t(kThreads)) {
+    const uint64_t T = select_rel(v, kl, hist, S);
+    emit_regs(v, T, 0, [&](int64_t pos, uint64_t val) { store_dev(&dst[pos], val); }, S.scan);
+    return T;
+  }
+  uint32_t pos = inc - uint32_t(cnt);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (v[u] != 0 && v[u] >= B) S.list[pos++] = v[u];
+  __syncthreads();
+  if (uint32_t(tid) < m) {
+    const uint64_t key = S.list[tid];
+    int rank = 0;
+#pragma unroll 8
+    for (uint32_t j = 0; j < m; ++j) rank += S.list[j] > key;
+    if (rank < kl) store_dev(&dst[rank], key);
+    if (rank == kl - 1) S.res = key;
+  }
+  __syncthreads();
+  const uint64_t T = S.res;
+  __syncthreads();
+  return T;
 }
 
 template <typename Get, typename Dst>
@@ -608,28 +639,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     return;
   }
 
-  // ---- several slices: exact local top-kloc + certificate, handed over with
-  // device-scope stores.
+  // ---- several slices.  Each hands over its exact local top-kloc, in
+  // decreasing order, and a certificate: every entry of the slice left off
+  // the list ranks below the certificate.  Lists are dense (kloc slots per
+  // slice; a short slice pads with zeros) and written with device-scope
+  // stores.
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
   RowCtrl* ctrl = reinterpret_cast<RowCtrl*>(ws + kIndexCtrlOff) + lr;
-  uint64_t* cand = reinterpret_cast<uint64_t*>(ws + p.off_cand) + lr * a.N_alloc;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(ws + p.off_cand) + lr * p.cand_row;
   uint64_t* tau = reinterpret_cast<uint64_t*>(ws + p.off_tau) + lr * p.slices;
   uint64_t* over = reinterpret_cast<uint64_t*>(ws + p.off_over) + lr * a.N_alloc;
-  const int64_t kl = n < ri.kloc ? n : ri.kloc;
-  const uint64_t Ts =
-      (n > kl) ? select_small(v, kl, reinterpret_cast<uint64_t*>(L.keys), L.keys, L.sel) : 1ull;
-  uint64_t* my_cand = cand + s * ri.kloc;
-  emit_regs(v, Ts, 0, [&](int64_t pos, uint64_t val) { store_dev(&my_cand[pos], val); }, L.sel.scan);
-  if (tid == 0) store_dev(&tau[s], uint64_t(n > kl ? Ts : 0ull));  // dropped entries are all below it
+  const int kl = int(ri.kloc);
+  uint64_t* my_cand = cand + s * kl;
+  uint64_t cert = 0;  // 0: the whole slice is listed
+  if (n > kl) {
+    cert = local_topk(v, kl, my_cand, reinterpret_cast<uint64_t*>(L.keys), L.keys, L.sel);
+  } else {
+    emit_regs(v, 1ull, 0, [&](int64_t pos, uint64_t val) { store_dev(&my_cand[pos], val); }, L.sel.scan);
+    for (int64_t x = n + tid; x < kl; x += kThreads) store_dev(&my_cand[x], uint64_t(0));
+  }
+  if (tid == 0) store_dev(&tau[s], cert);
   if (!arrive_last(&ctrl->arrive, uint32_t(ri.S), L.flag)) return;
 
-  // ---- last WG of the row.  Slice x's candidates sit at cand[x*kloc ...]; every
-  // slice but the last holds exactly kloc of them.
-  const int64_t last_n = ri.c - (ri.S - 1) * p.slice;
-  const int64_t total = (ri.S - 1) * ri.kloc + (last_n < ri.kloc ? last_n : ri.kloc);
+  // ---- last WG of the row: the lists of every slice (S * kloc slots in
+  // element order, zeros for the padding of a short slice) and the
+  // certificates, loaded in one batch, then the exact selection of the kk best.
+  const int64_t total = ri.S * int64_t(kl);
   auto get_c = [&](int64_t g) { return load_dev(&cand[g]); };
   const bool in_regs = total <= int64_t(kCandPerThread) * kThreads;
   uint64_t c[kCandPerThread];
+  uint64_t tmax_cert = 0;  // largest certificate (its slice may hold more winners iff it is above T)
   uint64_t T;
   if (in_regs) {
 #pragma unroll
@@ -637,14 +676,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int64_t g = int64_t(u) * kThreads + tid;  // element order: coalesced loads
       c[u] = g < total ? get_c(g) : 0ull;
     }
+    for (int64_t x = tid; x < ri.S; x += kThreads) {
+      const uint64_t tx = load_dev(&tau[x]);
+      tmax_cert = tx > tmax_cert ? tx : tmax_cert;
+    }
     T = select_rel(c, ri.kk, L.keys, L.sel);
   } else {
+    for (int64_t x = tid; x < ri.S; x += kThreads) {
+      const uint64_t tx = load_dev(&tau[x]);
+      tmax_cert = tx > tmax_cert ? tx : tmax_cert;
+    }
     T = select_get(total, ri.kk, get_c, L.keys, L.sel);
   }
-  // Certificate check: slice x may hold more winners iff its threshold is above T.
-  bool viol = false;
-  for (int64_t x = tid; x < ri.S; x += kThreads) viol |= load_dev(&tau[x]) > T;
-  if (!__syncthreads_or(viol)) {
+  if (!__syncthreads_or(tmax_cert > T)) {
     if (in_regs) emit_regs(c, T, 0, out_dst, L.sel.scan);
     else emit_get(total, T, get_c, 0, out_dst, L.wave);
     write_pads(a, r, ri.kk);
@@ -715,7 +759,9 @@ IndexPlan plan_index(int B, int64_t T, int H_I, int64_t N_alloc, int top_k, int 
     return o;
   };
   const size_t R = size_t(p.chunk_rows);
-  p.off_cand = take(R * size_t(N_alloc) * 8);
+  // Candidate slots of a row: kloc per slice, and S * kloc <= c + slice.
+  p.cand_row = N_alloc + p.slice;
+  p.off_cand = take(R * size_t(p.cand_row) * 8);
   p.off_tau = take(R * size_t(p.slices) * 8);
   p.off_over = take(R * size_t(N_alloc) * 8);
   p.ws_bytes = multi ? off : 0;

@@ -99,6 +99,7 @@ struct IndexPlan {
   size_t ws_bytes;     // workspace bytes
   // data offsets (after the header); indexed by the row's position in its chunk
   size_t off_cand, off_tau, off_over;
+  int64_t cand_row;    // candidate slots per row (rows x slices path)
 };
 constexpr int64_t kMaxSlice = 4096;
 IndexPlan plan_index(int B, int64_t T, int H_I, int64_t N_alloc, int top_k, int key_kind);

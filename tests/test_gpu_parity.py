@@ -266,6 +266,9 @@ INDEX_CASES = [
     ("bf16", 1, 96, 8, 64, 20000, 4 * 20000 - 96, 4, 2048, True),  # prefill, k = 2048
     ("f32", 1, 40, 4, 32, 1024, 4000, 4, 64, True),                # fp32 path
     ("f32", 2, 1, 4, 64, 6000, 4 * 6000 - 1, 4, 200, True),        # fp32, many slices
+    # 256 rows of 4097 entries: slices of 4096, so each row's second slice holds
+    # one entry and the first must list almost all of the 1024 winners
+    ("bf16", 256, 1, 8, 64, 4097, 4 * 4097 - 1, 4, 1024, True),
 ]
 
 
