@@ -14,6 +14,8 @@ pointers, shapes read from the tensors):
                    bf16_scores=False)
     csa_attend(q, k_cmp, v_cmp, m, idx, k_raw, v_raw, t0, window, scale, out, lse=None,
                raw_base=0, workspace=None)
+    csa_attend_noalloc(q, k_cmp, v_cmp, m, idx, k_raw, v_raw, t0, window, scale, out, lse=None,
+                       raw_base=0)
     hca_attend(q, k_cmp, v_cmp, m_heavy, k_raw, v_raw, t0, window, scale, out, lse=None,
                raw_base=0, workspace=None)
 """
@@ -50,6 +52,9 @@ SIGNATURES = {
     "csa_attend": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64,
                           _i64, _i32, _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz,
                           _vp]),
+    "csa_attend_noalloc": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp,
+                                  _i64, _i64, _i32, _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp,
+                                  _vp]),
     "hca_attend_workspace": (_sz, [_i32, _i64, _i32, _i32, _i64, _i32, _i32]),
     "hca_attend": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _vp, _i64, _i64,
                           _i32, _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
@@ -198,6 +203,20 @@ def csa_attend(q, k_cmp, v_cmp, m, idx, k_raw, v_raw, t0, window, scale, out, ls
                           window, float(scale), _ptr(out), _dt(out), _ptr(lse), _ptr(ws),
                           0 if ws is None else ws.numel(), _stream(q))
     _check("csa_attend", st)
+    return out
+
+
+def csa_attend_noalloc(q, k_cmp, v_cmp, m, idx, k_raw, v_raw, t0, window, scale, out, lse=None,
+                       raw_base=0, k_scale=None, v_scale=None):
+    """csa_attend on the library's own static scratch (no workspace argument)."""
+    B, T, H, d = q.shape
+    N_alloc = k_cmp.shape[1]
+    top_k = 0 if idx is None else idx.shape[-1]
+    st = lib().csa_attend_noalloc(_ptr(q), _dt(q), _ptr(k_cmp), _ptr(v_cmp), _dt(k_cmp), _ptr(k_scale),
+                                  _ptr(v_scale), N_alloc, m, _ptr(idx), top_k,
+                                  _ptr(k_raw), _ptr(v_raw), raw_base, k_raw.shape[1], B, T, H, d, t0,
+                                  window, float(scale), _ptr(out), _dt(out), _ptr(lse), _stream(q))
+    _check("csa_attend_noalloc", st)
     return out
 
 

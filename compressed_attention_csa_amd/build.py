@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
-SOURCES = ["compress.hip", "index.hip", "index_prefill.hip", "attend.hip", "api.cpp", "profile.cpp"]
+SOURCES = ["compress.hip", "index.hip", "index_prefill.hip", "attend.hip", "api.cpp", "profile.cpp",
+           "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

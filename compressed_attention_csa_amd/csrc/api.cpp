@@ -286,7 +286,8 @@ static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const v
                                 int top_k, const void* k_raw, const void* v_raw, int64_t raw_base,
                                 int64_t n_raw, int B, int64_t T, int H, int d, int64_t t0,
                                 int window, float scale, void* out, csa_dtype_t out_dt, float* lse,
-                                void* workspace, size_t workspace_bytes, csa_stream_t stream) {
+                                void* workspace, size_t workspace_bytes, csa_stream_t stream,
+                                bool launch = true) {
   csa_status_t st = check_attend_common(q, dt, k_cmp, v_cmp, N_alloc, m, k_raw, v_raw, raw_base,
                                         n_raw, B, T, H, d, t0, window, out, out_dt, lse);
   if (st != CSA_OK) return st;
@@ -313,11 +314,34 @@ static csa_status_t attend_impl(bool hca, const void* q, csa_dtype_t dt, const v
   REQUIRE(workspace_bytes >= p.ws_bytes, CSA_E_WORKSPACE, "workspace has %zu bytes, needs %zu",
           workspace_bytes, p.ws_bytes);
   REQUIRE(workspace == nullptr || aligned16(workspace), CSA_E_ALIGN, "workspace is not 16-byte aligned");
+  if (!launch) return CSA_OK;
   csa::AttendArgs a{hca, dt == CSA_BF16, q, k_cmp, v_cmp, kv8, k_scale, v_scale, N_alloc, m, hca ? nullptr : idx,
                     hca ? 0 : top_k, k_raw, v_raw, raw_base, n_raw, B, T, H, d, t0, window, scale,
                     out, out_dt == CSA_BF16, lse, workspace, reinterpret_cast<hipStream_t>(stream)};
   return hip_status(csa::launch_attend(a, p), hca ? "hca_attend launch" : "csa_attend launch");
 }
+
+}  // extern "C"
+
+namespace csa {
+
+csa_status_t csa_attend_checked(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
+                                csa_dtype_t kv_dt, const float* k_scale, const float* v_scale,
+                                int64_t N_alloc, int m, const int32_t* idx, int top_k, const void* k_raw,
+                                const void* v_raw, int64_t raw_base, int64_t n_raw, int B, int64_t T,
+                                int H, int d, int64_t t0, int window, float scale, void* out,
+                                csa_dtype_t out_dt, float* lse, void* workspace, size_t workspace_bytes,
+                                csa_stream_t stream, bool launch) {
+  return attend_impl(false, q, dt, k_cmp, v_cmp, kv_dt, k_scale, v_scale, N_alloc, m, idx, top_k, k_raw, v_raw,
+                     raw_base, n_raw, B, T, H, d, t0, window, scale, out, out_dt, lse, workspace,
+                     workspace_bytes, stream, launch);
+}
+
+csa_status_t set_error(csa_status_t s, const char* msg) { return fail(s, "%s", msg); }
+
+}  // namespace csa
+
+extern "C" {
 
 csa_status_t csa_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
                         csa_dtype_t kv_dt, const float* k_scale, const float* v_scale,

@@ -6,7 +6,21 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "csa.h"
+
 namespace csa {
+
+// csa_attend's validation and dispatch (api.cpp); with launch = false it only
+// validates.  Used by the entry point that brings its own scratch.
+csa_status_t csa_attend_checked(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
+                                csa_dtype_t kv_dt, const float* k_scale, const float* v_scale,
+                                int64_t N_alloc, int m, const int32_t* idx, int top_k, const void* k_raw,
+                                const void* v_raw, int64_t raw_base, int64_t n_raw, int B, int64_t T,
+                                int H, int d, int64_t t0, int window, float scale, void* out,
+                                csa_dtype_t out_dt, float* lse, void* workspace, size_t workspace_bytes,
+                                csa_stream_t stream, bool launch);
+// Records the thread-local error text of a status (csa_last_error) and returns it.
+csa_status_t set_error(csa_status_t s, const char* msg);
 
 // Brackets one kernel launch with HIP events when per-kernel timing is enabled
 // (csa_profile_enable); otherwise does nothing.

@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 typedef enum {
   CSA_F32 = 0,      /* IEEE binary32 */
@@ -263,6 +263,29 @@ csa_status_t csa_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const 
                         int H, int d, int64_t t0, int window, float scale, void* out,
                         csa_dtype_t out_dt, float* lse, void* workspace, size_t workspace_bytes,
                         csa_stream_t stream);
+
+/*
+ * csa_attend_noalloc -- csa_attend on scratch that the library holds itself.
+ *
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Arguments, layouts,
+ * numerics and errors are those of csa_attend, without the workspace pair:
+ * the scratch is a static device array of CSA_NOALLOC_SCRATCH_BYTES per GPU,
+ * held until the process ends, whose address is looked up on the first call
+ * on each device (that call also enqueues one small fill kernel on `stream`
+ * to clear its control words).  A shape whose csa_attend_workspace() exceeds
+ * the scratch is rejected with CSA_E_WORKSPACE before anything is enqueued.
+ * The call never allocates.  All calls on one GPU share its scratch, and each
+ * call leaves the control words at zero for the next: calls that overlap on
+ * one GPU (concurrent streams or threads) race and must be ordered.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+csa_status_t csa_attend_noalloc(const void* q, csa_dtype_t dt, const void* k_cmp, const void* v_cmp,
+                                csa_dtype_t kv_dt, const float* k_scale, const float* v_scale,
+                                int64_t N_alloc, int m, const int32_t* idx, int top_k, const void* k_raw,
+                                const void* v_raw, int64_t raw_base, int64_t n_raw, int B, int64_t T,
+                                int H, int d, int64_t t0, int window, float scale, void* out,
+                                csa_dtype_t out_dt, float* lse, csa_stream_t stream);
 
 /*
  * hca_attend -- HCA attention: every visible heavy entry + raw window, one softmax.

@@ -38,11 +38,11 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
         assert n in csa.SIGNATURES, n
-    assert L.csa_abi_version() == 4
+    assert L.csa_abi_version() == 5
     for s, name in enumerate(csa.STATUS):
         assert L.csa_status_string(s).decode() == name
 
@@ -198,6 +198,26 @@ def test_attend_validation(L, hca):
     big = dict(N=8192, m=128, n_raw=1 << 20, t0=(1 << 20) - 1) if hca else dict(top_k=1024)
     assert attend(L, hca, ws_bytes=need - 1, **big) == E_WS
     assert attend(L, hca, ws=None, **big) == E_WS
+
+
+def test_noalloc_attend_rejects_before_any_launch(L):
+    """csa_attend_noalloc checks its arguments and its scratch limit before any
+    HIP call (this runs without a GPU): a shape whose workspace exceeds the
+    library's scratch, and the ordinary argument errors of csa_attend."""
+    limit = (16 << 20)
+    def call(B=4, T=1, H=128, d=128, k=1024, W=128, q=P, out=P, idx=P, dt=BF16):
+        t0 = 4 * 300000 - 1
+        return L.csa_attend_noalloc(q, dt, P, P, dt, None, None, 300000, 4, idx, k, P, P, t0 - W + 1, W + T, B, T,
+                                    H, d, t0, W, 0.1, out, F32, None, None)
+    big = dict(B=200, T=1)  # 200 decode rows: partials far beyond the scratch
+    assert L.csa_attend_workspace(200, 1, 128, 128, 1024, 128) > limit
+    assert call(**big) == E_WS
+    assert b"scratch" in L.csa_last_error()
+    assert L.csa_attend_workspace(4, 1, 128, 128, 1024, 128) <= limit
+    assert call(q=None) == E_NULL
+    assert call(q=MIS) == E_ALIGN
+    assert call(d=96) == E_UNSUP
+    assert call(k=4096) == E_SHAPE
 
 
 def test_null_pointers_are_allowed_for_empty_arrays(L):
