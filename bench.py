@@ -56,6 +56,7 @@ class DecodeCSA:
     recall against the exact selection is reported beside the timing."""
 
     dominant = "index_topk"
+    dominant_kernels = ("index_topk",)
 
     def __init__(self, wl, seed, replicas, variant=""):
         assert variant in ("", "state", "bf16sel"), variant
@@ -164,6 +165,7 @@ class DecodeHCA:
     scales (as csa_compress writes them)."""
 
     dominant = "hca_attend"
+    dominant_kernels = ("hca_attend", "hca_attend_merge")  # the call: attention + split merge
 
     def __init__(self, wl, seed, replicas, variant=""):
         import torch
@@ -218,6 +220,7 @@ class PrefillCSA:
     query over all visible entries, attention."""
 
     dominant = "index_topk"
+    dominant_kernels = ("index_topk",)
 
     def __init__(self, wl, seed, replicas):
         import torch
@@ -266,6 +269,7 @@ class PrefillHCA:
     of every new query over the visible heavy entries and its window."""
 
     dominant = "hca_attend"
+    dominant_kernels = ("hca_attend",)
 
     def __init__(self, wl, seed, replicas):
         import torch
@@ -301,11 +305,127 @@ class PrefillHCA:
         return {"bytes": None, "flops": flops, "dominant_flops": flops, "queries": wl.B * wl.T}
 
 
+class TinyPrefill:
+    """The tiny fp32 configuration, whole: compress (CSA K, V, indexer keys; HCA K, V),
+    index + top-k for all 4096 positions, CSA attention, HCA attention.  A latency-bound
+    correctness configuration; its rate is reported against the fp32 vector peak."""
+
+    dominant = "csa_attend"
+    dominant_kernels = ("csa_attend", "csa_attend_merge")
+    peak = ("fp32", 157.3)
+
+    def __init__(self, wl, seed, replicas):
+        import torch
+        import compressed_attention_csa_amd as csa
+        import inputgen
+        self.wl, self.csa = wl, csa
+        x = inputgen.make_inputs(wl, seed=seed)
+        self.x = {k: v.to("cuda") for k, v in x.items()}
+        B, N, Nh, d, dI = wl.B, wl.N_c, wl.N_h, wl.d, wl.d_I
+        f = dict(dtype=torch.float32, device="cuda")
+        self.kc, self.vc = torch.empty((B, N, d), **f), torch.empty((B, N, d), **f)
+        self.ki = torch.empty((B, N, dI), **f)
+        self.hk, self.hv = torch.empty((B, Nh, d), **f), torch.empty((B, Nh, d), **f)
+        self.idx = torch.empty((B, wl.T, wl.k), dtype=torch.int32, device="cuda")
+        self.o = torch.empty((B, wl.T, wl.H, d), **f)
+        self.ho = torch.empty_like(self.o)
+        torch.cuda.synchronize()
+
+    def step(self, r):
+        wl, csa, x = self.wl, self.csa, self.x
+        for src, dst in ((x["k_raw"], self.kc), (x["v_raw"], self.vc), (x["k_idx_raw"], self.ki)):
+            csa.csa_compress(src, x["z_csa"], wl.m, dst)
+        csa.csa_compress(x["k_raw"], x["z_hca"], wl.m_heavy, self.hk)
+        csa.csa_compress(x["v_raw"], x["z_hca"], wl.m_heavy, self.hv)
+        csa.csa_index_topk(x["q_idx"], x["w"], self.ki, None, wl.t0, wl.m, wl.k, self.idx)
+        csa.csa_attend(x["q"], self.kc, self.vc, wl.m, self.idx, x["k_raw"], x["v_raw"], wl.t0, wl.W, wl.scale,
+                       self.o)
+        csa.hca_attend(x["q"], self.hk, self.hv, wl.m_heavy, x["k_raw"], x["v_raw"], wl.t0, wl.W, wl.scale,
+                       self.ho)
+
+    def algorithmic(self):
+        wl = self.wl
+        ts = range(wl.t0, wl.t0 + wl.T)
+        sum_c = sum(min(wl.N_c, (t + 1) // wl.m) for t in ts)
+        idx_flops = 2 * wl.B * wl.H_I * wl.d_I * sum_c
+        csa_slots = sum(min(wl.k, min(wl.N_c, (t + 1) // wl.m)) + min(wl.W, t + 1) for t in ts)
+        hca_slots = sum(min(wl.N_h, (t + 1) // wl.m_heavy) + min(wl.W, t + 1) for t in ts)
+        att = 4 * wl.B * wl.H * wl.d
+        return {"bytes": None, "flops": idx_flops + att * (csa_slots + hca_slots),
+                "dominant_flops": att * csa_slots, "queries": wl.B * wl.T}
+
+
+class CompressCache:
+    """The compressor's own throughput: building the Pro-like decode caches at 1M context
+    (K and V to bf16, the indexer keys to e4m3 with per-entry scales; 4 sequences,
+    m = 4).  One step = the three csa_compress calls over the whole history."""
+
+    dominant = "compress"
+    dominant_kernels = ("compress",)
+    calls_per_step = 3
+
+    def __init__(self, wl, seed, replicas):
+        import torch
+        import compressed_attention_csa_amd as csa
+        import inputgen
+        self.wl, self.csa = wl, csa
+        B, n, d, dI, N = wl.B, wl.n, wl.d, wl.d_I, wl.N_c
+        self.z = inputgen.normal("z_csa", (wl.m,), seed, "f32", std=0.5, device="cuda")
+        self.raw = {name: inputgen.normal(name, (B, n, dim), seed, "bf16", device="cuda")
+                    for name, dim in (("k_raw", d), ("v_raw", d), ("k_idx_raw", dI))}
+        self.kc = torch.empty((B, N, d), dtype=torch.bfloat16, device="cuda")
+        self.vc = torch.empty_like(self.kc)
+        self.ki = torch.empty((B, N, dI), dtype=torch.uint8, device="cuda")
+        self.ks = torch.empty((B, N), device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self, r):
+        wl, csa = self.wl, self.csa
+        csa.csa_compress(self.raw["k_raw"], self.z, wl.m, self.kc)
+        csa.csa_compress(self.raw["v_raw"], self.z, wl.m, self.vc)
+        csa.csa_compress(self.raw["k_idx_raw"], self.z, wl.m, self.ki, self.ks)
+
+    def algorithmic(self):
+        wl = self.wl
+        read = wl.B * wl.n * (2 * wl.d + wl.d_I) * 2
+        write = wl.B * wl.N_c * (2 * wl.d * 2 + wl.d_I + 4)
+        return {"bytes": read + write, "flops": 0, "dominant_bytes": read + write, "queries": 0}
+
+
+class StreamRead:
+    """The HBM read ceiling: a plain streaming read (csa_diag_stream_read) of a buffer of
+    the given size, cycling replicas so that every read is cache-cold."""
+
+    dominant = "stream_read"
+    dominant_kernels = ("stream_read",)
+
+    def __init__(self, nbytes, replicas):
+        import torch
+        import compressed_attention_csa_amd as csa
+        self.csa, self.nbytes = csa, nbytes
+        self.bufs = [torch.full((nbytes,), i + 1, dtype=torch.uint8, device="cuda") for i in range(replicas)]
+        self.sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self, r):
+        self.csa.diag_stream_read(self.bufs[r % len(self.bufs)], self.sink)
+
+    def algorithmic(self):
+        return {"bytes": self.nbytes, "flops": 0, "dominant_bytes": self.nbytes, "queries": 0}
+
+
 KINDS = {"csa_decode_pro_1m": DecodeCSA, "csa_decode_flash_128k": DecodeCSA,
          "hca_decode_1m": DecodeHCA, "csa_prefill_chunk_1m": PrefillCSA,
-         "hca_prefill_chunk_1m": PrefillHCA}
+         "hca_prefill_chunk_1m": PrefillHCA, "tiny_prefill_f32": TinyPrefill}
 REPLICAS = {"csa_decode_pro_1m": 8, "csa_decode_flash_128k": 16, "hca_decode_1m": 8,
-            "csa_prefill_chunk_1m": 1, "hca_prefill_chunk_1m": 1}
+            "csa_prefill_chunk_1m": 1, "hca_prefill_chunk_1m": 1, "tiny_prefill_f32": 1,
+            "csa_compress_pro_1m": 1, "hbm_read_71mb": 8, "hbm_read_2gb": 1}
+# Workloads that are not a configuration of the method: the compressor's cache build at the
+# Pro-like shape, and the HBM read ceiling at the Pro-like step's key bytes and at 2 GB.
+EXTRA = {"csa_compress_pro_1m": lambda seed, R: CompressCache(__import__("inputgen").WORKLOADS["csa_decode_pro_1m"],
+                                                              seed, R),
+         "hbm_read_71mb": lambda seed, R: StreamRead(71307392, R),
+         "hbm_read_2gb": lambda seed, R: StreamRead(2 << 30, R)}
 
 
 # ----------------------------------------------------------------------------- timing
@@ -316,16 +436,19 @@ def time_workload(name, seed, steps, warmup, graph=True):
     import compressed_attention_csa_amd as csa
     import inputgen
     base, _, variant = name.partition("+")  # "+state": the decode step also maintains the state cache
-    wl = inputgen.WORKLOADS[base]
     R = REPLICAS[base]
     log(f"[bench] {name}: setting up ({R} replica(s))")
     t = time.time()
-    w = KINDS[base](wl, seed, R, **({"variant": variant} if variant else {}))
+    if base in EXTRA:
+        w = EXTRA[base](seed, R)
+    else:
+        wl = inputgen.WORKLOADS[base]
+        w = KINDS[base](wl, seed, R, **({"variant": variant} if variant else {}))
     log(f"[bench] {name}: setup {time.time() - t:.1f}s; warmup {warmup}")
     for i in range(max(warmup, R)):
         w.step(i)
     torch.cuda.synchronize()
-    # Dominant kernel, timed per launch with the library's HIP events (eager).
+    # Per-kernel durations, with the library's HIP events around each launch (eager).
     csa.profile_enable(True)
     nprof = min(max(2 * R, 8), steps) if R > 1 else min(3, steps)
     for i in range(nprof):
@@ -333,8 +456,9 @@ def time_workload(name, seed, steps, warmup, graph=True):
     torch.cuda.synchronize()
     csa.profile_enable(False)
     prof = csa.profile_report()
-    # Headline timing: graph replay of R steps (one per replica).
-    reps = max(1, steps // R)
+    # Headline timing: a graph of R steps (one per replica), replayed at least
+    # ceil(steps / R) times; each replay is timed on its own.
+    reps = max(1, -(-steps // R))
     g = None
     if graph:
         s = torch.cuda.Stream()
@@ -351,24 +475,29 @@ def time_workload(name, seed, steps, warmup, graph=True):
         g.replay()
         torch.cuda.synchronize()
     log(f"[bench] {name}: timing {reps * R} steps")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
+    for e0, e1 in ev:
+        e0.record()
         if g is not None:
             g.replay()
         else:
             for i in range(R):
                 w.step(i)
-    e1.record()
+        e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / (reps * R)
+    per_step = sorted(e0.elapsed_time(e1) / R for e0, e1 in ev)
+    ms = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (per_step[len(per_step) // 2 - 1] +
+                                                                        per_step[len(per_step) // 2])
     alg = w.algorithmic()
-    res = {"workload": name, "ms_per_step": ms, "steps": reps * R, "replicas": R, "kernels": prof,
-           "alg": alg, "dominant": w.dominant}
-    dom = prof.get(w.dominant)
-    if dom:
-        res["dominant_ms"] = dom["total_ms"] / dom["launches"]
+    res = {"workload": name, "ms_per_step": ms, "ms_min": per_step[0], "ms_max": per_step[-1],
+           "steps": reps * R, "replicas": R, "kernels": prof, "alg": alg, "dominant": w.dominant,
+           "peak": getattr(w, "peak", None)}
+    # The dominant call's time per step: its kernels' event-timed durations, summed.
+    calls = prof.get(w.dominant_kernels[0], {}).get("launches", 0) / getattr(w, "calls_per_step", 1)
+    if calls:
+        res["dominant_ms"] = sum(prof[k]["total_ms"] for k in w.dominant_kernels if k in prof) / calls
+        res["dominant_parts_ms"] = {k: round(prof[k]["total_ms"] / calls, 6) for k in w.dominant_kernels if k in prof}
     q = w.quality() if hasattr(w, "quality") else None
     if q:
         res["quality"] = q
@@ -380,36 +509,49 @@ def time_workload(name, seed, steps, warmup, graph=True):
 
 def summarize(res):
     alg, ms = res["alg"], res["ms_per_step"]
-    out = {"ms_per_step": round(ms, 6), "steps": res["steps"], "cache_cold_replicas": res["replicas"],
-           "query_tokens_per_s": alg["queries"] / (ms * 1e-3)}
+    out = {"ms_per_step": round(ms, 6), "ms_per_step_min": round(res["ms_min"], 6),
+           "ms_per_step_max": round(res["ms_max"], 6), "steps": res["steps"],
+           "cache_cold_replicas": res["replicas"]}
+    if alg.get("queries"):
+        out["query_tokens_per_s"] = alg["queries"] / (ms * 1e-3)
     if alg.get("bytes"):
         gbps = alg["bytes"] / (ms * 1e-3) / 1e9
         out.update({"hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
                     "alg_bytes": alg["bytes"]})
-    tf = alg["flops"] / (ms * 1e-3) / 1e12
-    out.update({"tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                "alg_flops": alg["flops"]})
+    if alg.get("flops"):
+        tf = alg["flops"] / (ms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if res.get("peak") is None else res["peak"][1]
+        out.update({"tflops": round(tf, 3), ("mfma_frac" if res.get("peak") is None else "fp32_frac"):
+                    round(tf / peak, 4), "alg_flops": alg["flops"]})
     out["kernel_ms"] = {k: round(v["total_ms"] / v["launches"], 6) for k, v in res["kernels"].items()}
     out.update(res.get("quality") or {})
     return out
 
 
-def roofline(res):
+def roofline(res, ceiling_gbps=None):
     alg = res["alg"]
     dom_ms = res.get("dominant_ms")
     if dom_ms is None:
         return None
     key = f"{res['dominant']}@{res['workload']}"
     traffic = load_traffic(key)
+    common = {"traffic": traffic, "kernel": res["dominant"], "kernel_ms": round(dom_ms, 6),
+              "kernel_parts_ms": res.get("dominant_parts_ms")}
     if "dominant_bytes" in alg:
         achieved = alg["dominant_bytes"] / (dom_ms * 1e-3) / 1e9
-        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic, "kernel": res["dominant"],
-                "kernel_ms": round(dom_ms, 6), "alg_bytes_per_launch": alg["dominant_bytes"]}
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+             "frac": round(achieved / PEAK_HBM_GBPS, 4), **common, "alg_bytes_per_launch": alg["dominant_bytes"]}
+        if ceiling_gbps:
+            r["measured_read_ceiling_gbps"] = round(ceiling_gbps, 1)
+            r["frac_of_measured_ceiling"] = round(achieved / ceiling_gbps, 4)
+        return r
     achieved = alg["dominant_flops"] / (dom_ms * 1e-3) / 1e12
+    if res.get("peak") is not None:
+        return {"bound": "alu", "achieved": round(achieved, 3), "peak": res["peak"][1], "unit": "TFLOP/s",
+                "frac": round(achieved / res["peak"][1], 4), **common,
+                "alg_flops_per_launch": alg["dominant_flops"]}
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": res["dominant"],
-            "kernel_ms": round(dom_ms, 6), "alg_flops_per_launch": alg["dominant_flops"]}
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), **common, "alg_flops_per_launch": alg["dominant_flops"]}
 
 
 def kernel_source_digest() -> str:
@@ -513,9 +655,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="csa_decode_pro_1m")
-    ap.add_argument("--legs", default="hca_decode_1m,csa_prefill_chunk_1m,csa_decode_flash_128k,"
-                    "hca_prefill_chunk_1m,csa_decode_pro_1m+state,hca_decode_1m+fp8kv,"
-                    "csa_decode_pro_1m+bf16sel",
+    ap.add_argument("--legs", default="hbm_read_71mb,hbm_read_2gb,hca_decode_1m,csa_prefill_chunk_1m,"
+                    "csa_decode_flash_128k,hca_prefill_chunk_1m,tiny_prefill_f32,csa_compress_pro_1m,"
+                    "csa_decode_pro_1m+state,hca_decode_1m+fp8kv,csa_decode_pro_1m+bf16sel",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
@@ -546,13 +688,17 @@ def main():
     csa.lib()
 
     head = time_workload(args.workload, args.seed, args.steps, args.warmup, graph=not args.no_graph)
-    legs = {}
+    legs, ceiling = {}, None
     for name in [x for x in args.legs.split(",") if x]:
-        steps = 5 if name in ("csa_prefill_chunk_1m", "hca_prefill_chunk_1m") else args.steps
+        slow = name in ("csa_prefill_chunk_1m", "hca_prefill_chunk_1m", "csa_compress_pro_1m", "hbm_read_2gb",
+                        "tiny_prefill_f32")
+        steps = 5 if slow else args.steps
         r = time_workload(name, args.seed, steps, min(args.warmup, 3) if steps < 10 else args.warmup,
                           graph=not args.no_graph)
         s = summarize(r)
-        s["roofline"] = roofline(r)
+        if name == "hbm_read_71mb" and r.get("dominant_ms"):
+            ceiling = r["alg"]["bytes"] / (r["dominant_ms"] * 1e-3) / 1e9
+        s["roofline"] = roofline(r, ceiling)
         legs[name] = s
     hs = summarize(head)
     wl = __import__("inputgen").WORKLOADS[args.workload]
@@ -572,9 +718,11 @@ def main():
         "config": {"workload": args.workload, "B": wl.B, "context": wl.n, "H": wl.H, "d": wl.d,
                    "H_I": wl.H_I, "d_I": wl.d_I, "m": wl.m, "top_k": wl.k, "window": wl.W,
                    "indexer_keys": wl.idx_key_dtype, "cache_cold_replicas": head["replicas"]},
+        "ms_per_step_min": hs["ms_per_step_min"],
+        "ms_per_step_max": hs["ms_per_step_max"],
         "hbm_gbps": hs.get("hbm_gbps"),
         "hbm_frac": hs.get("hbm_frac"),
-        "roofline": roofline(head),
+        "roofline": roofline(head, ceiling),
         "kernel_ms": hs["kernel_ms"],
         "legs": legs,
     }

@@ -58,6 +58,7 @@ SIGNATURES = {
     "hca_attend_workspace": (_sz, [_i32, _i64, _i32, _i32, _i64, _i32, _i32]),
     "hca_attend": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _vp, _i64, _i64,
                           _i32, _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "csa_diag_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
     "csa_profile_enable": (_i32, [_i32]),
     "csa_profile_report": (_i32, [ctypes.c_char_p, _sz]),
 }
@@ -234,6 +235,12 @@ def hca_attend(q, k_cmp, v_cmp, m_heavy, k_raw, v_raw, t0, window, scale, out, l
                           0 if ws is None else ws.numel(), _stream(q))
     _check("hca_attend", st)
     return out
+
+
+def diag_stream_read(buf, sink):
+    """Plain streaming read of the device tensor ``buf`` (diagnostics: the HBM read ceiling)."""
+    st = lib().csa_diag_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf))
+    _check("csa_diag_stream_read", st)
 
 
 def profile_enable(on: bool = True) -> bool:

@@ -1422,11 +1422,15 @@ static void launch_bf16_nw(const AttendArgs& a, const AttendPlan& p, dim3 grid) 
 template <int D, bool HCA>
 static void launch_bf16(const AttendArgs& a, const AttendPlan& p) {
   const dim3 grid(unsigned(p.rows * p.splits));
-  // Split rows (decode) have one workgroup per CU: stage tiles in pairs.  Many
-  // unsplit rows (prefill) keep the smaller LDS footprint for occupancy.
-  if (p.splits > 1) a.kv8 ? launch_bf16_nw<D, HCA, 2, true>(a, p, grid) : launch_bf16_nw<D, HCA, 2, false>(a, p, grid);
-  else a.kv8 ? launch_bf16_nw<D, HCA, 1, true>(a, p, grid) : launch_bf16_nw<D, HCA, 1, false>(a, p, grid);
+  {
+    ProfScope prof(HCA ? "hca_attend" : "csa_attend", a.stream);
+    // Split rows (decode) have one workgroup per CU: stage tiles in pairs.  Many
+    // unsplit rows (prefill) keep the smaller LDS footprint for occupancy.
+    if (p.splits > 1) a.kv8 ? launch_bf16_nw<D, HCA, 2, true>(a, p, grid) : launch_bf16_nw<D, HCA, 2, false>(a, p, grid);
+    else a.kv8 ? launch_bf16_nw<D, HCA, 1, true>(a, p, grid) : launch_bf16_nw<D, HCA, 1, false>(a, p, grid);
+  }
   if (p.splits > 1) {
+    ProfScope prof(HCA ? "hca_attend_merge" : "csa_attend_merge", a.stream);
     const int64_t threads = p.rows * a.H * (D / 4);
     hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
                        a.stream, a, p);
@@ -1457,14 +1461,16 @@ constexpr int64_t kHcaMultiMinT = 16;
 
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p) {
   if (p.rows == 0) return hipSuccess;
-  ProfScope prof(a.hca ? "hca_attend" : "csa_attend", a.stream);
-  if (a.bf16 && a.hca && p.splits == 1 && a.T >= kHcaMultiMinT &&
-      (a.d == 128 ? hca_multi<128>(a) : hca_multi<64>(a)))
-    return hipGetLastError();
+  // The multi-token kernel takes 8 / (H / 16) tokens per wave pair: H / 16 must divide 8.
+  if (a.bf16 && a.hca && p.splits == 1 && a.T >= kHcaMultiMinT && 8 % (a.H / 16) == 0) {
+    ProfScope prof("hca_attend", a.stream);
+    if (a.d == 128 ? hca_multi<128>(a) : hca_multi<64>(a)) return hipGetLastError();
+  }
   if (a.bf16) {
     if (a.d == 128) a.hca ? launch_bf16<128, true>(a, p) : launch_bf16<128, false>(a, p);
     else a.hca ? launch_bf16<64, true>(a, p) : launch_bf16<64, false>(a, p);
   } else {
+    ProfScope prof(a.hca ? "hca_attend" : "csa_attend", a.stream);
     dim3 grid(unsigned(p.groups * p.group_stride)), block(kThreads);
     if (a.d == 128) hipLaunchKernelGGL(attend_f32_kernel<128>, grid, block, 0, a.stream, a, p);
     else if (a.d == 64) hipLaunchKernelGGL(attend_f32_kernel<64>, grid, block, 0, a.stream, a, p);

@@ -68,12 +68,51 @@ ProfScope::~ProfScope() {
 
 }  // namespace csa
 
+namespace {
+
+// Plain streaming read of a buffer (the HBM read ceiling): every workgroup reads
+// one contiguous chunk with 16-byte loads, 8 in flight per thread.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, size_t n16, uint32_t* sink) {
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = size_t(blockIdx.x) * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
+  uint32_t acc = 0;
+  size_t i = lo + threadIdx.x;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < hi; i += 256) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;  // keeps the loads; almost never taken
+}
+
+}  // namespace
+
 extern "C" {
 
 int csa_profile_enable(int on) {
   int was = g_prof.on ? 1 : 0;
   g_prof.on = on != 0;
   return was;
+}
+
+csa_status_t csa_diag_stream_read(const void* buf, size_t bytes, uint32_t* sink, csa_stream_t stream) {
+  if (bytes == 0) return CSA_OK;
+  if (buf == nullptr || sink == nullptr) return csa::set_error(CSA_E_NULL, "buf / sink is NULL");
+  if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0 || bytes % 16 != 0)
+    return csa::set_error(CSA_E_ALIGN, "buf must be 16-byte aligned and bytes a multiple of 16");
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  csa::ProfScope prof("stream_read", s);
+  hipLaunchKernelGGL(stream_read_kernel, dim3(8192), dim3(256), 0, s, static_cast<const uint4*>(buf), bytes / 16,
+                     sink);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? CSA_OK : csa::set_error(CSA_E_HIP, hipGetErrorString(e));
 }
 
 int csa_profile_report(char* buf, size_t n) {

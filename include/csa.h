@@ -317,6 +317,16 @@ csa_status_t hca_attend(const void* q, csa_dtype_t dt, const void* k_cmp, const 
 int csa_profile_enable(int on);
 int csa_profile_report(char* buf, size_t n);
 
+/*
+ * Diagnostics: the bandwidth a plain read reaches on the device (not part of
+ * the method; the benchmark quotes it beside the kernels' rooflines).  Reads
+ * `bytes` (a multiple of 16) from the device buffer `buf` (16-byte aligned)
+ * with a streaming kernel of 8192 workgroups, each reading one contiguous
+ * chunk with 16-byte loads, and writes to `sink` ([8192] uint32, device) only
+ * when a checksum hits one fixed value, so that the loads are kept.
+ */
+csa_status_t csa_diag_stream_read(const void* buf, size_t bytes, uint32_t* sink, csa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,7 +38,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
         assert n in csa.SIGNATURES, n
