@@ -205,6 +205,29 @@ def index_scores(q_idx, w, k_idx, t0: int, m: int):
     return out, visible
 
 
+def quantize_query_e4m3(q_idx) -> np.ndarray:
+    """The indexer query in fp8 e4m3: every (token, head) row quantised with the
+    key rule (formats.e4m3_quantize_rows: binary32 absmax / 448 scale, 1 where
+    that quotient is 0; codes rounded to nearest even).  Returns the stored
+    values code * scale as float64, shape of q_idx.
+
+    [digest] section 七: the indexer's QK path runs in low precision; with the
+    keys already cached as e4m3, the plainest reading of an fp8 x fp8 product
+    quantises the query the way the keys are quantised, one scale per head row.
+    """
+    q = np.asarray(q_idx, dtype=np.float64)
+    shape = q.shape
+    _, _, stored = formats.e4m3_quantize_rows(q.reshape(-1, shape[-1]).astype(np.float32))
+    return stored.reshape(shape)
+
+
+def index_scores_fp8q(q_idx, w, k_idx, t0: int, m: int):
+    """The fp8 x fp8 indexer variant: index_scores on the e4m3-quantised query
+    (quantize_query_e4m3) against the stored keys; fp64 arithmetic on the
+    stored values.  Returns (scores [T, N], visible [T]) as index_scores."""
+    return index_scores(quantize_query_e4m3(q_idx), w, k_idx, t0, m)
+
+
 def _rank_order(s, idx):
     """Indices ``idx`` ordered by the selection's total order on their scores s:
     NaN first, then decreasing value, then increasing index."""

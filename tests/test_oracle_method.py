@@ -320,6 +320,42 @@ def test_topk_validity_checker_accepts_oracle_and_rejects_planted_swap():
     assert ok and swaps == 1
 
 
+def test_fp8_query_variant_is_identity_on_e4m3_rows_with_unit_scale():
+    """Query rows already on the e4m3 grid with largest magnitude exactly 448
+    quantise to themselves (scale 1): the fp8 x fp8 scores equal the plain ones."""
+    rng = np.random.default_rng(41)
+    vals = formats.E4M3_VALUES[np.isfinite(formats.E4M3_VALUES)]
+    q = rng.choice(vals, size=(6, 3, 32))
+    q[:, :, 0] = 448.0
+    k = formats.round_to_bf16(rng.standard_normal((50, 32)))
+    w = rng.standard_normal((6, 3))
+    np.testing.assert_array_equal(method.quantize_query_e4m3(q), q)
+    np.testing.assert_array_equal(method.index_scores_fp8q(q, w, k, 199, 4)[0], method.index_scores(q, w, k, 199, 4)[0])
+
+
+def test_fp8_query_variant_matches_torch_e4m3_and_bounds_the_error():
+    rng = np.random.default_rng(42)
+    q = formats.round_to_bf16(rng.standard_normal((5, 4, 64)) * rng.uniform(0.01, 30, (5, 4, 1)))
+    k = formats.round_to_bf16(rng.standard_normal((40, 64)))
+    stored = method.quantize_query_e4m3(q)
+    # per row: torch's own e4m3 conversion of q / scale, times the scale
+    for t in range(5):
+        for h in range(4):
+            r = q[t, h].astype(np.float32)
+            sc = np.float32(np.abs(r).max() / np.float32(448.0))
+            y = torch.from_numpy(r / sc).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+            np.testing.assert_array_equal(stored[t, h], y * np.float64(sc))
+    # each quantised element is within half an e4m3 step (2^-4 relative, or the subnormal floor)
+    sc = np.abs(q).max(axis=-1, keepdims=True).astype(np.float32) / np.float32(448.0)
+    assert np.all(np.abs(stored - q) <= np.maximum(np.abs(q) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-6))
+    # so the scores move by at most sum_h |w_h| sum_i |dq_i| |k_i|
+    w = np.abs(rng.standard_normal((5, 4)))
+    s8 = method.index_scores_fp8q(q, w, k, 159, 4)[0]
+    s = method.index_scores(q, w, k, 159, 4)[0]
+    bound = np.einsum("th,thd,jd->tj", w, np.abs(stored - q), np.abs(k))
+    assert np.all(np.abs(s8 - s) <= bound * (1 + 1e-9) + 1e-12)
+
+
 # ----------------------------------------------------------------------------- non-finite inputs
 #
 # Contract: IEEE arithmetic throughout; the rectifier propagates NaN of either
