@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 METRIC = "decode query-tokens/s + HBM GB/s at 1M ctx; prefill TFLOP/s (frac. of peak)"
 
 
@@ -217,13 +218,21 @@ class DecodeHCA:
 
 class PrefillCSA:
     """Chunked prefill: compress the chunk's new blocks, index + top-k for every new
-    query over all visible entries, attention."""
+    query over all visible entries, attention.
+
+    Variant ``fp8k``: the indexer keys are cached as e4m3 codes with per-entry
+    scales (the products stay bf16); ``fp8q``: the same keys with the fp8 x fp8
+    indexer (query quantised to e4m3 in the kernel), priced against the fp8 peak."""
 
     dominant = "index_topk"
     dominant_kernels = ("index_topk",)
 
-    def __init__(self, wl, seed, replicas):
+    def __init__(self, wl, seed, replicas, variant=""):
         import torch
+        assert variant in ("", "fp8k", "fp8q"), variant
+        self.variant = variant
+        if variant == "fp8q":
+            self.mfma_peak = ("fp8", PEAK_FP8_TFLOPS)
         import compressed_attention_csa_amd as csa
         import inputgen
         self.wl, self.csa = wl, csa
@@ -238,8 +247,13 @@ class PrefillCSA:
         self.cmp = {"k_raw": torch.empty((B, N, d), dtype=torch.bfloat16, device=dev),
                     "v_raw": torch.empty((B, N, d), dtype=torch.bfloat16, device=dev),
                     "k_idx_raw": torch.empty((B, N, dI), dtype=torch.bfloat16, device=dev)}
+        self.scales = {}
+        if variant:
+            self.cmp["k_idx_raw"] = torch.empty((B, N, dI), dtype=torch.uint8, device=dev)
+            self.scales["k_idx_raw"] = torch.empty((B, N), dtype=torch.float32, device=dev)
         for name, out in self.cmp.items():  # the prior context, compressed before the step
-            csa.csa_compress(self.raw[name], self.z, wl.m, out, entry_begin=0, entry_end=wl.cmp_begin)
+            csa.csa_compress(self.raw[name], self.z, wl.m, out, out_scale=self.scales.get(name),
+                             entry_begin=0, entry_end=wl.cmp_begin)
         self.idx = torch.empty((B, wl.T, wl.k), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, wl.T, wl.H, d), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
@@ -247,9 +261,11 @@ class PrefillCSA:
     def step(self, r):
         wl, csa = self.wl, self.csa
         for name, out in self.cmp.items():
-            csa.csa_compress(self.raw[name], self.z, wl.m, out, entry_begin=wl.cmp_begin,
-                             entry_end=wl.N_c)
-        csa.csa_index_topk(self.q_idx, self.w, self.cmp["k_idx_raw"], None, wl.t0, wl.m, wl.k, self.idx)
+            csa.csa_compress(self.raw[name], self.z, wl.m, out, out_scale=self.scales.get(name),
+                             entry_begin=wl.cmp_begin, entry_end=wl.N_c)
+        index = csa.csa_index_topk_fp8 if self.variant == "fp8q" else csa.csa_index_topk
+        index(self.q_idx, self.w, self.cmp["k_idx_raw"], self.scales.get("k_idx_raw"), wl.t0, wl.m, wl.k,
+              self.idx)
         csa.csa_attend(self.q, self.cmp["k_raw"], self.cmp["v_raw"], wl.m, self.idx, self.raw["k_raw"],
                        self.raw["v_raw"], wl.t0, wl.W, wl.scale, self.out)
 
@@ -492,7 +508,7 @@ def time_workload(name, seed, steps, warmup, graph=True):
     alg = w.algorithmic()
     res = {"workload": name, "ms_per_step": ms, "ms_min": per_step[0], "ms_max": per_step[-1],
            "steps": reps * R, "replicas": R, "kernels": prof, "alg": alg, "dominant": w.dominant,
-           "peak": getattr(w, "peak", None)}
+           "peak": getattr(w, "peak", None), "mfma_peak": getattr(w, "mfma_peak", None)}
     # The dominant call's time per step: its kernels' event-timed durations, summed.
     calls = prof.get(w.dominant_kernels[0], {}).get("launches", 0) / getattr(w, "calls_per_step", 1)
     if calls:
@@ -550,8 +566,10 @@ def roofline(res, ceiling_gbps=None):
         return {"bound": "alu", "achieved": round(achieved, 3), "peak": res["peak"][1], "unit": "TFLOP/s",
                 "frac": round(achieved / res["peak"][1], 4), **common,
                 "alg_flops_per_launch": alg["dominant_flops"]}
-    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), **common, "alg_flops_per_launch": alg["dominant_flops"]}
+    dt, peak = res.get("mfma_peak") or ("bf16", PEAK_BF16_TFLOPS)
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "peak_dtype": dt, **common,
+            "alg_flops_per_launch": alg["dominant_flops"]}
 
 
 def kernel_source_digest() -> str:
@@ -657,7 +675,8 @@ def main():
     ap.add_argument("--workload", default="csa_decode_pro_1m")
     ap.add_argument("--legs", default="hbm_read_71mb,hbm_read_2gb,hca_decode_1m,csa_prefill_chunk_1m,"
                     "csa_decode_flash_128k,hca_prefill_chunk_1m,tiny_prefill_f32,csa_compress_pro_1m,"
-                    "csa_decode_pro_1m+state,hca_decode_1m+fp8kv,csa_decode_pro_1m+bf16sel",
+                    "csa_decode_pro_1m+state,hca_decode_1m+fp8kv,csa_decode_pro_1m+bf16sel,csa_prefill_chunk_1m+fp8k,"
+                    "csa_prefill_chunk_1m+fp8q",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")

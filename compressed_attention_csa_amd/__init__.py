@@ -48,6 +48,8 @@ SIGNATURES = {
                               _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_bf16": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i32, _i32, _i64,
                                    _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_fp8": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i64, _i64, _i32, _i32,
+                                  _vp, _vp, _vp, _sz, _vp]),
     "csa_attend_workspace": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "csa_attend": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i64,
                           _i64, _i32, _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz,
@@ -187,6 +189,21 @@ def csa_index_topk(q_idx, w, k_idx, k_scale, t0, m, top_k, out_idx, out_score=No
                               _ptr(out_score), _ptr(ws), 0 if ws is None else ws.numel(),
                               _stream(q_idx))
     _check(name, st)
+    return out_idx
+
+
+def csa_index_topk_fp8(q_idx, w, k_idx, k_scale, t0, m, top_k, out_idx, out_score=None,
+                       workspace_tensor=None):
+    """Exact top-k with fp8 x fp8 dot products (csa_index_topk_fp8): q_idx bf16,
+    k_idx uint8 e4m3 codes with per-entry k_scale."""
+    B, T, H_I, d_I = q_idx.shape
+    N_alloc = k_idx.shape[1]
+    need = index_topk_workspace_bytes(B, T, H_I, d_I, N_alloc, top_k, CSA_FP8_E4M3)
+    ws = workspace_tensor if workspace_tensor is not None else workspace(need, q_idx.device, "index")
+    st = lib().csa_index_topk_fp8(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), B, T, H_I, d_I, N_alloc,
+                                  t0, m, top_k, _ptr(out_idx), _ptr(out_score), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(q_idx))
+    _check("csa_index_topk_fp8", st)
     return out_idx
 
 

@@ -210,13 +210,16 @@ static csa_status_t index_topk(const void* q_idx, csa_dtype_t q_dt, const float*
                                csa_dtype_t k_dt, const float* k_scale, int B, int64_t T, int H_I,
                                int d_I, int64_t N_alloc, int64_t t0, int m, int top_k,
                                int32_t* out_idx, float* out_score, void* workspace,
-                               size_t workspace_bytes, csa_stream_t stream, bool bf16_scores) {
+                               size_t workspace_bytes, csa_stream_t stream, bool bf16_scores,
+                               bool fp8_query = false) {
   REQUIRE_PTR_IF(q_idx, T > 0);
   REQUIRE_PTR_IF(k_idx, N_alloc > 0);
   REQUIRE_PTR_IF(out_idx, T > 0 && top_k > 0);
   const bool ok_dt = (q_dt == CSA_F32 && k_dt == CSA_F32) || (q_dt == CSA_BF16 && k_dt == CSA_BF16) ||
                      (q_dt == CSA_BF16 && k_dt == CSA_FP8_E4M3);
   REQUIRE(ok_dt, CSA_E_DTYPE, "unsupported (q_dt, k_dt) = (%d, %d)", int(q_dt), int(k_dt));
+  REQUIRE(!fp8_query || (q_dt == CSA_BF16 && k_dt == CSA_FP8_E4M3), CSA_E_DTYPE,
+          "the fp8 x fp8 indexer takes (q_dt, k_dt) = (CSA_BF16, CSA_FP8_E4M3)");
   if (k_dt == CSA_FP8_E4M3) REQUIRE_PTR_IF(k_scale, N_alloc > 0);
   else REQUIRE(k_scale == nullptr, CSA_E_DTYPE, "k_scale must be NULL unless k_dt is CSA_FP8_E4M3");
   REQUIRE(B >= 1 && B <= 65535, CSA_E_SHAPE, "B=%d out of range [1, 65535]", B);
@@ -228,7 +231,10 @@ static csa_status_t index_topk(const void* q_idx, csa_dtype_t q_dt, const float*
   REQUIRE(t0 >= 0, CSA_E_SHAPE, "t0 < 0");
   REQUIRE(m >= 1, CSA_E_SHAPE, "m < 1");
   REQUIRE(top_k >= 1 && top_k <= 2048, CSA_E_SHAPE, "top_k=%d out of range [1, 2048]", top_k);
-  const int kind = k_dt == CSA_F32 ? csa::kKeyF32 : (k_dt == CSA_BF16 ? csa::kKeyBF16 : csa::kKeyE4M3);
+  const int kind = k_dt == CSA_F32    ? csa::kKeyF32
+                   : k_dt == CSA_BF16 ? csa::kKeyBF16
+                   : fp8_query        ? csa::kKeyE4M3Q8
+                                      : csa::kKeyE4M3;
   const csa::IndexPlan p = csa::plan_index(B, T, H_I, N_alloc, top_k, kind);
   REQUIRE(p.prefill ? (T + csa::kPrefillQPB - 1) / csa::kPrefillQPB <= kMaxGrid
                     : p.rows * p.slices <= kMaxGrid, CSA_E_SHAPE, "too many query rows");
@@ -242,9 +248,7 @@ static csa_status_t index_topk(const void* q_idx, csa_dtype_t q_dt, const float*
   REQUIRE(k_scale == nullptr || aligned16(k_scale), CSA_E_ALIGN, "k_scale is not 16-byte aligned");
   REQUIRE(out_score == nullptr || aligned16(out_score), CSA_E_ALIGN, "out_score is not 16-byte aligned");
   REQUIRE(workspace == nullptr || aligned16(workspace), CSA_E_ALIGN, "workspace is not 16-byte aligned");
-  csa::IndexArgs a{q_idx, w, k_idx, k_scale,
-                   k_dt == CSA_F32 ? csa::kKeyF32 : (k_dt == CSA_BF16 ? csa::kKeyBF16 : csa::kKeyE4M3),
-                   B, T, H_I, d_I, N_alloc, t0, m, top_k, out_idx, out_score, workspace,
+  csa::IndexArgs a{q_idx, w, k_idx, k_scale, kind, B, T, H_I, d_I, N_alloc, t0, m, top_k, out_idx, out_score, workspace,
                    reinterpret_cast<hipStream_t>(stream), bf16_scores};
   return hip_status(csa::launch_index_topk(a, p), "index_topk launch");
 }
@@ -265,6 +269,14 @@ csa_status_t csa_index_topk_bf16(const void* q_idx, csa_dtype_t q_dt, const floa
                                  size_t workspace_bytes, csa_stream_t stream) {
   return index_topk(q_idx, q_dt, w, k_idx, k_dt, k_scale, B, T, H_I, d_I, N_alloc, t0, m, top_k,
                     out_idx, out_score, workspace, workspace_bytes, stream, true);
+}
+
+csa_status_t csa_index_topk_fp8(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+                                int B, int64_t T, int H_I, int d_I, int64_t N_alloc, int64_t t0, int m,
+                                int top_k, int32_t* out_idx, float* out_score, void* workspace,
+                                size_t workspace_bytes, csa_stream_t stream) {
+  return index_topk(q_idx, CSA_BF16, w, k_idx, CSA_FP8_E4M3, k_scale, B, T, H_I, d_I, N_alloc, t0, m, top_k,
+                    out_idx, out_score, workspace, workspace_bytes, stream, false, true);
 }
 
 size_t csa_attend_workspace(int B, int64_t T, int H, int d, int top_k, int window) {

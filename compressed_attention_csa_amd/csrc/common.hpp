@@ -178,6 +178,50 @@ __device__ __forceinline__ bf16x8_t u32x4_as_bf16x8(uint4 v) {
   return r;
 }
 
+// The same product with OCP e4m3fn operands: a lane's 8 k-slots are 8 codes
+// packed little-endian in 64 bits (slot 8*(l/16) in the lowest byte).  Every
+// e4m3 x e4m3 product is exact in binary32.
+__device__ __forceinline__ f32x4_t mfma16x16x32_fp8(uint64_t a, uint64_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(static_cast<long>(a), static_cast<long>(b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- e4m3 query rows
+//
+// A bf16 row held 8 values per lane by lanes l, l^16, l^32, l^48 (the A
+// operand layout above) quantised to e4m3 with one binary32 scale per row, the
+// rule of the key cache: scale = absmax / 448 (NaN elements ignored), 1 where
+// that quotient is 0; code = e4m3 nearest-even of the binary32 quotient x / scale.
+
+// Largest magnitude of the 8 bf16 values of v that are not NaN.
+__device__ __forceinline__ float bf16x8_absmax(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, fabsf(u32_as_f32(w[i] << 16)));          // fmaxf returns the non-NaN operand
+    m = fmaxf(m, fabsf(u32_as_f32(w[i] & 0xffff0000u)));
+  }
+  return m;
+}
+// Row scale from this lane's part of the absmax (reduced over the 4 lanes of the row).
+__device__ __forceinline__ float e4m3_row_scale(float part) {
+  float m = fmaxf(part, __shfl_xor(part, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float s = m / 448.0f;
+  return s == 0.0f ? 1.0f : s;
+}
+// e4m3 codes of the 8 bf16 values of v divided by scale.
+__device__ __forceinline__ uint64_t bf16x8_to_e4m3x8(uint4 v, float scale) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint64_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r |= uint64_t(f32_to_e4m3(u32_as_f32(w[i] << 16) / scale)) << (16 * i);
+    r |= uint64_t(f32_to_e4m3(u32_as_f32(w[i] & 0xffff0000u) / scale)) << (16 * i + 8);
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------- cross-workgroup handoff
 //
 // Data that one workgroup hands to another inside the same kernel is written

@@ -134,6 +134,9 @@ __device__ __forceinline__ float sum_rows4(float x) {
 // round is scored.
 // Loads are unconditional (groups past the slice re-read its last key), so
 // the compiler's wait counts stay exact.
+// KK == kKeyE4M3Q8: the query rows are quantised to e4m3 and the products are
+// fp8 x fp8 MFMAs on the raw key codes; each head's query scale moves into its
+// weight (relu(s * x) = s * relu(x) for s > 0).
 template <int KK, int DI>
 __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowInfo& ri, uint32_t* keys,
                                                  int64_t qrow) {
@@ -152,7 +155,10 @@ __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowIn
   // A operands: row = head col (zero past H_I), k-slots 8g..8g+7.  For 64 dims
   // the k-slots of the two products map to dims 16g..16g+7 and 16g+8..16g+15,
   // so a lane reads 16 contiguous dims of its key.
+  constexpr bool Q8 = KK == kKeyE4M3Q8;
   bf16x8_t qa0, qa1;
+  uint64_t q80 = 0, q81 = 0;  // the same k-slots as e4m3 codes (Q8)
+  float qscale = 1.0f;        // scale of query head col (Q8)
   {
     uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
     if (col < H_I) {
@@ -165,6 +171,11 @@ __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowIn
     }
     qa0 = u32x4_as_bf16x8(v0);
     qa1 = u32x4_as_bf16x8(v1);
+    if (Q8) {
+      qscale = e4m3_row_scale(fmaxf(bf16x8_absmax(v0), bf16x8_absmax(v1)));
+      q80 = bf16x8_to_e4m3x8(v0, qscale);
+      q81 = bf16x8_to_e4m3x8(v1, qscale);
+    }
   }
   // Rows past H_I hold zeros; they are left out of the head sum rather than
   // weighted by 0, since their product with an infinite key element is NaN.
@@ -175,13 +186,14 @@ __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowIn
     const int h = 4 * g + j;
     hv[j] = h < H_I;
     wr[j] = hv[j] ? (a.w ? a.w[qrow + h] : 1.0f) : 0.0f;
+    if (Q8) wr[j] *= __shfl(qscale, h);  // A row h is lane h
   }
   const int64_t kb = ri.b * a.N_alloc + ri.lo;
   const int64_t ngroups = (n + 15) / 16;
   constexpr int RS = kWaves * U;  // groups per round
   const int nr = int((ngroups + RS - 1) / RS);
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_idx) + kb * DI * (KK == kKeyBF16 ? 2 : 1);
-  const float* sbase = KK == kKeyE4M3 ? a.k_scale + kb : nullptr;
+  const float* sbase = key_is_e4m3(KK) ? a.k_scale + kb : nullptr;
   const uint32_t last = uint32_t(n - 1);
   auto load = [&](Round& R, int rr) __attribute__((always_inline)) {
 #pragma unroll
@@ -213,6 +225,14 @@ __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowIn
     f32x4_t acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (Q8) {
+        // Raw codes: dims 16g..16g+15 (DI = 64) or 8g..8g+7 (DI = 32).
+        f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+        c = mfma16x16x32_fp8(q80, (uint64_t(R.k[CW * u + 1]) << 32) | R.k[CW * u], c);
+        if (DI == 64) c = mfma16x16x32_fp8(q81, (uint64_t(R.k[CW * u + 3]) << 32) | R.k[CW * u + 2], c);
+        acc[u] = c;
+        continue;
+      }
       uint4 b0, b1 = make_uint4(0, 0, 0, 0);
       if (KK == kKeyBF16) {
         b0 = make_uint4(R.k[CW * u], R.k[CW * u + 1], R.k[CW * u + 2], R.k[CW * u + 3]);
@@ -243,7 +263,7 @@ __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowIn
         part = hv[j] ? fmaf(wr[j], relu_nan(acc[u][j]), part) : part;
       }
       part = sum_rows4(part);
-      if (KK == kKeyE4M3) part *= R.sc[u];
+      if (key_is_e4m3(KK)) part *= R.sc[u];
       if (a.bf16_scores) part = round_bf16(part);
       const int64_t e = (int64_t(rr) * RS + u * kWaves + wid) * 16 + col;
       if (g == 0 && e < n) keys[e] = score_key(part);
@@ -788,7 +808,8 @@ hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p) {
     ProfScope prof("index_topk", a.stream);
     if (a.key_kind == kKeyF32) launch_kpt<kKeyF32>(a, p, row0, grid, block);
     else if (a.key_kind == kKeyBF16) launch_kpt<kKeyBF16>(a, p, row0, grid, block);
-    else launch_kpt<kKeyE4M3>(a, p, row0, grid, block);
+    else if (a.key_kind == kKeyE4M3) launch_kpt<kKeyE4M3>(a, p, row0, grid, block);
+    else launch_kpt<kKeyE4M3Q8>(a, p, row0, grid, block);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

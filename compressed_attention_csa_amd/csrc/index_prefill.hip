@@ -19,7 +19,11 @@
 // same 4 queries (row 4*q + h), so lane (g, col) receives all 8 head dots of
 // query g for entry col and forms sum_h w_h * ReLU(dot_h) without any
 // cross-lane exchange.  The products of the next 16 entries are issued before
-// the current ones are reduced.
+// the current ones are reduced.  With e4m3 keys, either the codes are widened
+// to bf16 when staged (bf16 products), or, in the fp8 x fp8 variant, they stay
+// 8-bit in LDS and the query rows are quantised to e4m3 once per workgroup;
+// then 16x16x32 fp8 products take the same lane layout, one 16-byte LDS read
+// per lane holding both k-steps of a 64-dim key.
 //
 // Exact top-k.  Each query keeps a candidate buffer in the workspace and a
 // threshold tau (a 64-bit rank key: score, then lower index first).  A binary32
@@ -215,12 +219,15 @@ __device__ int wave_compact(uint64_t* buf, int n, uint64_t T) {
 // FH: all 8 head rows of the products are real heads (H_I == 8).  Otherwise
 // the zero rows past H_I are left out of the head sum (0 times an infinite key
 // element is NaN, which a zero weight would not remove).
+// KK == kKeyE4M3Q8: the query rows are quantised to e4m3 on load and the
+// products are fp8 x fp8 MFMAs on the raw key codes, which stay 8-bit in LDS.
 template <int KK, int DI, bool FH>
 __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, IndexPlan p) {
   __shared__ LdsPrefill L;
-  constexpr int KB = (KK == kKeyE4M3) ? 1 : 2;  // key bytes per element
+  constexpr bool Q8 = KK == kKeyE4M3Q8;
+  constexpr int KB = key_is_e4m3(KK) ? 1 : 2;  // key bytes per element
   constexpr int CPG = DI * KB / 16;              // 16-byte chunks per entry in memory
-  constexpr int CPE = DI / 8;                    // 16-byte chunks per entry in LDS (bf16)
+  constexpr int CPE = Q8 ? CPG : DI / 8;         // 16-byte chunks per entry in LDS (bf16, or raw codes)
   constexpr int KSTEP = DI / 32;                 // 32-wide k-steps of one dot product
   constexpr int CHUNKS = kTileE * CPG;
   constexpr int LOADS = (CHUNKS + kThreads - 1) / kThreads;  // chunks per thread per tile
@@ -234,7 +241,10 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   // ---- A operands: row `col` = query col/4 of the wave, head 4*hf + col%4.
+  // k-slots 8g..8g+7 of k-step ks are dims 16g+8ks.. (DI = 64) or 8g.. (DI = 32).
   bf16x8_t qa[2][KSTEP];
+  uint64_t qa8[2][KSTEP];  // the same slots as e4m3 codes (Q8)
+  float qscale[2] = {1.0f, 1.0f};
   {
     const int64_t qi = qw0 + col / 4;
     const bf16_t* qbase = reinterpret_cast<const bf16_t*>(a.q_idx);
@@ -242,12 +252,22 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     for (int hf = 0; hf < 2; ++hf) {
       const int h = 4 * hf + col % 4;
       const bool ok = qi < a.T && h < H_I;
+      uint4 qraw[KSTEP];
       const bf16_t* qr = qbase + ((rowbase + qi) * H_I + h) * DI;
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (ok) v = *reinterpret_cast<const uint4*>(qr + (DI == 64 ? 16 * g + 8 * ks : 8 * g));
         qa[hf][ks] = u32x4_as_bf16x8(v);
+        qraw[ks] = v;
+      }
+      if (Q8) {
+        float part = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ++ks) part = fmaxf(part, bf16x8_absmax(qraw[ks]));
+        qscale[hf] = e4m3_row_scale(part);
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ++ks) qa8[hf][ks] = bf16x8_to_e4m3x8(qraw[ks], qscale[hf]);
       }
     }
   }
@@ -264,6 +284,12 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
 #pragma unroll
   for (int h = 0; h < 8; ++h)
     wv[h] = (qvalid && h < H_I) ? (a.w ? a.w[(rowbase + iq) * H_I + h] : 1.0f) : 0.0f;
+  if (Q8) {
+    // The query scale of head h moves into its weight (relu(s * x) = s * relu(x)
+    // for s > 0); it is held by A row 4g + h % 4, which is lane 4g + h % 4.
+#pragma unroll
+    for (int h = 0; h < 8; ++h) wv[h] *= __shfl(qscale[h / 4], 4 * g + h % 4);
+  }
   uint64_t tau = 0ull;             // every key appended from now on is > tau
   bool active = qvalid;            // this lane's query takes part in the current pass
   // Screening score of tau: NaN admits everything, +inf (a lane whose query
@@ -302,14 +328,22 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   auto fetch = [&](int t) {
     pre0 = *chunk_ptr(t, id0);
     if (LOADS > 1) pre1 = *chunk_ptr(t, id1);
-    if (KK == kKeyE4M3) psc = a.k_scale[b * a.N_alloc + min((t * kTileE + (tid & (kTileE - 1))) * ss, cmax - 1)];
+    if (key_is_e4m3(KK)) psc = a.k_scale[b * a.N_alloc + min((t * kTileE + (tid & (kTileE - 1))) * ss, cmax - 1)];
   };
-  // Writes the prefetched chunks to LDS buffer `buf`; fp8 keys are widened to
-  // bf16 here, once per workgroup, rather than by every wave that reads them.
+  // Writes the prefetched chunks to LDS buffer `buf`; fp8 keys for bf16
+  // products are widened to bf16 here, once per workgroup, rather than by every
+  // wave that reads them.  Raw codes of 32-dim keys are placed in 8-byte slots
+  // (dims 8s..8s+7 in slot s ^ ((e >> 2) & 3)), so that 16 lanes reading one
+  // slot of 16 consecutive entries hit distinct banks.
   auto put = [&](int buf, int id, const uint4& v) {
     const int e = id / CPG, c = id % CPG;
-    if (KK == kKeyBF16) {
+    if (KK == kKeyBF16 || (Q8 && DI == 64)) {
       L.tile[buf][chunk_pos(e, c, CPE)] = v;
+    } else if (Q8) {
+      uint2* t8 = reinterpret_cast<uint2*>(L.tile[buf]);
+      const int h = (e >> 2) & 3;
+      t8[e * 4 + ((2 * c) ^ h)] = make_uint2(v.x, v.y);
+      t8[e * 4 + ((2 * c + 1) ^ h)] = make_uint2(v.z, v.w);
     } else {
       uint4 lo, hi;
       e4m3x4_to_bf16x4(v.x, lo.x, lo.y);
@@ -323,13 +357,22 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   auto stage = [&](int buf) {
     if (tid < CHUNKS) put(buf, id0, pre0);
     if (LOADS > 1 && tid + kThreads < CHUNKS) put(buf, id1, pre1);
-    if (KK == kKeyE4M3 && tid < kTileE) L.scale[buf][tid] = psc;
+    if (key_is_e4m3(KK) && tid < kTileE) L.scale[buf][tid] = psc;
   };
   // B operands of entry group gi (16 entries) of LDS buffer `buf`: dims
   // 16g..16g+15 (DI = 64) or 8g..8g+7 (DI = 32) of entry 16*gi + col.
+  // Raw codes (Q8): dims 16g..16g+15 (DI = 64) or 8g..8g+7 (DI = 32) in b0.
   auto operands = [&](int buf, int gi, uint4& b0, uint4& b1) {
     const int e = gi * 16 + col;
-    if (DI == 64) {
+    if (Q8) {
+      b1 = make_uint4(0, 0, 0, 0);
+      if (DI == 64) {
+        b0 = L.tile[buf][chunk_pos(e, g, CPE)];
+      } else {
+        const uint2 v = reinterpret_cast<const uint2*>(L.tile[buf])[e * 4 + (g ^ ((e >> 2) & 3))];
+        b0 = make_uint4(v.x, v.y, 0, 0);
+      }
+    } else if (DI == 64) {
       b0 = L.tile[buf][chunk_pos(e, 2 * g, CPE)];
       b1 = L.tile[buf][chunk_pos(e, 2 * g + 1, CPE)];
     } else {
@@ -341,6 +384,12 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (Q8) {
+        z = mfma16x16x32_fp8(qa8[hf][0], (uint64_t(b0.y) << 32) | b0.x, z);
+        if (DI == 64) z = mfma16x16x32_fp8(qa8[hf][1], (uint64_t(b0.w) << 32) | b0.z, z);
+        acc[hf] = z;
+        continue;
+      }
       z = mfma16x16x32(qa[hf][0], u32x4_as_bf16x8(b0), z);
       if (DI == 64) z = mfma16x16x32(qa[hf][KSTEP - 1], u32x4_as_bf16x8(b1), z);
       acc[hf] = z;
@@ -523,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
               const float t = fmaf(wv[4 * hf + j], relu_nan(acc[hf][j]), s);
               s = (FH || 4 * hf + j < H_I) ? t : s;
             }
-          if (KK == kKeyE4M3) s *= L.scale[cur][e];
+          if (key_is_e4m3(KK)) s *= L.scale[cur][e];
           if (a.bf16_scores) s = round_bf16(s);  // screen and rank the rounded score
           // The screen admits every entry whose rank key can exceed tau (and a
           // few equal-score ones that cannot); the exact test runs when staged
@@ -650,6 +699,14 @@ hipError_t launch_index_prefill(const IndexArgs& a, const IndexPlan& p) {
     } else {
       if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 32, true>), grid, block, 0, a.stream, a, p);
       else hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 32, false>), grid, block, 0, a.stream, a, p);
+    }
+  } else if (a.key_kind == kKeyE4M3Q8) {
+    if (a.d_I == 64) {
+      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3Q8, 64, true>), grid, block, 0, a.stream, a, p);
+      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3Q8, 64, false>), grid, block, 0, a.stream, a, p);
+    } else {
+      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3Q8, 32, true>), grid, block, 0, a.stream, a, p);
+      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3Q8, 32, false>), grid, block, 0, a.stream, a, p);
     }
   } else {
     if (a.d_I == 64) {

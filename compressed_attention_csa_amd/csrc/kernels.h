@@ -61,7 +61,10 @@ hipError_t launch_append(const CompressArgs& a, const void* x_new, int64_t t0, i
 
 // ------------------------------------------------------------------ indexer + top-k
 
-enum KeyKind { kKeyF32 = 0, kKeyBF16 = 1, kKeyE4M3 = 2 };
+// kKeyE4M3Q8: e4m3 keys and a bf16 query quantised to e4m3 in the kernel (one
+// scale per (token, head) row), so the dot products are fp8 x fp8.
+enum KeyKind { kKeyF32 = 0, kKeyBF16 = 1, kKeyE4M3 = 2, kKeyE4M3Q8 = 3 };
+constexpr bool key_is_e4m3(int kk) { return kk == kKeyE4M3 || kk == kKeyE4M3Q8; }
 
 struct IndexArgs {
   const void* q_idx;  // [B, T, H_I, d_I]

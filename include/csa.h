@@ -9,6 +9,8 @@
  *                   the blocks each new token completes
  *   csa_index_topk  Lightning-Indexer scores of compressed entries + per-query top-k
  *   csa_index_topk_bf16  the same selection on scores rounded to bf16 (approximate)
+ *   csa_index_topk_fp8   the same selection with fp8 x fp8 dot products (query
+ *                   quantised to e4m3 like the keys)
  *   csa_attend      attention over the selected compressed entries and the raw
  *                   sliding window, under one softmax
  *   hca_attend      dense attention over every visible heavy entry and the window
@@ -78,7 +80,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 5
+#define CSA_ABI_VERSION 6
 
 typedef enum {
   CSA_F32 = 0,      /* IEEE binary32 */
@@ -225,6 +227,34 @@ csa_status_t csa_index_topk_bf16(const void* q_idx, csa_dtype_t q_dt, const floa
                                  int64_t T, int H_I, int d_I, int64_t N_alloc, int64_t t0, int m,
                                  int top_k, int32_t* out_idx, float* out_score, void* workspace,
                                  size_t workspace_bytes, csa_stream_t stream);
+
+/*
+ * csa_index_topk_fp8 -- csa_index_topk with fp8 x fp8 dot products.
+ *
+ * [digest] 七: the indexer's QK path runs in low precision, since its
+ * activations are cached, loaded and multiplied there; [summary] 五: fp8
+ * caches.  With keys already cached as e4m3 codes + one fp32 scale per entry,
+ * the query is quantised the same way, one scale per (token, head) row:
+ *     s[b,i,h] = max_d |q_idx[b,i,h,d]| / 448 in fp32 (NaN elements ignored;
+ *                1 where the quotient is 0),
+ *     code[d]  = e4m3 nearest-even of the fp32 quotient q_idx[b,i,h,d] / s,
+ * and I(t, j) is computed on the quantised rows code * s.  The code dot
+ * products run on the fp8 matrix cores, whose sums are not rounded like fp32
+ * ones: within each group of 8 consecutive dims the products are aligned to
+ * the largest one and the bits of the others below 2^-13 of its power of two
+ * are dropped (the group sums then add in fp32), so each dot product may be
+ * off by up to 7 * 2^-13 of its group's largest product per group, before the
+ * scales apply.  The selection, ties, outputs, limits, workspace
+ * (csa_index_topk_workspace with k_dt = CSA_FP8_E4M3) and errors are those of
+ * csa_index_topk, on the scores so computed.
+ *
+ *   q_idx     [B, T, H_I, d_I] bf16;  k_idx [B, N_alloc, d_I] e4m3 codes;
+ *   k_scale   [B, N_alloc] fp32 (required when N_alloc > 0).
+ */
+csa_status_t csa_index_topk_fp8(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+                                int B, int64_t T, int H_I, int d_I, int64_t N_alloc, int64_t t0, int m,
+                                int top_k, int32_t* out_idx, float* out_score, void* workspace,
+                                size_t workspace_bytes, csa_stream_t stream);
 
 /*
  * csa_attend -- CSA core attention: selected compressed entries + raw window.

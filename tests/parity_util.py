@@ -8,6 +8,19 @@ Criteria (each derived from the arithmetic of the two sides):
   quotient r/scale sits within binary32 rounding of a code midpoint.
 * top-k: the GPU set must be a valid top-k of the oracle's fp64 scores with a
   1e-5 relative tie band at the k-th score (several sets are correct there).
+* fp8 x fp8 top-k (csa_index_topk_fp8): the matrix cores sum e4m3 products in
+  groups of 8 k-slots (8 consecutive dims here), aligned to the group's
+  largest product, and drop the bits of every other product below 2^-13 of
+  that product's power of two (measured on gfx950: a product 2^-14 times the
+  largest vanishes, 2^-13 survives; the group sums then add in binary32).  So
+  each dot product carries an error below 7 * 2^-13 * (largest product) per
+  group plus binary32 rounding, and a score below
+  E = sum_h |w_h| (sum_groups 7 * 2^-12 * max_d |q_d k_d| + 2^-21 sum_d |q_d k_d|)
+  on the stored values (the bound doubled for margin; ReLU is 1-Lipschitz).
+  The GPU's scores must lie within E (plus the 1e-5 relative fp32 allowance)
+  of the oracle's, and its set must be a top-k of some scores within E of the
+  oracle's: min over members of (s + E) >= max over visible non-members of
+  (s - E), NaN scores ranking first as everywhere.
 * approximate (bf16-score) top-k: the GPU set must be exactly the top-k, ties
   to the lower index, of the oracle's scores rounded to binary32 and then to
   bf16; where a binary32 score lies within 2^-20 of a bf16 rounding midpoint
@@ -137,8 +150,10 @@ def check_topk_rows(idx_gpu, score_gpu, scores64, visible, k):
             same_inf = np.isinf(so) & (sg == so)
             reg = ~nan & ~np.isinf(so)
             assert np.all(same_inf | ~np.isinf(so)), f"row {i}: infinite scores"
-            assert np.all(np.abs(sg[reg] - so[reg]) <= 1e-5 * np.maximum(np.abs(so[reg]), 1e-2 * scale)), \
-                f"row {i}: scores"
+            err = np.abs(sg[reg] - so[reg]) / np.maximum(np.abs(so[reg]), 1e-2 * scale)
+            assert np.all(err <= 1e-5), \
+                f"row {i}: scores (worst relative error {err.max():.3e} at entry {row[:kk][reg][err.argmax()]}, " \
+                f"{int((err > 1e-5).sum())} of {err.size} above 1e-5)"
             assert np.all(np.isneginf(score_gpu[i, kk:]))
         swaps += sw
     return swaps
@@ -209,3 +224,63 @@ def check_attention_nonfinite(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, what="
         ok = ~nf & ~loose
         dl = np.abs(lse_gpu[ok] - lse_ref[ok])
         assert np.all(dl <= 1e-4 + 1e-5 * np.abs(lse_ref[ok])), f"{what}: lse"
+
+
+def fp8_score_error_bound(q_st, w, k_st):
+    """E [T, N] of the fp8 x fp8 criterion above, from the stored query
+    q_st [T, H, d], weights w [T, H] (None: ones) and stored keys k_st [N, d].
+    Entries whose stored values are not finite get +inf."""
+    T, H, d = q_st.shape
+    N = k_st.shape[0]
+    aq = np.abs(np.nan_to_num(q_st, nan=np.inf))
+    ak = np.abs(np.nan_to_num(k_st, nan=np.inf))
+    aw = np.ones((T, H)) if w is None else np.abs(np.asarray(w, dtype=np.float64))
+    E = np.zeros((T, N))
+    with np.errstate(invalid="ignore", over="ignore"):
+        for t in range(T):
+            for h in range(H):
+                prod = aq[t, h][None, :] * ak  # [N, d]
+                grp = prod.reshape(N, d // 8, 8).max(-1).sum(-1)
+                E[t] += aw[t, h] * (7 * 2.0 ** -12 * grp + 2.0 ** -21 * prod.sum(-1))
+    return np.where(np.isfinite(E), E, np.inf)
+
+
+def check_topk_rows_fp8(idx_gpu, score_gpu, scores64, visible, k, E):
+    """check_topk_rows under the fp8 x fp8 criterion (per-entry bound E [T, N])."""
+    for i in range(idx_gpu.shape[0]):
+        row = idx_gpu[i]
+        c = int(visible[i])
+        kk = min(k, c)
+        assert np.all(row[:kk] >= 0) and np.all(row[kk:] == -1), f"row {i}: padding"
+        G = row[:kk].astype(np.int64)
+        assert np.unique(G).size == kk and np.all(G < c), f"row {i}: members"
+        s = scores64[i, :c]
+        nan = np.isnan(s)
+        inG = np.zeros(c, dtype=bool)
+        inG[G] = True
+        nan_idx = np.nonzero(nan)[0]
+        if nan_idx.size >= kk:
+            assert np.array_equal(np.sort(G), nan_idx[:kk]), f"row {i}: not the lowest-indexed NaN entries"
+        else:
+            assert np.all(inG[nan_idx]), f"row {i}: a NaN-score entry is missing"
+            mem = G[~nan[G]]
+            out = np.nonzero(~nan & ~inG)[0]
+            if mem.size and out.size:
+                lo = np.min(s[mem] + E[i, mem])
+                hi = np.max(s[out] - E[i, out])
+                assert lo >= hi, f"row {i}: a member scores below a non-member beyond the bound ({lo} < {hi})"
+        if score_gpu is not None:
+            sg = score_gpu[i, :kk].astype(np.float64)
+            so = scores64[i, G]
+            fin = np.isfinite(s)
+            scale = np.abs(s[fin]).max() if fin.any() else 1.0
+            nn = np.isnan(so)
+            assert np.all(np.isnan(sg[nn])), f"row {i}: a NaN score reported as a number"
+            inf = np.isinf(so)
+            assert np.all(sg[inf] == so[inf]), f"row {i}: infinite scores"
+            reg = ~nn & ~inf
+            tol = E[i, G][reg] + 1e-5 * np.maximum(np.abs(so[reg]), 1e-2 * scale)
+            err = np.abs(sg[reg] - so[reg])
+            assert np.all(err <= tol), \
+                f"row {i}: scores (worst error / bound {np.max(err / tol):.3f} at entry {G[reg][np.argmax(err / tol)]})"
+            assert np.all(np.isneginf(score_gpu[i, kk:]))

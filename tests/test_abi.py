@@ -38,11 +38,11 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
         assert n in csa.SIGNATURES, n
-    assert L.csa_abi_version() == 5
+    assert L.csa_abi_version() == 6
     for s, name in enumerate(csa.STATUS):
         assert L.csa_status_string(s).decode() == name
 
@@ -122,6 +122,27 @@ def test_approximate_selector_validates_like_the_exact_one(L):
     for kw in (dict(q=None), dict(out=None), dict(q_dt=F32), dict(k_dt=FP8), dict(ks=P),
                dict(top_k=0), dict(top_k=2049), dict(H_I=17), dict(d_I=48), dict(q=MIS)):
         assert index(L, fn="csa_index_topk_bf16", **kw) == index(L, **kw) != OK, kw
+
+
+
+def index_fp8(L, q=P, w=P, k=P, ks=P, B=4, T=1, H_I=8, d_I=64, N=1024, t0=4095, m=4, top_k=64, out=P,
+              score=None, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.csa_index_topk_workspace(B, T, H_I, d_I, N, top_k, FP8)
+    return L.csa_index_topk_fp8(q, w, k, ks, B, T, H_I, d_I, N, t0, m, top_k, out, score, ws, ws_bytes, None)
+
+
+def test_fp8_indexer_validates_like_the_exact_one(L):
+    """csa_index_topk_fp8 is csa_index_topk on (bf16, e4m3) with the query quantised:
+    it rejects what the exact indexer rejects for those dtypes."""
+    assert index_fp8(L, ks=None) == E_NULL          # e4m3 keys need k_scale
+    for kw in (dict(q=None), dict(out=None), dict(top_k=0), dict(top_k=2049), dict(H_I=17), dict(d_I=48),
+               dict(q=MIS), dict(w=MIS), dict(ks=MIS), dict(m=0), dict(t0=-1), dict(T=-1)):
+        ref = dict(k_dt=FP8, ks=P)
+        ref.update(kw)
+        assert index_fp8(L, **kw) == index(L, **ref) != OK, kw
+    need = L.csa_index_topk_workspace(4, 1, 8, 64, 262144, 1024, FP8)
+    assert index_fp8(L, N=262144, top_k=1024, ws_bytes=need - 1) == E_WS
 
 
 def test_index_validation(L):

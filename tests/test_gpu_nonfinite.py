@@ -18,7 +18,8 @@ import torch
 import compressed_attention_csa_amd as csa
 import inputgen
 from oracle import formats, method
-from parity_util import check_attention_nonfinite, check_topk_rows, f64, to_dev_bf16
+from parity_util import (check_attention_nonfinite, check_topk_rows, check_topk_rows_fp8, f64,
+                         fp8_score_error_bound, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -110,6 +111,51 @@ def test_index_prefill_nan_inf():
     assert np.all(np.sort(idx[0, 10]) == np.arange(k)) and np.all(np.sort(idx[0, 20]) == np.arange(k))
     for i in (0, 40, 69):
         assert {64, 1001, 39000} <= set(idx[0, i].tolist())
+
+
+
+@pytest.mark.parametrize("T", [1, 70], ids=["decode", "prefill"])
+def test_index_fp8_query_nonfinite(T):
+    """The fp8 x fp8 indexer with non-finite and tiny query rows: a NaN query
+    element (its row's scale ignores it, its code is NaN, every score of the
+    query is NaN), an infinite one (the row's scale is infinite, so every
+    stored element is NaN), a head whose elements are all the smallest bf16
+    subnormal (a subnormal binary32 scale), and NaN / infinite key codes."""
+    B, H_I, d_I, N, m, k = 1, 8, 64, 20000 if T == 1 else 40000, 4, 64
+    t0 = 4 * N - T
+    say("index fp8 query non-finite T", T)
+    q = gen("nfq_q", (B, T, H_I, d_I), "bf16", seed=41)
+    w = gen("nfq_w", (B, T, H_I), "f32", seed=42).abs()
+    rows = [0, T // 2, T - 1] if T > 1 else [0, 0, 0]
+    q[0, rows[0], 0, :] = 2.0 ** -133
+    if T > 1:
+        q[0, rows[1], 2, 7] = NAN
+        q[0, rows[2], 1, 3] = INF
+    r = gen("nfq_k", (B, N, d_I), "f32", seed=43).numpy()
+    r[0, 777, 9] = INF  # quantised to an infinite scale with codes 0 and one NaN code
+    codes, scale, _ = formats.e4m3_quantize_rows(r)
+    codes[0, 64, 1] = 0x7F
+    codes[0, 19000, 5] = 0xFF
+    with np.errstate(invalid="ignore"):
+        k64 = formats.e4m3_decode(codes) * scale[..., None].astype(np.float64)
+    kd, ks = torch.from_numpy(codes).to(DEV), torch.from_numpy(scale).to(DEV)
+    out_idx = torch.full((B, T, k), 12345, dtype=torch.int32, device=DEV)
+    out_score = torch.full((B, T, k), 5.0, dtype=torch.float32, device=DEV)
+    csa.csa_index_topk_fp8(q.to(DEV), w.to(DEV), kd, ks, t0, m, k, out_idx, out_score)
+    torch.cuda.synchronize()
+    idx, sc = out_idx.cpu().numpy(), out_score.cpu().numpy()
+    scores, vis = method.index_scores_fp8q(f64(q[0]), f64(w[0]), k64[0], t0, m)
+    for e in (64, 777, 19000):
+        hit = np.nonzero(idx[0, rows[0]] == e)[0]
+        say(f"  entry {e}: oracle score {scores[rows[0], e]}, kernel "
+            f"{sc[0, rows[0], hit[0]] if hit.size else 'not selected'}")
+    E = fp8_score_error_bound(method.quantize_query_e4m3(f64(q[0])), f64(w[0]), k64[0])
+    check_topk_rows_fp8(idx[0], sc[0], scores, vis, k, E)
+    if T > 1:
+        for i in rows[1:]:
+            assert np.isnan(scores[i, : vis[i]]).all()
+            assert np.all(np.sort(idx[0, i]) == np.arange(k)), "every score NaN: the lowest indices win"
+    assert {64, 777, 19000} <= set(idx[0, rows[0]].tolist())
 
 
 def _attend(hca, q, kc, vc, idx, kr, vr, t0, W, m, scale, H, d):

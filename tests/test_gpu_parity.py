@@ -16,7 +16,8 @@ import torch
 import compressed_attention_csa_amd as csa
 import inputgen
 from oracle import formats, method
-from parity_util import (check_attention, check_bf16_selection_row, check_e4m3, check_topk_rows, f64, bf16_bits,
+from parity_util import (check_attention, check_bf16_selection_row, check_e4m3, check_topk_rows,
+                         check_topk_rows_fp8, fp8_score_error_bound, f64, bf16_bits,
                          to_dev_bf16, to_dev_f32, ulp_diff_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -298,6 +299,50 @@ def test_index_topk(case):
 
 
 BF16_SEL_CASES = [INDEX_CASES[i] for i in (0, 1, 3, 8, 9, 13)]
+
+
+FP8Q_CASES = [c for c in INDEX_CASES if c[0] == "e4m3"] + [
+    # kind, B, T, H_I, d_I, N, t0, m, k, with_w
+    ("e4m3", 2, 1, 16, 64, 12000, 4 * 12000 - 1, 4, 1, True),      # decode, 16 heads, k = 1
+    ("e4m3", 2, 100, 8, 64, 3000, 11900, 4, 256, True),            # prefill path
+    ("e4m3", 1, 130, 4, 32, 9000, 30000, 4, 512, False),           # prefill, 4 heads, d_I 32, ragged T
+    ("e4m3", 1, 96, 8, 64, 20000, 4 * 20000 - 96, 4, 2048, True),  # prefill, k = 2048
+]
+
+
+@pytest.mark.parametrize("case", FP8Q_CASES, ids=[f"{c[0]}-B{c[1]}T{c[2]}H{c[3]}d{c[4]}-N{c[5]}-k{c[8]}"
+                                                  for c in FP8Q_CASES])
+def test_index_topk_fp8_query(case):
+    """The fp8 x fp8 indexer (csa_index_topk_fp8): the query quantised to e4m3
+    per (token, head) row in the kernel; selection and scores against the
+    oracle's index_scores_fp8q, through the decode and prefill paths."""
+    kind, B, T, H_I, d_I, N, t0, m, k, with_w = case
+    say("index_topk fp8 query", case)
+    q = gen("idx_q", (B, T, H_I, d_I), "bf16", seed=N + T)
+    w = gen("idx_w", (B, T, H_I), "f32", seed=N + 1) if with_w else None
+    kd, ks, k64 = make_keys(kind, B, N, d_I, seed=N)
+    out_idx = torch.full((B, T, k), 12345, dtype=torch.int32, device=DEV)
+    out_score = torch.full((B, T, k), 5.0, dtype=torch.float32, device=DEV)
+    qd, wd = q.to(DEV), (None if w is None else w.to(DEV))
+    csa.csa_index_topk_fp8(qd, wd, kd, ks, t0, m, k, out_idx, out_score)
+    again = torch.full_like(out_idx, 777)
+    csa.csa_index_topk_fp8(qd, wd, kd, ks, t0, m, k, again)
+    torch.cuda.synchronize()
+    assert torch.equal(out_idx, again), "selection order is not deterministic"
+    idx, sc = out_idx.cpu().numpy(), out_score.cpu().numpy()
+    differ = 0
+    for b in range(B):
+        wb = None if w is None else f64(w[b])
+        scores, vis = method.index_scores_fp8q(f64(q[b]), wb, k64[b], t0, m)
+        E = fp8_score_error_bound(method.quantize_query_e4m3(f64(q[b])), wb, k64[b])
+        check_topk_rows_fp8(idx[b], sc[b], scores, vis, k, E)
+        exact, _ = method.index_scores(f64(q[b]), wb, k64[b], t0, m)
+        fin = np.isfinite(exact) & np.isfinite(scores)
+        differ += int(np.sum(np.abs(exact - scores)[fin] > E[fin]))
+        rel = E[fin] / np.maximum(np.abs(scores[fin]), 1e-30)
+        say(f"  b={b}: median error bound / |score| {np.median(rel):.2e}")
+    assert differ > 0, "no score moved beyond the bound by quantising the query: the case does not test it"
+
 
 
 @pytest.mark.parametrize("case", BF16_SEL_CASES,
