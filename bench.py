@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
+COPY_CALIBRATION_BYTES = 256 << 20
 METRIC = "decode query-tokens/s + HBM GB/s at 1M ctx; prefill TFLOP/s (frac. of peak)"
 
 
@@ -447,6 +448,9 @@ EXTRA = {"csa_compress_pro_1m": lambda seed, R: CompressCache(__import__("inputg
 # ----------------------------------------------------------------------------- timing
 
 
+PROFILE_MARKER = False  # --profile-marker: a spin kernel of torch's marks where the timed launches start
+
+
 def time_workload(name, seed, steps, warmup, graph=True):
     import torch
     import compressed_attention_csa_amd as csa
@@ -491,6 +495,8 @@ def time_workload(name, seed, steps, warmup, graph=True):
         g.replay()
         torch.cuda.synchronize()
     log(f"[bench] {name}: timing {reps * R} steps")
+    if PROFILE_MARKER:
+        torch.cuda._sleep(1000)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     torch.cuda.synchronize()
     for e0, e1 in ev:
@@ -596,6 +602,217 @@ def load_traffic(key):
     return ent.get("hbm_bytes_per_launch")
 
 
+# ----------------------------------------------------------------------------- rocprofv3 summaries
+#
+# One workload per profiler process: a kernel trace run, a FETCH_SIZE run, a WRITE_SIZE run and,
+# optionally, one run of SQ counters, each of `bench.py --no-graph --profile-marker --workload W
+# --legs ""`.  The program launches the same kernels in the same order in every run, so the
+# k-th dispatch of a (kernel, grid, workgroup) in one run is the k-th in the others; only the
+# dispatches after the marker (the timed steps) are summarised.
+
+
+def _read_csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _grid(row):
+    return int(row.get("Grid_Size") or row.get("Grid_Size_X") or 0)
+
+
+def _wg(row):
+    return int(row.get("Workgroup_Size") or row.get("Workgroup_Size_X") or 0)
+
+
+def _after_marker(rows, key="Dispatch_Id"):
+    """The dispatches after the last torch spin kernel, in dispatch order, keyed by their
+    ordinal within (kernel, grid, workgroup)."""
+    rows = sorted(rows, key=lambda r: int(r[key]))
+    cut = max((i for i, r in enumerate(rows) if "sleep" in r["Kernel_Name"] or "spin" in r["Kernel_Name"]),
+              default=None)
+    if cut is None:
+        raise SystemExit("no profiling marker in the dispatch list (run bench.py with --profile-marker)")
+    out, seen = {}, {}
+    for r in rows[cut + 1:]:
+        k = (r["Kernel_Name"], _grid(r), _wg(r))
+        n = seen.get(k, 0)
+        seen[k] = n + 1
+        out[(k, n)] = r
+    return out
+
+
+def _counter(directory, name):
+    """Per dispatch (after the marker): the value of counter `name`, summed over its rows."""
+    rows = [r for r in _read_csv_rows(directory, "counter_collection.csv") if r["Counter_Name"] == name]
+    by_id = {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        if d not in by_id:
+            by_id[d] = dict(r, Counter_Value=0.0)
+        by_id[d]["Counter_Value"] += float(r["Counter_Value"])
+    return {k: v["Counter_Value"] for k, v in _after_marker(list(by_id.values())).items()}
+
+
+def _role(kernel, workload):
+    kernel = _short(kernel)
+    att = "hca_attend" if workload.startswith("hca") else "csa_attend"
+    if kernel.startswith(("idx_topk_kernel", "idx_prefill_kernel")):
+        return "index_topk"
+    if kernel.startswith("attend_merge_kernel"):
+        return att + "_merge"
+    if kernel.startswith("attend_bf16_kernel"):
+        return "hca_attend" if ", true," in kernel.split("<", 1)[-1][:40] else "csa_attend"
+    if kernel.startswith("hca_multi_kernel"):
+        return "hca_attend"
+    if kernel.startswith("attend_f32_kernel"):
+        return "attend (fp32)"
+    if kernel.startswith("compress_kernel"):
+        return "append" if kernel.endswith("true>") else "compress"
+    if kernel.startswith("stream_read_kernel"):
+        return "stream_read"
+    return None
+
+
+def _short(kernel):
+    k = kernel[5:] if kernel.startswith("void ") else kernel
+    k = k.replace("(anonymous namespace)::", "").replace("csa::", "")
+    return k.split("(")[0].strip()
+
+
+def profile_summary(root, calib, workload, traffic_out=None, command_note=""):
+    trace = _after_marker(_read_csv_rows(os.path.join(root, "trace"), "kernel_trace.csv"))
+    fetch = _counter(os.path.join(root, "fetch"), "FETCH_SIZE")
+    write = _counter(os.path.join(root, "write"), "WRITE_SIZE")
+    scale = {"FETCH_SIZE": 1.0, "WRITE_SIZE": 1.0}
+    if calib:
+        for cname, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            rows = [r for r in _read_csv_rows(os.path.join(calib, sub), "counter_collection.csv")
+                    if r["Counter_Name"] == cname and "copy" in r["Kernel_Name"].lower()]
+            per = {}
+            for r in rows:
+                per[int(r["Dispatch_Id"])] = per.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+            vals = sorted(per.values())
+            if vals:
+                kib = vals[len(vals) // 2]
+                scale[cname] = COPY_CALIBRATION_BYTES / (kib * 1024.0)
+    sq_names = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_WAVE_CYCLES",
+                "SQ_WAIT_ANY", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+    sq = {}
+    if os.path.isdir(os.path.join(root, "sq")):
+        for n in sq_names:
+            try:
+                sq[n] = _counter(os.path.join(root, "sq"), n)
+            except SystemExit:
+                pass
+    # Per (kernel, grid, workgroup): durations from the trace, bytes per dispatch from the
+    # counter runs, paired dispatch by dispatch.
+    groups = {}
+    rejected = 0
+    for (k, n), r in trace.items():
+        g = groups.setdefault(k, {"us": [], "rd": [], "wr": [], "sq": {x: [] for x in sq}})
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        rd = fetch.get((k, n))
+        wr = write.get((k, n))
+        if rd is not None and wr is not None:
+            rd_b = rd * 1024.0 * scale["FETCH_SIZE"]
+            wr_b = wr * 1024.0 * scale["WRITE_SIZE"]
+            if (rd_b + wr_b) / (us * 1e-6) > PEAK_HBM_GBPS * 1e9:
+                rejected += 1  # more bytes than HBM can move in that time: not the same launch
+            else:
+                g["rd"].append(rd_b)
+                g["wr"].append(wr_b)
+        g["us"].append(us)
+        for x in sq:
+            v = sq[x].get((k, n))
+            if v is not None:
+                g["sq"][x].append(v)
+
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2] if v else None
+
+    lines = [f"# Kernels of `{workload}`: durations, HBM traffic" + (" and SQ counters" if sq else ""), ""]
+    lines += ["Commands (repository root on the MI355X box; each GPU step under `timeout`):", ""]
+    lines += ["    " + c for c in command_note.split(" ;; ") if c]
+    lines += ["", f"Kernel sources digest (bench.kernel_source_digest): `{kernel_source_digest()}`", "",
+              f"Counter scale factors from the plain device copy: FETCH_SIZE x {scale['FETCH_SIZE']:.4f}, "
+              f"WRITE_SIZE x {scale['WRITE_SIZE']:.4f}.", "",
+              "Only dispatches after the profiling marker (the timed steps) are listed.  Durations are "
+              "from the kernel trace (eager launches); bytes are medians per dispatch of the counter "
+              "runs, paired with the trace dispatch by dispatch (the k-th launch of the same kernel, "
+              f"grid and workgroup).  Pairs implying more than 8 TB/s are dropped: {rejected} dropped.", ""]
+    hdr = "| kernel | role | grid | wg | launches | avg us | min us | max us | HBM read MB | HBM write MB | GB/s |"
+    lines += [hdr, "|" + "---|" * 11]
+    role_tot = {}
+    for k in sorted(groups, key=lambda k: -sum(groups[k]["us"])):
+        g = groups[k]
+        avg = sum(g["us"]) / len(g["us"])
+        rd, wr = med(g["rd"]), med(g["wr"])
+        role = _role(k[0], workload) or "-"
+        gbps = "-" if rd is None else f"{(rd + wr) / (avg * 1e-6) / 1e9:.1f}"
+        lines.append(f"| {_short(k[0])} | {role} | {k[1]} | {k[2]} | {len(g['us'])} | {avg:.2f} | "
+                     f"{min(g['us']):.2f} | {max(g['us']):.2f} | "
+                     f"{'-' if rd is None else f'{rd / 1e6:.2f}'} | {'-' if wr is None else f'{wr / 1e6:.3f}'} | "
+                     f"{gbps} |")
+        t = role_tot.setdefault(role, {"us": 0.0, "rd": 0.0, "wr": 0.0, "n": 0, "bytes_ok": True})
+        t["us"] += avg
+        t["n"] = max(t["n"], len(g["us"]))
+        if rd is None:
+            t["bytes_ok"] = False
+        else:
+            t["rd"] += rd
+            t["wr"] += wr
+    if sq:
+        lines += ["", "SQ counters (medians per dispatch).  GRBM_GUI_ACTIVE counts busy cycles per XCD, summed "
+                  "over the 8 XCDs, so a kernel's cycles are C = GRBM_GUI_ACTIVE / 8 (the table's `cycles`, to be "
+                  "compared with the traced duration x clock).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (C x 1024 "
+                  "SIMDs); VALU busy = 4 x SQ_ACTIVE_INST_VALU / (C x 1024 SIMDs); co-issue = "
+                  "SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES:",
+                  ""]
+        lines += ["| kernel | " + " | ".join(sq_names) + " | cycles | MFMA busy | VALU busy | co-issue | waiting |",
+                  "|" + "---|" * (len(sq_names) + 6)]
+        for k in sorted(groups, key=lambda k: -sum(groups[k]["us"])):
+            v = {x: med(groups[k]["sq"][x]) for x in sq}
+            if any(x is None for x in v.values()):
+                continue
+            cyc = (v.get("GRBM_GUI_ACTIVE") or 0) / 8
+            mf = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 1024) if cyc else float("nan")
+            va = 4 * v["SQ_ACTIVE_INST_VALU"] / (cyc * 1024) if cyc else float("nan")
+            co = v["SQ_VALU_MFMA_COEXEC_CYCLES"] / v["SQ_VALU_MFMA_BUSY_CYCLES"] if v["SQ_VALU_MFMA_BUSY_CYCLES"] else 0
+            wt = v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"] if v["SQ_WAVE_CYCLES"] else 0
+            lines.append(f"| {_short(k[0])} | " + " | ".join(f"{v[x]:.0f}" for x in sq_names) +
+                         f" | {cyc:.0f} | {mf:.1%} | {va:.1%} | {co:.1%} | {wt:.1%} |")
+    lines += ["", "Per call of each role (all its kernels, summed):", ""]
+    traffic = {}
+    for role, t in sorted(role_tot.items()):
+        if role == "-":
+            continue
+        b = f"read {t['rd'] / 1e6:.2f} MB + write {t['wr'] / 1e6:.3f} MB" if t["bytes_ok"] else "bytes not paired"
+        lines.append(f"- `{role}`: {t['us']:.2f} us, {b}")
+        if t["bytes_ok"]:
+            traffic[f"{role}@{workload}"] = {"hbm_bytes_per_launch": int(t["rd"] + t["wr"]),
+                                             "read_bytes": int(t["rd"]), "write_bytes": int(t["wr"]),
+                                             "trace_us": round(t["us"], 3),
+                                             "source_digest": kernel_source_digest(),
+                                             "scale": {x: round(y, 4) for x, y in scale.items()}}
+    if traffic_out:
+        try:
+            with open(traffic_out) as f:
+                data = json.load(f)
+        except (OSError, ValueError):
+            data = {}
+        data.update(traffic)
+        with open(traffic_out, "w") as f:
+            json.dump(data, f, indent=1, sort_keys=True)
+            f.write("\n")
+    return "\n".join(lines) + "\n"
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 
@@ -683,10 +900,26 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (10 times) and exit; used to scale "
                          "the HBM byte counters of a profiler")
+    ap.add_argument("--profile-marker", action="store_true",
+                    help="launch one torch spin kernel right before the timed steps of each workload, so "
+                         "that a profiler's dispatch list can be cut at that point")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="no GPU: summarise rocprofv3 CSV runs of one workload under DIR (trace/, fetch/, "
+                         "write/, optionally sq/) with --calibration; prints markdown")
+    ap.add_argument("--calibration", metavar="DIR", help="rocprofv3 runs of --copy-calibration (fetch/, write/)")
+    ap.add_argument("--traffic-out", metavar="JSON", help="with --profile-summary: update this traffic file")
+    ap.add_argument("--command-note", default="", help="with --profile-summary: the commands, for the summary")
     args = ap.parse_args()
+    if args.profile_summary:
+        print(profile_summary(args.profile_summary, args.calibration, args.workload, args.traffic_out,
+                              args.command_note))
+        return
+    global PROFILE_MARKER
+    PROFILE_MARKER = args.profile_marker
     if args.copy_calibration:
         import torch
         n = args.copy_calibration << 20
+        assert n == COPY_CALIBRATION_BYTES, "the summaries scale counters by a 256 MiB copy"
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(10):
@@ -720,7 +953,12 @@ def main():
         s["roofline"] = roofline(r, ceiling)
         legs[name] = s
     hs = summarize(head)
-    wl = __import__("inputgen").WORKLOADS[args.workload]
+    base = args.workload.partition("+")[0]
+    if base not in __import__("inputgen").WORKLOADS or "query_tokens_per_s" not in hs:
+        # Not a decode configuration (a profiling run of one workload): its summary only.
+        print(json.dumps({"workload": args.workload, **hs, "roofline": roofline(head, ceiling)}), flush=True)
+        return
+    wl = __import__("inputgen").WORKLOADS[base]
     line = {
         "metric": METRIC,
         "value": round(hs["query_tokens_per_s"], 1),
