@@ -767,6 +767,21 @@ def profile_summary(root, calib, workload, traffic_out=None, command_note=""):
         else:
             t["rd"] += rd
             t["wr"] += wr
+    extra = {}
+    if os.path.isdir(os.path.join(root, "sq2")):
+        rows = _read_csv_rows(os.path.join(root, "sq2"), "counter_collection.csv")
+        for n in sorted({r["Counter_Name"] for r in rows}):
+            extra[n] = _counter(os.path.join(root, "sq2"), n)
+    if extra:
+        names = list(extra)
+        lines += ["", "Further SQ counters (medians per dispatch; a separate run):", "",
+                  "| kernel | " + " | ".join(names) + " |", "|" + "---|" * (len(names) + 1)]
+        for k in sorted(groups, key=lambda k: -sum(groups[k]["us"])):
+            vals = [med([extra[n][(k, i)] for i in range(len(groups[k]["us"])) if (k, i) in extra[n]])
+                    for n in names]
+            if any(v is None for v in vals):
+                continue
+            lines.append(f"| {_short(k[0])} | " + " | ".join(f"{v:.0f}" for v in vals) + " |")
     if sq:
         lines += ["", "SQ counters (medians per dispatch).  GRBM_GUI_ACTIVE counts busy cycles per XCD, summed "
                   "over the 8 XCDs, so a kernel's cycles are C = GRBM_GUI_ACTIVE / 8 (the table's `cycles`, to be "

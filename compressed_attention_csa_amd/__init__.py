@@ -28,6 +28,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libcsa_debug.so")  # CSA_DEBUG build: NaN-poisoned scratch, plan checks
 
 CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
 STATUS = ["CSA_OK", "CSA_E_NULL", "CSA_E_SHAPE", "CSA_E_DTYPE", "CSA_E_ALIGN",
@@ -75,20 +76,44 @@ class CsaError(RuntimeError):
         super().__init__(f"{fn}: {name}: {detail}")
 
 
+def load(path: str) -> ctypes.CDLL:
+    """The library at ``path`` with every declared signature bound."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m compressed_attention_csa_amd.build`"
+                           + (" --debug" if path == DEBUG_LIB_PATH else ""))
+    L = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """The loaded libcsa.so (built by ``python -m compressed_attention_csa_amd.build``)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m compressed_attention_csa_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            f = getattr(L, name)
-            f.restype = res
-            f.argtypes = args
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+class use_library:
+    """Within the block, every call of this module goes to the library at ``path``
+    (for instance DEBUG_LIB_PATH); the previous one is restored on exit."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.prev = _lib
+        _lib = load(self.path)
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.prev
+        return False
 
 
 def _check(fn, status):

@@ -1,7 +1,10 @@
 """Build libcsa.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-Usage: python -m compressed_attention_csa_amd.build   (or call build()).
+Usage: python -m compressed_attention_csa_amd.build [--debug]   (or call build()).
 Every source is compiled to an object under _build/ in parallel, then linked.
+build(debug=True) makes libcsa_debug.so instead, compiled with CSA_DEBUG: it
+poisons workspace scratch and LDS with NaN words before use and checks launch
+plans on the host (the same kernels otherwise).
 """
 from __future__ import annotations
 
@@ -15,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
+DEBUG_LIB = os.path.join(PKG, "libcsa_debug.so")
 SOURCES = ["compress.hip", "index.hip", "index_prefill.hip", "attend.hip", "api.cpp", "profile.cpp",
            "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -26,32 +30,33 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src + ".o")
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(BUILD, "debug" if debug else "", src + ".o")
     lang = [] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *(["-DCSA_DEBUG=1"] if debug else []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, debug), srcs))
+    out = DEBUG_LIB if debug else LIB
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, debug="--debug" in sys.argv[1:])
     sys.exit(0)

@@ -236,6 +236,7 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
   constexpr int DVT = D / 16;                    // 16-column tiles of the output
   constexpr int NB = 2 * PAIR;                   // LDS tile buffers
   __shared__ LdsB<D, NB> L;
+  debug_poison_lds(L);
   const int64_t r = div64(blockIdx.x, p.splits), s = blockIdx.x - r * p.splits;
   const RowSlots x = row_slots(a, p, r, s);
   if (s >= x.S) return;
@@ -656,6 +657,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 8
   constexpr bool F16 = !KV8;  // binary16 path available
   static_assert(NW <= 8, "one V range flag per wave");
   __shared__ LdsM<D> L;
+  debug_poison_lds(L);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, col = lane & 15;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, HW = H / 16;
@@ -1218,6 +1220,7 @@ struct LdsF32 {
 template <int D>
 __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, AttendPlan p) {
   __shared__ LdsF32<D> L;
+  debug_poison_lds(L);
   int64_t hg, r, s;
   if (!decode_block(p, hg, r, s)) return;
   const RowSlots x = row_slots(a, p, r, s);
@@ -1461,6 +1464,18 @@ constexpr int64_t kHcaMultiMinT = 16;
 
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p) {
   if (p.rows == 0) return hipSuccess;
+  CSA_HOST_CHECK(p.splits >= 1 && p.per_split >= 1 && p.splits * p.per_split >= p.slots);
+  CSA_HOST_CHECK(p.splits == 1 || (a.ws != nullptr && p.off_part >= kHeaderBytes && p.off_ml > p.off_part &&
+                                   p.off_ml <= p.ws_bytes));
+  if (kDebug && p.splits > 1 && p.ws_bytes > kHeaderBytes) {
+    const hipError_t e = debug_poison(static_cast<uint8_t*>(a.ws) + kHeaderBytes, p.ws_bytes - kHeaderBytes, a.stream);
+    if (e != hipSuccess) return e;
+  }
+  const bool multi = a.bf16 && a.hca && p.splits == 1 && a.T >= kHcaMultiMinT && 8 % (a.H / 16) == 0;
+  log_dispatch("%s: B=%d T=%lld H=%d d=%d %s -> %s, %lld rows x %lld splits of %lld slots%s", a.hca ? "hca_attend" : "csa_attend",
+               a.B, (long long)a.T, a.H, a.d, a.bf16 ? (a.kv8 ? "bf16, fp8 cache" : "bf16") : "fp32",
+               multi ? "multi-token kernel" : (a.bf16 ? "bf16 kernel" : "fp32 kernel"), (long long)p.rows,
+               (long long)p.splits, (long long)p.per_split, p.splits > 1 ? " + merge" : "");
   // The multi-token kernel takes 8 / (H / 16) tokens per wave pair: H / 16 must divide 8.
   if (a.bf16 && a.hca && p.splits == 1 && a.T >= kHcaMultiMinT && 8 % (a.H / 16) == 0) {
     ProfScope prof("hca_attend", a.stream);

@@ -222,6 +222,22 @@ __device__ __forceinline__ uint64_t bf16x8_to_e4m3x8(uint4 v, float scale) {
   return r;
 }
 
+// ---------------------------------------------------------------- debug builds
+
+// Builds with CSA_DEBUG: fill a kernel's LDS object with all-ones words (NaN as
+// fp32 and bf16) and wait for every thread, before the kernel uses it.  Called
+// first thing in a kernel, where every thread of the workgroup reaches it.
+template <typename T>
+__device__ __forceinline__ void debug_poison_lds(T& obj) {
+#ifdef CSA_DEBUG
+  uint32_t* p = reinterpret_cast<uint32_t*>(&obj);
+  for (uint32_t i = threadIdx.x; i < uint32_t(sizeof(T) / 4); i += blockDim.x) p[i] = 0xffffffffu;
+  __syncthreads();
+#else
+  (void)obj;
+#endif
+}
+
 // ---------------------------------------------------------------- cross-workgroup handoff
 //
 // Data that one workgroup hands to another inside the same kernel is written

@@ -63,6 +63,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     void* __restrict__ out, float* __restrict__ out_scale, AppendTail at) {
   __shared__ double alpha[128];
   __shared__ float zmax_s;
+  debug_poison_lds(alpha);
+  debug_poison_lds(zmax_s);
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
   const TIn* xn = reinterpret_cast<const TIn*>(at.x_new) + int64_t(b) * at.T_new * d;
@@ -185,6 +187,9 @@ hipError_t launch(const CompressArgs& a, const AppendTail& at) {
   int64_t blocks = t.cmp_blocks;
   if (APPEND) blocks += (int64_t(t.T_new) * (a.d * int64_t(sizeof(TIn)) / 16) + kThreads - 1) / kThreads;
   dim3 grid(unsigned(blocks), unsigned(a.B));
+  CSA_HOST_CHECK(blocks >= 1 && a.m >= 1 && a.m + a.overlap <= 128);
+  log_dispatch("%s: B=%d d=%d m=%d overlap=%d entries [%lld, %lld) -> grid %lld x %d", APPEND ? "append" : "compress",
+               a.B, a.d, a.m, a.overlap, (long long)a.entry_begin, (long long)a.entry_end, (long long)blocks, a.B);
   ProfScope prof(APPEND ? "append" : "compress", a.stream);
   hipLaunchKernelGGL((compress_kernel<TIn, OUT, APPEND>), grid, dim3(kThreads), 0, a.stream,
                      reinterpret_cast<const TIn*>(a.x), a.n_raw, a.d, a.raw_base, a.logits, a.m, a.overlap,

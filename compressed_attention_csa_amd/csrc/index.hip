@@ -631,6 +631,7 @@ template <int KK, int KPT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void idx_topk_kernel(
     IndexArgs a, IndexPlan p, int64_t row0) {
   __shared__ LdsIdx L;
+  debug_poison_lds(L);
   const int64_t lr = div64(blockIdx.x, p.slices);  // row within this launch
   const int64_t r = row0 + lr;
   const int64_t s = blockIdx.x - lr * p.slices;
@@ -800,7 +801,22 @@ static void launch_kpt(const IndexArgs& a, const IndexPlan& p, int64_t row0, dim
 
 hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p) {
   if (p.rows == 0) return hipSuccess;
+  static const char* const kKinds[] = {"f32", "bf16", "e4m3", "e4m3 (fp8 query)"};
+  log_dispatch("index_topk: B=%d T=%lld H_I=%d d_I=%d N=%lld k=%d keys=%s%s -> %s path, ws %zu B", a.B,
+               (long long)a.T, a.H_I, a.d_I, (long long)a.N_alloc, a.top_k, kKinds[a.key_kind & 3],
+               a.bf16_scores ? " bf16 scores" : "", p.prefill ? "prefill" : "rows x slices", p.ws_bytes);
+  CSA_HOST_CHECK(p.ws_bytes == 0 || a.ws != nullptr);
+  if (kDebug && p.ws_bytes > kHeaderBytes) {
+    const hipError_t e = debug_poison(static_cast<uint8_t*>(a.ws) + kHeaderBytes, p.ws_bytes - kHeaderBytes, a.stream);
+    if (e != hipSuccess) return e;
+  }
   if (p.prefill) return launch_index_prefill(a, p);
+  CSA_HOST_CHECK(p.slice >= 256 && p.slice <= kMaxSlice && p.slice % 256 == 0);
+  CSA_HOST_CHECK(p.slices >= 1 && p.slices * p.slice >= p.c_max);
+  CSA_HOST_CHECK(p.slices == 1 || (p.off_over + size_t(p.chunk_rows) * size_t(a.N_alloc) * 8 <= p.ws_bytes &&
+                                   p.off_cand >= kHeaderBytes && p.chunk_rows <= kIndexChunkRows));
+  log_dispatch("index_topk: %lld rows, %lld slices of %lld entries, %lld rows per launch", (long long)p.rows,
+               (long long)p.slices, (long long)p.slice, (long long)p.chunk_rows);
   const dim3 block(kThreads);
   for (int64_t row0 = 0; row0 < p.rows; row0 += p.chunk_rows) {
     const int64_t nr = (p.rows - row0) < p.chunk_rows ? (p.rows - row0) : p.chunk_rows;

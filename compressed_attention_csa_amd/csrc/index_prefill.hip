@@ -224,6 +224,7 @@ __device__ int wave_compact(uint64_t* buf, int n, uint64_t T) {
 template <int KK, int DI, bool FH>
 __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, IndexPlan p) {
   __shared__ LdsPrefill L;
+  debug_poison_lds(L);
   constexpr bool Q8 = KK == kKeyE4M3Q8;
   constexpr int KB = key_is_e4m3(KK) ? 1 : 2;  // key bytes per element
   constexpr int CPG = DI * KB / 16;              // 16-byte chunks per entry in memory
@@ -690,6 +691,11 @@ bool prefill_path(int64_t T, int H_I, int key_kind) {
 
 hipError_t launch_index_prefill(const IndexArgs& a, const IndexPlan& p) {
   const dim3 grid(unsigned((a.T + kPrefillQPB - 1) / kPrefillQPB), unsigned(a.B)), block(kThreads);
+  CSA_HOST_CHECK(p.cap >= 2 * int64_t(a.top_k) + 512 && p.cap >= 4096);
+  CSA_HOST_CHECK(p.off_cand >= kHeaderBytes &&
+                 p.off_cand + size_t(a.B) * size_t(a.T) * size_t(p.cap) * 8 <= p.ws_bytes);
+  log_dispatch("index_topk prefill: grid %u x %u of %d threads, %d queries per workgroup, buffer %lld keys",
+               grid.x, grid.y, kThreads, kPrefillQPB, (long long)p.cap);
   ProfScope prof("index_topk", a.stream);
   const bool fh = a.H_I == 8;
   if (a.key_kind == kKeyBF16) {

@@ -22,6 +22,33 @@ csa_status_t csa_attend_checked(const void* q, csa_dtype_t dt, const void* k_cmp
 // Records the thread-local error text of a status (csa_last_error) and returns it.
 csa_status_t set_error(csa_status_t s, const char* msg);
 
+// ------------------------------------------------------------------ diagnostics
+//
+// CSA_LOG=1 in the environment: every launch decision (path, plan, grid) is
+// printed to stderr.  Builds with CSA_DEBUG defined (libcsa_debug.so) also fill
+// the scratch part of every workspace, and every kernel's LDS, with all-ones
+// words (NaN as fp32 and as bf16) before use, so that a read of memory nothing
+// wrote shows up in the results, and check the launch plans' invariants on the
+// host before every launch (a failed check is reported as CSA_E_HIP with
+// hipErrorInvalidValue and launches nothing).
+#ifdef CSA_DEBUG
+constexpr bool kDebug = true;
+#else
+constexpr bool kDebug = false;
+#endif
+bool log_enabled();
+void log_dispatch(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+// Debug builds: bytes [0, n) at p set to 0xff, by a fill kernel on s.
+hipError_t debug_poison(void* p, size_t n, hipStream_t s);
+void debug_check_failed(const char* cond, const char* file, int line);
+#define CSA_HOST_CHECK(cond)                                  \
+  do {                                                        \
+    if (::csa::kDebug && !(cond)) {                           \
+      ::csa::debug_check_failed(#cond, __FILE__, __LINE__);   \
+      return hipErrorInvalidValue;                            \
+    }                                                         \
+  } while (0)
+
 // Brackets one kernel launch with HIP events when per-kernel timing is enabled
 // (csa_profile_enable); otherwise does nothing.
 class ProfScope {

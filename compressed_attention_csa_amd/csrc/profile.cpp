@@ -6,7 +6,9 @@
 // kernel, so timing runs should not be captured into graphs.
 #include <hip/hip_runtime.h>
 
+#include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <map>
 #include <string>
 #include <vector>
@@ -92,7 +94,47 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;  // keeps the loads; almost never taken
 }
 
+// Fills n16 16-byte words with all-ones (debug builds only).
+__global__ __launch_bounds__(256) void poison_kernel(uint4* p, size_t n16) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256)
+    p[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
+}
+
 }  // namespace
+
+namespace csa {
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("CSA_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+void log_dispatch(const char* fmt, ...) {
+  if (!log_enabled()) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[csa] %s\n", buf);
+}
+
+hipError_t debug_poison(void* p, size_t n, hipStream_t s) {
+  if (!kDebug || p == nullptr || n < 16) return hipSuccess;
+  const size_t n16 = n / 16;
+  const size_t blocks = n16 / 256 + 1 < 4096 ? n16 / 256 + 1 : 4096;
+  hipLaunchKernelGGL(poison_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, static_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+void debug_check_failed(const char* cond, const char* file, int line) {
+  fprintf(stderr, "[csa] debug check failed: %s (%s:%d)\n", cond, file, line);
+}
+
+}  // namespace csa
 
 extern "C" {
 
