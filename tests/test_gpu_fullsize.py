@@ -255,6 +255,16 @@ def test_hca_decode_fp8_caches_full_size():
 # ----------------------------------------------------------------------------- CSA prefill
 
 
+def sample_rows(T, fixed, seed, count=64):
+    """count query rows of a prefill chunk: the fixed ones (chunk edges, workgroup
+    boundaries) and seeded random ones spread over every part of the chunk."""
+    rng = np.random.default_rng(seed)
+    rows = set(fixed)
+    while len(rows) < count:
+        rows.add(int(rng.integers(0, T)))
+    return sorted(rows)
+
+
 def test_csa_prefill_chunk_full_size():
     name = "csa_prefill_chunk_1m"
     wl = inputgen.WORKLOADS[name]
@@ -278,7 +288,7 @@ def test_csa_prefill_chunk_full_size():
     score = torch.empty((1, T, k), dtype=torch.float32, device=DEV)
     csa.csa_index_topk(P.q_idx, P.w, kbf, None, wl.t0, m, k, idx, score)
     torch.cuda.synchronize()
-    rows = [0, 1, 2047, 4096, 5000, T - 2, T - 1]
+    rows = sample_rows(T, [0, 1, 2047, 4096, 5000, T - 2, T - 1], seed=21)
     q_idx64, w64 = f64(P.q_idx[0]), f64(P.w[0])
     idx_h, score_h = idx[0].cpu().numpy(), score[0].cpu().numpy()
     sel = {}
@@ -348,7 +358,7 @@ def test_hca_prefill_chunk_full_size():
                    wl.t0, W, wl.scale, out, lse)
     torch.cuda.synchronize()
     q64 = f64(P.q[0])
-    for i in [0, 1, 127, 128, 4095, 5000, T - 2, T - 1]:
+    for i in sample_rows(T, [0, 1, 127, 128, 4095, 5000, T - 2, T - 1], seed=22):
         t = wl.t0 + i
         win = method.window_positions(t, W)
         kr = f64(P.raw["k_raw"][0, int(win[0]):int(win[-1]) + 1])

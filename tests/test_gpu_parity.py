@@ -800,6 +800,64 @@ def test_attend_is_deterministic_and_consistent_across_splits():
 # ----------------------------------------------------------------------------- end to end, fp32
 
 
+def test_chunked_prefill_rows_equal_full_prefill():
+    """A prefill processed in chunks, each call continuing at t0 plus the rows
+    already done, gives the rows of one call over the whole prefill.  Indexer:
+    every chunk takes the prefill path, where a query's scores and selection do
+    not depend on the other rows of the call, so lists and scores agree bit for
+    bit.  Attention: the chunks run as split rows (three to four splits and a
+    merge) where the whole prefill runs unsplit, so CSA rows agree to fp32
+    summation order, 1e-4 of the row's largest output.  The whole HCA prefill
+    runs on the multi-token kernel, whose softmax weights enter the value product
+    as binary16 (relative error at most 2^-11 each) where V is in the binary16
+    range, so there a row may move by up to 2^-11 of the largest |V| on top."""
+    B, T, H, d, HI, dI, m, mh, k, W = 1, 320, 64, 128, 8, 64, 4, 128, 256, 128
+    t0 = 20000
+    n_raw = t0 + T
+    N, Nh = n_raw // m, n_raw // mh
+    chunks = [100, 64, 156]
+    say("chunked vs full prefill", chunks)
+    q_idx = gen("ch_qi", (B, T, HI, dI), "bf16", seed=1).to(DEV)
+    w = gen("ch_w", (B, T, HI), "f32", seed=2).to(DEV)
+    keys = gen("ch_ki", (B, N, dI), "bf16", seed=3).to(DEV)
+    q = gen("ch_q", (B, T, H, d), "bf16", seed=4).to(DEV)
+    kc, vc = gen("ch_kc", (B, N, d), "bf16", seed=5).to(DEV), gen("ch_vc", (B, N, d), "bf16", seed=6).to(DEV)
+    kh, vh = gen("ch_kh", (B, Nh, d), "bf16", seed=7).to(DEV), gen("ch_vh", (B, Nh, d), "bf16", seed=8).to(DEV)
+    kr, vr = gen("ch_kr", (B, n_raw, d), "bf16", seed=9).to(DEV), gen("ch_vr", (B, n_raw, d), "bf16", seed=10).to(DEV)
+    scale = 1.0 / math.sqrt(d)
+
+    def run(lo, hi, idx, sc, o_csa, l_csa, o_hca, l_hca):
+        csa.csa_index_topk(q_idx[:, lo:hi], w[:, lo:hi], keys, None, t0 + lo, m, k, idx[:, lo:hi], sc[:, lo:hi])
+        csa.csa_attend(q[:, lo:hi], kc, vc, m, idx[:, lo:hi], kr, vr, t0 + lo, W, scale, o_csa[:, lo:hi],
+                       l_csa[:, lo:hi])
+        csa.hca_attend(q[:, lo:hi], kh, vh, mh, kr, vr, t0 + lo, W, scale, o_hca[:, lo:hi], l_hca[:, lo:hi])
+
+    def buffers():
+        return (torch.full((B, T, k), -7, dtype=torch.int32, device=DEV),
+                torch.full((B, T, k), 7.0, device=DEV),
+                torch.full((B, T, H, d), 7.0, device=DEV), torch.full((B, T, H), 7.0, device=DEV),
+                torch.full((B, T, H, d), 7.0, device=DEV), torch.full((B, T, H), 7.0, device=DEV))
+
+    full, part = buffers(), buffers()
+    run(0, T, *full)
+    lo = 0
+    for c in chunks:
+        run(lo, lo + c, *part)
+        lo += c
+    torch.cuda.synchronize()
+    assert torch.equal(full[0], part[0]), "indexer lists differ between chunked and whole prefill"
+    assert torch.equal(full[1], part[1]), "indexer scores differ between chunked and whole prefill"
+    vmax = max(float(f64(vh).__abs__().max()), float(f64(vr).__abs__().max()))
+    for name, o_f, o_p, l_f, l_p, extra in (("csa", full[2], part[2], full[3], part[3], 0.0),
+                                            ("hca", full[4], part[4], full[5], part[5], 2.0 ** -11 * vmax)):
+        of, op = f64(o_f), f64(o_p)
+        row_max = np.abs(of).max(axis=-1, keepdims=True)
+        err = np.abs(of - op).max(axis=-1, keepdims=True)
+        assert np.all(err <= 1e-4 * np.maximum(row_max, 1e-30) + extra), f"{name}: worst {np.max(err / row_max):.2e}"
+        assert np.allclose(f64(l_f), f64(l_p), rtol=1e-6, atol=1e-5), f"{name}: lse"
+        say(f"  {name}: worst row difference {np.max(err / np.maximum(row_max, 1e-30)):.2e} of the row maximum")
+
+
 def test_tiny_prefill_f32_end_to_end():
     """Tiny CSA + HCA prefill in fp32, fully independent: the GPU runs compress ->
     index/top-k -> attend on its own outputs; the oracle runs its own pipeline.
