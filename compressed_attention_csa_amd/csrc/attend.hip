@@ -8,20 +8,26 @@
 //     then raw positions max(0, t-W+1) .. t
 // and every head h computes o = softmax(scale * q_h . K) V over all slots.
 //
-// Work split.  A workgroup handles one row, one group of up to 64 heads and one
-// contiguous range of slots ("split").  All query heads share the one KV head,
-// so a K/V row fetched once feeds every head of the group; the head groups of
-// one (row, split) get block ids that are equal modulo 8, which places them on
-// the same XCD so that the second group finds the rows in that XCD's L2.
+// Work split.  All query heads share the one KV head, so a K/V row fetched
+// once feeds every head that a workgroup holds.
 //
-// bf16 path: 32-slot tiles are gathered into LDS (K row-major, V transposed)
-// while the next tile's rows are already being loaded into registers.
-// S^T = K Q^T on 16x16x32 MFMA puts one head per lane column and 8 slots per
-// lane, which is exactly the B-operand layout of O^T = V^T P^T, so the softmax
-// weights never move between lanes.  P enters the MFMA as a bf16 hi + lo pair
-// (16 significant bits).  fp32 path: fp32 FMA with one slot per lane.
-// With several splits, each writes (O, max, sum) partials and the last split of
-// the (row, head group) to finish merges them (log-sum-exp).
+// bf16 path: a workgroup handles one row, every head of it (wave w owns heads
+// 16w .. 16w+15) and one contiguous range of slots ("split").  32-slot tiles
+// are gathered into LDS (K row-major, V transposed) while the next tiles' rows
+// are already being loaded into registers.  S^T = K Q^T on 16x16x32 MFMA puts
+// one head per lane column and 8 slots per lane, which is exactly the
+// B-operand layout of O^T = V^T P^T, so the softmax weights never move between
+// lanes.  P enters the MFMA as a bf16 hi + lo pair (16 significant bits).  With
+// several splits, each writes (O, max, sum) partials to the workspace and a
+// separate merge kernel (one thread per row, head and 16-byte column chunk)
+// combines them by log-sum-exp.  HCA over many consecutive query tokens uses
+// the multi-token kernel below instead (no splits).
+//
+// fp32 path: fp32 FMA with one slot per lane; a workgroup handles one row, one
+// group of up to 64 heads and one split.  The head groups of one (row, split)
+// get block ids that are equal modulo 8, which places them on the same XCD so
+// that the second group finds the rows in that XCD's L2, and the last split of
+// a (row, head group) to finish merges the partials (log-sum-exp).
 #include <type_traits>
 
 #include "common.hpp"
