@@ -221,7 +221,9 @@ __device__ int wave_compact(uint64_t* buf, int n, uint64_t T) {
 // element is NaN, which a zero weight would not remove).
 // KK == kKeyE4M3Q8: the query rows are quantised to e4m3 on load and the
 // products are fp8 x fp8 MFMAs on the raw key codes, which stay 8-bit in LDS.
-template <int KK, int DI, bool FH>
+// BS: the approximate selector (scores rounded to bf16), a template argument so
+// that the exact selector's inner loop carries no rounding instructions.
+template <int KK, int DI, bool FH, bool BS>
 __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, IndexPlan p) {
   __shared__ LdsPrefill L;
   debug_poison_lds(L);
@@ -574,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
               s = (FH || 4 * hf + j < H_I) ? t : s;
             }
           if (key_is_e4m3(KK)) s *= L.scale[cur][e];
-          if (a.bf16_scores) s = round_bf16(s);  // screen and rank the rounded score
+          if (BS) s = round_bf16(s);  // screen and rank the rounded score
           // The screen admits every entry whose rank key can exceed tau (and a
           // few equal-score ones that cannot); the exact test runs when staged
           // entries are drained.  The passing lanes write their pairs to
@@ -683,6 +685,18 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   }
 }
 
+template <int KK, int DI, bool FH>
+void launch_prefill_bs(const IndexArgs& a, const IndexPlan& p, dim3 grid, dim3 block) {
+  if (a.bf16_scores) hipLaunchKernelGGL((idx_prefill_kernel<KK, DI, FH, true>), grid, block, 0, a.stream, a, p);
+  else hipLaunchKernelGGL((idx_prefill_kernel<KK, DI, FH, false>), grid, block, 0, a.stream, a, p);
+}
+
+template <int KK>
+void dispatch_prefill(const IndexArgs& a, const IndexPlan& p, dim3 grid, dim3 block, bool fh) {
+  if (a.d_I == 64) fh ? launch_prefill_bs<KK, 64, true>(a, p, grid, block) : launch_prefill_bs<KK, 64, false>(a, p, grid, block);
+  else fh ? launch_prefill_bs<KK, 32, true>(a, p, grid, block) : launch_prefill_bs<KK, 32, false>(a, p, grid, block);
+}
+
 }  // namespace
 
 bool prefill_path(int64_t T, int H_I, int key_kind) {
@@ -698,31 +712,9 @@ hipError_t launch_index_prefill(const IndexArgs& a, const IndexPlan& p) {
                grid.x, grid.y, kThreads, kPrefillQPB, (long long)p.cap);
   ProfScope prof("index_topk", a.stream);
   const bool fh = a.H_I == 8;
-  if (a.key_kind == kKeyBF16) {
-    if (a.d_I == 64) {
-      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 64, true>), grid, block, 0, a.stream, a, p);
-      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 64, false>), grid, block, 0, a.stream, a, p);
-    } else {
-      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 32, true>), grid, block, 0, a.stream, a, p);
-      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyBF16, 32, false>), grid, block, 0, a.stream, a, p);
-    }
-  } else if (a.key_kind == kKeyE4M3Q8) {
-    if (a.d_I == 64) {
-      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3Q8, 64, true>), grid, block, 0, a.stream, a, p);
-      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3Q8, 64, false>), grid, block, 0, a.stream, a, p);
-    } else {
-      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3Q8, 32, true>), grid, block, 0, a.stream, a, p);
-      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3Q8, 32, false>), grid, block, 0, a.stream, a, p);
-    }
-  } else {
-    if (a.d_I == 64) {
-      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 64, true>), grid, block, 0, a.stream, a, p);
-      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 64, false>), grid, block, 0, a.stream, a, p);
-    } else {
-      if (fh) hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 32, true>), grid, block, 0, a.stream, a, p);
-      else hipLaunchKernelGGL((idx_prefill_kernel<kKeyE4M3, 32, false>), grid, block, 0, a.stream, a, p);
-    }
-  }
+  if (a.key_kind == kKeyBF16) dispatch_prefill<kKeyBF16>(a, p, grid, block, fh);
+  else if (a.key_kind == kKeyE4M3Q8) dispatch_prefill<kKeyE4M3Q8>(a, p, grid, block, fh);
+  else dispatch_prefill<kKeyE4M3>(a, p, grid, block, fh);
   return hipGetLastError();
 }
 
