@@ -507,6 +507,8 @@ def time_workload(name, seed, steps, warmup, graph=True):
             for i in range(R):
                 w.step(i)
         e1.record()
+    if PROFILE_MARKER:
+        torch.cuda._sleep(1000)  # end of the timed launches
     torch.cuda.synchronize()
     per_step = sorted(e0.elapsed_time(e1) / R for e0, e1 in ev)
     ms = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (per_step[len(per_step) // 2 - 1] +
@@ -514,6 +516,7 @@ def time_workload(name, seed, steps, warmup, graph=True):
     alg = w.algorithmic()
     res = {"workload": name, "ms_per_step": ms, "ms_min": per_step[0], "ms_max": per_step[-1],
            "steps": reps * R, "replicas": R, "kernels": prof, "alg": alg, "dominant": w.dominant,
+           "dominant_kernels": list(w.dominant_kernels),
            "peak": getattr(w, "peak", None), "mfma_peak": getattr(w, "mfma_peak", None)}
     # The dominant call's time per step: its kernels' event-timed durations, summed.
     calls = prof.get(w.dominant_kernels[0], {}).get("launches", 0) / getattr(w, "calls_per_step", 1)
@@ -555,8 +558,9 @@ def roofline(res, ceiling_gbps=None):
     dom_ms = res.get("dominant_ms")
     if dom_ms is None:
         return None
-    key = f"{res['dominant']}@{res['workload']}"
-    traffic = load_traffic(key)
+    # Counter bytes of every kernel of the dominant call (e.g. attention and its split merge).
+    parts = [load_traffic(f"{k}@{res['workload']}") for k in res.get("dominant_kernels", [res["dominant"]])]
+    traffic = sum(parts) if parts and all(x is not None for x in parts) else None
     common = {"traffic": traffic, "kernel": res["dominant"], "kernel_ms": round(dom_ms, 6),
               "kernel_parts_ms": res.get("dominant_parts_ms")}
     if "dominant_bytes" in alg:
@@ -622,23 +626,30 @@ def _read_csv_rows(directory, suffix):
 
 
 def _grid(row):
-    return int(row.get("Grid_Size") or row.get("Grid_Size_X") or 0)
+    """Total work-items (the kernel trace lists x, y, z; the counter runs their product)."""
+    if row.get("Grid_Size"):
+        return int(row["Grid_Size"])
+    return int(row.get("Grid_Size_X") or 0) * int(row.get("Grid_Size_Y") or 1) * int(row.get("Grid_Size_Z") or 1)
 
 
 def _wg(row):
-    return int(row.get("Workgroup_Size") or row.get("Workgroup_Size_X") or 0)
+    if row.get("Workgroup_Size"):
+        return int(row["Workgroup_Size"])
+    return (int(row.get("Workgroup_Size_X") or 0) * int(row.get("Workgroup_Size_Y") or 1) *
+            int(row.get("Workgroup_Size_Z") or 1))
 
 
 def _after_marker(rows, key="Dispatch_Id"):
-    """The dispatches after the last torch spin kernel, in dispatch order, keyed by their
-    ordinal within (kernel, grid, workgroup)."""
+    """The dispatches between the two torch spin kernels that bracket the timed steps (or
+    after the only one), in dispatch order, keyed by their ordinal within (kernel, grid,
+    workgroup)."""
     rows = sorted(rows, key=lambda r: int(r[key]))
-    cut = max((i for i, r in enumerate(rows) if "sleep" in r["Kernel_Name"] or "spin" in r["Kernel_Name"]),
-              default=None)
-    if cut is None:
+    marks = [i for i, r in enumerate(rows) if "sleep" in r["Kernel_Name"] or "spin" in r["Kernel_Name"]]
+    if not marks:
         raise SystemExit("no profiling marker in the dispatch list (run bench.py with --profile-marker)")
+    lo, hi = (marks[-2], marks[-1]) if len(marks) >= 2 else (marks[-1], len(rows))
     out, seen = {}, {}
-    for r in rows[cut + 1:]:
+    for r in rows[lo + 1:hi]:
         k = (r["Kernel_Name"], _grid(r), _wg(r))
         n = seen.get(k, 0)
         seen[k] = n + 1
@@ -684,7 +695,7 @@ def _short(kernel):
     return k.split("(")[0].strip()
 
 
-def profile_summary(root, calib, workload, traffic_out=None, command_note=""):
+def profile_summary(root, calib, workload, traffic_out=None, command_note="", timed_steps=0):
     trace = _after_marker(_read_csv_rows(os.path.join(root, "trace"), "kernel_trace.csv"))
     fetch = _counter(os.path.join(root, "fetch"), "FETCH_SIZE")
     write = _counter(os.path.join(root, "write"), "WRITE_SIZE")
@@ -749,6 +760,7 @@ def profile_summary(root, calib, workload, traffic_out=None, command_note=""):
     hdr = "| kernel | role | grid | wg | launches | avg us | min us | max us | HBM read MB | HBM write MB | GB/s |"
     lines += [hdr, "|" + "---|" * 11]
     role_tot = {}
+    n_steps = timed_steps or (min(len(g["us"]) for g in groups.values()) if groups else 1)
     for k in sorted(groups, key=lambda k: -sum(groups[k]["us"])):
         g = groups[k]
         avg = sum(g["us"]) / len(g["us"])
@@ -760,13 +772,14 @@ def profile_summary(root, calib, workload, traffic_out=None, command_note=""):
                      f"{'-' if rd is None else f'{rd / 1e6:.2f}'} | {'-' if wr is None else f'{wr / 1e6:.3f}'} | "
                      f"{gbps} |")
         t = role_tot.setdefault(role, {"us": 0.0, "rd": 0.0, "wr": 0.0, "n": 0, "bytes_ok": True})
-        t["us"] += avg
-        t["n"] = max(t["n"], len(g["us"]))
+        per = len(g["us"]) / n_steps  # launches of this kernel per step
+        t["us"] += per * avg
+        t["n"] += len(g["us"])
         if rd is None:
             t["bytes_ok"] = False
         else:
-            t["rd"] += rd
-            t["wr"] += wr
+            t["rd"] += per * rd
+            t["wr"] += per * wr
     extra = {}
     if os.path.isdir(os.path.join(root, "sq2")):
         rows = _read_csv_rows(os.path.join(root, "sq2"), "counter_collection.csv")
@@ -802,17 +815,20 @@ def profile_summary(root, calib, workload, traffic_out=None, command_note=""):
             wt = v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"] if v["SQ_WAVE_CYCLES"] else 0
             lines.append(f"| {_short(k[0])} | " + " | ".join(f"{v[x]:.0f}" for x in sq_names) +
                          f" | {cyc:.0f} | {mf:.1%} | {va:.1%} | {co:.1%} | {wt:.1%} |")
-    lines += ["", "Per call of each role (all its kernels, summed):", ""]
+    lines += ["", f"Per timed step ({n_steps} steps) of each role, all its kernels summed, and per call "
+              "(the step's share divided by the role's launches per step):", ""]
     traffic = {}
     for role, t in sorted(role_tot.items()):
         if role == "-":
             continue
+        calls = t["n"] / n_steps
         b = f"read {t['rd'] / 1e6:.2f} MB + write {t['wr'] / 1e6:.3f} MB" if t["bytes_ok"] else "bytes not paired"
-        lines.append(f"- `{role}`: {t['us']:.2f} us, {b}")
+        lines.append(f"- `{role}`: {t['us']:.2f} us per step, {b} per step; {calls:g} launch(es) per step")
         if t["bytes_ok"]:
-            traffic[f"{role}@{workload}"] = {"hbm_bytes_per_launch": int(t["rd"] + t["wr"]),
-                                             "read_bytes": int(t["rd"]), "write_bytes": int(t["wr"]),
-                                             "trace_us": round(t["us"], 3),
+            traffic[f"{role}@{workload}"] = {"hbm_bytes_per_launch": int((t["rd"] + t["wr"]) / calls),
+                                             "hbm_bytes_per_step": int(t["rd"] + t["wr"]),
+                                             "read_bytes_per_step": int(t["rd"]), "write_bytes_per_step": int(t["wr"]),
+                                             "trace_us_per_step": round(t["us"], 3),
                                              "source_digest": kernel_source_digest(),
                                              "scale": {x: round(y, 4) for x, y in scale.items()}}
     if traffic_out:
@@ -924,10 +940,12 @@ def main():
     ap.add_argument("--calibration", metavar="DIR", help="rocprofv3 runs of --copy-calibration (fetch/, write/)")
     ap.add_argument("--traffic-out", metavar="JSON", help="with --profile-summary: update this traffic file")
     ap.add_argument("--command-note", default="", help="with --profile-summary: the commands, for the summary")
+    ap.add_argument("--timed-steps", type=int, default=0,
+                    help="with --profile-summary: the timed steps of the profiled run (the --steps it ran with)")
     args = ap.parse_args()
     if args.profile_summary:
         print(profile_summary(args.profile_summary, args.calibration, args.workload, args.traffic_out,
-                              args.command_note))
+                              args.command_note, args.timed_steps))
         return
     global PROFILE_MARKER
     PROFILE_MARKER = args.profile_marker
