@@ -975,8 +975,8 @@ def main():
     head = time_workload(args.workload, args.seed, args.steps, args.warmup, graph=not args.no_graph)
     legs, ceiling = {}, None
     for name in [x for x in args.legs.split(",") if x]:
-        slow = name in ("csa_prefill_chunk_1m", "hca_prefill_chunk_1m", "csa_compress_pro_1m", "hbm_read_2gb",
-                        "tiny_prefill_f32")
+        slow = name.partition("+")[0] in ("csa_prefill_chunk_1m", "hca_prefill_chunk_1m", "csa_compress_pro_1m",
+                                          "hbm_read_2gb", "tiny_prefill_f32")
         steps = 5 if slow else args.steps
         r = time_workload(name, args.seed, steps, min(args.warmup, 3) if steps < 10 else args.warmup,
                           graph=not args.no_graph)
