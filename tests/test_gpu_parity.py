@@ -858,6 +858,66 @@ def test_chunked_prefill_rows_equal_full_prefill():
         say(f"  {name}: worst row difference {np.max(err / np.maximum(row_max, 1e-30)):.2e} of the row maximum")
 
 
+def test_decode_row_equals_the_last_prefill_row():
+    """A decode call for the token at t = n - 1 (the rows x slices indexer, split
+    attention with a merge) gives the last row of a prefill call ending at that
+    token (the streaming prefill indexer, unsplit attention; HCA: the multi-token
+    kernel): both selections are valid top-k sets of the oracle's scores, the
+    decode scores of the shared winners agree with the prefill ones to fp32
+    rounding, and, given the same selection, the attention rows agree to
+    summation order (HCA also to its multi-token kernel's binary16 weights,
+    2^-11 of the largest |V|)."""
+    B, T, H, d, HI, dI, m, mh, k, W = 2, 128, 128, 128, 8, 64, 4, 128, 512, 128
+    n = 24000
+    t0 = n - T
+    N, Nh = n // m, n // mh
+    say("decode row vs last prefill row")
+    q_idx = gen("dp_qi", (B, T, HI, dI), "bf16", seed=1)
+    w = gen("dp_w", (B, T, HI), "f32", seed=2)
+    keys = gen("dp_ki", (B, N, dI), "bf16", seed=3)
+    q = gen("dp_q", (B, T, H, d), "bf16", seed=4).to(DEV)
+    kc, vc = gen("dp_kc", (B, N, d), "bf16", seed=5).to(DEV), gen("dp_vc", (B, N, d), "bf16", seed=6).to(DEV)
+    kh, vh = gen("dp_kh", (B, Nh, d), "bf16", seed=7).to(DEV), gen("dp_vh", (B, Nh, d), "bf16", seed=8).to(DEV)
+    kr, vr = gen("dp_kr", (B, n, d), "bf16", seed=9).to(DEV), gen("dp_vr", (B, n, d), "bf16", seed=10).to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    qd_idx, wd, kd = q_idx.to(DEV), w.to(DEV), keys.to(DEV)
+    idx_p = torch.full((B, T, k), -7, dtype=torch.int32, device=DEV)
+    sc_p = torch.full((B, T, k), 7.0, device=DEV)
+    csa.csa_index_topk(qd_idx, wd, kd, None, t0, m, k, idx_p, sc_p)
+    idx_d = torch.full((B, 1, k), -7, dtype=torch.int32, device=DEV)
+    sc_d = torch.full((B, 1, k), 7.0, device=DEV)
+    csa.csa_index_topk(qd_idx[:, T - 1:].contiguous(), wd[:, T - 1:].contiguous(), kd, None, n - 1, m, k, idx_d, sc_d)
+    o_p = torch.empty((B, T, H, d), device=DEV)
+    o_d = torch.empty((B, 1, H, d), device=DEV)
+    csa.csa_attend(q, kc, vc, m, idx_p, kr, vr, t0, W, scale, o_p)
+    last = idx_p[:, T - 1:].contiguous()
+    csa.csa_attend(q[:, T - 1:].contiguous(), kc, vc, m, last, kr, vr, n - 1, W, scale, o_d)
+    h_p = torch.empty((B, T, H, d), device=DEV)
+    h_d = torch.empty((B, 1, H, d), device=DEV)
+    csa.hca_attend(q, kh, vh, mh, kr, vr, t0, W, scale, h_p)
+    csa.hca_attend(q[:, T - 1:].contiguous(), kh, vh, mh, kr, vr, n - 1, W, scale, h_d)
+    torch.cuda.synchronize()
+    ip, idd = idx_p.cpu().numpy(), idx_d.cpu().numpy()
+    sp, sd = sc_p.cpu().numpy(), sc_d.cpu().numpy()
+    for b in range(B):
+        scores, vis = method.index_scores(f64(q_idx[b, T - 1:]), f64(w[b, T - 1:]), f64(keys[b]), n - 1, m)
+        check_topk_rows(ip[b, T - 1:], sp[b, T - 1:], scores, vis, k)
+        check_topk_rows(idd[b], sd[b], scores, vis, k)
+        common = np.intersect1d(ip[b, T - 1], idd[b, 0])
+        assert common.size >= k - 2, "the two selections differ beyond ties"
+        a = dict(zip(ip[b, T - 1].tolist(), sp[b, T - 1].tolist()))
+        c = dict(zip(idd[b, 0].tolist(), sd[b, 0].tolist()))
+        rel = max(abs(a[j] - c[j]) / max(abs(a[j]), 1e-30) for j in common.tolist())
+        assert rel <= 1e-5, rel
+    vmax = max(float(f64(vh).__abs__().max()), float(f64(vr).__abs__().max()))
+    for name, full, one, extra in (("csa", o_p, o_d, 0.0), ("hca", h_p, h_d, 2.0 ** -11 * vmax)):
+        a, b_ = f64(full[:, T - 1]), f64(one[:, 0])
+        err = np.abs(a - b_).max(axis=-1)
+        ref = np.abs(a).max(axis=-1)
+        say(f"  {name}: worst row difference {np.max(err / ref):.2e} of the row maximum")
+        assert np.all(err <= 1e-4 * ref + extra), name
+
+
 def test_tiny_prefill_f32_end_to_end():
     """Tiny CSA + HCA prefill in fp32, fully independent: the GPU runs compress ->
     index/top-k -> attend on its own outputs; the oracle runs its own pipeline.
