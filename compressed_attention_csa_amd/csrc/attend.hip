@@ -12,7 +12,8 @@
 // once feeds every head that a workgroup holds.
 //
 // bf16 path: a workgroup handles one row, every head of it (wave w owns heads
-// 16w .. 16w+15) and one contiguous range of slots ("split").  32-slot tiles
+// 16w .. 16w+15; split rows with few workgroups split the heads into two
+// groups instead) and one contiguous range of slots ("split").  32-slot tiles
 // are gathered into LDS (K row-major, V transposed) while the next tiles' rows
 // are already being loaded into registers.  S^T = K Q^T on 16x16x32 MFMA puts
 // one head per lane column and 8 slots per lane, which is exactly the
@@ -40,6 +41,11 @@ constexpr int kThreads = 256;
 constexpr int kTile = 32;      // bf16 slots per tile
 constexpr int kTileF32 = 64;   // fp32 slots per tile
 constexpr int kMaxSplits = 64;
+// bf16 decode with fewer than 128 (row, split) workgroups: the heads are split
+// into this many groups, each a workgroup of its own (twice the workgroups, each
+// with half the products; the K / V rows of a split are gathered once per group,
+// the second time mostly from the XCD's L2).
+constexpr int kFewSplitHeadGroups = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -169,9 +175,9 @@ __device__ void finish_split(const AttendArgs& a, const AttendPlan& p, const Row
   if (threadIdx.x == 0) ctrl->arrive = 0;
 }
 
-// Block id -> (head group, row, split).  Each group spans group_stride ids (a
-// multiple of 8), so the groups of one (row, split) share id mod 8 and hence
-// an XCD.  Returns false for the padding ids.
+// Block id -> (head group, row, split).  With several groups, each spans
+// group_stride ids (a multiple of 8), so the groups of one (row, split) share
+// id mod 8 and hence an XCD.  Returns false for the padding ids.
 __device__ __forceinline__ bool decode_block(const AttendPlan& p, int64_t& hg, int64_t& r, int64_t& s) {
   hg = blockIdx.x / p.group_stride;
   const int64_t rem = blockIdx.x % p.group_stride;
@@ -183,8 +189,9 @@ __device__ __forceinline__ bool decode_block(const AttendPlan& p, int64_t& hg, i
 
 // ---------------------------------------------------------------- bf16 MFMA kernel
 //
-// One workgroup = one (row, split) and every head of the row: wave w owns heads
-// 16w .. 16w+15, so each K/V row is read from memory once per split.  Tiles of
+// One workgroup = one (row, split) and every head of the row (or of one head
+// group, for split rows with few workgroups): wave w owns heads 16w .. 16w+15
+// of its group, so each K/V row is read from memory once per split and group.  Tiles of
 // 32 slots go through two LDS buffers; SETS further tiles are always in flight
 // in registers (about 64 KB per workgroup), enough to cover memory latency in
 // decode, where a split is a few tiles long.  Loads are issued unconditionally
@@ -243,12 +250,13 @@ __global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, Atte
   constexpr int NB = 2 * PAIR;                   // LDS tile buffers
   __shared__ LdsB<D, NB> L;
   debug_poison_lds(L);
-  const int64_t r = div64(blockIdx.x, p.splits), s = blockIdx.x - r * p.splits;
+  int64_t hg, r, s;
+  if (!decode_block(p, hg, r, s)) return;
   const RowSlots x = row_slots(a, p, r, s);
   if (s >= x.S) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
   const int H = a.H;
-  const int h0 = wid * 16;  // this wave's 16 heads
+  const int h0 = int(hg) * (NW * 16) + wid * 16;  // this wave's 16 heads
   const bool has = h0 < H;
   const int64_t nsel = HCA ? x.c : int64_t(a.top_k);
 
@@ -1364,26 +1372,30 @@ AttendPlan plan_attend(bool bf16, int B, int64_t T, int H, int d, int64_t max_en
     return o;
   };
   if (bf16) {
-    // Every head of a row in one workgroup; split the slots until there are
-    // about 256 workgroups, keeping at least 4 tiles of 32 per split (2 with
-    // at most 64 heads, whose split partials are half the size to merge).
-    p.groups = 1;
-    int64_t splits = 1;
-    if (p.rows > 0 && p.rows < 256) {
-      splits = (256 + p.rows - 1) / p.rows;
+    // Split the slots until there are about 256 workgroups, keeping at least 4
+    // tiles of 32 per split (2 with at most 64 heads, whose split partials are
+    // half the size to merge).  Every head of a row in one workgroup, except
+    // for split rows with few workgroups (kFewSplitHeadGroups).
+    auto split_plan = [&](int64_t target) {
+      int64_t splits = target;
       const int64_t min_slots = (H > 64 ? 4 : 2) * kTB;
       const int64_t max_splits = (p.slots + min_slots - 1) / min_slots;
       if (splits > max_splits) splits = max_splits;
       if (splits > kMaxSplits) splits = kMaxSplits;
       if (splits < 1) splits = 1;
-    }
-    int64_t per = (p.slots + splits - 1) / splits;
-    per = ((per + kTB - 1) / kTB) * kTB;
-    if (per < kTB) per = kTB;
-    p.per_split = per;
-    p.splits = (p.slots + per - 1) / per;
-    if (p.splits < 1) p.splits = 1;
-    p.group_stride = p.rows * p.splits;
+      int64_t per = (p.slots + splits - 1) / splits;
+      per = ((per + kTB - 1) / kTB) * kTB;
+      if (per < kTB) per = kTB;
+      p.per_split = per;
+      p.splits = (p.slots + per - 1) / per;
+      if (p.splits < 1) p.splits = 1;
+    };
+    p.groups = 1;
+    split_plan((p.rows > 0 && p.rows < 256) ? (256 + p.rows - 1) / p.rows : 1);
+    if (p.splits > 1 && p.rows * p.splits < 128 && H % (16 * kFewSplitHeadGroups) == 0)
+      p.groups = kFewSplitHeadGroups;
+    // Head groups of one (row, split) get block ids equal modulo 8 (one XCD).
+    p.group_stride = p.groups > 1 ? (p.rows * p.splits + 7) / 8 * 8 : p.rows * p.splits;
     p.off_part = take(size_t(p.rows * p.splits) * size_t(H) * size_t(d) * 4);
     p.off_ml = take(size_t(p.rows * p.splits) * size_t(H) * 2 * 4);
     p.ws_bytes = p.splits > 1 ? off : 0;
@@ -1417,12 +1429,13 @@ AttendPlan plan_attend(bool bf16, int B, int64_t T, int H, int d, int64_t max_en
 }
 
 int64_t attend_grid(const AttendPlan& p, bool bf16) {
-  return bf16 ? p.rows * p.splits : p.groups * p.group_stride;
+  (void)bf16;
+  return p.groups * p.group_stride;
 }
 
 template <int D, bool HCA, int PAIR, bool KV8>
 static void launch_bf16_nw(const AttendArgs& a, const AttendPlan& p, dim3 grid) {
-  const int nw = (a.H + 15) / 16;
+  const int nw = int((a.H / p.groups + 15) / 16);  // waves: 16 heads each, the heads of one group
   if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2, HCA, PAIR, KV8>), grid, dim3(128), 0, a.stream, a, p);
   else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4, HCA, PAIR, KV8>), grid, dim3(256), 0, a.stream, a, p);
   else hipLaunchKernelGGL((attend_bf16_kernel<D, 8, HCA, PAIR, KV8>), grid, dim3(512), 0, a.stream, a, p);
@@ -1430,7 +1443,7 @@ static void launch_bf16_nw(const AttendArgs& a, const AttendPlan& p, dim3 grid) 
 
 template <int D, bool HCA>
 static void launch_bf16(const AttendArgs& a, const AttendPlan& p) {
-  const dim3 grid(unsigned(p.rows * p.splits));
+  const dim3 grid(unsigned(attend_grid(p, true)));
   {
     ProfScope prof(HCA ? "hca_attend" : "csa_attend", a.stream);
     // Split rows (decode) have one workgroup per CU: stage tiles in pairs.  Many
