@@ -751,9 +751,9 @@ IndexPlan plan_index(int B, int64_t T, int H_I, int64_t N_alloc, int top_k, int 
   p.rows = int64_t(B) * T;
   if (prefill_path(T, H_I, key_kind) && N_alloc > 0) {
     p.prefill = true;
-    // Room for a full LDS staging area (the 1536 pairs of one wave, all of
+    // Room for a full LDS staging area (the 1216 pairs of one wave, all of
     // which may belong to one query) above the 5k/4 keys a compaction may keep:
-    // 5k/4 + 1536 <= max(4096, 2k + 512) for every k <= 2048.
+    // 5k/4 + 1216 <= max(4096, 2k + 512) for every k <= 2048.
     static_assert(5 * 2048 / 4 + kPrefillStage <= 2 * 2048 + 512, "staging room at k = 2048");
     static_assert(5 * 1792 / 4 + kPrefillStage <= 4096, "staging room at 2k + 512 = 4096");
     p.cap = 4096;

@@ -8,7 +8,7 @@
 // Work split.  A workgroup owns 32 query tokens of one sequence, 4 per wave over
 // 8 waves (two waves per SIMD, so one wave's matrix products overlap the other
 // wave's vector epilogue), and sweeps every entry visible to any of them.  Entry
-// keys are staged in LDS in tiles of 128 entries (16-byte chunks XOR-swizzled by
+// keys are staged in LDS in tiles of 256 entries (16-byte chunks XOR-swizzled by
 // entry so the operand reads are conflict-free), double-buffered: while a tile
 // is scored, the next one is already in LDS and the one after is in flight in
 // registers.  All workgroups sweep the entries in the same order, so the
@@ -52,7 +52,7 @@ namespace {
 
 constexpr int kWaves = kPrefillWaves;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kTileE = 128;  // entries per LDS tile
+constexpr int kTileE = 256;  // entries per LDS tile
 constexpr int kHBits = 9;    // histogram digit
 constexpr int kHBins = 1 << kHBits;
 constexpr int kBatch = 8;    // buffer keys per lane per batch of loads
@@ -232,9 +232,10 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   constexpr int CPG = DI * KB / 16;              // 16-byte chunks per entry in memory
   constexpr int CPE = Q8 ? CPG : DI / 8;         // 16-byte chunks per entry in LDS (bf16, or raw codes)
   constexpr int KSTEP = DI / 32;                 // 32-wide k-steps of one dot product
-  constexpr int CHUNKS = kTileE * CPG;
+  constexpr int TE = kTileE;                      // entries per tile
+  constexpr int CHUNKS = TE * CPG;
   constexpr int LOADS = (CHUNKS + kThreads - 1) / kThreads;  // chunks per thread per tile
-  constexpr int GROUPS = kTileE / 16;
+  constexpr int GROUPS = TE / 16;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
   const int64_t b = blockIdx.y;
   const int64_t i0 = int64_t(blockIdx.x) * kPrefillQPB;
@@ -307,31 +308,36 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   int64_t cmax64 = (a.t0 + ilast + 1) / a.m;
   if (cmax64 > a.N_alloc) cmax64 = a.N_alloc;
   const int cmax = int(cmax64);
-  const int ntiles = (cmax + kTileE - 1) / kTileE;
+  const int ntiles = (cmax + TE - 1) / TE;
   uint64_t* bufs = reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(a.ws) + p.off_cand);
   const int cap = int(p.cap);
   uint64_t* const stg = L.stg[wid];
   const uint32_t coltag = uint32_t(col) | (uint32_t(g) << kTagShift);  // staged entry, less e0 + 16 gi
 
   const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(a.k_idx) + b * a.N_alloc * int64_t(DI * KB);
-  // Tile prefetch registers (at most two 16-byte chunks per thread).  Every
+  // Tile prefetch registers (at most four 16-byte chunks per thread).  Every
   // thread always issues the same loads (entries past the last visible one read
   // that entry again; their scores are never candidates), so the number of loads
   // issued after any append store is fixed and the waits for those stores never
   // have to drain the prefetch too.
-  static_assert(LOADS >= 1 && LOADS <= 2, "tile chunks per thread");
-  uint4 pre0 = make_uint4(0, 0, 0, 0), pre1 = make_uint4(0, 0, 0, 0);
+  static_assert(LOADS >= 1 && LOADS <= 4, "tile chunks per thread");
+  uint4 pre[LOADS];
+  int pid[LOADS];
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    pre[u] = make_uint4(0, 0, 0, 0);
+    pid[u] = (tid + u * kThreads) % CHUNKS;
+  }
   float psc = 1.0f;
-  const int id0 = tid % CHUNKS, id1 = (tid + kThreads) % CHUNKS;
   int ss = 1;  // entry stride of the sweep (the sample stride in the sampling pass)
   auto chunk_ptr = [&](int t, int id) {
-    const int ge = min((t * kTileE + id / CPG) * ss, cmax - 1);
+    const int ge = min((t * TE + id / CPG) * ss, cmax - 1);
     return reinterpret_cast<const uint4*>(kbytes + int64_t(ge) * (DI * KB) + (id % CPG) * 16);
   };
   auto fetch = [&](int t) {
-    pre0 = *chunk_ptr(t, id0);
-    if (LOADS > 1) pre1 = *chunk_ptr(t, id1);
-    if (key_is_e4m3(KK)) psc = a.k_scale[b * a.N_alloc + min((t * kTileE + (tid & (kTileE - 1))) * ss, cmax - 1)];
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) pre[u] = *chunk_ptr(t, pid[u]);
+    if (key_is_e4m3(KK)) psc = a.k_scale[b * a.N_alloc + min((t * TE + (tid & (TE - 1))) * ss, cmax - 1)];
   };
   // Writes the prefetched chunks to LDS buffer `buf`; fp8 keys for bf16
   // products are widened to bf16 here, once per workgroup, rather than by every
@@ -358,9 +364,10 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     }
   };
   auto stage = [&](int buf) {
-    if (tid < CHUNKS) put(buf, id0, pre0);
-    if (LOADS > 1 && tid + kThreads < CHUNKS) put(buf, id1, pre1);
-    if (key_is_e4m3(KK) && tid < kTileE) L.scale[buf][tid] = psc;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      if (tid + u * kThreads < CHUNKS) put(buf, pid[u], pre[u]);
+    if (key_is_e4m3(KK) && tid < TE) L.scale[buf][tid] = psc;
   };
   // B operands of entry group gi (16 entries) of LDS buffer `buf`: dims
   // 16g..16g+15 (DI = 64) or 8g..8g+7 (DI = 32) of entry 16*gi + col.
@@ -494,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   // full sweep kept fewer than need candidates (possible only when more than r
   // of the sampled entries rank among its true top-k) is swept again with no
   // threshold, so the result stays exact for any input.
-  const bool sampling = a.top_k > 0 && cmax >= 16 * a.top_k && cmax >= 64 * kTileE;
+  const bool sampling = a.top_k > 0 && cmax >= 16 * a.top_k && cmax >= 8192;
   int sstride = 2;
   while (sampling && int64_t(sstride) * 8192 < cmax) sstride *= 2;
   // r = lambda + 6 * ceil(sqrt(lambda)) + 8 sampled keys above the starting
@@ -527,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     // rises fast; the full sweeps keep at least k.
     cap_pass = pass == 0 ? min(cap, max(1024, 8 * int(wave_max_u32(uint32_t(r_l))))) : cap;
     target_l = pass == 0 ? min(r_l, max(need_l, 1)) : need_l;
-    const int ntp = pass == 0 ? ((cmax + ss - 1) / ss + kTileE - 1) / kTileE : ntiles;
+    const int ntp = pass == 0 ? ((cmax + ss - 1) / ss + TE - 1) / TE : ntiles;
     const int cqv = pass == 0 ? (cq + ss - 1) / ss : cq;
     // Tiles every query of the workgroup sees in full need no visibility test
     // (its first query sees the fewest entries).
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
 
     for (int t = 0; t < ntp; ++t) {
       const int cur = t & 1;
-      const int e0 = t * kTileE;
+      const int e0 = t * TE;
       // Tile t+1 (loaded during the previous tile) goes to the other buffer, which
       // every wave finished reading before the last barrier; tile t+2 then stays
       // in flight for the whole of this tile.
@@ -599,10 +606,10 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
           }
         }
       };
-      if (e0 + kTileE <= cfull) groups(std::integral_constant<bool, true>());
+      if (e0 + TE <= cfull) groups(std::integral_constant<bool, true>());
       else groups(std::integral_constant<bool, false>());
       // The staging area is drained when it cannot take another tile.
-      if (scnt > kStage - kTileE * kPrefillQPW) drain();
+      if (scnt > kStage - TE * kPrefillQPW) drain();
       __syncthreads();
     }
     if (scnt > 0) drain();

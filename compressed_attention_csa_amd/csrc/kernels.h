@@ -129,7 +129,7 @@ constexpr int64_t kIndexChunkRows = 64;       // rows per multi-slice launch
 constexpr int kPrefillQPW = 4;                        // queries per wave
 constexpr int kPrefillWaves = 8;                      // waves per workgroup
 constexpr int kPrefillQPB = kPrefillWaves * kPrefillQPW;  // queries per workgroup
-constexpr int kPrefillStage = 384 * kPrefillQPW;          // LDS staging slots per wave
+constexpr int kPrefillStage = 304 * kPrefillQPW;          // LDS staging slots per wave
 constexpr int64_t kPrefillMinT = 64;                  // rows per sequence to use it
 
 struct IndexPlan {
