@@ -550,11 +550,6 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
     for (int t = 0; t < ntp; ++t) {
       const int cur = t & 1;
       const int e0 = t * TE;
-      // Tile t+1 (loaded during the previous tile) goes to the other buffer, which
-      // every wave finished reading before the last barrier; tile t+2 then stays
-      // in flight for the whole of this tile.
-      if (t + 1 < ntp) stage(cur ^ 1);
-      fetch(t + 2 < ntp ? t + 2 : ntp - 1);
       // B operands are read two groups ahead of their products: each read has
       // a group's work to land, and the reads of the 8 waves, which leave the
       // barrier together, spread over the tile instead of queueing at its start.
@@ -610,6 +605,13 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
       else groups(std::integral_constant<bool, false>());
       // The staging area is drained when it cannot take another tile.
       if (scnt > kStage - TE * kPrefillQPW) drain();
+      // Tile t+1 (loaded during the previous tile) goes to the other buffer, which
+      // every wave finished reading before the last barrier; each wave writes its
+      // part when it is done with tile t, so the writes of the 8 waves spread out
+      // instead of meeting their operand reads at the tile start.  Tile t+2 then
+      // stays in flight for the whole of the next tile.
+      if (t + 1 < ntp) stage(cur ^ 1);
+      fetch(t + 2 < ntp ? t + 2 : ntp - 1);
       __syncthreads();
     }
     if (scnt > 0) drain();
