@@ -238,8 +238,13 @@ __device__ __forceinline__ float mask_or_neg_inf(float x, uint32_t mask) {
 // (K and V each).  The codes are widened exactly to bf16 when a tile is
 // staged; the K scale joins the per-slot score factor and the V scale the
 // slot's weight in O^T += V^T P^T (not in the softmax sum).
+// Registers are capped at 256 per lane (two waves per SIMD) for bf16 caches: a
+// workgroup of fewer than 8 waves could otherwise take 512 (one wave per SIMD);
+// the cap measured faster (CSA prefill attention 0.79 -> 0.72 ms, the Pro-like
+// decode 1.7%).  The fp8-cache variants keep the default, since the cap would
+// make them spill.
 template <int D, int NW, bool HCA, int PAIR, bool KV8>
-__global__ __launch_bounds__(NW * 64) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1 : 2))) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
   constexpr int kT = NW * 64;
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
   constexpr int CT = kTB * CPR;                  // chunks per tensor per tile
