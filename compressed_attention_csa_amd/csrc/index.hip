@@ -137,7 +137,7 @@ __device__ __forceinline__ float sum_rows4(float x) {
 // KK == kKeyE4M3Q8: the query rows are quantised to e4m3 and the products are
 // fp8 x fp8 MFMAs on the raw key codes; each head's query scale moves into its
 // weight (relu(s * x) = s * relu(x) for s > 0).
-template <int KK, int DI>
+template <int KK, int DI, bool PEEL>
 __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowInfo& ri, uint32_t* keys,
                                                  int64_t qrow) {
   constexpr int CW = KK == kKeyBF16 ? 2 * DI / 16 : DI / 16;  // dwords of key per lane
@@ -269,23 +269,47 @@ __device__ __forceinline__ void score_slice_mfma(const IndexArgs& a, const RowIn
       if (g == 0 && e < n) keys[e] = score_key(part);
     }
   };
+  // Two rounds alternate.  PEEL: the last one or two are peeled off so that
+  // no load past the final round is issued (its wait would otherwise come due
+  // before the selection that follows: 2% of a 1M-entry decode call).  The
+  // variants with 16 slice keys per thread keep the plain loop, which needs
+  // fewer registers.
   if (nr > 0) {
     Round R0, R1;
     load(R0, 0);
-    for (int rr = 0; rr < nr; rr += 2) {
-      load(R1, rr + 1);
-      score(R0, rr);
-      if (rr + 1 >= nr) break;
-      load(R0, rr + 2);
-      score(R1, rr + 1);
+    if (PEEL) {
+      int rr = 0;
+      for (; rr + 2 < nr; rr += 2) {
+        load(R1, rr + 1);
+        score(R0, rr);
+        load(R0, rr + 2);
+        score(R1, rr + 1);
+      }
+      if (rr + 1 < nr) {
+        load(R1, rr + 1);
+        score(R0, rr);
+        score(R1, rr + 1);
+      } else {
+        score(R0, rr);
+      }
+    } else {
+      for (int rr = 0; rr < nr; rr += 2) {
+        load(R1, rr + 1);
+        score(R0, rr);
+        if (rr + 1 >= nr) break;
+        load(R0, rr + 2);
+        score(R1, rr + 1);
+      }
     }
   }
   __syncthreads();
 }
 
 // Scores of entries [lo, hi) of row ri into keys[0 .. hi-lo).
-template <int KK>
-__device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* keys, float* s_q) {
+// Inlined at both call sites (a call would pass the arguments through scratch
+// memory).
+template <int KK, bool PEEL = true>
+__device__ __forceinline__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* keys, float* s_q) {
   const int tid = threadIdx.x;
   const int64_t n = ri.hi - ri.lo;
   const int H_I = a.H_I, d_I = a.d_I;
@@ -316,9 +340,9 @@ __device__ void score_slice(const IndexArgs& a, const RowInfo& ri, uint32_t* key
     __syncthreads();
     return;
   } else if (d_I == 64) {
-    score_slice_mfma<KK, 64>(a, ri, keys, qrow);
+    score_slice_mfma<KK, 64, PEEL>(a, ri, keys, qrow);
   } else {
-    score_slice_mfma<KK, 32>(a, ri, keys, qrow);
+    score_slice_mfma<KK, 32, PEEL>(a, ri, keys, qrow);
   }
 }
 
@@ -468,7 +492,7 @@ __device__ __forceinline__ uint64_t select_rel(const uint64_t (&v)[KPT], int64_t
 
 // The same selection over n keys produced by get(i) (used for long candidate lists).
 template <typename Get>
-__device__ uint64_t select_get(int64_t n, int64_t need, Get get, uint32_t* hist, SelLds& S) {
+__device__ __forceinline__ uint64_t select_get(int64_t n, int64_t need, Get get, uint32_t* hist, SelLds& S) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0;
   int hi_bit = 64;
@@ -564,7 +588,7 @@ __device__ __forceinline__ void emit_regs(const uint64_t (&v)[KPT], uint64_t T, 
 // keys reach the bound, a radix select finds the threshold instead and the
 // winners are written in thread order.
 template <int KPT>
-__device__ uint64_t local_topk(const uint64_t (&v)[KPT], int kl, uint64_t* dst, uint64_t* scratch, uint32_t* hist,
+__device__ __forceinline__ uint64_t local_topk(const uint64_t (&v)[KPT], int kl, uint64_t* dst, uint64_t* scratch, uint32_t* hist,
                                SelLds& S) {
   const int tid = threadIdx.x;
   const uint64_t B = lane_max_bound(v, kl, scratch, S);
@@ -600,7 +624,7 @@ __device__ uint64_t local_topk(const uint64_t (&v)[KPT], int kl, uint64_t* dst, 
 }
 
 template <typename Get, typename Dst>
-__device__ int64_t emit_get(int64_t n, uint64_t T, Get get, int64_t from, Dst dst, int* s_wave) {
+__device__ __forceinline__ int64_t emit_get(int64_t n, uint64_t T, Get get, int64_t from, Dst dst, int* s_wave) {
   int64_t done = from;
   for (int64_t x0 = 0; x0 < n; x0 += kThreads) {
     const int64_t x = x0 + threadIdx.x;
@@ -640,7 +664,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tid = threadIdx.x;
   const int64_t n = ri.hi - ri.lo;
 
-  score_slice<KK>(a, ri, L.keys, L.q);
+  score_slice<KK, (KPT <= 8)>(a, ri, L.keys, L.q);
   const uint32_t base = uint32_t(ri.lo);
   uint64_t v[KPT];  // thread tid: slice elements tid + 256 u
 #pragma unroll
@@ -723,7 +747,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint64_t tx = load_dev(&tau[x]);
     if (tx <= T) continue;
     RowInfo rx = row_info(a, p, r, x);
-    score_slice<KK>(a, rx, L.keys, L.q);
+    score_slice<KK, (KPT <= 8)>(a, rx, L.keys, L.q);
     const uint32_t bx = uint32_t(rx.lo);
     const int64_t nx = rx.hi - rx.lo;
     for (int64_t y0 = 0; y0 < nx; y0 += kThreads) {
