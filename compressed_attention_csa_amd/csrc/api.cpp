@@ -200,10 +200,9 @@ csa_status_t csa_append(const void* x_new, csa_dtype_t dt, int B, int T_new, int
 
 size_t csa_index_topk_workspace(int B, int64_t T, int H_I, int d_I, int64_t N_alloc, int top_k,
                                 csa_dtype_t k_dt) {
-  (void)d_I;
   if (B < 1 || T < 0 || N_alloc < 0) return 0;
   const int kind = k_dt == CSA_F32 ? csa::kKeyF32 : (k_dt == CSA_BF16 ? csa::kKeyBF16 : csa::kKeyE4M3);
-  return csa::plan_index(B, T, H_I, N_alloc, top_k, kind).ws_bytes;
+  return csa::plan_index(B, T, H_I, d_I, N_alloc, top_k, kind).ws_bytes;
 }
 
 static csa_status_t index_topk(const void* q_idx, csa_dtype_t q_dt, const float* w, const void* k_idx,
@@ -235,7 +234,7 @@ static csa_status_t index_topk(const void* q_idx, csa_dtype_t q_dt, const float*
                    : k_dt == CSA_BF16 ? csa::kKeyBF16
                    : fp8_query        ? csa::kKeyE4M3Q8
                                       : csa::kKeyE4M3;
-  const csa::IndexPlan p = csa::plan_index(B, T, H_I, N_alloc, top_k, kind);
+  const csa::IndexPlan p = csa::plan_index(B, T, H_I, d_I, N_alloc, top_k, kind);
   REQUIRE(p.prefill ? (T + csa::kPrefillQPB - 1) / csa::kPrefillQPB <= kMaxGrid
                     : p.rows * p.slices <= kMaxGrid, CSA_E_SHAPE, "too many query rows");
   REQUIRE(p.ws_bytes == 0 || workspace != nullptr, CSA_E_WORKSPACE, "workspace is NULL");

@@ -146,7 +146,7 @@ struct IndexPlan {
   int64_t cand_row;    // candidate slots per row (rows x slices path)
 };
 constexpr int64_t kMaxSlice = 4096;
-IndexPlan plan_index(int B, int64_t T, int H_I, int64_t N_alloc, int top_k, int key_kind);
+IndexPlan plan_index(int B, int64_t T, int H_I, int d_I, int64_t N_alloc, int top_k, int key_kind);
 hipError_t launch_index_topk(const IndexArgs& a, const IndexPlan& p);
 bool prefill_path(int64_t T, int H_I, int key_kind);
 hipError_t launch_index_prefill(const IndexArgs& a, const IndexPlan& p);
