@@ -1181,7 +1181,8 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, AttendP
   const uint8_t* ws = reinterpret_cast<const uint8_t*>(a.ws);
   const float* part = reinterpret_cast<const float*>(ws + p.off_part) + (r * p.splits * H + h) * int64_t(D) + cc;
   const float* ml = reinterpret_cast<const float*>(ws + p.off_ml) + (r * p.splits * H + h) * 2;
-  const int64_t pstride = int64_t(H) * D, mstride = int64_t(H) * 2;
+  // 32-bit strides (the workspace offsets of one row fit; checked at launch).
+  const uint32_t pstride = uint32_t(H) * D, mstride = uint32_t(H) * 2;
   float M = -INFINITY, Lsum = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int s0 = 0; s0 < S; s0 += G) {
@@ -1189,10 +1190,14 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, AttendP
     float4 v[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const int sp = (s0 + u) < S ? s0 + u : S - 1;  // clamped: every load is issued
+      const uint32_t sp = uint32_t((s0 + u) < S ? s0 + u : S - 1);  // clamped: every load is issued
       m2[u] = *reinterpret_cast<const float2*>(ml + sp * mstride);
       v[u] = *reinterpret_cast<const float4*>(part + sp * pstride);
     }
+    // Every load above is issued before any result is used (otherwise the
+    // compiler interleaves the weights' arithmetic with the loads and waits
+    // for each partial in turn, serialising their latencies).
+    __builtin_amdgcn_sched_barrier(0);
     float mc = M;
 #pragma unroll
     for (int u = 0; u < G; ++u)
