@@ -243,9 +243,15 @@ __device__ __forceinline__ float mask_or_neg_inf(float x, uint32_t mask) {
 // the cap measured faster (CSA prefill attention 0.79 -> 0.72 ms, the Pro-like
 // decode 1.7%).  The fp8-cache variants keep the default, since the cap would
 // make them spill.
-template <int D, int NW, bool HCA, int PAIR, bool KV8>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1 : 2))) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
-  constexpr int kT = NW * 64;
+// TH = 2 (split rows with at most 4 waves of heads): two sets of NW waves share
+// the heads, and of each staged tile pair the first set computes one tile and
+// the second set the other; the two online softmax states are combined in LDS
+// at the end.  With one wave per SIMD the product / softmax chain of a tile is
+// latency-bound, so two tiles at once on different waves halve the chain.
+template <int D, int NW, bool HCA, int PAIR, bool KV8, int TH = 1>
+__global__ __launch_bounds__(NW * TH * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1 : 2))) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
+  static_assert(TH == 1 || PAIR == 2, "tile halves take the two tiles of a pair");
+  constexpr int kT = NW * TH * 64;
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
   constexpr int CT = kTB * CPR;                  // chunks per tensor per tile
   constexpr int CPT = CT >= kT ? CT / kT : 1;    // chunks per thread per tensor per tile
@@ -261,7 +267,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1
   if (s >= x.S) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 4, col = lane & 15;
   const int H = a.H;
-  const int h0 = int(hg) * (NW * 16) + wid * 16;  // this wave's 16 heads
+  const int hw = wid % NW, half = wid / NW;        // head wave, tile half (TH = 2)
+  const int h0 = int(hg) * (NW * 16) + hw * 16;   // this wave's 16 heads
   const bool has = h0 < H;
   const int64_t nsel = HCA ? x.c : int64_t(a.top_k);
 
@@ -454,25 +461,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1
   // them, one reference check for the group, then weights and O^T updates.
   // A tile past the split was staged with every slot skipped, so it adds
   // nothing and needs no branch.
+  constexpr int CP = TH == 2 ? 1 : PAIR;  // tiles one wave computes per staged group
   auto compute = [&](int b0) __attribute__((always_inline)) {
-    f32x4_t sc[PAIR][2];
+    f32x4_t sc[CP][2];
 #pragma unroll
-    for (int i = 0; i < PAIR; ++i) qk(b0 + i, sc[i]);
+    for (int i = 0; i < CP; ++i) qk(b0 + i, sc[i]);
     // Paired tiles read the first tile's V^T operands while the products run;
     // single tiles read them just before use (fewer registers, for occupancy).
     bf16x8_t va[DVT];
-    if (PAIR == 2) {
+    if (CP == 2) {
 #pragma unroll
       for (int v = 0; v < DVT; ++v) va[v] = vfrag(b0, v);
     }
     // u = score - reference (log2 units); skipped slots get -inf (a bit
     // select with the slot's mask, which also holds while the reference is
     // -inf).
-    float u[PAIR][2][4];
+    float u[CP][2][4];
     float umax = -INFINITY;
     const float nref = -mref;
 #pragma unroll
-    for (int i = 0; i < PAIR; ++i)
+    for (int i = 0; i < CP; ++i)
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) {
         const uint4 lm = *reinterpret_cast<const uint4*>(&L.live[b0 + i][cg * 16 + 4 * g]);
@@ -492,7 +500,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1
     if (__builtin_expect(__ballot(umax > kSlack) != 0, 0)) {
       float tmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < PAIR; ++i)
+      for (int i = 0; i < CP; ++i)
 #pragma unroll
         for (int cg = 0; cg < 2; ++cg) {
           const uint4 lm = *reinterpret_cast<const uint4*>(&L.live[b0 + i][cg * 16 + 4 * g]);
@@ -519,14 +527,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[v][j] *= corr;
 #pragma unroll
-      for (int i = 0; i < PAIR; ++i)
+      for (int i = 0; i < CP; ++i)
 #pragma unroll
         for (int cg = 0; cg < 2; ++cg)
 #pragma unroll
           for (int j = 0; j < 4; ++j) u[i][cg][j] -= msafe;
     }
 #pragma unroll
-    for (int i = 0; i < PAIR; ++i) {
+    for (int i = 0; i < CP; ++i) {
       f32x2_t ps = {0.0f, 0.0f};
       uint32_t phi[4], plo[4];
 #pragma unroll
@@ -551,7 +559,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1
       lpart += ps[0] + ps[1];
       const bf16x8_t pb_hi = u32x4_as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
       const bf16x8_t pb_lo = u32x4_as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
-      if (PAIR == 1 || i == 1) {
+      if (CP == 1 || i == 1) {
 #pragma unroll
         for (int v = 0; v < DVT; ++v) va[v] = vfrag(b0 + i, v);
       }
@@ -576,7 +584,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1
     __syncthreads();
     fetch(P0, t + SETS);
     if (PAIR == 2) fetch(P1, t + 1 + SETS);
-    if (has && t < nt) compute(b0);
+    if (TH == 2) {
+      if (has && t + half < nt) compute(b0 + half);
+    } else if (has && t < nt) {
+      compute(b0);
+    }
   };
   Pre P[SETS];
 #pragma unroll
@@ -586,6 +598,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1
     for (int i = 0; i < SETS; i += PAIR) step(P[i], P[i + PAIR - 1], t0 + i);
   }
 
+  if constexpr (TH == 2) {
+    // The second set's state (O, reference, partial sums) through LDS (the
+    // tile buffers, free once every wave is past its last tile); the first
+    // set combines it with its own under the larger reference.
+    static_assert(sizeof(L.k) + sizeof(L.v) >= size_t(NW) * (DVT * 4 + 2) * 64 * 4, "exchange fits");
+    float* xo = reinterpret_cast<float*>(&L.k[0][0]) + hw * ((DVT * 4 + 2) * 64);
+    __syncthreads();
+    if (half == 1) {
+#pragma unroll
+      for (int v = 0; v < DVT; ++v)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xo[(v * 4 + j) * 64 + lane] = o[v][j];
+      xo[(DVT * 4) * 64 + lane] = mref;
+      xo[(DVT * 4 + 1) * 64 + lane] = lpart;
+    }
+    __syncthreads();
+    if (half == 1) return;
+    const float m1 = xo[(DVT * 4) * 64 + lane], l1 = xo[(DVT * 4 + 1) * 64 + lane];
+    const float mn = fmaxf(mref, m1);
+    // A reference of -inf means no live slot so far: its state is all zero.
+    const float s0 = mref == -INFINITY ? 0.0f : exp2f(mref - mn);
+    const float s1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - mn);
+#pragma unroll
+    for (int v = 0; v < DVT; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[v][j] = o[v][j] * s0 + xo[(v * 4 + j) * 64 + lane] * s1;
+    lpart = lpart * s0 + l1 * s1;
+    mref = mn;
+  }
   // Per-head totals; lane (g, col) holds head h0 + col, columns 16v + 4g + j.
   float lt = lpart;
   lt += __shfl_xor(lt, 16);
@@ -1446,8 +1487,10 @@ int64_t attend_grid(const AttendPlan& p, bool bf16) {
 template <int D, bool HCA, int PAIR, bool KV8>
 static void launch_bf16_nw(const AttendArgs& a, const AttendPlan& p, dim3 grid) {
   const int nw = int((a.H / p.groups + 15) / 16);  // waves: 16 heads each, the heads of one group
-  if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2, HCA, PAIR, KV8>), grid, dim3(128), 0, a.stream, a, p);
-  else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4, HCA, PAIR, KV8>), grid, dim3(256), 0, a.stream, a, p);
+  // Split rows of at most 4 head waves: two tile halves (twice the waves).
+  constexpr int TH = PAIR == 2 ? 2 : 1;
+  if (nw <= 2) hipLaunchKernelGGL((attend_bf16_kernel<D, 2, HCA, PAIR, KV8, TH>), grid, dim3(128 * TH), 0, a.stream, a, p);
+  else if (nw <= 4) hipLaunchKernelGGL((attend_bf16_kernel<D, 4, HCA, PAIR, KV8, TH>), grid, dim3(256 * TH), 0, a.stream, a, p);
   else hipLaunchKernelGGL((attend_bf16_kernel<D, 8, HCA, PAIR, KV8>), grid, dim3(512), 0, a.stream, a, p);
 }
 
