@@ -54,16 +54,20 @@ class DecodeCSA:
     With ``state`` the step first appends the new token's K, V and indexer-key
     rows to the state-cache rings (compressing the block the token completes)
     and the attention reads its window from the K / V rings.  With ``bf16sel``
-    the selection is the approximate one (top-k of bf16-rounded scores); its
-    recall against the exact selection is reported beside the timing."""
+    the selection is the approximate one (top-k of bf16-rounded scores), with
+    ``fp8q`` the fp8 x fp8 indexer (csa_index_topk_fp8: the query rows quantised to
+    e4m3); the recall of either against the exact selection is reported beside
+    the timing."""
 
     dominant = "index_topk"
     dominant_kernels = ("index_topk",)
 
     def __init__(self, wl, seed, replicas, variant=""):
-        assert variant in ("", "state", "bf16sel"), variant
+        assert variant in ("", "state", "bf16sel", "fp8q"), variant
         state = variant == "state"
         self.bf16sel = variant == "bf16sel"
+        self.fp8q = variant == "fp8q"
+        assert not self.fp8q or wl.idx_key_dtype == "e4m3", "the fp8 x fp8 indexer takes e4m3 keys"
         import torch
         import compressed_attention_csa_amd as csa
         import inputgen
@@ -118,8 +122,11 @@ class DecodeCSA:
             csa.csa_append(self.new["v_raw"], c["ring_v_raw"], wl.t0, self.z, wl.m, c["v_cmp"])
             csa.csa_append(self.new["k_idx_raw"], c["ring_k_idx_raw"], wl.t0, self.z, wl.m, c["k_idx"],
                            c["k_scale"])
-        csa.csa_index_topk(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, self.idx,
-                           bf16_scores=self.bf16sel)
+        if self.fp8q:
+            csa.csa_index_topk_fp8(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, self.idx)
+        else:
+            csa.csa_index_topk(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, self.idx,
+                               bf16_scores=self.bf16sel)
         if self.state:
             kr, base = csa.ring_window(c["ring_k_raw"], wl.t0 - wl.W + 1)
             csa.csa_attend(self.q, c["k_cmp"], c["v_cmp"], wl.m, self.idx, kr, c["ring_v_raw"], wl.t0,
@@ -129,15 +136,19 @@ class DecodeCSA:
                            wl.W, wl.scale, self.out, raw_base=self.raw_base)
 
     def quality(self):
-        """Recall of the approximate selection against the exact one (replica 0)."""
-        if not self.bf16sel:
+        """Recall of the approximate (bf16-score or fp8 x fp8) selection against the
+        exact one (replica 0)."""
+        if not (self.bf16sel or self.fp8q):
             return None
         wl, csa, torch, c = self.wl, self.csa, self.torch, self.reps[0]
         sel = {}
         for approx in (False, True):
             idx = torch.empty_like(self.idx)
-            csa.csa_index_topk(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, idx,
-                               bf16_scores=approx)
+            if approx and self.fp8q:
+                csa.csa_index_topk_fp8(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, idx)
+            else:
+                csa.csa_index_topk(self.q_idx, self.w, c["k_idx"], c["k_scale"], wl.t0, wl.m, wl.k, idx,
+                                   bf16_scores=approx)
             sel[approx] = idx.cpu()
         hits = sum(len(set(sel[True][b, 0].tolist()) & set(sel[False][b, 0].tolist())) for b in range(wl.B))
         return {"recall_vs_exact": round(hits / (wl.B * wl.k), 5)}
@@ -924,7 +935,7 @@ def main():
     ap.add_argument("--legs", default="hbm_read_71mb,hbm_read_2gb,hca_decode_1m,csa_prefill_chunk_1m,"
                     "csa_decode_flash_128k,hca_prefill_chunk_1m,tiny_prefill_f32,csa_compress_pro_1m,"
                     "csa_decode_pro_1m+state,hca_decode_1m+fp8kv,csa_decode_pro_1m+bf16sel,csa_prefill_chunk_1m+fp8k,"
-                    "csa_prefill_chunk_1m+fp8q",
+                    "csa_prefill_chunk_1m+fp8q,csa_decode_pro_1m+fp8q",
                     help="comma-separated extra workloads ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
