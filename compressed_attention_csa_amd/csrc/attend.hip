@@ -13,7 +13,9 @@
 //
 // bf16 path: a workgroup handles one row, every head of it (wave w owns heads
 // 16w .. 16w+15; split rows with few workgroups split the heads into two
-// groups instead) and one contiguous range of slots ("split").  32-slot tiles
+// groups instead, and split rows of at most four head waves have two wave sets
+// that take the two tiles of each staged pair) and one contiguous range of
+// slots ("split").  32-slot tiles
 // are gathered into LDS (K row-major, V transposed) while the next tiles' rows
 // are already being loaded into registers.  S^T = K Q^T on 16x16x32 MFMA puts
 // one head per lane column and 8 slots per lane, which is exactly the
