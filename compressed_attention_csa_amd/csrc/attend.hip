@@ -244,20 +244,24 @@ __device__ __forceinline__ float mask_or_neg_inf(float x, uint32_t mask) {
 // workgroup of fewer than 8 waves could otherwise take 512 (one wave per SIMD);
 // the cap measured faster (CSA prefill attention 0.79 -> 0.72 ms, the Pro-like
 // decode 1.7%).  The fp8-cache variants keep the default, since the cap would
-// make them spill.
+// make them spill.  The unsplit CSA rows of 64 heads (prefill) go further: 168
+// registers, three waves per SIMD (three workgroups per CU, which their LDS
+// allows), with two tiles in flight instead of four so that nothing spills
+// (CSA prefill attention at 1M 0.72 -> 0.63 ms: more gathers in flight per CU
+// from more waves, each with fewer).
 // TH = 2 (split rows with at most 4 waves of heads): two sets of NW waves share
 // the heads, and of each staged tile pair the first set computes one tile and
 // the second set the other; the two online softmax states are combined in LDS
 // at the end.  With one wave per SIMD the product / softmax chain of a tile is
 // latency-bound, so two tiles at once on different waves halve the chain.
 template <int D, int NW, bool HCA, int PAIR, bool KV8, int TH = 1>
-__global__ __launch_bounds__(NW * TH * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1 : 2))) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
+__global__ __launch_bounds__(NW * TH * 64) __attribute__((amdgpu_waves_per_eu(KV8 ? 1 : (PAIR == 1 && NW == 4 && !HCA ? 3 : 2)))) void attend_bf16_kernel(AttendArgs a, AttendPlan p) {
   static_assert(TH == 1 || PAIR == 2, "tile halves take the two tiles of a pair");
   constexpr int kT = NW * TH * 64;
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
   constexpr int CT = kTB * CPR;                  // chunks per tensor per tile
   constexpr int CPT = CT >= kT ? CT / kT : 1;    // chunks per thread per tensor per tile
-  constexpr int SETS = CPT >= 4 ? 2 : 4;         // tiles in flight in registers
+  constexpr int SETS = CPT >= 4 ? 2 : (PAIR == 1 && NW == 4 && !HCA ? 2 : 4);  // tiles in flight in registers
   constexpr int KS = D / 32;                     // k-steps of the QK product
   constexpr int DVT = D / 16;                    // 16-column tiles of the output
   constexpr int NB = 2 * PAIR;                   // LDS tile buffers

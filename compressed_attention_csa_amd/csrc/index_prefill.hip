@@ -330,14 +330,34 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
   }
   float psc = 1.0f;
   int ss = 1;  // entry stride of the sweep (the sample stride in the sampling pass)
-  auto chunk_ptr = [&](int t, int id) {
-    const int ge = min((t * TE + id / CPG) * ss, cmax - 1);
-    return reinterpret_cast<const uint4*>(kbytes + int64_t(ge) * (DI * KB) + (id % CPG) * 16);
-  };
-  auto fetch = [&](int t) {
+  // Byte offsets of this thread's chunks (and of its scale) from the first byte
+  // of a tile, fixed for a pass: a tile whose entries all lie below cmax is
+  // then read from one scalar base per tile; only the last tile clamps its
+  // entries one by one.  (A tile spans TE * ss < 2^31 / 128 entries, so the
+  // offsets fit 32 bits.)
+  uint32_t coff[LOADS], soff = 0;
+  auto set_stride = [&](int stride) {
+    ss = stride;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) pre[u] = *chunk_ptr(t, pid[u]);
-    if (key_is_e4m3(KK)) psc = a.k_scale[b * a.N_alloc + min((t * TE + (tid & (TE - 1))) * ss, cmax - 1)];
+    for (int u = 0; u < LOADS; ++u) coff[u] = uint32_t((pid[u] / CPG) * ss * (DI * KB) + (pid[u] % CPG) * 16);
+    soff = uint32_t((tid & (TE - 1)) * ss) * 4u;
+  };
+  const float* sbytes = key_is_e4m3(KK) ? a.k_scale + b * a.N_alloc : nullptr;
+  auto fetch = [&](int t) {
+    if ((t * TE + TE - 1) * ss < cmax) {
+      const uint8_t* tb = kbytes + int64_t(t) * (TE * ss) * (DI * KB);
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) pre[u] = *reinterpret_cast<const uint4*>(tb + coff[u]);
+      if (key_is_e4m3(KK))
+        psc = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(sbytes + int64_t(t) * (TE * ss)) + soff);
+    } else {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int ge = min((t * TE + pid[u] / CPG) * ss, cmax - 1);
+        pre[u] = *reinterpret_cast<const uint4*>(kbytes + int64_t(ge) * (DI * KB) + (pid[u] % CPG) * 16);
+      }
+      if (key_is_e4m3(KK)) psc = sbytes[min((t * TE + (tid & (TE - 1))) * ss, cmax - 1)];
+    }
   };
   // Writes the prefetched chunks to LDS buffer `buf`; fp8 keys for bf16
   // products are widened to bf16 here, once per workgroup, rather than by every
@@ -529,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void idx_prefill_kernel(IndexArgs a, Inde
         top_hi = 0u;
       }
     }
-    ss = pass == 0 ? sstride : 1;
+    set_stride(pass == 0 ? sstride : 1);
     // The sampling pass compacts early, to about r keys, so that its threshold
     // rises fast; the full sweeps keep at least k.
     cap_pass = pass == 0 ? min(cap, max(1024, 8 * int(wave_max_u32(uint32_t(r_l))))) : cap;
