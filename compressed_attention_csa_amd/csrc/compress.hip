@@ -7,6 +7,11 @@
 // 16-byte (bf16) or 32-byte (fp32) loads: consecutive threads read consecutive
 // 16 B of a row, a wave covers whole rows, and every byte is read once.
 // Sums are accumulated in fp64 and rounded once to the output type.
+// Long blocks (HCA, m' = 128) are also split over slots: P groups of threads
+// each sum about 8 of the entry's slots and the P partial sums are added in
+// group order through LDS, so a thread has all of its loads in flight at once
+// instead of streaming 128 rows one after another (the same order for every
+// call, so appends still reproduce the whole-history compression bit for bit).
 #include "common.hpp"
 #include "kernels.h"
 
@@ -56,15 +61,25 @@ struct AppendTail {
 // Overlap o > 0 (a method variant): entry j folds the m + o rows of positions
 // j*m - o .. j*m + m - 1 with the softmax of m + o logits; the first entries,
 // whose leading slots fall before position 0, renormalise over the rest.
-template <typename TIn, int OUT, bool APPEND>
+// Slot groups of an entry: about 8 slots each, as many as the threads allow.
+__host__ __device__ __forceinline__ int slot_parts(int ms, int tpe) {
+  int parts = (ms + 7) / 8;
+  const int most = kThreads / tpe;
+  return parts < most ? parts : most;
+}
+
+// SPLIT: the entry's slots are split over several thread groups (P > 1).
+template <typename TIn, int OUT, bool APPEND, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
     const TIn* __restrict__ x, int64_t n_raw, int d, int64_t raw_base,
     const float* __restrict__ logits, int m, int o, int64_t entry_begin, int64_t n_ent, int64_t N_alloc,
     void* __restrict__ out, float* __restrict__ out_scale, AppendTail at) {
   __shared__ double alpha[128];
   __shared__ float zmax_s;
+  __shared__ double partial[SPLIT ? kThreads : 1][8];  // slot-group sums
   debug_poison_lds(alpha);
   debug_poison_lds(zmax_s);
+  debug_poison_lds(partial);
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
   const TIn* xn = reinterpret_cast<const TIn*>(at.x_new) + int64_t(b) * at.T_new * d;
@@ -101,22 +116,25 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   for (int s = tid; s < ms; s += kThreads) alpha[s] = alpha[s] / total;
   __syncthreads();
 
-  const int tpe = d >> 3;  // threads per entry, 8 columns each
-  const int epb = kThreads / tpe;
-  const int64_t e_local = int64_t(blockIdx.x) * epb + tid / tpe;
+  const int tpe = d >> 3;  // threads per entry and slot group, 8 columns each
+  const int P = SPLIT ? slot_parts(ms, tpe) : 1;
+  const int sper = (ms + P - 1) / P;  // slots per group
+  const int epb = kThreads / (tpe * P);
+  const int part = (tid / tpe) % P;
+  const int64_t e_local = int64_t(blockIdx.x) * epb + tid / (tpe * P);
   const int seg = tid % tpe;
-  const bool valid = tid < epb * tpe && e_local < n_ent;
+  const bool valid = tid < epb * tpe * P && e_local < n_ent;
   const int64_t j = entry_begin + e_local;
+  const int64_t p0 = j * m - o;  // position of slot 0
 
   double acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0;
   if (valid) {
     const TIn* xb = x + int64_t(b) * n_raw * d + seg * 8;
-    const int64_t p0 = j * m - o;  // position of slot 0
-    double wsum = 0.0;             // weight of the slots at positions >= 0
+    const int s_end = (part + 1) * sper < ms ? (part + 1) * sper : ms;
 #pragma unroll 8
-    for (int s = 0; s < ms; ++s) {
+    for (int s = part * sper; s < s_end; ++s) {
       const int64_t pos = p0 + s;
       if (pos < 0) continue;
       double v[8];
@@ -124,24 +142,37 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
       if (APPEND && pos >= at.t0) rp = xn + (pos - at.t0) * d + seg * 8;
       Row8<TIn>::load(rp, v);
       const double a = alpha[s];
-      wsum += a;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fma(a, v[i], acc[i]);
     }
-    if (p0 < 0)
+  }
+  if (SPLIT) {  // group 0 adds the other groups' sums, in group order
+    if (valid && part > 0)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] /= wsum;
+      for (int i = 0; i < 8; ++i) partial[tid][i] = acc[i];
+    __syncthreads();
+    if (valid && part == 0)
+      for (int q = 1; q < P; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += partial[tid + q * tpe][i];
+  }
+  if (valid && p0 < 0) {
+    double wsum = 0.0;  // weight of the slots at positions >= 0
+    for (int s = 0; s < ms; ++s) wsum += (p0 + s >= 0) ? alpha[s] : 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] /= wsum;
   }
 
+  const bool writer = valid && part == 0;  // the first slot group holds the sum
   const int64_t orow = int64_t(b) * N_alloc + j;
   if (OUT == 0) {
-    if (valid) {
+    if (writer) {
       float* o = reinterpret_cast<float*>(out) + orow * d + seg * 8;
       *reinterpret_cast<float4*>(o) = make_float4(float(acc[0]), float(acc[1]), float(acc[2]), float(acc[3]));
       *reinterpret_cast<float4*>(o + 4) = make_float4(float(acc[4]), float(acc[5]), float(acc[6]), float(acc[7]));
     }
   } else if (OUT == 1) {
-    if (valid) {
+    if (writer) {
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -163,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     // or a largest magnitude below 448 * 2^-150, which underflows) takes scale 1.
     float scale = amax / 448.0f;
     if (scale == 0.0f) scale = 1.0f;
-    if (valid) {
+    if (writer) {
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -180,7 +211,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 template <typename TIn, int OUT, bool APPEND>
 hipError_t launch(const CompressArgs& a, const AppendTail& at) {
   const int tpe = a.d / 8;
-  const int epb = kThreads / tpe;
+  const int parts = slot_parts(a.m + a.overlap, tpe);
+  const int epb = kThreads / (tpe * parts);
   const int64_t n_ent = a.entry_end - a.entry_begin;
   AppendTail t = at;
   t.cmp_blocks = int((n_ent + epb - 1) / epb);
@@ -188,10 +220,12 @@ hipError_t launch(const CompressArgs& a, const AppendTail& at) {
   if (APPEND) blocks += (int64_t(t.T_new) * (a.d * int64_t(sizeof(TIn)) / 16) + kThreads - 1) / kThreads;
   dim3 grid(unsigned(blocks), unsigned(a.B));
   CSA_HOST_CHECK(blocks >= 1 && a.m >= 1 && a.m + a.overlap <= 128);
-  log_dispatch("%s: B=%d d=%d m=%d overlap=%d entries [%lld, %lld) -> grid %lld x %d", APPEND ? "append" : "compress",
-               a.B, a.d, a.m, a.overlap, (long long)a.entry_begin, (long long)a.entry_end, (long long)blocks, a.B);
+  log_dispatch("%s: B=%d d=%d m=%d overlap=%d entries [%lld, %lld) -> grid %lld x %d, %d slot group(s)",
+               APPEND ? "append" : "compress", a.B, a.d, a.m, a.overlap, (long long)a.entry_begin,
+               (long long)a.entry_end, (long long)blocks, a.B, parts);
   ProfScope prof(APPEND ? "append" : "compress", a.stream);
-  hipLaunchKernelGGL((compress_kernel<TIn, OUT, APPEND>), grid, dim3(kThreads), 0, a.stream,
+  auto kernel = parts > 1 ? compress_kernel<TIn, OUT, APPEND, true> : compress_kernel<TIn, OUT, APPEND, false>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, a.stream,
                      reinterpret_cast<const TIn*>(a.x), a.n_raw, a.d, a.raw_base, a.logits, a.m, a.overlap,
                      a.entry_begin, n_ent, a.N_alloc, a.out, a.out_scale, t);
   return hipGetLastError();
