@@ -195,8 +195,13 @@ __device__ __forceinline__ bool decode_block(const AttendPlan& p, int64_t& hg, i
 // group, for split rows with few workgroups): wave w owns heads 16w .. 16w+15
 // of its group, so each K/V row is read from memory once per split and group.  Tiles of
 // 32 slots go through two LDS buffers; SETS further tiles are always in flight
-// in registers (about 64 KB per workgroup), enough to cover memory latency in
-// decode, where a split is a few tiles long.  Loads are issued unconditionally
+// in registers (about 64 KB per workgroup; 32 KB for unsplit 64-head rows, which
+// run three workgroups per CU), enough to cover memory latency in decode, where
+// a split is a few tiles long.  A CU gathers only about 50 GB/s of scattered
+// 256-byte rows however many loads it has in flight, so a decode row is split
+// over many workgroups (a workgroup gathering all 1152 slots of a Pro-like row
+// would take about 12 us for the gather alone, against 3.4 us for 72 workgroups
+// of 128 slots each), and the splits are merged afterwards.  Loads are issued unconditionally
 // (dead slots read the query row instead), so the compiler's wait counts stay
 // exact and no wait drains the prefetch.
 

@@ -46,6 +46,11 @@ COMPRESS_CASES = [
     ("bf16", "bf16", 4, 128, 300, 100, 25, 100, 120),  # sub-range after raw_base
     ("bf16", "bf16", 1, 64, 77, 0, 0, 77, 77),         # m = 1 copies
     ("bf16", "bf16", 5, 16, 103, 0, 3, 20, 20),        # odd block, narrow rows
+    # long blocks split over slot groups: 4 groups of 32 slots (wide rows cap the
+    # groups), 8 groups of 13 slots with a short last one, 3 groups on 3-thread rows
+    ("bf16", "e4m3", 128, 512, 1024, 0, 0, 8, 8),
+    ("f32", "f32", 100, 256, 1000, 0, 0, 10, 10),
+    ("bf16", "bf16", 17, 24, 200, 0, 0, 11, 11),
 ]
 
 
@@ -94,6 +99,7 @@ OVERLAP_CASES = [
     ("bf16", "e4m3", 4, 4, 64, 300, 40, 11, 70, 80),
     ("f32", "f32", 5, 3, 32, 203, 0, 0, 40, 41),
     ("bf16", "bf16", 64, 64, 128, 1024, 0, 0, 16, 16),
+    ("f32", "f32", 12, 5, 64, 300, 0, 0, 24, 24),  # 17 slots in 3 groups; the first entry renormalised
 ]
 
 
