@@ -694,7 +694,9 @@ def _role(kernel, workload):
     if kernel.startswith("attend_f32_kernel"):
         return "attend (fp32)"
     if kernel.startswith("compress_kernel"):
-        return "append" if kernel.endswith("true>") else "compress"
+        # compress_kernel<input type, output kind, APPEND, SPLIT>
+        args = [x.strip() for x in kernel.split("<", 1)[-1].rstrip(">").split(",")]
+        return "append" if len(args) > 2 and args[2] == "true" else "compress"
     if kernel.startswith("stream_read_kernel"):
         return "stream_read"
     return None

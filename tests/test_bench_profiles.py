@@ -11,7 +11,8 @@ import bench
 
 SPIN = "at::cuda::(anonymous namespace)::spin_kernel(long)"
 IDX = "void csa::(anonymous namespace)::idx_topk_kernel<2, 8>(csa::IndexArgs, csa::IndexPlan, long)"
-APP = "void csa::(anonymous namespace)::compress_kernel<unsigned short, 1, true>(unsigned short const*)"
+APP = "void csa::(anonymous namespace)::compress_kernel<unsigned short, 1, true, false>(unsigned short const*)"
+CMP = "void csa::(anonymous namespace)::compress_kernel<unsigned short, 1, false, true>(unsigned short const*)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -66,7 +67,7 @@ def test_summary_pairs_timed_dispatches_and_scales_counters(tmp_path):
     md = bench.profile_summary(run, cal, "csa_decode_pro_1m", out, "cmd one ;; cmd two", timed_steps=2)
     assert "    cmd one" in md and "    cmd two" in md
     assert "idx_topk_kernel<2, 8> | index_topk | 131072 | 256 | 2 | 29.00 |" in md   # setup and late ones cut
-    assert "compress_kernel<unsigned short, 1, true> | append | 2048 | 256 | 2 |" in md  # 512 x 4 = 2048
+    assert "compress_kernel<unsigned short, 1, true, false> | append | 2048 | 256 | 2 |" in md  # 512 x 4 = 2048
     t = json.load(open(out))
     idx = t["index_topk@csa_decode_pro_1m"]
     assert idx["scale"] == {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
@@ -83,3 +84,13 @@ def test_summary_drops_pairs_above_peak_bandwidth(tmp_path):
     make_calibration(cal)
     md = bench.profile_summary(run, cal, "csa_decode_pro_1m", None, "", timed_steps=2)
     assert "1 dropped" in md
+
+
+def test_kernel_roles():
+    """Roles follow the template arguments: the third compressor argument is APPEND
+    (the fourth, SPLIT, splits long blocks over slot groups)."""
+    assert bench._role(APP, "csa_decode_pro_1m+state") == "append"
+    assert bench._role(CMP, "hca_prefill_chunk_1m") == "compress"
+    assert bench._role(IDX, "csa_decode_pro_1m") == "index_topk"
+    att = "void csa::(anonymous namespace)::attend_bf16_kernel<128, 8, true, 2, false, 1>(csa::AttendArgs)"
+    assert bench._role(att, "hca_decode_1m") == "hca_attend"
