@@ -24,7 +24,8 @@ import bench
 import compressed_attention_csa_amd as csa
 import inputgen
 from oracle import formats, method
-from parity_util import check_attention, check_e4m3, check_topk_rows, f64, bf16_bits, ulp_diff_bf16
+from parity_util import (bf16_bits, check_attention, check_bf16_selection_row, check_e4m3, check_topk_rows,
+                         check_topk_rows_fp8, f64, fp8_score_error_bound, ulp_diff_bf16)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -165,6 +166,49 @@ def test_csa_decode_full_size(name):
                                          wl.t0, W, m, wl.scale)
         check_attention(f64(out[b]), f64(lse[b]), o_ref, l_ref, "bf16", what=f"{name} b={b}")
     say("  attention rows ok")
+
+
+def test_csa_decode_selector_variants_full_size():
+    """The two selector variants the benchmark times beside the Pro-like decode
+    (1M context, e4m3 keys), at that size and launch plan: the bf16 selector
+    must be exactly the top-k of the oracle's scores rounded to binary32 and
+    then bf16, and the fp8 x fp8 indexer a top-k of scores within the fp8 bound
+    of the oracle's index_scores_fp8q.  Keys come from the oracle's compression."""
+    name = "csa_decode_pro_1m"
+    wl = inputgen.WORKLOADS[name]
+    say("full-size selector variants", name)
+    B, n, N, dI, m, k = wl.B, wl.n, wl.N_c, wl.d_I, wl.m, wl.k
+    z64 = f64(inputgen.normal("z_csa", (m,), SEED, "f32", std=0.5, device=DEV))
+    q_idx = inputgen.normal("q_idx", (B, 1, wl.H_I, dI), SEED, "bf16", device=DEV)
+    w = inputgen.normal("w", (B, 1, wl.H_I), SEED, "f32", device=DEV)
+    raw = inputgen.normal("k_idx_raw", (B, n, dI), SEED, "bf16", device=DEV)
+    codes = torch.empty((B, N, dI), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((B, N), dtype=torch.float32, device=DEV)
+    keys64 = []
+    for b in range(B):
+        st = oracle_compress(raw[b], z64, m, "e4m3")
+        keys64.append(st["values"])
+        codes[b] = torch.from_numpy(st["codes"]).to(DEV)
+        scales[b] = torch.from_numpy(st["scale"]).to(DEV)
+    del raw
+    sel_b = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    sc_b = torch.empty((B, 1, k), dtype=torch.float32, device=DEV)
+    csa.csa_index_topk(q_idx, w, codes, scales, wl.t0, m, k, sel_b, sc_b, bf16_scores=True)
+    sel_q = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    sc_q = torch.empty((B, 1, k), dtype=torch.float32, device=DEV)
+    csa.csa_index_topk_fp8(q_idx, w, codes, scales, wl.t0, m, k, sel_q, sc_q)
+    torch.cuda.synchronize()
+    q64, w64 = f64(q_idx), f64(w)
+    total = hits = 0
+    for b in range(B):
+        s64, vis = method.index_scores(q64[b], w64[b], keys64[b], wl.t0, m)
+        kk, h = check_bf16_selection_row(sel_b[b, 0].cpu().numpy(), sc_b[b, 0].cpu().numpy(), s64[0], vis[0], k)
+        total, hits = total + kk, hits + h
+        s8, vis8 = method.index_scores_fp8q(q64[b], w64[b], keys64[b], wl.t0, m)
+        E = fp8_score_error_bound(method.quantize_query_e4m3(q64[b]), w64[b], keys64[b])
+        check_topk_rows_fp8(sel_q[b].cpu().numpy(), sc_q[b].cpu().numpy(), s8, vis8, k, E)
+    say(f"  bf16 selector recall against the exact top-k: {hits / total:.4f}; fp8 x fp8 rows ok")
+    assert hits >= 0.95 * total
 
 
 # ----------------------------------------------------------------------------- HCA decode
