@@ -585,9 +585,15 @@ def test_attend(case):
     odt = torch.bfloat16 if out_dt == "bf16" else torch.float32
     out = torch.full((B, T, H, d), 9.0, dtype=odt, device=DEV)
     lse = torch.full((B, T, H), 9.0, device=DEV)
+    out_nolse = None
     if hca:
         csa.hca_attend(q.to(DEV), kc.to(DEV), vc.to(DEV), m, kr.to(DEV), vr.to(DEV), t0, W, scale,
                        out, lse)
+        # without an lse output the multi-token kernel sums its binary16 weights on
+        # the matrix cores: the output alone is held to the same criterion
+        out_nolse = torch.full_like(out, 9.0)
+        csa.hca_attend(q.to(DEV), kc.to(DEV), vc.to(DEV), m, kr.to(DEV), vr.to(DEV), t0, W, scale,
+                       out_nolse)
     else:
         idx = make_idx(B, T, k, t0, m, N, seed=N + k)
         csa.csa_attend(q.to(DEV), kc.to(DEV), vc.to(DEV), m, torch.from_numpy(idx).to(DEV),
@@ -602,6 +608,9 @@ def test_attend(case):
                                              f64(vr[b]), 0, t0, W, m, scale)
         check_attention(f64(out[b]), f64(lse[b]), o_ref, l_ref, dt, what=f"{name} b={b}",
                         out_bf16=(out_dt == "bf16"))
+        if out_nolse is not None:
+            check_attention(f64(out_nolse[b]), None, o_ref, l_ref, dt, what=f"{name} b={b}, no lse",
+                            out_bf16=(out_dt == "bf16"))
 
 
 @pytest.mark.parametrize("T", [64, 1], ids=["prefill-multi", "decode"])
@@ -636,11 +645,15 @@ def test_hca_many_tiny_weights(T):
     lse = torch.full((B, T, H), 9.0, device=DEV)
     csa.hca_attend(to_dev_bf16(q), to_dev_bf16(kc), to_dev_bf16(vc), m, to_dev_bf16(kr), to_dev_bf16(vr),
                    t0, W, scale, out, lse)
+    out2 = torch.full((B, T, H, d), 9.0, device=DEV)  # no lse: weight sums on the matrix cores
+    csa.hca_attend(to_dev_bf16(q), to_dev_bf16(kc), to_dev_bf16(vc), m, to_dev_bf16(kr), to_dev_bf16(vr),
+                   t0, W, scale, out2)
     torch.cuda.synchronize()
     o_ref, l_ref = method.hca_attend(q[0], kc[0], vc[0], m, kr[0], vr[0], 0, t0, W, scale)
     shift = np.abs(o_ref - vc[0, 0]).max()
     assert shift > 0.02, shift  # the tiny weights matter
     check_attention(f64(out[0]), f64(lse[0]), o_ref, l_ref, "bf16", what="tiny weights")
+    check_attention(f64(out2[0]), None, o_ref, l_ref, "bf16", what="tiny weights, no lse")
 
 
 @pytest.mark.parametrize("T", [301, 1], ids=["prefill-multi", "decode"])
@@ -672,10 +685,14 @@ def test_hca_v_outside_binary16_range(T):
     lse = torch.full((B, T, H), 9.0, device=DEV)
     csa.hca_attend(q.to(DEV), kc.to(DEV), to_dev_bf16(vc), m, kr.to(DEV), to_dev_bf16(vr), t0, W, scale,
                    out, lse)
+    out2 = torch.full((B, T, H, d), 9.0, device=DEV)  # no lse: weight sums on the matrix cores
+    csa.hca_attend(q.to(DEV), kc.to(DEV), to_dev_bf16(vc), m, kr.to(DEV), to_dev_bf16(vr), t0, W, scale,
+                   out2)
     torch.cuda.synchronize()
     for b in range(B):
         o_ref, l_ref = method.hca_attend(f64(q[b]), f64(kc[b]), vc[b], m, f64(kr[b]), vr[b], 0, t0, W, scale)
         check_attention(f64(out[b]), f64(lse[b]), o_ref, l_ref, "bf16", what=f"v range b={b}")
+        check_attention(f64(out2[b]), None, o_ref, l_ref, "bf16", what=f"v range b={b}, no lse")
 
 
 FP8_KV_CASES = [
