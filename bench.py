@@ -442,18 +442,65 @@ class StreamRead:
         return {"bytes": self.nbytes, "flops": 0, "dominant_bytes": self.nbytes, "queries": 0}
 
 
+class GatherRead:
+    """The rate at which workgroups gather scattered K / V rows (csa_diag_gather_read), the
+    decode attention's access pattern at the Pro-like shape: four sequences of 262144 rows
+    of 256 bytes per tensor, 1152 rows selected per sequence (its 1024 entries and 128
+    window rows), gathered either split as the attention's plan does (per sequence 2 head
+    groups x 9 splits of 128 rows: 72 workgroups) or whole (per sequence 8 head groups of 16
+    heads, each gathering all 1152 rows: 32 workgroups).  Replicas are cycled so that every
+    gather is cache-cold; ``bytes`` counts every workgroup's reads (the head groups of one
+    split read the same rows)."""
+
+    dominant = "gather_read"
+    dominant_kernels = ("gather_read",)
+
+    def __init__(self, split, replicas, seed=0):
+        import torch
+        import compressed_attention_csa_amd as csa
+        self.csa = csa
+        rows, N, sel = 4, 262144, 1152
+        self.k = [torch.full((rows * N, 128), float(i + 1), dtype=torch.bfloat16, device="cuda")
+                  for i in range(replicas)]
+        self.v = [torch.full((rows * N, 128), float(i + 2), dtype=torch.bfloat16, device="cuda")
+                  for i in range(replicas)]
+        g = torch.Generator().manual_seed(seed)
+        chosen = [torch.randint(0, N, (sel,), generator=g, dtype=torch.int64) + r * N for r in range(rows)]
+        if split:
+            self.per, groups = 128, 72
+            parts = [chosen[w % rows][((w // rows) % 9) * 128:((w // rows) % 9 + 1) * 128] for w in range(groups)]
+        else:
+            self.per, groups = sel, 32
+            parts = [chosen[w % rows] for w in range(groups)]
+        self.idx = torch.cat(parts).to(torch.int32).to("cuda")
+        self.sink = torch.zeros(groups, dtype=torch.int32, device="cuda")
+        self.groups = groups
+        torch.cuda.synchronize()
+
+    def step(self, r):
+        self.csa.diag_gather_read(self.k[r % len(self.k)], self.v[r % len(self.v)], self.idx, self.per, self.sink)
+
+    def algorithmic(self):
+        b = self.groups * self.per * 512
+        return {"bytes": b, "flops": 0, "dominant_bytes": b, "queries": 0}
+
+
 KINDS = {"csa_decode_pro_1m": DecodeCSA, "csa_decode_flash_128k": DecodeCSA,
          "hca_decode_1m": DecodeHCA, "csa_prefill_chunk_1m": PrefillCSA,
          "hca_prefill_chunk_1m": PrefillHCA, "tiny_prefill_f32": TinyPrefill}
 REPLICAS = {"csa_decode_pro_1m": 8, "csa_decode_flash_128k": 16, "hca_decode_1m": 8,
             "csa_prefill_chunk_1m": 1, "hca_prefill_chunk_1m": 1, "tiny_prefill_f32": 1,
-            "csa_compress_pro_1m": 1, "hbm_read_71mb": 8, "hbm_read_2gb": 1}
+            "csa_compress_pro_1m": 1, "hbm_read_71mb": 8, "hbm_read_2gb": 1, "gather_split_72": 8,
+            "gather_whole_32": 8}
 # Workloads that are not a configuration of the method: the compressor's cache build at the
-# Pro-like shape, and the HBM read ceiling at the Pro-like step's key bytes and at 2 GB.
+# Pro-like shape, the HBM read ceiling at the Pro-like step's key bytes and at 2 GB, and the
+# decode attention's row gather, split and whole.
 EXTRA = {"csa_compress_pro_1m": lambda seed, R: CompressCache(__import__("inputgen").WORKLOADS["csa_decode_pro_1m"],
                                                               seed, R),
          "hbm_read_71mb": lambda seed, R: StreamRead(71307392, R),
-         "hbm_read_2gb": lambda seed, R: StreamRead(2 << 30, R)}
+         "hbm_read_2gb": lambda seed, R: StreamRead(2 << 30, R),
+         "gather_split_72": lambda seed, R: GatherRead(True, R, seed),
+         "gather_whole_32": lambda seed, R: GatherRead(False, R, seed)}
 
 
 # ----------------------------------------------------------------------------- timing
@@ -699,6 +746,8 @@ def _role(kernel, workload):
         return "append" if len(args) > 2 and args[2] == "true" else "compress"
     if kernel.startswith("stream_read_kernel"):
         return "stream_read"
+    if kernel.startswith("gather_read_kernel"):
+        return "gather_read"
     return None
 
 
@@ -934,7 +983,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="csa_decode_pro_1m")
-    ap.add_argument("--legs", default="hbm_read_71mb,hbm_read_2gb,hca_decode_1m,csa_prefill_chunk_1m,"
+    ap.add_argument("--legs", default="hbm_read_71mb,hbm_read_2gb,gather_split_72,gather_whole_32,hca_decode_1m,csa_prefill_chunk_1m,"
                     "csa_decode_flash_128k,hca_prefill_chunk_1m,tiny_prefill_f32,csa_compress_pro_1m,"
                     "csa_decode_pro_1m+state,hca_decode_1m+fp8kv,csa_decode_pro_1m+bf16sel,csa_prefill_chunk_1m+fp8k,"
                     "csa_prefill_chunk_1m+fp8q,csa_decode_pro_1m+fp8q",

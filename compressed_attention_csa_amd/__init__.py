@@ -62,6 +62,7 @@ SIGNATURES = {
     "hca_attend": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _vp, _vp, _i64, _i64,
                           _i32, _i64, _i32, _i32, _i64, _i32, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
     "csa_diag_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "csa_diag_gather_read": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp]),
     "csa_profile_enable": (_i32, [_i32]),
     "csa_profile_report": (_i32, [ctypes.c_char_p, _sz]),
 }
@@ -283,6 +284,15 @@ def diag_stream_read(buf, sink):
     """Plain streaming read of the device tensor ``buf`` (diagnostics: the HBM read ceiling)."""
     st = lib().csa_diag_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf))
     _check("csa_diag_stream_read", st)
+
+
+def diag_gather_read(k, v, idx, per_group, sink):
+    """Row gather of 256-byte rows of the device tensors ``k`` and ``v`` at the int32
+    indices ``idx`` (groups of ``per_group``; diagnostics: the gather rate)."""
+    n_rows = k.numel() * k.element_size() // 256
+    st = lib().csa_diag_gather_read(_ptr(k), _ptr(v), n_rows, _ptr(idx), idx.numel() // per_group, per_group,
+                                    _ptr(sink), _stream(k))
+    _check("csa_diag_gather_read", st)
 
 
 def profile_enable(on: bool = True) -> bool:

@@ -199,9 +199,10 @@ __device__ __forceinline__ bool decode_block(const AttendPlan& p, int64_t& hg, i
 // run three workgroups per CU), enough to cover memory latency in decode, where
 // a split is a few tiles long.  A CU gathers only about 50 GB/s of scattered
 // 256-byte rows however many loads it has in flight, so a decode row is split
-// over many workgroups (a workgroup gathering all 1152 slots of a Pro-like row
-// would take about 12 us for the gather alone, against 3.4 us for 72 workgroups
-// of 128 slots each), and the splits are merged afterwards.  Loads are issued unconditionally
+// over many workgroups (csa_diag_gather_read, the Pro-like step's 4 rows of 1152
+// slots: 32 workgroups, one per row and 16-head group, each gathering a whole
+// row take 12.7 us; 72 workgroups of 128 slots, the split plan, 4.0 us), and the
+// splits are merged afterwards.  Loads are issued unconditionally
 // (dead slots read the query row instead), so the compiler's wait counts stay
 // exact and no wait drains the prefetch.
 

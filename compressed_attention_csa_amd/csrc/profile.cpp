@@ -94,6 +94,42 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;  // keeps the loads; almost never taken
 }
 
+// Row gather (the decode attention's access pattern): workgroup g reads rows
+// idx[g * per_group + s] of k and v, 256 bytes each, 16 lanes per row, four
+// rows of each per 16 lanes in flight.  Indices are staged in LDS first, as
+// the attention stages its selection list, and clamped into [0, n_rows).
+constexpr int kGatherThreads = 512;
+constexpr int kGatherMaxPerGroup = 4096;
+__global__ __launch_bounds__(kGatherThreads) void gather_read_kernel(const uint4* __restrict__ k,
+                                                                     const uint4* __restrict__ v, int32_t n_rows,
+                                                                     const int32_t* __restrict__ idx, int per_group,
+                                                                     uint32_t* sink) {
+  __shared__ int32_t src[kGatherMaxPerGroup];
+  const int tid = threadIdx.x;
+  const int32_t* id = idx + int64_t(blockIdx.x) * per_group;
+  for (int s = tid; s < per_group; s += kGatherThreads) {
+    const int32_t j = id[s];
+    src[s] = j < 0 ? 0 : (j >= n_rows ? n_rows - 1 : j);
+  }
+  __syncthreads();
+  constexpr int kSlots = kGatherThreads / 16;  // rows per round of loads
+  uint32_t acc = 0;
+  for (int s0 = 0; s0 < per_group; s0 += 4 * kSlots) {
+    uint4 kv[4], vv[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      int s = s0 + d * kSlots + tid / 16;
+      s = s < per_group ? s : per_group - 1;
+      const int64_t j = src[s];
+      kv[d] = k[j * 16 + (tid & 15)];
+      vv[d] = v[j * 16 + (tid & 15)];
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) acc ^= kv[d].x ^ kv[d].w ^ vv[d].y ^ vv[d].z;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;  // keeps the loads; almost never taken
+}
+
 // Fills n16 16-byte words with all-ones (debug builds only).
 __global__ __launch_bounds__(256) void poison_kernel(uint4* p, size_t n16) {
   for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += size_t(gridDim.x) * 256)
@@ -153,6 +189,24 @@ csa_status_t csa_diag_stream_read(const void* buf, size_t bytes, uint32_t* sink,
   csa::ProfScope prof("stream_read", s);
   hipLaunchKernelGGL(stream_read_kernel, dim3(8192), dim3(256), 0, s, static_cast<const uint4*>(buf), bytes / 16,
                      sink);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? CSA_OK : csa::set_error(CSA_E_HIP, hipGetErrorString(e));
+}
+
+csa_status_t csa_diag_gather_read(const void* k, const void* v, int64_t n_rows, const int32_t* idx,
+                                  int64_t groups, int64_t per_group, uint32_t* sink, csa_stream_t stream) {
+  if (k == nullptr || v == nullptr || idx == nullptr || sink == nullptr)
+    return csa::set_error(CSA_E_NULL, "k / v / idx / sink is NULL");
+  if ((reinterpret_cast<uintptr_t>(k) & 15u) != 0 || (reinterpret_cast<uintptr_t>(v) & 15u) != 0)
+    return csa::set_error(CSA_E_ALIGN, "k and v must be 16-byte aligned");
+  if (groups < 1 || groups > 65536 || per_group < 1 || per_group > kGatherMaxPerGroup || n_rows < 1 ||
+      n_rows >= (int64_t(1) << 31))
+    return csa::set_error(CSA_E_SHAPE, "need 1 <= groups <= 65536, 1 <= per_group <= 4096, 1 <= n_rows < 2^31");
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  csa::ProfScope prof("gather_read", s);
+  hipLaunchKernelGGL(gather_read_kernel, dim3(unsigned(groups)), dim3(kGatherThreads), 0, s,
+                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), int32_t(n_rows), idx,
+                     int(per_group), sink);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? CSA_OK : csa::set_error(CSA_E_HIP, hipGetErrorString(e));
 }

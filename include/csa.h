@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 6
+#define CSA_ABI_VERSION 7
 
 typedef enum {
   CSA_F32 = 0,      /* IEEE binary32 */
@@ -356,6 +356,23 @@ int csa_profile_report(char* buf, size_t n);
  * when a checksum hits one fixed value, so that the loads are kept.
  */
 csa_status_t csa_diag_stream_read(const void* buf, size_t bytes, uint32_t* sink, csa_stream_t stream);
+
+/*
+ * Diagnostics: the rate at which workgroups gather scattered rows, the access
+ * pattern of the decode attention's selected entries (not part of the method;
+ * the benchmark quotes it for the choice between split and whole decode rows).
+ * `groups` workgroups of 512 threads; workgroup g reads, for each s <
+ * per_group, row idx[g * per_group + s] of `k` and of `v` (n_rows rows of 256
+ * bytes each: d = 128 in bf16; both 16-byte aligned, device), 16 lanes per
+ * row and four rows of each per 16 lanes in flight, and writes to `sink`
+ * ([groups] uint32, device) only when a checksum hits one fixed value, so that
+ * the loads are kept.  idx: [groups * per_group] int32 (device); an index
+ * outside [0, n_rows) is clamped into it, so no read leaves the buffers.
+ * Errors: CSA_E_NULL (a NULL pointer), CSA_E_ALIGN, CSA_E_SHAPE (groups not
+ * in [1, 65536], per_group not in [1, 4096], n_rows not in [1, 2^31)).
+ */
+csa_status_t csa_diag_gather_read(const void* k, const void* v, int64_t n_rows, const int32_t* idx,
+                                  int64_t groups, int64_t per_group, uint32_t* sink, csa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -38,11 +38,11 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
         assert n in csa.SIGNATURES, n
-    assert L.csa_abi_version() == 6
+    assert L.csa_abi_version() == 7
     for s, name in enumerate(csa.STATUS):
         assert L.csa_status_string(s).decode() == name
 
@@ -275,3 +275,14 @@ def test_binding_refuses_host_tensors():
     out = torch.zeros(1, 16, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device tensors"):
         csa.csa_compress(x, logits, 4, out, entry_end=16)
+
+
+def test_gather_diagnostic_validation(L):
+    """csa_diag_gather_read rejects bad arguments before any launch."""
+    def g(k=P, v=P, n_rows=1024, idx=P, groups=4, per=128, sink=P):
+        return L.csa_diag_gather_read(k, v, n_rows, idx, groups, per, sink, None)
+    assert g(k=None) == E_NULL and g(v=None) == E_NULL and g(idx=None) == E_NULL and g(sink=None) == E_NULL
+    assert g(k=MIS) == E_ALIGN and g(v=MIS) == E_ALIGN
+    assert g(groups=0) == E_SHAPE and g(groups=65537) == E_SHAPE
+    assert g(per=0) == E_SHAPE and g(per=4097) == E_SHAPE
+    assert g(n_rows=0) == E_SHAPE and g(n_rows=1 << 31) == E_SHAPE

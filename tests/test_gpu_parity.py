@@ -992,3 +992,17 @@ def test_tiny_prefill_f32_end_to_end():
                             f64(x["z_hca"]), wl.m_heavy, wl.W, wl.scale, wl.t0)
     np.testing.assert_array_equal(f64(hk[0]), href["k_cmp"]["values"])
     check_attention(f64(ho[0]), f64(hl[0]), href["o"], href["lse"], "f32", "hca e2e")
+
+
+def test_gather_diagnostic_runs_in_bounds():
+    """csa_diag_gather_read (the benchmark's gather-rate legs) on a small buffer with
+    indices outside [0, n_rows) (clamped) and a ragged last round: it returns OK and the
+    checksum sink is untouched (the buffers hold a constant, so it cannot hit the key)."""
+    n_rows, per, groups = 1000, 77, 5
+    k = torch.full((n_rows, 128), 1.0, dtype=torch.bfloat16, device=DEV)
+    v = torch.full((n_rows, 128), 2.0, dtype=torch.bfloat16, device=DEV)
+    idx = torch.randint(-50, n_rows + 50, (groups * per,), dtype=torch.int32, device=DEV)
+    sink = torch.full((groups,), 7, dtype=torch.int32, device=DEV)
+    csa.diag_gather_read(k, v, idx, per, sink)
+    torch.cuda.synchronize()
+    assert (sink == 7).all()
