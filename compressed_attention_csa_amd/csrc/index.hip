@@ -320,22 +320,49 @@ __device__ __forceinline__ void score_slice(const IndexArgs& a, const RowInfo& r
     if (tid < 16) s_q[16 * 64 + tid] = (tid < H_I) ? (a.w ? a.w[qrow + tid] : 1.0f) : 0.0f;
     __syncthreads();
     const float* kbase = reinterpret_cast<const float*>(a.k_idx) + (ri.b * a.N_alloc + ri.lo) * d_I;
-    for (int64_t e = tid; e < n; e += kThreads) {
-      const float4* kp = reinterpret_cast<const float4*>(kbase + e * d_I);
-      float score = 0.0f;
-      for (int h = 0; h < H_I; ++h) {
-        const float* qh = s_q + h * d_I;
-        float dot = 0.0f;
-        for (int v = 0; v < d_I / 4; ++v) {
-          const float4 x = kp[v];
-          dot = fmaf(qh[4 * v], x.x, dot);
-          dot = fmaf(qh[4 * v + 1], x.y, dot);
-          dot = fmaf(qh[4 * v + 2], x.z, dot);
-          dot = fmaf(qh[4 * v + 3], x.w, dot);
+    if (d_I == 32) {
+      // The key row is loaded once (8 x 16 bytes).  Each head's dot product
+      // runs four partial sums: one sequential chain of fused multiply-adds per
+      // entry and head made this loop latency-bound (0.18 -> 0.07 ms for 4096
+      // rows of up to 1024 entries, 4 heads x 32 dims).
+      for (int64_t e = tid; e < n; e += kThreads) {
+        const float4* kp = reinterpret_cast<const float4*>(kbase + e * 32);
+        float4 kr[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) kr[v] = kp[v];
+        float score = 0.0f;
+        for (int h = 0; h < H_I; ++h) {
+          const float* qh = s_q + h * 32;
+          float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            d0 = fmaf(qh[4 * v], kr[v].x, d0);
+            d1 = fmaf(qh[4 * v + 1], kr[v].y, d1);
+            d2 = fmaf(qh[4 * v + 2], kr[v].z, d2);
+            d3 = fmaf(qh[4 * v + 3], kr[v].w, d3);
+          }
+          score = fmaf(s_q[16 * 64 + h], relu_nan((d0 + d1) + (d2 + d3)), score);
         }
-        score = fmaf(s_q[16 * 64 + h], relu_nan(dot), score);
+        keys[e] = score_key(a.bf16_scores ? round_bf16(score) : score);
       }
-      keys[e] = score_key(a.bf16_scores ? round_bf16(score) : score);
+    } else {
+      for (int64_t e = tid; e < n; e += kThreads) {
+        const float4* kp = reinterpret_cast<const float4*>(kbase + e * d_I);
+        float score = 0.0f;
+        for (int h = 0; h < H_I; ++h) {
+          const float* qh = s_q + h * d_I;
+          float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
+          for (int v = 0; v < d_I / 4; ++v) {
+            const float4 x = kp[v];
+            d0 = fmaf(qh[4 * v], x.x, d0);
+            d1 = fmaf(qh[4 * v + 1], x.y, d1);
+            d2 = fmaf(qh[4 * v + 2], x.z, d2);
+            d3 = fmaf(qh[4 * v + 3], x.w, d3);
+          }
+          score = fmaf(s_q[16 * 64 + h], relu_nan((d0 + d1) + (d2 + d3)), score);
+        }
+        keys[e] = score_key(a.bf16_scores ? round_bf16(score) : score);
+      }
     }
     __syncthreads();
     return;
