@@ -26,11 +26,9 @@
 // combines them by log-sum-exp.  HCA over many consecutive query tokens uses
 // the multi-token kernel below instead (no splits).
 //
-// fp32 path: fp32 FMA with one slot per lane; a workgroup handles one row, one
-// group of up to 64 heads and one split.  The head groups of one (row, split)
-// get block ids that are equal modulo 8, which places them on the same XCD so
-// that the second group finds the rows in that XCD's L2, and the last split of
-// a (row, head group) to finish merges the partials (log-sum-exp).
+// fp32 path: fp32 FMA, scores with one slot per lane and outputs with one
+// column per lane; a workgroup handles one row (up to 32 heads) and one split,
+// and the last split of a row to finish merges the partials (log-sum-exp).
 #include <type_traits>
 
 #include "common.hpp"
@@ -1283,48 +1281,70 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, AttendP
 }
 
 // ---------------------------------------------------------------- fp32 kernel
+//
+// One workgroup = one (row, split) of at most 32 heads, four waves: wave w owns
+// heads w, w + 4, ... (HPW of them).  Tiles of 64 slots go through LDS, K as
+// rows (scores: lane = slot) and V transposed (O: lane = output column), while
+// the next tile's rows are already being loaded into registers.  Each K or V
+// value read from LDS serves every head of the wave, and each dot product runs
+// as two interleaved partial sums (one chain of dependent fused multiply-adds
+// per head made the loop latency-bound).
 
-template <int D>
-struct LdsF32 {
-  float k[kTileF32][D + 1];
-  float v[kTileF32][D];
-  float q[32][D];
-  float pr[32][kTileF32];
-  uint32_t flag[4];
-  MergeLds merge;
+template <int D, int HPW>
+struct TileF32 {
+  static constexpr int KS = D + 4;         // K row stride in floats: 16-byte reads of 16 lanes hit distinct banks
+  static constexpr int VS = kTileF32 + 4;  // V^T row stride in floats
+  alignas(16) float k[kTileF32][KS];  // 16-byte aligned rows: one 16-byte LDS access per float4
+  alignas(16) float vt[D][VS];
+  alignas(16) float q[4 * HPW][D];
+  alignas(16) float pr[4 * HPW][kTileF32];
+  uint32_t live[kTileF32];  // all ones for a live slot, 0 for a skipped one
 };
 
-template <int D>
+template <int D, int HPW>
+struct LdsF32 {
+  union U {
+    TileF32<D, HPW> t;
+    MergeLds merge;  // used once every wave is past the last tile (arrive_last synchronises first)
+  } u;
+  uint32_t flag[4];
+};
+
+template <int D, int HPW>
 __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, AttendPlan p) {
-  __shared__ LdsF32<D> L;
+  __shared__ LdsF32<D, HPW> L;
   debug_poison_lds(L);
   int64_t hg, r, s;
   if (!decode_block(p, hg, r, s)) return;
   const RowSlots x = row_slots(a, p, r, s);
   if (s >= x.S) return;
+  TileF32<D, HPW>& T = L.u.t;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int H = a.H;  // <= 32: one head group
-  constexpr int DPL = (D + 63) / 64;  // output columns per lane
+  const int H = a.H;  // <= 4 * HPW
+  constexpr int DPL = (D + 63) / 64;               // output columns per lane
+  constexpr int CPR = D / 4;                       // float4 chunks per row
+  constexpr int NCH = kTileF32 * CPR / kThreads;   // chunks per thread per tensor per tile
+  static_assert(NCH >= 1 && NCH * kThreads == kTileF32 * CPR, "whole chunks per thread");
   const float* qrow = reinterpret_cast<const float*>(a.q) + r * int64_t(H) * D;
-  for (int i = tid; i < H * D; i += kThreads) L.q[i / D][i % D] = qrow[i];
+  for (int i = tid; i < H * D; i += kThreads) T.q[i / D][i % D] = qrow[i];
   const float sl2 = a.scale * kLog2e;
   const float* kc = reinterpret_cast<const float*>(a.k_cmp);
   const float* vc = reinterpret_cast<const float*>(a.v_cmp);
   const float* kr = reinterpret_cast<const float*>(a.k_raw);
   const float* vr = reinterpret_cast<const float*>(a.v_raw);
-  float o[8][DPL];
-  float mrun[8], lpart[8];
+
+  // Chunk i of a tile: a wave covers 16 slots x 4 chunks, so that the
+  // transposing V writes of a wave hit 64 distinct banks.
+  auto slot_of = [](int i) { return (i & 15) + 16 * ((i >> 4) / CPR); };
+  auto chunk_of = [](int i) { return (i >> 4) % CPR; };
+  // Rows of one tile in flight; a skipped slot or one past the split holds zeros.
+  float4 pk[NCH], pv[NCH];
+  uint32_t plive = 0;
+  auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
+    plive = 0;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    mrun[u] = -INFINITY;
-    lpart[u] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < DPL; ++c) o[u][c] = 0.0f;
-  }
-  for (int64_t t0 = x.lo; t0 < x.hi; t0 += kTileF32) {
-    __syncthreads();
-    for (int i = tid; i < kTileF32 * (D / 4); i += kThreads) {
-      const int sl = i / (D / 4), ch = i % (D / 4);
+    for (int c = 0; c < NCH; ++c) {
+      const int i = tid + c * kThreads, sl = slot_of(i), ch = chunk_of(i);
       const int64_t slot = t0 + sl;
       float4 kv = make_float4(0, 0, 0, 0), vv = make_float4(0, 0, 0, 0);
       if (slot < x.hi) {
@@ -1333,55 +1353,128 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
         if (off >= 0) {
           kv = *reinterpret_cast<const float4*>((cmp ? kc : kr) + off + ch * 4);
           vv = *reinterpret_cast<const float4*>((cmp ? vc : vr) + off + ch * 4);
+          plive |= 1u << c;
         }
       }
-      L.k[sl][ch * 4] = kv.x; L.k[sl][ch * 4 + 1] = kv.y; L.k[sl][ch * 4 + 2] = kv.z; L.k[sl][ch * 4 + 3] = kv.w;
-      *reinterpret_cast<float4*>(&L.v[sl][ch * 4]) = vv;
+      pk[c] = kv;
+      pv[c] = vv;
     }
-    __syncthreads();
-    const int64_t slot = t0 + lane;
-    bool cmp;
-    const bool live = slot < x.hi && slot_offset(a, x, slot, cmp) >= 0;
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int c = 0; c < NCH; ++c) {
+      const int i = tid + c * kThreads, sl = slot_of(i), ch = chunk_of(i);
+      *reinterpret_cast<float4*>(&T.k[sl][ch * 4]) = pk[c];
+      T.vt[ch * 4][sl] = pv[c].x;
+      T.vt[ch * 4 + 1][sl] = pv[c].y;
+      T.vt[ch * 4 + 2][sl] = pv[c].z;
+      T.vt[ch * 4 + 3][sl] = pv[c].w;
+      if (ch == 0) T.live[sl] = ((plive >> c) & 1u) ? 0xffffffffu : 0u;
+    }
+  };
+
+  float o[HPW][DPL];
+  float mrun[HPW], lpart[HPW];
+#pragma unroll
+  for (int u = 0; u < HPW; ++u) {
+    mrun[u] = -INFINITY;
+    lpart[u] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) o[u][c] = 0.0f;
+  }
+  fetch(x.lo);
+  for (int64_t t0 = x.lo; t0 < x.hi; t0 += kTileF32) {
+    __syncthreads();  // every wave is done with the previous tile
+    stage();
+    __syncthreads();
+    if (t0 + kTileF32 < x.hi) fetch(t0 + kTileF32);
+    // Scores of slot `lane` for the wave's heads.
+    const bool live = T.live[lane] != 0u;
+    float d0[HPW], d1[HPW];
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) d0[u] = d1[u] = 0.0f;
+#pragma unroll
+    for (int dd = 0; dd < D; dd += 8) {
+      const float4 k0 = *reinterpret_cast<const float4*>(&T.k[lane][dd]);
+      const float4 k1 = *reinterpret_cast<const float4*>(&T.k[lane][dd + 4]);
+#pragma unroll
+      for (int u = 0; u < HPW; ++u) {
+        const int h = wid + 4 * u;
+        if (h < H) {
+          const float4 q0 = *reinterpret_cast<const float4*>(&T.q[h][dd]);
+          const float4 q1 = *reinterpret_cast<const float4*>(&T.q[h][dd + 4]);
+          d0[u] = fmaf(q0.x, k0.x, d0[u]); d1[u] = fmaf(q1.x, k1.x, d1[u]);
+          d0[u] = fmaf(q0.y, k0.y, d0[u]); d1[u] = fmaf(q1.y, k1.y, d1[u]);
+          d0[u] = fmaf(q0.z, k0.z, d0[u]); d1[u] = fmaf(q1.z, k1.z, d1[u]);
+          d0[u] = fmaf(q0.w, k0.w, d0[u]); d1[u] = fmaf(q1.w, k1.w, d1[u]);
+        }
+      }
+    }
+    // Online softmax per head (log2 units); the weights go to LDS for O.
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
       const int h = wid + 4 * u;
       if (h < H) {
-        float dot = 0.0f;
-        for (int dd = 0; dd < D; ++dd) dot = fmaf(L.q[h][dd], L.k[lane][dd], dot);
-        const float sv = live ? dot * sl2 : -INFINITY;
-        const float mnew = fmaxf(mrun[u], wave_max(sv));
+        const float sv = live ? (d0[u] + d1[u]) * sl2 : -INFINITY;
+        const float mnew = fmaxf(mrun[u], wave_max_dpp(sv));
         const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun[u] - mnew);
-        const float pv = (mnew == -INFINITY) ? 0.0f : exp2f(sv - mnew);
+        const float pw = (mnew == -INFINITY) ? 0.0f : exp2f(sv - mnew);
         mrun[u] = mnew;
-        lpart[u] = lpart[u] * corr + pv;
-        L.pr[h][lane] = pv;
+        lpart[u] = lpart[u] * corr + pw;
+        T.pr[h][lane] = pw;
 #pragma unroll
         for (int c = 0; c < DPL; ++c) o[u][c] *= corr;
       }
     }
-    __syncthreads();
+    // O += P V for output column lane + 64 c (the weights were written by this
+    // same wave, whose LDS accesses complete in order).
+    float oa[HPW][DPL], ob[HPW][DPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int h = wid + 4 * u;
-      if (h < H) {
+    for (int u = 0; u < HPW; ++u)
 #pragma unroll
-        for (int c = 0; c < DPL; ++c) {
-          const int dv = lane + 64 * c;
-          if (dv < D) {
-            float acc = o[u][c];
-            for (int e = 0; e < kTileF32; ++e) acc = fmaf(L.pr[h][e], L.v[e][dv], acc);
-            o[u][c] = acc;
+      for (int c = 0; c < DPL; ++c) {
+        oa[u][c] = o[u][c];
+        ob[u][c] = 0.0f;
+      }
+#pragma unroll 2
+    for (int e = 0; e < kTileF32; e += 8) {
+      float4 v0[DPL], v1[DPL];
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) {
+        const int dv = lane + 64 * c;
+        v0[c] = v1[c] = make_float4(0, 0, 0, 0);
+        if (dv < D) {
+          v0[c] = *reinterpret_cast<const float4*>(&T.vt[dv][e]);
+          v1[c] = *reinterpret_cast<const float4*>(&T.vt[dv][e + 4]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < HPW; ++u) {
+        const int h = wid + 4 * u;
+        if (h < H) {
+          const float4 p0 = *reinterpret_cast<const float4*>(&T.pr[h][e]);
+          const float4 p1 = *reinterpret_cast<const float4*>(&T.pr[h][e + 4]);
+#pragma unroll
+          for (int c = 0; c < DPL; ++c) {
+            oa[u][c] = fmaf(p0.x, v0[c].x, oa[u][c]); ob[u][c] = fmaf(p1.x, v1[c].x, ob[u][c]);
+            oa[u][c] = fmaf(p0.y, v0[c].y, oa[u][c]); ob[u][c] = fmaf(p1.y, v1[c].y, ob[u][c]);
+            oa[u][c] = fmaf(p0.z, v0[c].z, oa[u][c]); ob[u][c] = fmaf(p1.z, v1[c].z, ob[u][c]);
+            oa[u][c] = fmaf(p0.w, v0[c].w, oa[u][c]); ob[u][c] = fmaf(p1.w, v1[c].w, ob[u][c]);
           }
         }
       }
     }
-  }
-  float lt[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) lt[u] = wave_sum(lpart[u]);
+    for (int u = 0; u < HPW; ++u)
+#pragma unroll
+      for (int c = 0; c < DPL; ++c) o[u][c] = oa[u][c] + ob[u][c];
+  }
+  float lt[HPW];
+#pragma unroll
+  for (int u = 0; u < HPW; ++u) lt[u] = wave_sum(lpart[u]);
   if (x.S == 1) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < HPW; ++u) {
       const int h = wid + 4 * u;
       if (h < H) {
         const float inv = lt[u] > 0.0f ? 1.0f / lt[u] : 0.0f;
@@ -1405,7 +1498,7 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
   float* part = reinterpret_cast<float*>(ws + p.off_part) + (unit * p.splits + s) * int64_t(H) * D;
   float* ml = reinterpret_cast<float*>(ws + p.off_ml) + (unit * p.splits + s) * int64_t(H) * 2;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < HPW; ++u) {
     const int h = wid + 4 * u;
     if (h < H) {
 #pragma unroll
@@ -1419,7 +1512,7 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
       }
     }
   }
-  finish_split(a, p, x, unit, 0, H, H, L.flag, L.merge);
+  finish_split(a, p, x, unit, 0, H, H, L.flag, L.u.merge);
 }
 
 }  // namespace
@@ -1524,6 +1617,15 @@ static void launch_bf16(const AttendArgs& a, const AttendPlan& p) {
   }
 }
 
+// fp32: heads per wave from the head count (at most 32 heads, four waves).
+template <int D>
+static void launch_f32(const AttendArgs& a, const AttendPlan& p, dim3 grid, dim3 block) {
+  if (a.H <= 4) hipLaunchKernelGGL((attend_f32_kernel<D, 1>), grid, block, 0, a.stream, a, p);
+  else if (a.H <= 8) hipLaunchKernelGGL((attend_f32_kernel<D, 2>), grid, block, 0, a.stream, a, p);
+  else if (a.H <= 16) hipLaunchKernelGGL((attend_f32_kernel<D, 4>), grid, block, 0, a.stream, a, p);
+  else hipLaunchKernelGGL((attend_f32_kernel<D, 8>), grid, block, 0, a.stream, a, p);
+}
+
 // HCA prefill: QT = RB * NW / (H / 16) consecutive tokens per workgroup.
 template <int D, int NW, int RB>
 static bool launch_hca_multi(const AttendArgs& a) {
@@ -1571,9 +1673,9 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p) {
   } else {
     ProfScope prof(a.hca ? "hca_attend" : "csa_attend", a.stream);
     dim3 grid(unsigned(p.groups * p.group_stride)), block(kThreads);
-    if (a.d == 128) hipLaunchKernelGGL(attend_f32_kernel<128>, grid, block, 0, a.stream, a, p);
-    else if (a.d == 64) hipLaunchKernelGGL(attend_f32_kernel<64>, grid, block, 0, a.stream, a, p);
-    else hipLaunchKernelGGL(attend_f32_kernel<32>, grid, block, 0, a.stream, a, p);
+    if (a.d == 128) launch_f32<128>(a, p, grid, block);
+    else if (a.d == 64) launch_f32<64>(a, p, grid, block);
+    else launch_f32<32>(a, p, grid, block);
   }
   return hipGetLastError();
 }

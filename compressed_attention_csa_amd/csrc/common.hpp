@@ -319,6 +319,22 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
+// wave_max by DPP row shifts and row broadcasts (no LDS traffic): a lane with
+// no source keeps its own value, so the result follows fmaxf over the 64
+// values (NaN only if all are NaN), broadcast from lane 63.
+__device__ __forceinline__ float dpp_max_step(float v, int moved) { return fmaxf(v, __builtin_bit_cast(float, moved)); }
+__device__ __forceinline__ float wave_max_dpp(float v) {
+#define CSA_DPP_MAX(ctrl, rows) \
+  v = dpp_max_step(v, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v), ctrl, rows, 0xf, false))
+  CSA_DPP_MAX(0x111, 0xf);  // row_shr:1
+  CSA_DPP_MAX(0x112, 0xf);  // row_shr:2
+  CSA_DPP_MAX(0x114, 0xf);  // row_shr:4
+  CSA_DPP_MAX(0x118, 0xf);  // row_shr:8
+  CSA_DPP_MAX(0x142, 0xa);  // row_bcast:15
+  CSA_DPP_MAX(0x143, 0xc);  // row_bcast:31
+#undef CSA_DPP_MAX
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);

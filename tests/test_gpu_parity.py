@@ -550,6 +550,9 @@ ATTEND_CASES = [
     ("csa-f32", "f32", 1, 50, 8, 64, 1024, 4, 64, 128, 3000, "f32"),
     ("csa-f32-d32", "f32", 2, 9, 3, 32, 200, 4, 100, 7, 700, "f32"),
     ("csa-f32-decode", "f32", 2, 1, 8, 128, 3000, 4, 1024, 128, 4 * 3000 - 1, "f32"),
+    ("csa-f32-h32", "f32", 1, 20, 32, 64, 300, 4, 64, 128, 1200, "f32"),     # 8 heads per wave
+    ("hca-f32-h13-decode", "f32", 2, 1, 13, 128, 400, 128, 0, 128, 128 * 400 - 1, "f32"),  # split, merged
+    ("csa-f32-h2-d32", "f32", 1, 70, 2, 32, 90, 4, 16, 5, 300, "f32"),
     ("csa-decode-h80", "bf16", 3, 1, 80, 128, 3000, 4, 1024, 128, 4 * 3000 - 1, "f32"),
     ("hca-decode", "bf16", 2, 1, 128, 128, 2000, 128, 0, 128, 128 * 2000 - 1, "f32"),
     ("hca-decode-b16", "bf16", 16, 1, 128, 128, 700, 128, 0, 128, 128 * 700 - 1, "f32"),
