@@ -1324,7 +1324,7 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
   constexpr int DPL = (D + 63) / 64;               // output columns per lane
   constexpr int CPR = D / 4;                       // float4 chunks per row
   constexpr int NCH = kTileF32 * CPR / kThreads;   // chunks per thread per tensor per tile
-  static_assert(NCH >= 1 && NCH * kThreads == kTileF32 * CPR, "whole chunks per thread");
+  static_assert(NCH >= 1 && NCH * kThreads == kTileF32 * CPR && kTileF32 == 64, "a lane per slot, whole chunks per wave");
   const float* qrow = reinterpret_cast<const float*>(a.q) + r * int64_t(H) * D;
   for (int i = tid; i < H * D; i += kThreads) T.q[i / D][i % D] = qrow[i];
   const float sl2 = a.scale * kLog2e;
@@ -1333,44 +1333,37 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
   const float* kr = reinterpret_cast<const float*>(a.k_raw);
   const float* vr = reinterpret_cast<const float*>(a.v_raw);
 
-  // Chunk i of a tile: a wave covers 16 slots x 4 chunks, so that the
-  // transposing V writes of a wave hit 64 distinct banks.
-  auto slot_of = [](int i) { return (i & 15) + 16 * ((i >> 4) / CPR); };
-  auto chunk_of = [](int i) { return (i >> 4) % CPR; };
-  // Rows of one tile in flight; a skipped slot or one past the split holds zeros.
+  // Tile rows in flight: lane l of every wave loads slot t0 + l, wave w its
+  // chunks w * NCH .. w * NCH + NCH - 1 (so a thread finds one source row per
+  // tile, and the transposing V writes of a wave hit 64 distinct banks).  A
+  // skipped slot or one past the split holds zeros.
   float4 pk[NCH], pv[NCH];
-  uint32_t plive = 0;
+  bool plive = false;
   auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
-    plive = 0;
+    const int64_t slot = t0 + lane;
+    int64_t off = -1;
+    bool cmp = false;
+    if (slot < x.hi) off = slot_offset(a, x, slot, cmp);
+    plive = off >= 0;
+    const float* kp = (cmp ? kc : kr) + (plive ? off : 0) + wid * NCH * 4;
+    const float* vp = (cmp ? vc : vr) + (plive ? off : 0) + wid * NCH * 4;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int i = tid + c * kThreads, sl = slot_of(i), ch = chunk_of(i);
-      const int64_t slot = t0 + sl;
-      float4 kv = make_float4(0, 0, 0, 0), vv = make_float4(0, 0, 0, 0);
-      if (slot < x.hi) {
-        bool cmp;
-        const int64_t off = slot_offset(a, x, slot, cmp);
-        if (off >= 0) {
-          kv = *reinterpret_cast<const float4*>((cmp ? kc : kr) + off + ch * 4);
-          vv = *reinterpret_cast<const float4*>((cmp ? vc : vr) + off + ch * 4);
-          plive |= 1u << c;
-        }
-      }
-      pk[c] = kv;
-      pv[c] = vv;
+      pk[c] = plive ? *reinterpret_cast<const float4*>(kp + c * 4) : make_float4(0, 0, 0, 0);
+      pv[c] = plive ? *reinterpret_cast<const float4*>(vp + c * 4) : make_float4(0, 0, 0, 0);
     }
   };
   auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int i = tid + c * kThreads, sl = slot_of(i), ch = chunk_of(i);
-      *reinterpret_cast<float4*>(&T.k[sl][ch * 4]) = pk[c];
-      T.vt[ch * 4][sl] = pv[c].x;
-      T.vt[ch * 4 + 1][sl] = pv[c].y;
-      T.vt[ch * 4 + 2][sl] = pv[c].z;
-      T.vt[ch * 4 + 3][sl] = pv[c].w;
-      if (ch == 0) T.live[sl] = ((plive >> c) & 1u) ? 0xffffffffu : 0u;
+      const int ch = wid * NCH + c;
+      *reinterpret_cast<float4*>(&T.k[lane][ch * 4]) = pk[c];
+      T.vt[ch * 4][lane] = pv[c].x;
+      T.vt[ch * 4 + 1][lane] = pv[c].y;
+      T.vt[ch * 4 + 2][lane] = pv[c].z;
+      T.vt[ch * 4 + 3][lane] = pv[c].w;
     }
+    if (wid == 0) T.live[lane] = plive ? 0xffffffffu : 0u;
   };
 
   float o[HPW][DPL];
