@@ -826,6 +826,10 @@ IndexPlan plan_index(int B, int64_t T, int H_I, int d_I, int64_t N_alloc, int to
   int64_t slice = ((want + 255) / 256) * 256;
   if (slice < 256) slice = 256;
   if (slice > kMaxSlice) slice = kMaxSlice;
+  // No longer than the longest row needs: the registers per thread follow the
+  // slice, and keys past the row's end are dead weight in every selection pass.
+  const int64_t c_round = ((p.c_max + 255) / 256) * 256;
+  if (slice > c_round && c_round >= 256) slice = c_round;
   p.slice = slice;
   p.slices = (p.c_max + slice - 1) / slice;
   if (p.slices < 1) p.slices = 1;
