@@ -1326,7 +1326,9 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
   constexpr int NCH = kTileF32 * CPR / kThreads;   // chunks per thread per tensor per tile
   static_assert(NCH >= 1 && NCH * kThreads == kTileF32 * CPR && kTileF32 == 64, "a lane per slot, whole chunks per wave");
   const float* qrow = reinterpret_cast<const float*>(a.q) + r * int64_t(H) * D;
-  for (int i = tid; i < H * D; i += kThreads) T.q[i / D][i % D] = qrow[i];
+  // Query rows of the heads; the rows past H are zeros, so that the loops below
+  // run every head slot of a wave without a branch (their results are dropped).
+  for (int i = tid; i < 4 * HPW * D; i += kThreads) T.q[i / D][i % D] = i < H * D ? qrow[i] : 0.0f;
   const float sl2 = a.scale * kLog2e;
   const float* kc = reinterpret_cast<const float*>(a.k_cmp);
   const float* vc = reinterpret_cast<const float*>(a.v_cmp);
@@ -1393,31 +1395,27 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
 #pragma unroll
       for (int u = 0; u < HPW; ++u) {
         const int h = wid + 4 * u;
-        if (h < H) {
-          const float4 q0 = *reinterpret_cast<const float4*>(&T.q[h][dd]);
-          const float4 q1 = *reinterpret_cast<const float4*>(&T.q[h][dd + 4]);
-          d0[u] = fmaf(q0.x, k0.x, d0[u]); d1[u] = fmaf(q1.x, k1.x, d1[u]);
-          d0[u] = fmaf(q0.y, k0.y, d0[u]); d1[u] = fmaf(q1.y, k1.y, d1[u]);
-          d0[u] = fmaf(q0.z, k0.z, d0[u]); d1[u] = fmaf(q1.z, k1.z, d1[u]);
-          d0[u] = fmaf(q0.w, k0.w, d0[u]); d1[u] = fmaf(q1.w, k1.w, d1[u]);
-        }
+        const float4 q0 = *reinterpret_cast<const float4*>(&T.q[h][dd]);
+        const float4 q1 = *reinterpret_cast<const float4*>(&T.q[h][dd + 4]);
+        d0[u] = fmaf(q0.x, k0.x, d0[u]); d1[u] = fmaf(q1.x, k1.x, d1[u]);
+        d0[u] = fmaf(q0.y, k0.y, d0[u]); d1[u] = fmaf(q1.y, k1.y, d1[u]);
+        d0[u] = fmaf(q0.z, k0.z, d0[u]); d1[u] = fmaf(q1.z, k1.z, d1[u]);
+        d0[u] = fmaf(q0.w, k0.w, d0[u]); d1[u] = fmaf(q1.w, k1.w, d1[u]);
       }
     }
     // Online softmax per head (log2 units); the weights go to LDS for O.
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
       const int h = wid + 4 * u;
-      if (h < H) {
-        const float sv = live ? (d0[u] + d1[u]) * sl2 : -INFINITY;
-        const float mnew = fmaxf(mrun[u], wave_max_dpp(sv));
-        const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun[u] - mnew);
-        const float pw = (mnew == -INFINITY) ? 0.0f : exp2f(sv - mnew);
-        mrun[u] = mnew;
-        lpart[u] = lpart[u] * corr + pw;
-        T.pr[h][lane] = pw;
+      const float sv = live ? (d0[u] + d1[u]) * sl2 : -INFINITY;
+      const float mnew = fmaxf(mrun[u], wave_max_dpp(sv));
+      const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun[u] - mnew);
+      const float pw = (mnew == -INFINITY) ? 0.0f : exp2f(sv - mnew);
+      mrun[u] = mnew;
+      lpart[u] = lpart[u] * corr + pw;
+      T.pr[h][lane] = pw;
 #pragma unroll
-        for (int c = 0; c < DPL; ++c) o[u][c] *= corr;
-      }
+      for (int c = 0; c < DPL; ++c) o[u][c] *= corr;
     }
     // O += P V for output column lane + 64 c (the weights were written by this
     // same wave, whose LDS accesses complete in order).
@@ -1444,16 +1442,14 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
 #pragma unroll
       for (int u = 0; u < HPW; ++u) {
         const int h = wid + 4 * u;
-        if (h < H) {
-          const float4 p0 = *reinterpret_cast<const float4*>(&T.pr[h][e]);
-          const float4 p1 = *reinterpret_cast<const float4*>(&T.pr[h][e + 4]);
+        const float4 p0 = *reinterpret_cast<const float4*>(&T.pr[h][e]);
+        const float4 p1 = *reinterpret_cast<const float4*>(&T.pr[h][e + 4]);
 #pragma unroll
-          for (int c = 0; c < DPL; ++c) {
-            oa[u][c] = fmaf(p0.x, v0[c].x, oa[u][c]); ob[u][c] = fmaf(p1.x, v1[c].x, ob[u][c]);
-            oa[u][c] = fmaf(p0.y, v0[c].y, oa[u][c]); ob[u][c] = fmaf(p1.y, v1[c].y, ob[u][c]);
-            oa[u][c] = fmaf(p0.z, v0[c].z, oa[u][c]); ob[u][c] = fmaf(p1.z, v1[c].z, ob[u][c]);
-            oa[u][c] = fmaf(p0.w, v0[c].w, oa[u][c]); ob[u][c] = fmaf(p1.w, v1[c].w, ob[u][c]);
-          }
+        for (int c = 0; c < DPL; ++c) {
+          oa[u][c] = fmaf(p0.x, v0[c].x, oa[u][c]); ob[u][c] = fmaf(p1.x, v1[c].x, ob[u][c]);
+          oa[u][c] = fmaf(p0.y, v0[c].y, oa[u][c]); ob[u][c] = fmaf(p1.y, v1[c].y, ob[u][c]);
+          oa[u][c] = fmaf(p0.z, v0[c].z, oa[u][c]); ob[u][c] = fmaf(p1.z, v1[c].z, ob[u][c]);
+          oa[u][c] = fmaf(p0.w, v0[c].w, oa[u][c]); ob[u][c] = fmaf(p1.w, v1[c].w, ob[u][c]);
         }
       }
     }
