@@ -1347,23 +1347,27 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
     bool cmp = false;
     if (slot < x.hi) off = slot_offset(a, x, slot, cmp);
     plive = off >= 0;
-    const float* kp = (cmp ? kc : kr) + (plive ? off : 0) + wid * NCH * 4;
-    const float* vp = (cmp ? vc : vr) + (plive ? off : 0) + wid * NCH * 4;
+    // A dead slot reads the query row instead (at least D floats), so that every
+    // load is issued unconditionally; its values are replaced by zeros when staged.
+    const float* kp = (plive ? (cmp ? kc : kr) + off : qrow) + wid * NCH * 4;
+    const float* vp = (plive ? (cmp ? vc : vr) + off : qrow) + wid * NCH * 4;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      pk[c] = plive ? *reinterpret_cast<const float4*>(kp + c * 4) : make_float4(0, 0, 0, 0);
-      pv[c] = plive ? *reinterpret_cast<const float4*>(vp + c * 4) : make_float4(0, 0, 0, 0);
+      pk[c] = *reinterpret_cast<const float4*>(kp + c * 4);
+      pv[c] = *reinterpret_cast<const float4*>(vp + c * 4);
     }
   };
   auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = wid * NCH + c;
-      *reinterpret_cast<float4*>(&T.k[lane][ch * 4]) = pk[c];
-      T.vt[ch * 4][lane] = pv[c].x;
-      T.vt[ch * 4 + 1][lane] = pv[c].y;
-      T.vt[ch * 4 + 2][lane] = pv[c].z;
-      T.vt[ch * 4 + 3][lane] = pv[c].w;
+      const float4 z = make_float4(0, 0, 0, 0);
+      const float4 kw = plive ? pk[c] : z, vw = plive ? pv[c] : z;
+      *reinterpret_cast<float4*>(&T.k[lane][ch * 4]) = kw;
+      T.vt[ch * 4][lane] = vw.x;
+      T.vt[ch * 4 + 1][lane] = vw.y;
+      T.vt[ch * 4 + 2][lane] = vw.z;
+      T.vt[ch * 4 + 3][lane] = vw.w;
     }
     if (wid == 0) T.live[lane] = plive ? 0xffffffffu : 0u;
   };
