@@ -79,7 +79,8 @@ def test_index_topk_prefill_sampled_threshold_falls_back():
 
 
 ATTEND = [c for c in P.ATTEND_CASES if c[0] in (
-    "csa-decode", "csa-prefill", "csa-empty-rows", "csa-f32", "csa-f32-decode", "hca-decode-b16",
+    "csa-decode", "csa-prefill", "csa-empty-rows", "csa-f32", "csa-f32-decode", "hca-f32-h13-decode",
+    "csa-f32-h2-d32", "hca-decode-b16",
     "hca-prefill", "hca-prefill-multi", "hca-prefill-multi-h128-d64", "csa-max-k-window")]
 
 
