@@ -1287,8 +1287,9 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, AttendP
 // rows (scores: lane = slot) and V transposed (O: lane = output column), while
 // the next tile's rows are already being loaded into registers.  Each K or V
 // value read from LDS serves every head of the wave, and each dot product runs
-// as two interleaved partial sums (one chain of dependent fused multiply-adds
-// per head made the loop latency-bound).
+// as two interleaved partial sums.  LDS traffic and vector instructions bound
+// it (16-byte accesses throughout; the tile arrays are 16-byte aligned, which
+// the compiler needs in order to emit them).
 
 template <int D, int HPW>
 struct TileF32 {
