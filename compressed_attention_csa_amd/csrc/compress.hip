@@ -45,6 +45,35 @@ struct Row8<bf16_t> {
   }
 };
 
+// The 16 or 32 bytes of 8 consecutive elements, loaded ahead of their use.
+template <typename TIn>
+struct Raw8;
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void to_double(double (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+template <>
+struct Raw8<bf16_t> {
+  uint4 a;
+  __device__ __forceinline__ void load(const bf16_t* p) { a = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void to_double(double (&v)[8]) const {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = u32_as_f32(w[i] << 16);
+      v[2 * i + 1] = u32_as_f32(w[i] & 0xffff0000u);
+    }
+  }
+};
+
 // The new rows of an append (state-cache ring, see csa_append): workgroups
 // past the compression ones copy them into both ring rows of their position,
 // and the compression reads positions >= t0 from them instead of the ring, so
@@ -99,8 +128,39 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     return;
   }
 
-  // Slot weights: softmax of the logits, in fp64.
   const int ms = m + o;  // slots per entry
+  const int tpe = d >> 3;  // threads per entry and slot group, 8 columns each
+  const int P = SPLIT ? slot_parts(ms, tpe) : 1;
+  const int sper = (ms + P - 1) / P;  // slots per group
+  const int epb = kThreads / (tpe * P);
+  const int part = (tid / tpe) % P;
+  const int64_t e_local = int64_t(blockIdx.x) * epb + tid / (tpe * P);
+  const int seg = tid % tpe;
+  const bool valid = tid < epb * tpe * P && e_local < n_ent;
+  const int64_t j = entry_begin + e_local;
+  const int64_t p0 = j * m - o;  // position of slot 0
+  const TIn* xb = x + int64_t(b) * n_raw * d + seg * 8;
+  const int s_begin = part * sper;
+  const int s_end = (part + 1) * sper < ms ? (part + 1) * sper : ms;
+  auto row_of = [&](int s) __attribute__((always_inline)) {
+    const int64_t pos = p0 + s;
+    if (APPEND && pos >= at.t0) return xn + (pos - at.t0) * d + seg * 8;
+    return xb + (pos - raw_base) * d;
+  };
+  // The group's first kAhead rows are loaded before the weights are formed, so
+  // that their latency overlaps the softmax (a decode step's append is one
+  // chain of such latencies).
+  constexpr int kAhead = sizeof(TIn) == 4 ? 4 : 8;  // fp32 rows take twice the registers
+  Raw8<TIn> ahead[kAhead];
+  if (valid) {
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int s = s_begin + u;
+      if (s < s_end && p0 + s >= 0) ahead[u].load(row_of(s));
+    }
+  }
+
+  // Slot weights: softmax of the logits, in fp64.
   if (tid < kWave) {
     float v = -INFINITY;
     for (int s = tid; s < ms; s += kWave) v = fmaxf(v, logits[s]);
@@ -116,31 +176,27 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   for (int s = tid; s < ms; s += kThreads) alpha[s] = alpha[s] / total;
   __syncthreads();
 
-  const int tpe = d >> 3;  // threads per entry and slot group, 8 columns each
-  const int P = SPLIT ? slot_parts(ms, tpe) : 1;
-  const int sper = (ms + P - 1) / P;  // slots per group
-  const int epb = kThreads / (tpe * P);
-  const int part = (tid / tpe) % P;
-  const int64_t e_local = int64_t(blockIdx.x) * epb + tid / (tpe * P);
-  const int seg = tid % tpe;
-  const bool valid = tid < epb * tpe * P && e_local < n_ent;
-  const int64_t j = entry_begin + e_local;
-  const int64_t p0 = j * m - o;  // position of slot 0
-
   double acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0;
   if (valid) {
-    const TIn* xb = x + int64_t(b) * n_raw * d + seg * 8;
-    const int s_end = (part + 1) * sper < ms ? (part + 1) * sper : ms;
+    // Slot order throughout: the rows loaded ahead, then the rest.
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int s = s_begin + u;
+      if (s < s_end && p0 + s >= 0) {
+        double v[8];
+        ahead[u].to_double(v);
+        const double a = alpha[s];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fma(a, v[i], acc[i]);
+      }
+    }
 #pragma unroll 8
-    for (int s = part * sper; s < s_end; ++s) {
-      const int64_t pos = p0 + s;
-      if (pos < 0) continue;
+    for (int s = s_begin + kAhead; s < s_end; ++s) {
+      if (p0 + s < 0) continue;
       double v[8];
-      const TIn* rp = xb + (pos - raw_base) * d;
-      if (APPEND && pos >= at.t0) rp = xn + (pos - at.t0) * d + seg * 8;
-      Row8<TIn>::load(rp, v);
+      Row8<TIn>::load(row_of(s), v);
       const double a = alpha[s];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fma(a, v[i], acc[i]);
