@@ -1414,8 +1414,10 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a, Atte
       const int h = wid + 4 * u;
       const float sv = live ? (d0[u] + d1[u]) * sl2 : -INFINITY;
       const float mnew = fmaxf(mrun[u], wave_max_dpp(sv));
-      const float corr = (mnew == -INFINITY) ? 1.0f : exp2f(mrun[u] - mnew);
-      const float pw = (mnew == -INFINITY) ? 0.0f : exp2f(sv - mnew);
+      // Hardware 2^x: results below the normal range flush to 0, far below what
+      // can matter next to the row maximum's weight of 1.
+      const float corr = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mrun[u] - mnew);
+      const float pw = (mnew == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sv - mnew);
       mrun[u] = mnew;
       lpart[u] = lpart[u] * corr + pw;
       T.pr[h][lane] = pw;
